@@ -1,0 +1,305 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the BF16x9 emulated FP32 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * Pages followed (cited by title and section, no line numbers):
+ *   [NVB] NVIDIA Technical Blog, "Unlocking Tensor Core Performance for Machine
+ *         Learning Interatomic Potentials" (2026-10-29), Chinese edition.
+ *   [KR]  discuss.pytorch.kr summary of the same post, "NVIDIA, 재학습 없이 MLIP
+ *         분자 동역학을 최대 1.7배 가속한 Tensor Core FP32 기법 실측 기법 공개".
+ *
+ * What the pages fix:
+ *   - every FP32 operand becomes three scaled BF16 components,
+ *     x = x0 + 2^-8 x1 + 2^-16 x2, each holding 8 significant bits, 24 in all
+ *     ([KR] "Blackwell의 BF16x9: 세 조각, 아홉 번의 곱"; [NVB] Fig. 1 caption);
+ *   - the nine pairwise products are grouped into five anti-diagonal bands of
+ *     equal significance and the bands are added into an FP32 accumulator,
+ *     smallest band first ([KR] same section; [NVB] Fig. 1 caption);
+ *   - the products are recombined "with the required scaling"
+ *     ([NVB] "How Tensor Core FP32 closes the hardware gap");
+ *   - the TF32x3 form keeps hi*hi + hi*lo + lo*hi and drops lo*lo
+ *     ([NVB] same section, the equation under Fig. 2; [KR] "Ampere의 TF32x3").
+ *
+ * Readings taken where the pages are silent (each listed in the design notes):
+ *   - the split truncates (rounds toward zero) at each stage;
+ *   - components are stored scaled, the band weight 2^-8s is applied once per
+ *     band when the bands are recombined;
+ *   - one FP32 accumulator per band over the whole K range, recombined once;
+ *   - within a band: k ascending, then p ascending (q = s - p);
+ *   - the recombination is acc = 2^-32 S4, then acc = fma(S_s, 2^-8s, acc)
+ *     for s = 3, 2, 1, then C = acc + S0;
+ *   - Inf and NaN inputs: Inf -> (Inf, +0, +0); NaN -> (quiet NaN keeping the
+ *     sign and high payload, +0, +0).
+ *
+ * Build: plain C99, -O2 -fno-fast-math -ffp-contract=off -fopenmp.  OpenMP only
+ * distributes independent output rows over threads; no element's arithmetic
+ * is reordered.  All loops run each output element's k index in ascending
+ * order; the j loop is innermost only so a row's accumulators advance together.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL (-1)
+#define ORC_ENOMEM (-2)
+
+static uint32_t bits_of(float f) { uint32_t u; memcpy(&u, &f, sizeof u); return u; }
+static float float_of(uint32_t u) { float f; memcpy(&f, &u, sizeof f); return f; }
+
+/* BF16 value (as a uint16 bit pattern) widened to the FP32 value it denotes. */
+static float bf16_value(uint16_t h) { return float_of((uint32_t)h << 16); }
+
+/* Round a float toward zero to BF16: keep sign, exponent and the top 7
+ * explicit mantissa bits (8 significant bits with the hidden one). */
+static uint16_t trunc_bf16(float v) { return (uint16_t)(bits_of(v) >> 16); }
+
+/*
+ * Split of one FP32 value into three scaled BF16 components.
+ * [KR] "Blackwell의 BF16x9": x = x0 + 2^-8 x1 + 2^-16 x2, 8 bits per piece.
+ * Done in double so every step is visibly exact: x, x0 and 2^8 (x - x0) all
+ * have at most 24 significant bits within a 53-bit double.
+ */
+void orc_split_one(float x, uint16_t *c0, uint16_t *c1, uint16_t *c2)
+{
+    uint32_t u = bits_of(x);
+    if ((u & 0x7F800000u) == 0x7F800000u) {          /* Inf or NaN */
+        uint16_t hi = (uint16_t)(u >> 16);
+        if (u & 0x007FFFFFu) hi |= 0x0040u;             /* NaN: force quiet bit */
+        *c0 = hi; *c1 = 0; *c2 = 0;
+        return;
+    }
+    uint16_t h0 = trunc_bf16(x);                        /* x0 = RZ_bf16(x) */
+    double r = (double)x - (double)bf16_value(h0);      /* exact remainder */
+    double t = r * 256.0;                               /* 2^8 (x - x0) */
+    float tf = (float)t;                                /* exact: <= 16 bits */
+    uint16_t h1 = trunc_bf16(tf);                       /* x1 = RZ_bf16(t) */
+    double s = (t - (double)bf16_value(h1)) * 256.0;    /* x2 = 2^8 (t - x1) */
+    float sf = (float)s;                                /* exact: <= 8 bits */
+    uint16_t h2 = trunc_bf16(sf);
+    /* +0 for zero residuals (IEEE x - x = +0 in round-to-nearest). */
+    if (tf == 0.0f) h1 = 0;
+    if (sf == 0.0f) h2 = 0;
+    *c0 = h0; *c1 = h1; *c2 = h2;
+}
+
+/* Elementwise split of a rows x cols matrix with leading dimensions. */
+int orc_split(int64_t rows, int64_t cols, const float *X, int64_t ldx,
+              uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo)
+{
+    if (rows < 0 || cols < 0 || ldx < cols || ldo < cols) return ORC_EINVAL;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j)
+            orc_split_one(X[i * ldx + j], &X0[i * ldo + j], &X1[i * ldo + j], &X2[i * ldo + j]);
+    return ORC_OK;
+}
+
+/* Row index helper: rows == NULL means "all rows 0..nrows-1". */
+static int64_t row_at(const int64_t *rows, int64_t r) { return rows ? rows[r] : r; }
+
+/*
+ * FP64 reference: Cref[r,j] = sum_k (double)A[i,k] * (double)B[k,j], k ascending,
+ * and G[r,j] = sum_k |A[i,k] * B[k,j]| (the magnitude used in the error bound).
+ * The product of two floats is exact in double (48 <= 53 bits).
+ * Output row r holds input row i = rows[r] (or r when rows is NULL).
+ */
+int orc_gemm_f64(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
+                 const float *A, int64_t lda, const float *B, int64_t ldb,
+                 double *Cref, int64_t ldc, double *G, int64_t ldg)
+{
+    if (nrows < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N || (G && ldg < N))
+        return ORC_EINVAL;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = row_at(rows, r);
+        double *c = Cref + r * ldc;
+        double *g = G ? G + r * ldg : NULL;
+        for (int64_t j = 0; j < N; ++j) { c[j] = 0.0; if (g) g[j] = 0.0; }
+        for (int64_t k = 0; k < K; ++k) {
+            double a = (double)A[i * lda + k];
+            const float *b = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j) c[j] += a * (double)b[j];
+            if (g)
+                for (int64_t j = 0; j < N; ++j) g[j] += fabs(a * (double)b[j]);
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Naive FP32 SGEMM: one float accumulator per element, k ascending, the product
+ * and the sum each rounded to FP32 (no fused multiply-add).
+ */
+int orc_sgemm_naive_f32(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
+                        const float *A, int64_t lda, const float *B, int64_t ldb,
+                        float *C, int64_t ldc)
+{
+    if (nrows < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return ORC_EINVAL;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = row_at(rows, r);
+        float *c = C + r * ldc;
+        for (int64_t j = 0; j < N; ++j) c[j] = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = A[i * lda + k];
+            const float *b = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j) {
+                float p = a * b[j];
+                c[j] = c[j] + p;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* Flags of the scalar emulation (only used to model hardware behaviour). */
+#define ORC_FLUSH_PRODUCT_SUBNORMALS 1  /* product below 2^-126 becomes +-0 */
+
+/*
+ * Scalar band emulation of the BF16x9 GEMM.
+ *
+ * Steps, in the pages' order:
+ *   1. split every element of A and B into (x0, x1, x2)  ([KR] BF16x9 section);
+ *   2. form the pairwise products A_p[i,k] * B_q[k,j]; a BF16 x BF16 product
+ *      has at most 16 significant bits, so it is exact in FP32 unless it
+ *      leaves FP32's normal range;
+ *   3. add each product into the FP32 accumulator of its band s = p + q
+ *      (five anti-diagonal bands, [NVB] Fig. 1 caption), k ascending and
+ *      within each k, p ascending;
+ *   4. recombine the bands with their weights 2^-8s, smallest band first:
+ *      acc = 2^-32 S4; acc = fma(S3, 2^-24, acc); acc = fma(S2, 2^-16, acc);
+ *      acc = fma(S1, 2^-8, acc); C = acc + S0.
+ * nbands = b keeps only the bands s < b (1, 3, 6, 8 or 9 products); b = 2 is
+ * the TF32x3 form hi*hi + hi*lo + lo*hi with hi = x0, lo = 2^-8 x1.
+ */
+int orc_gemm_emu(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
+                 const float *A, int64_t lda, const float *B, int64_t ldb,
+                 float *C, int64_t ldc, int nbands, int flags,
+                 float *bands_out /* optional: 5 x nrows x N band sums */)
+{
+    if (nrows < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return ORC_EINVAL;
+    if (nbands < 1 || nbands > 5) return ORC_EINVAL;
+
+    /* Step 1 for B: three component planes, each K x N, as FP32 values. */
+    size_t plane = (size_t)K * (size_t)N;
+    float *Bc = (float *)malloc(3 * plane * sizeof(float) + 1);
+    if (!Bc) return ORC_ENOMEM;
+    #pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j) {
+            uint16_t h[3];
+            orc_split_one(B[k * ldb + j], &h[0], &h[1], &h[2]);
+            for (int q = 0; q < 3; ++q) Bc[q * plane + (size_t)k * N + j] = bf16_value(h[q]);
+        }
+
+    int rc = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = row_at(rows, r);
+        float *S = (float *)malloc(5 * (size_t)N * sizeof(float) + 1);   /* band sums */
+        if (!S) { rc = ORC_ENOMEM; continue; }
+        for (int64_t j = 0; j < 5 * N; ++j) S[j] = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t h[3];
+            orc_split_one(A[i * lda + k], &h[0], &h[1], &h[2]);       /* step 1 for A */
+            for (int p = 0; p < 3; ++p) {
+                float ap = bf16_value(h[p]);
+                for (int q = 0; q < 3; ++q) {
+                    int s = p + q;
+                    if (s >= nbands) continue;
+                    const float *bq = Bc + q * plane + (size_t)k * N;
+                    float *Ss = S + (size_t)s * N;
+                    for (int64_t j = 0; j < N; ++j) {
+                        float prod = ap * bq[j];                              /* step 2 */
+                        if ((flags & ORC_FLUSH_PRODUCT_SUBNORMALS) && fabsf(prod) < 0x1p-126f)
+                            prod = copysignf(0.0f, prod);
+                        Ss[j] = Ss[j] + prod;                                 /* step 3 */
+                    }
+                }
+            }
+        }
+        for (int64_t j = 0; j < N; ++j) {                                     /* step 4 */
+            float acc = 0x1p-32f * S[4 * N + j];
+            acc = fmaf(S[3 * N + j], 0x1p-24f, acc);
+            acc = fmaf(S[2 * N + j], 0x1p-16f, acc);
+            acc = fmaf(S[1 * N + j], 0x1p-8f, acc);
+            C[r * ldc + j] = acc + S[j];
+            if (bands_out)
+                for (int s = 0; s < 5; ++s)
+                    bands_out[((size_t)s * nrows + r) * N + j] = S[(size_t)s * N + j];
+        }
+        free(S);
+    }
+    free(Bc);
+    return rc;
+}
+
+/*
+ * Truncated-band value in FP64: T[r,j] = sum_k sum_{p+q<nbands} 2^-8(p+q) A_p[i,k] B_q[k,j].
+ * Each term is a product of two BF16 values times a power of two, exact in
+ * double; the sum runs k ascending, then p ascending.  With nbands = 5 this is
+ * the exact algebraic value of the nine-product sum; with nbands = 2 it is the
+ * TF32x3 form hi*hi + hi*lo + lo*hi ([NVB] the equation under Fig. 2).
+ */
+int orc_gemm_trunc_f64(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
+                       const float *A, int64_t lda, const float *B, int64_t ldb,
+                       double *T, int64_t ldt, int nbands)
+{
+    if (nrows < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldt < N) return ORC_EINVAL;
+    if (nbands < 1 || nbands > 5) return ORC_EINVAL;
+    static const double weight[5] = {1.0, 0x1p-8, 0x1p-16, 0x1p-24, 0x1p-32};
+    int rc = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = row_at(rows, r);
+        double *t = T + r * ldt;
+        for (int64_t j = 0; j < N; ++j) t[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t a[3];
+            orc_split_one(A[i * lda + k], &a[0], &a[1], &a[2]);
+            for (int64_t j = 0; j < N; ++j) {
+                uint16_t b[3];
+                orc_split_one(B[k * ldb + j], &b[0], &b[1], &b[2]);
+                for (int p = 0; p < 3; ++p)
+                    for (int q = 0; q < 3; ++q)
+                        if (p + q < nbands)
+                            t[j] += weight[p + q] * ((double)bf16_value(a[p]) * (double)bf16_value(b[q]));
+            }
+        }
+    }
+    return rc;
+}
+
+/*
+ * GELU with the error function, y = fp32_RNE(0.5 x (1 + erf(x / sqrt 2))), taken
+ * in double.  Used only to build the hidden activations between the two
+ * linear layers of the small PET-like workload (the pages name no activation;
+ * the workload does).
+ */
+int orc_gelu_f64_to_f32(int64_t n, const double *x, float *y)
+{
+    if (n < 0) return ORC_EINVAL;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = (float)(0.5 * x[i] * (1.0 + erf(x[i] / sqrt(2.0))));
+    return ORC_OK;
+}
+
+/* Threads the OpenMP runtime will use for the parallel loops above. */
+int orc_num_threads(void)
+{
+    int n = 1;
+    #pragma omp parallel
+    {
+        #pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}
