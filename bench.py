@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the BF16x9 emulated SGEMM on one MI355X.
+
+One step is one pass of the whole path over the large PET-like workload
+(17,280 atoms x 32 neighbour tokens = 552,960 rows, d = 256, FFN = 1024):
+    split W1 [256 x 1024] and W2 [1024 x 256] into BF16 planes   (standalone split)
+    C1 = X [552960 x 256]  . W1     (A split inside the GEMM, nine products)
+    C2 = H [552960 x 1024] . W2
+Inputs are seeded synthetic data already resident in HBM when timing starts.
+Reported value: effective FP32 TFLOP/s = (2 M N1 K1 + 2 M N2 K2) / t_step.
+
+Also reported on the same line:
+  roofline      the GEMM kernel against the BF16 dense MFMA peak, counting the
+                nine BF16 products (18 M N K flops per launch), from HIP events
+                recorded around every GEMM launch of the timed steps on the
+                stream the kernels run on;
+  cpu_baseline  the oracle's naive FP32 SGEMM on a bounded sample of the same
+                rows, timed on this host's cores;
+  context       torch.matmul FP32 (rocBLAS/hipBLASLt) on the same GEMMs and
+                the fused-B entry point sgemm_bf16x9, for comparison only.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-context]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+MI355X_BF16_DENSE_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk/CU
+MI355X_FP32_VECTOR_TFLOPS = 157.3
+MI355X_HBM_GBS = 8000.0
+METRIC = "BF16x9 SGEMM effective FP32 TFLOP/s (2MNK/t) and % of bf16 MFMA peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-context", action="store_true", help="skip torch.matmul / fused-B context timings")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import fp32_emulated_gemm_amd as fe
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+
+    t0 = time.perf_counter()
+    w = workloads.pet_large()
+    log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+    X, W1, W2, H = w["X"], w["W1"], w["W2"], w["H"]
+    M, D = X.shape
+    F = W1.shape[1]
+    Xd = torch.from_numpy(X).to(dev)
+    Hd = torch.from_numpy(H).to(dev)
+    W1d = torch.from_numpy(W1).to(dev)
+    W2d = torch.from_numpy(W2).to(dev)
+    C1 = torch.empty((M, F), dtype=torch.float32, device=dev)
+    C2 = torch.empty((M, D), dtype=torch.float32, device=dev)
+    P1 = [torch.empty((D, F), dtype=torch.int16, device=dev) for _ in range(3)]
+    P2 = [torch.empty((F, D), dtype=torch.int16, device=dev) for _ in range(3)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    ev = []
+
+    def step(record):
+        fe.split_f32_bf16x3(D, F, W1d, F, *P1, F, sp)
+        fe.split_f32_bf16x3(F, D, W2d, D, *P2, D, sp)
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+        fe.sgemm_emu_presplit_b(M, F, D, Xd, D, *P1, F, C1, F, 5, sp)
+        if record:
+            e[1].record(stream)
+            e[2].record(stream)
+        fe.sgemm_emu_presplit_b(M, D, F, Hd, F, *P2, D, C2, D, 5, sp)
+        if record:
+            e[3].record(stream)
+            ev.append(e)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+
+    flops_eff = 2.0 * M * F * D + 2.0 * M * D * F
+    value = flops_eff / (ms_step * 1e-3) / 1e12
+    g1 = [e[0].elapsed_time(e[1]) for e in ev]
+    g2 = [e[2].elapsed_time(e[3]) for e in ev]
+    g1_ms, g2_ms = float(np.mean(g1)), float(np.mean(g2))
+    # roofline of the GEMM kernel: nine BF16 products per FP32 multiply-add pair
+    bf16_flops_per_launch = [18.0 * M * F * D, 18.0 * M * D * F]
+    achieved = sum(bf16_flops_per_launch) / ((g1_ms + g2_ms) * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms); GEMM1 {g1_ms:.3f} ms, GEMM2 {g2_ms:.3f} ms")
+
+    # correctness spot check of the timed outputs against torch FP32 (sanity, not parity)
+    ref1 = torch.matmul(Xd[:256], W1d)
+    rel = float((C1[:256] - ref1).norm() / ref1.norm())
+    if not rel < 1e-5:
+        raise SystemExit(f"bench: output check failed (relative error {rel:.3g})")
+
+    context = None
+    if not args.no_context:
+        context = context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(X, W1, H, W2, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "pet_large: X[552960x256] @ W1[256x1024] and H[552960x1024] @ W2[1024x256] "
+                        "(17280 atoms x 32 tokens), weights split once per step, all nine products",
+            "M": M, "d": D, "ffn": F, "nbands": 5, "entry": "split_f32_bf16x3 + sgemm_emu_presplit_b",
+        },
+        "pct_bf16_peak_9products": round(100.0 * value * 9 / MI355X_BF16_DENSE_TFLOPS, 2),
+        "pct_fp32_vector_peak": round(100.0 * value / MI355X_FP32_VECTOR_TFLOPS, 2),
+        "gemm_ms": {"X@W1": round(g1_ms, 4), "H@W2": round(g2_ms, 4)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "gemm_bf16x9_kernel<5, A vector loads, B planes>",
+            "flops_per_launch": bf16_flops_per_launch,
+        },
+        "cpu_baseline": cpu,
+        "context": context,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def timed(fn, stream, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
+    """torch.matmul FP32 and the fused-B entry point on the same GEMMs (context only)."""
+    res = {}
+    fl = 2.0 * M * F * D
+    t = timed(lambda: torch.matmul(Xd, W1d, out=C1), stream, 5)
+    res["torch_fp32_X@W1_tflops"] = round(fl / t / 1e9, 2)
+    t = timed(lambda: torch.matmul(Hd, W2d, out=C2), stream, 5)
+    res["torch_fp32_H@W2_tflops"] = round(fl / t / 1e9, 2)
+    t = timed(lambda: fe.sgemm_bf16x9(M, F, D, Xd, D, W1d, F, C1, F, sp), stream, 5)
+    res["sgemm_bf16x9_X@W1_tflops"] = round(fl / t / 1e9, 2)
+    t = timed(lambda: fe.sgemm_bf16x9(M, D, F, Hd, F, W2d, D, C2, D, sp), stream, 5)
+    res["sgemm_bf16x9_H@W2_tflops"] = round(fl / t / 1e9, 2)
+    n = 4096
+    g = torch.Generator(device="cuda").manual_seed(1)
+    A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+    B = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+    C = torch.empty((n, n), device="cuda")
+    t = timed(lambda: fe.sgemm_bf16x9(n, n, n, A, n, B, n, C, n, sp), stream, 10)
+    res["sgemm_bf16x9_4096^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
+    t = timed(lambda: torch.matmul(A, B, out=C), stream, 10)
+    res["torch_fp32_4096^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
+    log(f"context: {res}")
+    return res
+
+
+def cpu_baseline(X, W1, H, W2, target_s):
+    """The oracle's naive FP32 SGEMM on a row sample of both GEMMs, all host cores."""
+    import numpy as np
+    import oracle
+    M = X.shape[0]
+    flops_per_row = 2.0 * (W1.shape[0] * W1.shape[1] + W2.shape[0] * W2.shape[1])
+
+    def run(nrows):
+        rows = np.linspace(0, M - 1, nrows).astype(np.int64)
+        t = time.perf_counter()
+        oracle.sgemm_naive_f32(X, W1, rows=rows)
+        oracle.sgemm_naive_f32(H, W2, rows=rows)
+        return time.perf_counter() - t
+
+    probe_rows = 256
+    tp = run(probe_rows)
+    nrows = int(min(M, max(probe_rows, probe_rows * target_s / max(tp, 1e-6))))
+    t = run(nrows)
+    val = flops_per_row * nrows / t / 1e12
+    log(f"cpu baseline: {nrows} rows in {t:.2f} s on {oracle.num_threads()} threads")
+    return {"value": round(val, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"naive FP32 SGEMM (oracle) on {nrows} of {M} rows of X@W1 and H@W2, "
+                      f"{t:.1f} s; value = 2*rows*(256*1024+1024*256)/t"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+"""Python binding of libsgemm_emu -- FP32 GEMM emulated on MI355X BF16 MFMA (BF16x9).
+
+Thin ctypes marshalling over the C ABI in ``include/sgemm_emu.h``; every step
+of the computation runs in the library's HIP kernels.  PyTorch supplies device
+memory and streams only.  The functions keep the C names and argument order:
+
+    sgemm_bf16x9(M, N, K, A, lda, B, ldb, C, ldc, stream=None)
+    sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream=None)
+    sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, C, ldc, nbands, stream=None)
+    split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
+    sgemm_emu_products(nbands), sgemm_emu_strerror(status), sgemm_emu_version()
+
+Matrix arguments may be torch tensors (their data pointer is passed; they must
+live on the current HIP device) or raw integer device addresses.  `stream`
+defaults to torch's current stream.  A nonzero status raises SgemmEmuError.
+
+Convenience wrappers that allocate outputs: ``matmul``, ``split``.
+
+The library links the same HIP runtime soname as PyTorch, so torch is imported
+first: the library then binds to the runtime torch already loaded and both see
+the same devices, pointers and streams.  If the built library is missing, the
+import of the GPU functions fails loudly; there is no fallback.
+"""
+import ctypes
+import os
+
+import torch  # noqa: F401  (must be loaded before the library, see above)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsgemm_emu.so")
+
+SGEMM_EMU_OK = 0
+SGEMM_EMU_EINVAL = -1
+SGEMM_EMU_ENULL = -2
+SGEMM_EMU_EARCH = -3
+SGEMM_EMU_ELAUNCH = -4
+
+EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "split_f32_bf16x3",
+           "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
+
+
+class SgemmEmuError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({sgemm_emu_strerror(status)})")
+
+
+_LIB = None
+
+
+def lib():
+    """Load libsgemm_emu.so (built in-tree by fp32_emulated_gemm_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m fp32_emulated_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.sgemm_bf16x9.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+        L.sgemm_emu.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+        L.sgemm_emu_presplit_b.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, i64, ci, vp]
+        L.split_f32_bf16x3.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
+        L.sgemm_emu_products.argtypes = [ci]
+        L.sgemm_emu_strerror.argtypes = [ci]
+        L.sgemm_emu_strerror.restype = ctypes.c_char_p
+        L.sgemm_emu_version.argtypes = []
+        L.sgemm_emu_version.restype = ctypes.c_char_p
+        for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "split_f32_bf16x3",
+                  "sgemm_emu_products"):
+            getattr(L, n).restype = ci
+        _LIB = L
+    return _LIB
+
+
+def hip_runtimes_loaded():
+    """Paths of the HIP runtime libraries mapped into this process (expect one)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            p = line.split()[-1]
+            if "libamdhip64.so" in p:
+                paths.add(os.path.realpath(p))
+    return sorted(paths)
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr() if x.numel() else (x.data_ptr() or None)
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, torch.cuda.Stream):
+        return s.cuda_stream
+    return int(s)
+
+
+def _ok(status, where):
+    if status != SGEMM_EMU_OK:
+        raise SgemmEmuError(status, where)
+    return status
+
+
+def sgemm_bf16x9(M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    return _ok(lib().sgemm_bf16x9(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream)),
+               "sgemm_bf16x9")
+
+
+def sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream=None):
+    return _ok(lib().sgemm_emu(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, nbands, _stream(stream)),
+               "sgemm_emu")
+
+
+def sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, C, ldc, nbands, stream=None):
+    return _ok(lib().sgemm_emu_presplit_b(M, N, K, _addr(A), lda, _addr(B0), _addr(B1), _addr(B2), ldb,
+                                          _addr(C), ldc, nbands, _stream(stream)), "sgemm_emu_presplit_b")
+
+
+def split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):
+    return _ok(lib().split_f32_bf16x3(rows, cols, _addr(X), ldx, _addr(X0), _addr(X1), _addr(X2), ldo,
+                                      _stream(stream)), "split_f32_bf16x3")
+
+
+def sgemm_emu_products(nbands):
+    return lib().sgemm_emu_products(nbands)
+
+
+def sgemm_emu_strerror(status):
+    return lib().sgemm_emu_strerror(status).decode()
+
+
+def sgemm_emu_version():
+    return lib().sgemm_emu_version().decode()
+
+
+# ---------------------------------------------------------------- tensor conveniences
+
+def _ld(t):
+    """Leading dimension of a row-major 2-D tensor (unit stride along columns)."""
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return max(t.stride(0), t.size(1), 1)
+
+
+def matmul(A, B, nbands=5, out=None, stream=None):
+    """C = A @ B for float32 CUDA tensors, through sgemm_emu (nbands=5: sgemm_bf16x9)."""
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if nbands == 5:
+        sgemm_bf16x9(M, N, K, A, _ld(A), B, _ld(B), C, _ld(C), stream)
+    else:
+        sgemm_emu(M, N, K, A, _ld(A), B, _ld(B), C, _ld(C), nbands, stream)
+    return C
+
+
+def split(X, stream=None):
+    """Three uint16 tensors (BF16 bit patterns, stored as int16) holding X's components."""
+    rows, cols = X.shape
+    outs = [torch.empty((rows, cols), dtype=torch.int16, device=X.device) for _ in range(3)]
+    split_f32_bf16x3(rows, cols, X, _ld(X), outs[0], outs[1], outs[2], max(cols, 1), stream)
+    return tuple(outs)
+
+
+def matmul_presplit(A, Bparts, nbands=5, out=None, stream=None):
+    """C = A @ B with B given as its three component planes (from `split`)."""
+    M, K = A.shape
+    K2, N = Bparts[0].shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=A.device)
+    ldb = _ld(Bparts[0])
+    sgemm_emu_presplit_b(M, N, K, A, _ld(A), Bparts[0], Bparts[1], Bparts[2], ldb, C, _ld(C), nbands, stream)
+    return C

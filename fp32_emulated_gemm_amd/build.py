@@ -1,0 +1,46 @@
+"""Compile the HIP sources into libsgemm_emu.so (gfx950 only).
+
+    python -m fp32_emulated_gemm_amd.build
+
+Flags:
+  --offload-arch=gfx950              the only target (MI355X)
+  -ffp-contract=off                  no implicit FMA: the split's sub/mul stay exact
+                                     and the epilogue's FMAs are written explicitly
+  -fno-gpu-flush-denormals-to-zero   FP32 subnormals kept (the split is exact for them)
+  -target-feature -packed-fp32-ops   keep the compiler from emitting packed FP32 ops
+  -mcode-object-version=5            loadable by the ROCm runtime that PyTorch bundles
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libsgemm_emu.so")
+SOURCES = ["api.hip", "gemm.hip", "split.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-mcode-object-version=5",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function"]
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles; returns the path of the shared library."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,177 @@
+// api.hip -- the C ABI declared in include/sgemm_emu.h: argument validation,
+// the gfx950 device check, and dispatch to the kernels.
+//
+// Every argument is checked before the first HIP call, so an invalid call
+// returns an error status without touching the GPU (and works on machines
+// without one).  The library allocates no device memory and keeps no state
+// besides a per-device cache of "is this a gfx950" and its CU count.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/sgemm_emu.h"
+#include "launch.hpp"
+
+using namespace sgemm_emu_dev;
+
+namespace {
+
+constexpr int64_t kMaxBytes = INT64_MAX / 8;
+
+// Largest element offset touched by a rows x cols matrix with leading dimension ld.
+bool extent_ok(int64_t rows, int64_t cols, int64_t ld)
+{
+    if (rows == 0 || cols == 0) return true;
+    if (rows - 1 > (kMaxBytes - cols) / ld) return false;
+    return true;
+}
+
+int check_matrix(int64_t rows, int64_t cols, const void *p, int64_t ld, uintptr_t align)
+{
+    if (ld < (cols > 1 ? cols : 1)) return SGEMM_EMU_EINVAL;
+    if (!extent_ok(rows, cols, ld)) return SGEMM_EMU_EINVAL;
+    if (rows > 0 && cols > 0 && p == nullptr) return SGEMM_EMU_ENULL;
+    if (((uintptr_t)p % align) != 0) return SGEMM_EMU_EINVAL;
+    return SGEMM_EMU_OK;
+}
+
+int check_dims(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0) return SGEMM_EMU_EINVAL;
+    // One workgroup per 128 x 128 tile; the grid is a 31-bit count.
+    const int64_t tm = (M + 127) / 128, tn = (N + 127) / 128;
+    if (tm > 0 && tn > (int64_t)0x7FFFFFFF / tm) return SGEMM_EMU_EINVAL;
+    return SGEMM_EMU_OK;
+}
+
+struct DeviceInfo {
+    int checked = 0;   // 0 unknown, 1 gfx950, -1 other
+    int num_cus = 0;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_mutex;
+
+// Current device if it is a gfx950, with its CU count; SGEMM_EMU_EARCH otherwise.
+int current_device(int *num_cus)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return SGEMM_EMU_EARCH;
+    }
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceInfo &d = g_devices[dev];
+    if (d.checked == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return SGEMM_EMU_EARCH;
+        }
+        d.checked = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+        d.num_cus = prop.multiProcessorCount;
+    }
+    if (d.checked != 1) return SGEMM_EMU_EARCH;
+    *num_cus = d.num_cus;
+    return SGEMM_EMU_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_ELAUNCH; }
+
+int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
+                int64_t ldc, int nbands, BSource bsrc, hipStream_t stream)
+{
+    int rc;
+    if ((rc = check_dims(M, N, K)) != SGEMM_EMU_OK) return rc;
+    if (nbands < 1 || nbands > 5) return SGEMM_EMU_EINVAL;
+    // A and B only matter when the product is nonempty.
+    const int64_t ma = (N > 0) ? M : 0, nb = (M > 0) ? N : 0;
+    if ((rc = check_matrix(ma, K, A, lda, 4)) != SGEMM_EMU_OK) return rc;
+    if (bsrc == B_FP32) {
+        if ((rc = check_matrix(K, nb, B, ldb, 4)) != SGEMM_EMU_OK) return rc;
+    } else {
+        if ((rc = check_matrix(K, nb, B0, ldb, 2)) != SGEMM_EMU_OK) return rc;
+        if ((rc = check_matrix(K, nb, B1, ldb, 2)) != SGEMM_EMU_OK) return rc;
+        if ((rc = check_matrix(K, nb, B2, ldb, 2)) != SGEMM_EMU_OK) return rc;
+    }
+    if ((rc = check_matrix(M, N, C, ldc, 4)) != SGEMM_EMU_OK) return rc;
+    if (M == 0 || N == 0) return SGEMM_EMU_OK;
+
+    int num_cus = 0;
+    if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
+    if (K == 0) return launched(launch_zero(M, N, C, ldc, num_cus, stream));
+
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda;
+    g.B = B; g.B0 = B0; g.B1 = B1; g.B2 = B2; g.ldb = ldb;
+    g.C = C; g.ldc = ldc;
+    return launched(launch_gemm(g, nbands, bsrc, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm_bf16x9(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                 int64_t ldb, float *C, int64_t ldc, sgemm_emu_stream_t stream)
+{
+    return gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, 5, B_FP32,
+                       (hipStream_t)stream);
+}
+
+int sgemm_emu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+              float *C, int64_t ldc, int nbands, sgemm_emu_stream_t stream)
+{
+    return gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32,
+                       (hipStream_t)stream);
+}
+
+int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const uint16_t *B0,
+                         const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C, int64_t ldc,
+                         int nbands, sgemm_emu_stream_t stream)
+{
+    return gemm_common(M, N, K, A, lda, nullptr, B0, B1, B2, ldb, C, ldc, nbands, B_PLANES,
+                       (hipStream_t)stream);
+}
+
+int split_f32_bf16x3(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0, uint16_t *X1,
+                     uint16_t *X2, int64_t ldo, sgemm_emu_stream_t stream)
+{
+    int rc;
+    if (rows < 0 || cols < 0) return SGEMM_EMU_EINVAL;
+    if ((rc = check_matrix(rows, cols, X, ldx, 4)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(rows, cols, X0, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(rows, cols, X1, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(rows, cols, X2, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if (rows == 0 || cols == 0) return SGEMM_EMU_OK;
+    int num_cus = 0;
+    if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
+    return launched(launch_split(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, (hipStream_t)stream));
+}
+
+int sgemm_emu_products(int nbands)
+{
+    static const int products[6] = {-1, 1, 3, 6, 8, 9};
+    return (nbands >= 1 && nbands <= 5) ? products[nbands] : -1;
+}
+
+const char *sgemm_emu_strerror(int status)
+{
+    switch (status) {
+    case SGEMM_EMU_OK: return "success";
+    case SGEMM_EMU_EINVAL: return "invalid argument (size, leading dimension, nbands or alignment)";
+    case SGEMM_EMU_ENULL: return "null pointer for a nonempty operand";
+    case SGEMM_EMU_EARCH: return "no HIP device, or the current device is not gfx950";
+    case SGEMM_EMU_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *sgemm_emu_version(void) { return "libsgemm_emu 0.1.0 (gfx950, BF16x9)"; }
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// launch.hpp -- internal launch interface between the C-ABI layer (api.hip)
+// and the kernel files.  Not part of the public header.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm_emu_dev {
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// B operand source of the GEMM kernel.
+enum BSource { B_FP32 = 0, B_PLANES = 1 };
+
+struct GemmArgs {
+    int64_t M, N, K;
+    const float *A;
+    int64_t lda;
+    const float *B;          // B_FP32
+    const uint16_t *B0;      // B_PLANES
+    const uint16_t *B1;
+    const uint16_t *B2;
+    int64_t ldb;
+    float *C;
+    int64_t ldc;
+    int tiles_m, tiles_n;
+};
+
+hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                        uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream);
+
+hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream);
+
+hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, int num_cus, hipStream_t stream);
+
+}  // namespace sgemm_emu_dev

@@ -1,0 +1,80 @@
+// split_device.hpp -- device-side split of FP32 values into three scaled BF16
+// components, shared by the standalone split kernel and the GEMM's staging.
+//
+// Definition (NVIDIA Technical Blog, "Unlocking Tensor Core Performance for
+// Machine Learning Interatomic Potentials", Fig. 1 caption; discuss.pytorch.kr
+// summary, section "Blackwell의 BF16x9"): x = x0 + 2^-8 x1 + 2^-16 x2, each
+// piece carrying 8 significant bits.  Each stage rounds toward zero:
+//   x0 = high half of x's bit pattern,
+//   t  = 2^8 (x - x0)            exact (at most 16 significant bits),
+//   x1 = high half of t,
+//   x2 = 2^8 (t - x1)            exact, at most 8 significant bits, so its
+//                                 bit pattern already has a zero low half.
+// The subtractions are exact provided FP32 subnormals are not flushed; the
+// library is compiled with FP32 denormals enabled.
+// Inf and NaN: t is NaN exactly when x is not finite (Inf - Inf, NaN - ...),
+// which the callers use to take the rare fix-up path:
+//   +-Inf -> (+-Inf, +0, +0);  NaN -> (high half with the quiet bit set, +0, +0).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm_emu_dev {
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+
+// Components of a finite x as FP32 bit patterns with zero low halves.
+// Returns t = 2^8 (x - x0); t is NaN iff x is Inf or NaN.
+__device__ __forceinline__ float split_finite(float x, uint32_t &c0, uint32_t &c1, uint32_t &c2)
+{
+    c0 = f2u(x) & 0xFFFF0000u;
+    float t = (x - u2f(c0)) * 256.0f;
+    c1 = f2u(t) & 0xFFFF0000u;
+    c2 = f2u((t - u2f(c1)) * 256.0f);
+    return t;
+}
+
+// Overwrite the components of a non-finite x with the defined special split.
+__device__ __forceinline__ void split_fix_special(float x, uint32_t &c0, uint32_t &c1, uint32_t &c2)
+{
+    uint32_t u = f2u(x);
+    if ((u & 0x7F800000u) == 0x7F800000u) {
+        c0 = (u & 0xFFFF0000u) | ((u & 0x007FFFFFu) ? 0x00400000u : 0u);
+        c1 = 0u;
+        c2 = 0u;
+    }
+}
+
+// One dword holding two BF16 values: `lo` (high half of an FP32 pattern) in
+// bits 0..15 and `hi` in bits 16..31.
+__device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo, uint32_t hi)
+{
+    return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
+// Split 8 values and pack each component into 4 dwords (element e in half e%2
+// of dword e/2).
+__device__ __forceinline__ void split8_packed(const float (&x)[8], uint32_t (&p0)[4],
+                                              uint32_t (&p1)[4], uint32_t (&p2)[4])
+{
+    uint32_t c0[8], c1[8], c2[8];
+    bool special = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float t = split_finite(x[e], c0[e], c1[e], c2[e]);
+        special |= (t != t);
+    }
+    if (__builtin_expect(special, 0)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_fix_special(x[e], c0[e], c1[e], c2[e]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p0[i] = pack_bf16x2(c0[2 * i], c0[2 * i + 1]);
+        p1[i] = pack_bf16x2(c1[2 * i], c1[2 * i + 1]);
+        p2[i] = pack_bf16x2(c2[2 * i], c2[2 * i + 1]);
+    }
+}
+
+}  // namespace sgemm_emu_dev

@@ -1,0 +1,131 @@
+/*
+ * sgemm_emu.h -- C ABI of libsgemm_emu: FP32 matrix multiplication emulated on
+ * the BF16 matrix cores (MFMA) of AMD Instinct MI355X (gfx950).
+ *
+ * Method (NVIDIA Technical Blog, "Unlocking Tensor Core Performance for Machine
+ * Learning Interatomic Potentials", section "How Tensor Core FP32 closes the
+ * hardware gap", Fig. 1 and its caption; discuss.pytorch.kr summary of the same
+ * post, section "Blackwell의 BF16x9: 세 조각, 아홉 번의 곱"):
+ *   each FP32 operand x is split into three scaled BF16 components,
+ *   x = x0 + 2^-8 x1 + 2^-16 x2, each carrying 8 significant bits;
+ *   the nine pairwise products A_p * B_q run on BF16 matrix units with FP32
+ *   accumulation, grouped into five anti-diagonal bands s = p + q;
+ *   the bands are recombined with their weights 2^-8s, smallest band first.
+ * Inputs and outputs stay FP32 (same section: "inputs and outputs remain FP32").
+ *
+ * Readings where the pages are silent (this library's definitions):
+ *   - the split rounds toward zero at each stage: x0 = RZ_bf16(x),
+ *     x1 = RZ_bf16(2^8 (x - x0)), x2 = 2^16 (x - x0 - 2^-8 x1) exactly;
+ *   - +-Inf splits into (+-Inf, +0, +0); NaN into (quiet NaN with the sign and
+ *     the high payload bits kept, +0, +0);
+ *   - one FP32 accumulator per band over the whole K range; the epilogue forms
+ *     acc = 2^-32 S4, acc = fma(S3, 2^-24, acc), acc = fma(S2, 2^-16, acc),
+ *     acc = fma(S1, 2^-8, acc), C = acc + S0;
+ *   - the order of additions inside a band is the matrix unit's; results are
+ *     deterministic (no atomics, no split-K) but not bitwise equal to a
+ *     sequential sum.
+ *   - non-finite inputs follow IEEE rules on the components (Inf times a zero
+ *     component is NaN), so results are not IEEE-754 SGEMM results for them.
+ *
+ * Conventions shared by every entry point:
+ *   Matrices are row-major.  A is M x K with A[i*lda + k]; B is K x N with
+ *   B[k*ldb + j]; C is M x N with C[i*ldc + j].  C := A * B (no alpha, beta).
+ *   All matrix pointers are DEVICE pointers on the current HIP device.  The
+ *   caller owns every buffer; the library keeps no per-call state.
+ *   `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *   asynchronously; faults inside kernels surface at the caller's next
+ *   synchronisation, as in BLAS libraries.
+ *   Arguments are validated before any HIP call; on an error status nothing
+ *   has been enqueued.
+ *   Float pointers must be 4-byte aligned, BF16 plane pointers 2-byte aligned.
+ *   16-byte aligned A with lda % 4 == 0 takes the vector-load path; any other
+ *   layout takes a scalar-load path with the same arithmetic.
+ *   M == 0 or N == 0: nothing is done.  K == 0: C is set to zero.
+ *   C must not overlap A or B (not checked).
+ *   Column-major callers compute C^T = B^T A^T by swapping the operands.
+ */
+#ifndef SGEMM_EMU_H
+#define SGEMM_EMU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *sgemm_emu_stream_t;
+
+enum sgemm_emu_status {
+    SGEMM_EMU_OK = 0,
+    SGEMM_EMU_EINVAL = -1,  /* negative size, leading dimension too small, bad nbands,
+                               misaligned pointer, or a size whose byte offsets overflow */
+    SGEMM_EMU_ENULL = -2,   /* null pointer for an operand with a nonzero extent */
+    SGEMM_EMU_EARCH = -3,   /* no HIP device, or the current device is not gfx950 */
+    SGEMM_EMU_ELAUNCH = -4  /* the kernel launch itself failed (hipGetLastError) */
+};
+
+/*
+ * sgemm_bf16x9 -- C = A * B with all nine products (five bands).
+ * Defined by the pages' BF16x9 scheme (see the top of this file).
+ * A: M x K FP32 (lda >= max(1, K)); B: K x N FP32 (ldb >= max(1, N));
+ * C: M x N FP32 (ldc >= max(1, N)), written, never read.
+ * Returns SGEMM_EMU_OK or an error status.
+ */
+int sgemm_bf16x9(int64_t M, int64_t N, int64_t K,
+                 const float *A, int64_t lda,
+                 const float *B, int64_t ldb,
+                 float *C, int64_t ldc,
+                 sgemm_emu_stream_t stream);
+
+/*
+ * sgemm_emu -- band-drop / product-count variant: keeps only the bands
+ * s = p + q < nbands.  nbands = 5, 4, 3, 2, 1 evaluates 9, 8, 6, 3, 1 products.
+ * nbands = 2 is the TF32x3 form a_hi b_hi + a_hi b_lo + a_lo b_hi (NVIDIA blog,
+ * same section, the equation under Fig. 2) built from BF16 components with
+ * hi = x0 and lo = 2^-8 x1.  nbands = 5 is identical to sgemm_bf16x9.
+ * Other arguments as sgemm_bf16x9; nbands outside 1..5 gives SGEMM_EMU_EINVAL.
+ */
+int sgemm_emu(int64_t M, int64_t N, int64_t K,
+              const float *A, int64_t lda,
+              const float *B, int64_t ldb,
+              float *C, int64_t ldc,
+              int nbands, sgemm_emu_stream_t stream);
+
+/*
+ * sgemm_emu_presplit_b -- as sgemm_emu, with B already split into its three
+ * BF16 component planes by split_f32_bf16x3 (for weights split once and reused,
+ * as the linear layers of an interatomic potential do).  B0, B1, B2 are K x N
+ * row-major uint16 BF16 bit patterns with leading dimension ldb >= max(1, N).
+ * A is split inside the kernel.  The result equals sgemm_emu on the FP32 B.
+ */
+int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
+                         const float *A, int64_t lda,
+                         const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb,
+                         float *C, int64_t ldc,
+                         int nbands, sgemm_emu_stream_t stream);
+
+/*
+ * split_f32_bf16x3 -- the split alone, as its own kernel: for every element of
+ * the rows x cols FP32 matrix X (leading dimension ldx >= max(1, cols)) writes
+ * its components to X0, X1, X2 (uint16 BF16 bit patterns, leading dimension
+ * ldo >= max(1, cols)).  Bit-exact with the definition at the top of this file.
+ */
+int split_f32_bf16x3(int64_t rows, int64_t cols,
+                     const float *X, int64_t ldx,
+                     uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo,
+                     sgemm_emu_stream_t stream);
+
+/* Number of BF16 products evaluated for nbands (1, 3, 6, 8, 9), or -1 if invalid. */
+int sgemm_emu_products(int nbands);
+
+/* Static, human-readable text for a status code. */
+const char *sgemm_emu_strerror(int status);
+
+/* Library version string. */
+const char *sgemm_emu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_EMU_H */

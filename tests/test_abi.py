@@ -1,0 +1,97 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm_emu.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import fp32_emulated_gemm_amd as fe
+    return fe.lib()
+
+
+def test_header_declares_expected_functions():
+    import fp32_emulated_gemm_amd as fe
+    assert _declared_functions() == sorted(fe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_single_hip_runtime_loaded(L):
+    import fp32_emulated_gemm_amd as fe
+    assert len(fe.hip_runtimes_loaded()) == 1, fe.hip_runtimes_loaded()
+
+
+def test_products_and_strings(L):
+    import fp32_emulated_gemm_amd as fe
+    assert [fe.sgemm_emu_products(b) for b in range(0, 7)] == [-1, 1, 3, 6, 8, 9, -1]
+    for s in (0, -1, -2, -3, -4):
+        assert fe.sgemm_emu_strerror(s) != "unknown status"
+    assert fe.sgemm_emu_strerror(7) == "unknown status"
+    assert "gfx950" in fe.sgemm_emu_version()
+
+
+P = 0x10000  # any nonzero, 16-byte aligned address: never dereferenced on these paths
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 4, P, 4, P, 4, P, 4), -1),          # negative M
+    ((4, -1, 4, P, 4, P, 4, P, 4), -1),          # negative N
+    ((4, 4, -1, P, 4, P, 4, P, 4), -1),          # negative K
+    ((4, 4, 8, P, 7, P, 4, P, 4), -1),           # lda < K
+    ((4, 8, 4, P, 4, P, 7, P, 8), -1),           # ldb < N
+    ((4, 8, 4, P, 4, P, 8, P, 7), -1),           # ldc < N
+    ((4, 4, 4, 0, 4, P, 4, P, 4), -2),           # null A
+    ((4, 4, 4, P, 4, 0, 4, P, 4), -2),           # null B
+    ((4, 4, 4, P, 4, P, 4, 0, 4), -2),           # null C
+    ((4, 4, 4, P + 2, 4, P, 4, P, 4), -1),       # misaligned float pointer
+    ((1 << 40, 1 << 40, 4, P, 4, P, 1 << 40, P, 1 << 40), -1),  # byte offsets overflow
+    ((0, 4, 4, 0, 4, 0, 4, 0, 4), 0),            # empty: no-op, no device needed
+    ((4, 0, 4, 0, 4, 0, 1, 0, 1), 0),
+])
+def test_sgemm_validation_before_any_hip_call(L, args, status):
+    assert L.sgemm_bf16x9(*args, None) == status
+    assert L.sgemm_emu(*args, 5, None) == status
+
+
+@pytest.mark.parametrize("nbands", [0, 6, -3])
+def test_bad_nbands(L, nbands):
+    assert L.sgemm_emu(4, 4, 4, P, 4, P, 4, P, 4, nbands, None) == -1
+    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, P, P, 4, P, 4, nbands, None) == -1
+
+
+def test_presplit_validation(L):
+    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, 0, P, 4, P, 4, 5, None) == -2
+    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P + 1, P, P, 4, P, 4, 5, None) == -1
+    assert L.sgemm_emu_presplit_b(4, 8, 4, P, 4, P, P, P, 7, P, 8, 5, None) == -1
+
+
+def test_split_validation(L):
+    assert L.split_f32_bf16x3(-1, 4, P, 4, P, P, P, 4, None) == -1
+    assert L.split_f32_bf16x3(4, 4, P, 3, P, P, P, 4, None) == -1
+    assert L.split_f32_bf16x3(4, 4, P, 4, P, P, P, 3, None) == -1
+    assert L.split_f32_bf16x3(4, 4, 0, 4, P, P, P, 4, None) == -2
+    assert L.split_f32_bf16x3(0, 4, 0, 4, 0, 0, 0, 4, None) == 0
+
+
+def test_valid_call_without_gpu_reports_arch(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert L.sgemm_bf16x9(4, 4, 4, P, 4, P, 4, P, 4, None) == -3
+    assert L.split_f32_bf16x3(4, 4, P, 4, P, P, P, 4, None) == -3

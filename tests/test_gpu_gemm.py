@@ -1,0 +1,234 @@
+"""GPU GEMM parity against the oracle, through the C ABI (small and ragged sizes).
+
+Bit-exact where the result is unique (identity, permutation, exact-class
+inputs, the smallest-band-first case, special-value classes); within the
+FP64-referenced bound and the normwise gate elsewhere.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import check_against_fp64, dev, exact_class_mask, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fe():
+    import fp32_emulated_gemm_amd as fe
+    return fe
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.Philox(key=seed))
+
+
+def run(fe, A, B, nbands=5, entry="fused", ldc_pad=0, a_offset=0):
+    """C = A B on the GPU; `entry` picks sgemm_bf16x9/sgemm_emu or the pre-split path."""
+    M, K = A.shape
+    N = B.shape[1]
+    print(f"gemm {entry} M={M} N={N} K={K} nbands={nbands}", flush=True, file=sys.stderr)
+    if a_offset:
+        buf = np.zeros(M * K + a_offset, np.float32)
+        buf[a_offset:] = A.reshape(-1)
+        Ad_full = dev(buf)
+        Ad = Ad_full[a_offset:]
+    else:
+        Ad = dev(A)
+    Bd = dev(B)
+    ldc = N + ldc_pad
+    Cd = torch.full((max(M, 1) * max(ldc, 1),), float("nan"), dtype=torch.float32, device="cuda")
+    lda = max(K, 1)
+    if entry == "presplit":
+        planes = [torch.empty(max(K * N, 1), dtype=torch.int16, device="cuda") for _ in range(3)]
+        fe.split_f32_bf16x3(K, N, Bd, max(N, 1), *planes, max(N, 1))
+        fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, max(N, 1), Cd, max(ldc, 1), nbands)
+    elif nbands == 5 and entry == "fused":
+        fe.sgemm_bf16x9(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1))
+    else:
+        fe.sgemm_emu(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1), nbands)
+    C = host(Cd)[: M * ldc].reshape(M, ldc) if M * ldc else np.zeros((M, N), np.float32)
+    if ldc_pad:
+        assert np.all(np.isnan(C[:, N:])), "padding columns of C were written"
+    return C[:, :N]
+
+
+SHAPES = [(1, 1, 1), (7, 13, 5), (128, 128, 32), (129, 130, 33), (64, 300, 17), (300, 257, 100),
+          (256, 384, 64), (100, 50, 1000), (31, 33, 257)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("entry", ["fused", "presplit"])
+def test_random_shapes_within_bound(fe, shape, entry):
+    M, N, K = shape
+    g = _rng(M * 7919 + N * 31 + K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry=entry)
+    check_against_fp64(C, A, B, label=f"{entry} {shape}")
+
+
+def test_presplit_equals_fused_bitwise(fe):
+    g = _rng(5)
+    A = g.standard_normal((200, 150)).astype(np.float32)
+    B = g.standard_normal((150, 190)).astype(np.float32)
+    for nb in (1, 3, 5):
+        assert np.array_equal(run(fe, A, B, nb, "fused").view(np.uint32),
+                              run(fe, A, B, nb, "presplit").view(np.uint32))
+
+
+def test_unaligned_a_and_padded_c(fe):
+    """A at a 4-byte (not 16-byte) offset takes the scalar-load path; C with
+    ldc > N leaves the padding untouched."""
+    g = _rng(6)
+    A = g.standard_normal((70, 45)).astype(np.float32)
+    B = g.standard_normal((45, 66)).astype(np.float32)
+    C1 = run(fe, A, B, a_offset=1, ldc_pad=3)
+    C0 = run(fe, A, B)
+    check_against_fp64(C1, A, B, label="unaligned")
+    assert np.array_equal(C0.view(np.uint32), C1.view(np.uint32))
+
+
+def _full24(g, shape):
+    m = g.integers(1 << 23, 1 << 24, size=shape) | 1
+    s = np.where(g.integers(0, 2, size=shape) == 1, -1.0, 1.0)
+    return (s * np.ldexp(m.astype(np.float64), g.integers(-20, 20, size=shape) - 23)).astype(np.float32)
+
+
+@pytest.mark.parametrize("entry", ["fused", "presplit"])
+def test_identity_and_scaled_permutation_exact(fe, entry):
+    g = _rng(7)
+    n = 160
+    X = _full24(g, (n, n))
+    I = np.eye(n, dtype=np.float32)
+    assert np.array_equal(run(fe, I, X, entry=entry).view(np.uint32), X.view(np.uint32))
+    assert np.array_equal(run(fe, X, I, entry=entry).view(np.uint32), X.view(np.uint32))
+    P = np.eye(n, dtype=np.float32)[g.permutation(n)]
+    D = np.diag(np.ldexp(1.0, g.integers(-10, 10, size=n))).astype(np.float32)
+    A = P @ D
+    want = (A.astype(np.float64) @ X.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(run(fe, A, X, entry=entry), want)
+
+
+def test_smallest_band_first_case(fe):
+    """Bands S0 = 1 + 2^-7 + 2^-16, S1 = 2^-7 + 2^-16, S2 = 2^-8 (exact): the
+    smallest-first recombination gives 1 + 2^-7 + 2^-15 + 2^-16 + 2^-23."""
+    a = np.array([[1.0, 2.0 ** -16 + 2.0 ** -24, 2.0 ** -7 + 2.0 ** -15 + 2.0 ** -24]], np.float32)
+    b = np.ones((3, 1), np.float32)
+    C = run(fe, a, b)
+    assert C[0, 0] == np.float32(1.0 + 2.0 ** -7 + 2.0 ** -15 + 2.0 ** -16 + 2.0 ** -23)
+
+
+@pytest.mark.parametrize("lo,hi,emax,K", [(1 << 15, 1 << 16, 0, 64), (1 << 11, 1 << 12, 2, 16),
+                                          (1 << 9, 1 << 13, 1, 16), (1 << 19, 1 << 20, 0, 4),
+                                          (1 << 23, 1 << 24, 0, 2), (1 << 23, 1 << 24, 2, 5)])
+@pytest.mark.parametrize("nbands", [5, 4, 3, 2, 1])
+def test_exact_class_bitwise_vs_oracle(fe, orc, lo, hi, emax, K, nbands):
+    """On elements whose band sums are exact in any order, GPU == oracle emulation."""
+    g = _rng(lo + K + emax)
+    M, N = 40, 36
+
+    def draw(shape):
+        m = g.integers(lo, hi, size=shape).astype(np.float64)
+        m *= np.where(g.integers(0, 2, size=shape) == 1, -1.0, 1.0)
+        return np.ldexp(m, g.integers(-emax, emax + 1, size=shape)).astype(np.float32)
+
+    A, B = draw((M, K)), draw((K, N))
+    mask = exact_class_mask(A, B)
+    assert mask.mean() > 0.3
+    C = run(fe, A, B, nbands)
+    E = orc.gemm_emu(A, B, nbands)
+    assert np.array_equal(C.view(np.uint32)[mask], E.view(np.uint32)[mask])
+
+
+@pytest.mark.parametrize("nbands,bound", [(1, 2.0 ** -6 + 2.0 ** -13 + 2.0 ** -21 + 2.0 ** -30),
+                                          (2, 2.0 ** -13 + 2.0 ** -21 + 2.0 ** -30),
+                                          (3, 2.0 ** -21 + 2.0 ** -30), (4, 2.0 ** -30)])
+def test_band_drop_ablation(fe, orc, nbands, bound):
+    """Keeping bands s < nbands: within bound_b G of the FP64 product and within
+    the accumulation bound of the oracle's FP64 truncated-band value."""
+    g = _rng(40 + nbands)
+    M, N, K = 96, 80, 300
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, nbands).astype(np.float64)
+    ref, G = orc.gemm_f64(A, B)
+    T = orc.gemm_trunc_f64(A, B, nbands)
+    U = 2.0 ** -24
+    assert np.all(np.abs(C - T) <= 2 * K * U * G)
+    assert np.all(np.abs(C - ref) <= (bound + 2 * K * U) * G)
+
+
+def test_special_values_class(fe, orc):
+    """Inf / NaN inputs: the class of each output (NaN, +Inf, -Inf, finite)
+    matches the oracle emulation's class."""
+    g = _rng(9)
+    M, N, K = 48, 40, 70
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    B[3, :] = np.float32(np.pi)
+    A[2, 3] = np.inf
+    A[5, 3] = -np.inf
+    A[7, 9] = np.nan
+    A[11, 3] = np.inf
+    B[3, 4] = 1.0                         # Inf * 1.0 meets a zero component -> NaN
+    B[20, 30] = np.inf
+    A[13, 20] = 0.0                       # Inf * 0 -> NaN in row 13, column 30
+    C = run(fe, A, B)
+    E = orc.gemm_emu(A, B)
+
+    def cls(X):
+        return np.where(np.isnan(X), 0, np.where(X == np.inf, 1, np.where(X == -np.inf, 2, 3)))
+    assert np.array_equal(cls(C), cls(E))
+    fin = np.isfinite(E)
+    assert np.allclose(C[fin], E[fin], rtol=1e-5, atol=1e-5)
+
+
+def test_subnormals_and_zeros(fe):
+    g = _rng(10)
+    M, N, K = 64, 64, 64
+    A = (g.standard_normal((M, K)) * 2.0 ** -130).astype(np.float32)   # mostly subnormal
+    B = g.standard_normal((K, N)).astype(np.float32) * np.float32(2.0 ** 10)
+    C = run(fe, A, B)
+    check_against_fp64(C, A, B, label="subnormal A", normwise=False)
+    Z = np.zeros((M, K), np.float32)
+    Z[0, 0] = -0.0
+    assert np.all(run(fe, Z, B) == 0)
+
+
+def test_k_zero_sets_c_to_zero(fe):
+    Cd = torch.full((5 * 7,), 3.0, device="cuda")
+    fe.sgemm_bf16x9(5, 7, 0, None, 1, None, 7, Cd, 7)
+    assert np.all(host(Cd) == 0)
+
+
+def test_m_or_n_zero_is_noop(fe):
+    fe.sgemm_bf16x9(0, 7, 3, None, 3, None, 7, None, 7)
+    fe.sgemm_bf16x9(4, 0, 3, None, 3, None, 1, None, 1)
+
+
+def test_deterministic_bitwise(fe):
+    g = _rng(12)
+    A = g.standard_normal((513, 700)).astype(np.float32)
+    B = g.standard_normal((700, 390)).astype(np.float32)
+    c1 = run(fe, A, B)
+    c2 = run(fe, A, B)
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+
+
+def test_error_status_raises(fe):
+    with pytest.raises(fe.SgemmEmuError):
+        fe.sgemm_emu(4, 4, 4, 16, 4, 16, 4, 16, 4, 9)
+
+
+def test_matmul_helpers(fe):
+    g = _rng(13)
+    A = torch.from_numpy(g.standard_normal((90, 60)).astype(np.float32)).cuda()
+    B = torch.from_numpy(g.standard_normal((60, 70)).astype(np.float32)).cuda()
+    C = fe.matmul(A, B)
+    Cp = fe.matmul_presplit(A, fe.split(B))
+    torch.cuda.synchronize()
+    assert torch.equal(C, Cp)
+    check_against_fp64(C.cpu().numpy(), A.cpu().numpy(), B.cpu().numpy(), label="matmul")

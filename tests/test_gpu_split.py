@@ -1,0 +1,65 @@
+"""GPU split kernel vs the oracle's split: bit-exact (through the C ABI)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fe():
+    import fp32_emulated_gemm_amd as fe
+    return fe
+
+
+def _planes_host(planes):
+    torch.cuda.synchronize()
+    return [p.cpu().numpy().view(np.uint16) for p in planes]
+
+
+def test_split_all_encodings_bit_exact(fe, orc):
+    """All 2^32 FP32 encodings, in chunks of 2^28, through split_f32_bf16x3."""
+    chunk = 1 << 28
+    for start in range(0, 1 << 32, chunk):
+        print(f"split chunk {start:#x}", flush=True, file=sys.stderr)
+        x = torch.arange(start, start + chunk, dtype=torch.int64, device="cuda").to(torch.int32).view(torch.float32)
+        planes = [torch.empty(chunk, dtype=torch.int16, device="cuda") for _ in range(3)]
+        fe.split_f32_bf16x3(1, chunk, x, chunk, *planes, chunk)
+        got = _planes_host(planes)
+        xh = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        want = orc.split(xh)
+        for c in range(3):
+            if not np.array_equal(got[c], want[c]):
+                bad = np.nonzero(got[c] != want[c])[0][0]
+                raise AssertionError(f"component {c} differs at encoding {start + bad:#010x}: "
+                                     f"gpu {got[c][bad]:#06x} oracle {want[c][bad]:#06x}")
+        del x, planes
+
+
+@pytest.mark.parametrize("rows,cols,ldx,ldo,offset", [
+    (37, 53, 53, 53, 0),        # odd widths: scalar kernel
+    (64, 256, 256, 256, 0),     # contiguous: folded vector kernel
+    (33, 64, 72, 80, 0),        # strided rows, vector kernel
+    (16, 40, 41, 40, 1),        # misaligned start: scalar kernel
+    (1, 8, 8, 8, 0),
+])
+def test_split_layouts(fe, orc, rows, cols, ldx, ldo, offset):
+    g = np.random.Generator(np.random.Philox(key=rows * 1000 + cols))
+    buf = (g.standard_normal(rows * ldx + offset + 8) * 2.0 ** g.integers(-60, 60, rows * ldx + offset + 8))
+    buf = buf.astype(np.float32)
+    X = torch.from_numpy(buf).cuda()
+    Xv = X[offset:offset + rows * ldx].view(rows, ldx)
+    planes = [torch.full((rows * ldo,), -1, dtype=torch.int16, device="cuda") for _ in range(3)]
+    fe.split_f32_bf16x3(rows, cols, Xv, ldx, *planes, ldo)
+    got = [p.reshape(rows, ldo) for p in _planes_host(planes)]
+    want = orc.split(buf[offset:offset + rows * ldx].reshape(rows, ldx)[:, :cols])
+    for c in range(3):
+        assert np.array_equal(got[c][:, :cols], want[c])
+        if ldo > cols:
+            assert np.all(got[c][:, cols:] == 0xFFFF)   # padding untouched
+
+
+def test_split_empty_is_noop(fe):
+    fe.split_f32_bf16x3(0, 16, None, 16, None, None, None, 16)
