@@ -90,11 +90,11 @@ def main():
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record(stream)
-        fe.sgemm_emu_presplit_b(M, F, D, Xd, D, *P1, F, C1, F, 5, sp)
+        fe.sgemm_emu_presplit_b(M, F, D, Xd, D, *P1, F, fe.SGEMM_EMU_B_KN, C1, F, 5, sp)
         if record:
             e[1].record(stream)
             e[2].record(stream)
-        fe.sgemm_emu_presplit_b(M, D, F, Hd, F, *P2, D, C2, D, 5, sp)
+        fe.sgemm_emu_presplit_b(M, D, F, Hd, F, *P2, D, fe.SGEMM_EMU_B_KN, C2, D, 5, sp)
         if record:
             e[3].record(stream)
             ev.append(e)

@@ -6,7 +6,7 @@ memory and streams only.  The functions keep the C names and argument order:
 
     sgemm_bf16x9(M, N, K, A, lda, B, ldb, C, ldc, stream=None)
     sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream=None)
-    sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, C, ldc, nbands, stream=None)
+    sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nbands, stream=None)
     split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     sgemm_emu_products(nbands), sgemm_emu_strerror(status), sgemm_emu_version()
 
@@ -34,6 +34,8 @@ SGEMM_EMU_EINVAL = -1
 SGEMM_EMU_ENULL = -2
 SGEMM_EMU_EARCH = -3
 SGEMM_EMU_ELAUNCH = -4
+SGEMM_EMU_B_KN = 0   # pre-split planes K x N (split of B)
+SGEMM_EMU_B_NK = 1   # pre-split planes N x K (split of B^T, e.g. a weight stored [out][in])
 
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "split_f32_bf16x3",
            "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
@@ -58,7 +60,7 @@ def lib():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.sgemm_bf16x9.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.sgemm_emu.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp]
-        L.sgemm_emu_presplit_b.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, i64, ci, vp]
+        L.sgemm_emu_presplit_b.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, ci, vp, i64, ci, vp]
         L.split_f32_bf16x3.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.sgemm_emu_products.argtypes = [ci]
         L.sgemm_emu_strerror.argtypes = [ci]
@@ -115,9 +117,10 @@ def sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream=None):
                "sgemm_emu")
 
 
-def sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, C, ldc, nbands, stream=None):
+def sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nbands, stream=None):
     return _ok(lib().sgemm_emu_presplit_b(M, N, K, _addr(A), lda, _addr(B0), _addr(B1), _addr(B2), ldb,
-                                          _addr(C), ldc, nbands, _stream(stream)), "sgemm_emu_presplit_b")
+                                          b_layout, _addr(C), ldc, nbands, _stream(stream)),
+               "sgemm_emu_presplit_b")
 
 
 def split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):
@@ -168,13 +171,18 @@ def split(X, stream=None):
     return tuple(outs)
 
 
-def matmul_presplit(A, Bparts, nbands=5, out=None, stream=None):
-    """C = A @ B with B given as its three component planes (from `split`)."""
+def matmul_presplit(A, Bparts, nbands=5, out=None, stream=None, b_layout=SGEMM_EMU_B_KN):
+    """C = A @ B with B given as its three component planes (from `split`):
+    planes of B (K x N) for SGEMM_EMU_B_KN, planes of B^T (N x K) for SGEMM_EMU_B_NK."""
     M, K = A.shape
-    K2, N = Bparts[0].shape
+    if b_layout == SGEMM_EMU_B_KN:
+        K2, N = Bparts[0].shape
+    else:
+        N, K2 = Bparts[0].shape
     if K2 != K:
         raise ValueError("inner dimensions differ")
     C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=A.device)
     ldb = _ld(Bparts[0])
-    sgemm_emu_presplit_b(M, N, K, A, _ld(A), Bparts[0], Bparts[1], Bparts[2], ldb, C, _ld(C), nbands, stream)
+    sgemm_emu_presplit_b(M, N, K, A, _ld(A), Bparts[0], Bparts[1], Bparts[2], ldb, b_layout, C, _ld(C),
+                         nbands, stream)
     return C

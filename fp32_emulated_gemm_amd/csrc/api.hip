@@ -7,6 +7,7 @@
 // besides a per-device cache of "is this a gfx950" and its CU count.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -19,6 +20,8 @@ using namespace sgemm_emu_dev;
 namespace {
 
 constexpr int64_t kMaxBytes = INT64_MAX / 8;
+// Largest leading dimension (elements) whose 128-row tile span fits 32-bit byte offsets.
+constexpr int64_t kMaxTileLd = ((int64_t)1 << 32) / (128 * 4) - 64;
 
 // Largest element offset touched by a rows x cols matrix with leading dimension ld.
 bool extent_ok(int64_t rows, int64_t cols, int64_t ld)
@@ -81,6 +84,16 @@ int current_device(int *num_cus)
 
 int launched(hipError_t e) { return e == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_ELAUNCH; }
 
+// Kernel configuration; SGEMM_EMU_KERNEL_VARIANT selects another one for measurement.
+int kernel_variant()
+{
+    static const int v = [] {
+        const char *e = getenv("SGEMM_EMU_KERNEL_VARIANT");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
                 int64_t ldc, int nbands, BSource bsrc, hipStream_t stream)
@@ -94,11 +107,16 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     if (bsrc == B_FP32) {
         if ((rc = check_matrix(K, nb, B, ldb, 4)) != SGEMM_EMU_OK) return rc;
     } else {
-        if ((rc = check_matrix(K, nb, B0, ldb, 2)) != SGEMM_EMU_OK) return rc;
-        if ((rc = check_matrix(K, nb, B1, ldb, 2)) != SGEMM_EMU_OK) return rc;
-        if ((rc = check_matrix(K, nb, B2, ldb, 2)) != SGEMM_EMU_OK) return rc;
+        // planes are K x N, or N x K for the transposed layout
+        const int64_t pr = (bsrc == B_PLANES_NK) ? nb : K, pc = (bsrc == B_PLANES_NK) ? K : nb;
+        const int64_t rows = (pr > 0 && pc > 0) ? pr : 0;
+        if ((rc = check_matrix(rows, pc, B0, ldb, 2)) != SGEMM_EMU_OK) return rc;
+        if ((rc = check_matrix(rows, pc, B1, ldb, 2)) != SGEMM_EMU_OK) return rc;
+        if ((rc = check_matrix(rows, pc, B2, ldb, 2)) != SGEMM_EMU_OK) return rc;
     }
     if ((rc = check_matrix(M, N, C, ldc, 4)) != SGEMM_EMU_OK) return rc;
+    // The kernels address one K step of a 128 x 128 tile with 32-bit byte offsets.
+    if (lda > kMaxTileLd || ldb > kMaxTileLd) return SGEMM_EMU_EINVAL;
     if (M == 0 || N == 0) return SGEMM_EMU_OK;
 
     int num_cus = 0;
@@ -106,6 +124,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     if (K == 0) return launched(launch_zero(M, N, C, ldc, num_cus, stream));
 
     GemmArgs g{};
+    g.variant = kernel_variant();
     g.M = M; g.N = N; g.K = K;
     g.A = A; g.lda = lda;
     g.B = B; g.B0 = B0; g.B1 = B1; g.B2 = B2; g.ldb = ldb;
@@ -132,11 +151,12 @@ int sgemm_emu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
 }
 
 int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const uint16_t *B0,
-                         const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C, int64_t ldc,
-                         int nbands, sgemm_emu_stream_t stream)
+                         const uint16_t *B1, const uint16_t *B2, int64_t ldb, int b_layout, float *C,
+                         int64_t ldc, int nbands, sgemm_emu_stream_t stream)
 {
-    return gemm_common(M, N, K, A, lda, nullptr, B0, B1, B2, ldb, C, ldc, nbands, B_PLANES,
-                       (hipStream_t)stream);
+    if (b_layout != SGEMM_EMU_B_KN && b_layout != SGEMM_EMU_B_NK) return SGEMM_EMU_EINVAL;
+    return gemm_common(M, N, K, A, lda, nullptr, B0, B1, B2, ldb, C, ldc, nbands,
+                       b_layout == SGEMM_EMU_B_NK ? B_PLANES_NK : B_PLANES_KN, (hipStream_t)stream);
 }
 
 int split_f32_bf16x3(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0, uint16_t *X1,

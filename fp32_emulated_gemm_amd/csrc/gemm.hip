@@ -8,22 +8,25 @@
 // p + q share one of five band accumulators; the bands are recombined with
 // weights 2^-8s, smallest band first.
 //
-// Kernel structure (one workgroup per 128 x 128 tile of C, 512 threads):
-//   * 8 waves in a 2 (M) x 4 (N) grid; each wave owns a 64 x 32 sub-tile,
-//     i.e. two 32 x 32 MFMA blocks, each with NB band accumulators of 16
-//     FP32 registers per lane (v_mfma_f32_32x32x16_bf16).
-//   * K advances in steps of 32.  Each thread loads 8 FP32 values of A (one
-//     row, 8 consecutive k) and 8 of B (one column, 8 consecutive k) into
-//     registers one step ahead, splits them in registers and writes the three
-//     BF16 component tiles into LDS, k-contiguous for both operands (B is
-//     transposed on the way in).  LDS is double-buffered, so one barrier per
-//     step separates producers from consumers.
+// Kernel structure (one workgroup per BM x BN tile of C):
+//   * The waves form a WAVES_M x WAVES_N grid; each wave owns a WTM x WTN
+//     sub-tile made of 32 x 32 MFMA blocks, each with NB band accumulators of
+//     16 FP32 registers per lane (v_mfma_f32_32x32x16_bf16).
+//   * K advances in steps of BK = 32.  Threads load their share of the next
+//     step's A and B into registers one step ahead, split FP32 values in
+//     registers, and write the three BF16 component tiles into LDS,
+//     k-contiguous for both operands (B is transposed on the way in).  LDS is
+//     double-buffered, so one barrier per step separates producers from
+//     consumers.
+//   * B sources: FP32 K x N (split in the kernel), BF16 planes K x N (pairs of
+//     columns transposed with byte permutes), or BF16 planes N x K (already
+//     k-contiguous: copied to LDS as is).
 //   * LDS rows are 32 BF16 plus 8 BF16 of padding (80 bytes): the 128-bit
 //     fragment reads of 16 consecutive rows then touch 64 distinct banks.
 //   * Tile order: workgroups are dealt round-robin to the 8 XCDs, so the
 //     block index is remapped to give each XCD a contiguous run of tiles, and
-//     tiles run in groups of 8 tile-rows so concurrent tiles share A panels
-//     and B panels in the XCD's L2.
+//     tiles run in groups of 8 tile-rows so concurrent tiles share A and B
+//     panels in the XCD's L2.
 //   * Epilogue: per output, acc = 2^-32 S4; acc = fma(S3, 2^-24, acc);
 //     acc = fma(S2, 2^-16, acc); acc = fma(S1, 2^-8, acc); C = acc + S0.
 // Edges: rows of A beyond M and columns of B beyond N are clamped to valid
@@ -37,14 +40,32 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int KP = BK + 8;                      // LDS row pitch in BF16 elements (80 bytes)
-constexpr int NTHREADS = 512;
-constexpr int WAVES_N = 4;
-constexpr int WTM = 64, WTN = 32;               // wave tile
-constexpr int MI = WTM / 32, NI = WTN / 32;     // MFMA blocks per wave
-constexpr int TILE_ELEMS = (BM + BN) * KP;      // one component plane of A and B
+constexpr int BK = 32;
+constexpr int KP = BK + 8;          // LDS row pitch in BF16 elements (80 bytes)
+constexpr int KG = BK / 8;          // 8-wide k groups per row
 constexpr int GROUP_M = 8;
+
+template <int WAVES_M_, int WAVES_N_, int WTM_, int WTN_>
+struct Cfg {
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int WTM = WTM_, WTN = WTN_;
+    static constexpr int MI = WTM / 32, NI = WTN / 32;
+    static constexpr int BM = WAVES_M * WTM, BN = WAVES_N * WTN;
+    static constexpr int TILE = (BM + BN) * KP;                 // one component plane, A then B
+    static constexpr int A_CHUNKS = BM * KG / NT;               // 8-element chunks of A per thread
+    static constexpr int B_CHUNKS = BN * KG / NT;               // 8-element chunks of B per thread
+    // 2-column x 4-k chunks of K x N planes (one dword = two columns per row).
+    static constexpr int B_PAIRS = (BN / 2) * (BK / 4) / NT;
+    static constexpr int B_SLOTS = (B_CHUNKS > 2 * B_PAIRS) ? B_CHUNKS : 2 * B_PAIRS;
+    static_assert((BN / 2) * (BK / 4) % NT == 0, "K x N plane chunks not divisible among threads");
+    static_assert(BM * KG % NT == 0 && BN * KG % NT == 0, "tile not divisible among threads");
+    static_assert(NT % 16 == 0 && (BM % 16) == 0 && (BN % 16) == 0, "loader mapping");
+};
+
+using Cfg8 = Cfg<2, 4, 64, 32>;     // 8 waves, 2 per SIMD, 128 x 128 tile
+using Cfg4 = Cfg<2, 2, 64, 64>;     // 4 waves, 1 per SIMD, 128 x 128 tile
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -64,53 +85,55 @@ __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int &tm,
     tn = in / gm;
 }
 
-// ---------------------------------------------------------------- operand staging
-
-// 8 FP32 values of A's row `arow`, starting at column k (k is a multiple of 8).
-template <bool AVEC, bool TAIL>
-__device__ __forceinline__ void load_a8(const float *__restrict__ arow, int64_t k, int64_t K, float (&x)[8])
+// Chunk q of a tile side with `rows` rows (A: rows of A, B: columns of B) ->
+// (row, k group).  Within each 64-lane wave, 16 consecutive lanes take 16
+// consecutive rows of one k group, so both the global loads (4 lanes per
+// 128-byte row segment) and the 128-bit LDS writes (16 rows x 80 bytes) are
+// conflict-free.
+__device__ __forceinline__ void chunk_rc(int q, int &row, int &kg)
 {
-    if (AVEC && (!TAIL || k + 8 <= K)) {
-        const float4 *p = reinterpret_cast<const float4 *>(arow + k);
-        float4 v0 = p[0], v1 = p[1];
-        x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-        x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (!TAIL || k + e < K) ? arow[k + e] : 0.0f;
-    }
+    const int lane = q & 63, blk = q >> 6;
+    row = blk * 16 + (lane & 15);
+    kg = lane >> 4;
 }
 
-// 8 FP32 values of B's column: rows k .. k+7 (bcol points at row 0 of the column).
-template <bool TAIL>
-__device__ __forceinline__ void load_b8(const float *__restrict__ bcol, int64_t ldb, int64_t k, int64_t K,
-                                        float (&x)[8])
+// ---------------------------------------------------------------- global loads
+//
+// All global loads are raw buffer loads.  Each K step gets fresh buffer
+// descriptors (wave-uniform, so they live in scalar registers and are rebased
+// with scalar adds) whose base sits at the step's first row / column, so the
+// per-thread offsets are small 32-bit values shared across the three B planes.
+// Descriptor sizes end at the last element the step may touch, so a stray
+// offset reads zero instead of leaving the operand; the K tail is still masked
+// explicitly (the scalar offset is not part of the hardware range check).
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_WORD3 = 0x00020000;   // raw, untyped buffer on gfx9-family GPUs
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
 {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (!TAIL || k + e < K) ? bcol[(k + e) * ldb] : 0.0f;
+    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, RSRC_WORD3);
 }
 
-// 8 BF16 values of one column of each B plane, packed two per dword along k.
-template <bool TAIL>
-__device__ __forceinline__ void load_b8_planes(const uint16_t *__restrict__ b0, const uint16_t *__restrict__ b1,
-                                               const uint16_t *__restrict__ b2, int64_t ldb, int64_t k, int64_t K,
-                                               uint32_t (&p0)[4], uint32_t (&p1)[4], uint32_t (&p2)[4])
+__device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off, uint32_t soff)
 {
-    uint32_t h0[8], h1[8], h2[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const bool ok = !TAIL || k + e < K;
-        const int64_t o = (k + e) * ldb;
-        h0[e] = ok ? b0[o] : 0u;
-        h1[e] = ok ? b1[o] : 0u;
-        h2[e] = ok ? b2[o] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        p0[i] = h0[2 * i] | (h0[2 * i + 1] << 16);
-        p1[i] = h1[2 * i] | (h1[2 * i + 1] << 16);
-        p2[i] = h2[2 * i] | (h2[2 * i + 1] << 16);
-    }
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, (int)soff, 0));
+}
+
+__device__ __forceinline__ uint32_t bload_u32(rsrc_t r, uint32_t off, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, (int)soff, 0);
+}
+
+__device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t off, uint32_t soff)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, (int)soff, 0);
+}
+
+__device__ __forceinline__ u32x4_t bload_u32x4(rsrc_t r, uint32_t off, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0);
 }
 
 __device__ __forceinline__ void st_lds16(uint16_t *p, const uint32_t (&v)[4])
@@ -118,42 +141,10 @@ __device__ __forceinline__ void st_lds16(uint16_t *p, const uint32_t (&v)[4])
     *reinterpret_cast<u32x4_t *>(p) = u32x4_t{v[0], v[1], v[2], v[3]};
 }
 
-// Registers holding one thread's share of the next K step.
-template <int BSRC>
-struct Stage {
-    float a[8];
-    float b[8];                 // B_FP32
-    uint32_t bp[3][4];          // B_PLANES
-};
-
-template <bool AVEC, int BSRC, bool TAIL>
-__device__ __forceinline__ void load_stage(Stage<BSRC> &st, const GemmArgs &g, const float *arow,
-                                           const float *bcol, const uint16_t *bc0, const uint16_t *bc1,
-                                           const uint16_t *bc2, int64_t ka, int64_t kb)
+__device__ __forceinline__ void st_lds8(uint16_t *p, const uint32_t (&v)[2])
 {
-    load_a8<AVEC, TAIL>(arow, ka, g.K, st.a);
-    if constexpr (BSRC == B_FP32) load_b8<TAIL>(bcol, g.ldb, kb, g.K, st.b);
-    else load_b8_planes<TAIL>(bc0, bc1, bc2, g.ldb, kb, g.K, st.bp[0], st.bp[1], st.bp[2]);
-}
-
-template <int BSRC>
-__device__ __forceinline__ void store_stage(const Stage<BSRC> &st, uint16_t *buf, int a_off, int b_off)
-{
-    uint32_t p0[4], p1[4], p2[4];
-    split8_packed(st.a, p0, p1, p2);
-    st_lds16(buf + 0 * TILE_ELEMS + a_off, p0);
-    st_lds16(buf + 1 * TILE_ELEMS + a_off, p1);
-    st_lds16(buf + 2 * TILE_ELEMS + a_off, p2);
-    if constexpr (BSRC == B_FP32) {
-        split8_packed(st.b, p0, p1, p2);
-        st_lds16(buf + 0 * TILE_ELEMS + b_off, p0);
-        st_lds16(buf + 1 * TILE_ELEMS + b_off, p1);
-        st_lds16(buf + 2 * TILE_ELEMS + b_off, p2);
-    } else {
-        st_lds16(buf + 0 * TILE_ELEMS + b_off, st.bp[0]);
-        st_lds16(buf + 1 * TILE_ELEMS + b_off, st.bp[1]);
-        st_lds16(buf + 2 * TILE_ELEMS + b_off, st.bp[2]);
-    }
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2_t *>(p) = u32x2_t{v[0], v[1]};
 }
 
 __device__ __forceinline__ bf16x8_t ld_frag(const uint16_t *p)
@@ -161,77 +152,267 @@ __device__ __forceinline__ bf16x8_t ld_frag(const uint16_t *p)
     return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(p));
 }
 
+// ---------------------------------------------------------------- staging
+
+// One thread's share of one K step, held in registers between load and store.
+template <class C, int BSRC>
+struct Stage {
+    float a[C::A_CHUNKS][8];
+    float b[BSRC == B_FP32 ? C::B_CHUNKS : 1][8];
+    uint32_t bn[BSRC == B_PLANES_NK ? C::B_CHUNKS : 1][3][4];
+    uint32_t bk[BSRC == B_PLANES_KN ? C::B_PAIRS : 1][3][2][2];
+};
+
+// Per-thread byte offsets (relative to the step's descriptor bases) and LDS
+// offsets, fixed for the whole tile.
+template <class C, int BSRC>
+struct Roles {
+    uint32_t a_off[C::A_CHUNKS];
+    int a_lds[C::A_CHUNKS], a_kg[C::A_CHUNKS];
+    uint32_t b_off[C::B_SLOTS];
+    int b_lds[C::B_SLOTS], b_kg[C::B_SLOTS];
+    bool b_second_ok[C::B_PAIRS];
+};
+
+template <class C, int BSRC, bool BVEC>
+__device__ __forceinline__ void make_roles(Roles<C, BSRC> &R, const GemmArgs &g, int64_t m0, int64_t n0)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        int row, kg;
+        chunk_rc(c * C::NT + tid, row, kg);
+        // rows past M re-read row M-1 (valid memory); their results are not stored
+        const int64_t r = lmin(m0 + row, g.M - 1) - m0;
+        R.a_off[c] = (uint32_t)((r * g.lda + kg * 8) * 4);
+        R.a_lds[c] = row * KP + kg * 8;
+        R.a_kg[c] = kg;
+    }
+    if constexpr (BSRC == B_FP32) {
+        // thread -> (column, 8-wide k group): lanes run along n for coalesced loads.
+#pragma unroll
+        for (int c = 0; c < C::B_CHUNKS; ++c) {
+            const int q = c * C::NT + tid, col = q % C::BN, kg = q / C::BN;
+            const int64_t n = lmin(n0 + col, g.N - 1);
+            R.b_off[c] = (uint32_t)(((int64_t)kg * 8 * g.ldb + n) * 4);
+            R.b_lds[c] = (C::BM + col) * KP + kg * 8;
+            R.b_kg[c] = kg;
+        }
+    } else if constexpr (BSRC == B_PLANES_NK) {
+#pragma unroll
+        for (int c = 0; c < C::B_CHUNKS; ++c) {
+            int col, kg;
+            chunk_rc(c * C::NT + tid, col, kg);
+            const int64_t n = lmin(n0 + col, g.N - 1) - n0;
+            R.b_off[c] = (uint32_t)((n * g.ldb + kg * 8) * 2);
+            R.b_lds[c] = (C::BM + col) * KP + kg * 8;
+            R.b_kg[c] = kg;
+        }
+    } else {
+        // thread -> (column pair, 4-wide k group): lanes run along n.
+#pragma unroll
+        for (int c = 0; c < C::B_PAIRS; ++c) {
+            const int q = c * C::NT + tid, pair = q % (C::BN / 2), kq = q / (C::BN / 2);
+            const int64_t n = n0 + 2 * pair;
+            // Clamp to valid memory; columns past N are discarded at the store.
+            // With dword loads (N even) the pair must start on an even column.
+            const int64_t nc = BVEC ? lmin(n, (g.N - 1) & ~(int64_t)1) : lmin(n, g.N - 1);
+            R.b_off[c] = (uint32_t)(((int64_t)kq * 4 * g.ldb + nc) * 2);
+            R.b_second_ok[c] = nc + 1 < g.N;
+            R.b_lds[2 * c] = (C::BM + 2 * pair) * KP + kq * 4;
+            R.b_lds[2 * c + 1] = (C::BM + 2 * pair + 1) * KP + kq * 4;
+            R.b_kg[2 * c] = kq;
+            R.b_kg[2 * c + 1] = kq;
+        }
+    }
+}
+
+// Load the K step starting at k0 into registers.
+template <class C, int BSRC, bool AVEC, bool BVEC, bool TAIL>
+__device__ __forceinline__ void load_stage(Stage<C, BSRC> &st, const Roles<C, BSRC> &R, const GemmArgs &g,
+                                           int64_t m0, int64_t n0, int64_t k0)
+{
+    // A: base at (m0, k0); covers the tile's rows.
+    {
+        const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
+        const rsrc_t ra = make_rsrc(g.A + m0 * g.lda + k0, ((rows - 1) * g.lda + (g.K - k0)) * 4);
+#pragma unroll
+        for (int c = 0; c < C::A_CHUNKS; ++c) {
+            const int64_t k = k0 + R.a_kg[c] * 8;
+            float(&x)[8] = st.a[c];
+            if (AVEC && (!TAIL || k + 8 <= g.K)) {
+                const u32x4_t v0 = bload_u32x4(ra, R.a_off[c], 0);
+                const u32x4_t v1 = bload_u32x4(ra, R.a_off[c] + 16, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { x[e] = __uint_as_float(v0[e]); x[4 + e] = __uint_as_float(v1[e]); }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (!TAIL || k + e < g.K) ? bload_f32(ra, R.a_off[c] + 4 * e, 0) : 0.0f;
+            }
+        }
+    }
+    if constexpr (BSRC == B_FP32) {
+        // base at row k0; the row within the 8-row group goes in the scalar offset
+        const rsrc_t rb = make_rsrc(g.B + k0 * g.ldb, ((g.K - 1 - k0) * g.ldb + g.N) * 4);
+        const uint32_t row_bytes = (uint32_t)(g.ldb * 4);
+#pragma unroll
+        for (int c = 0; c < C::B_CHUNKS; ++c) {
+            const int64_t k = k0 + R.b_kg[c] * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                st.b[c][e] = (!TAIL || k + e < g.K) ? bload_f32(rb, R.b_off[c], e * row_bytes) : 0.0f;
+        }
+    } else if constexpr (BSRC == B_PLANES_NK) {
+        // base at (n0, k0); k past K is masked per element
+        const int64_t cols = lmin((int64_t)C::BN, g.N - n0);
+        const int64_t bytes = ((cols - 1) * g.ldb + (g.K - k0)) * 2;
+        const int64_t base = n0 * g.ldb + k0;
+        const rsrc_t r0 = make_rsrc(g.B0 + base, bytes), r1 = make_rsrc(g.B1 + base, bytes),
+                     r2 = make_rsrc(g.B2 + base, bytes);
+#pragma unroll
+        for (int c = 0; c < C::B_CHUNKS; ++c) {
+            const int64_t k = k0 + R.b_kg[c] * 8;
+            if (BVEC && (!TAIL || k + 8 <= g.K)) {
+                const u32x4_t v0 = bload_u32x4(r0, R.b_off[c], 0), v1 = bload_u32x4(r1, R.b_off[c], 0),
+                              v2 = bload_u32x4(r2, R.b_off[c], 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { st.bn[c][0][i] = v0[i]; st.bn[c][1][i] = v1[i]; st.bn[c][2][i] = v2[i]; }
+            } else {
+                const rsrc_t rr[3] = {r0, r1, r2};
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t lo = (!TAIL || k + 2 * i < g.K) ? bload_u16(rr[p], R.b_off[c] + 4 * i, 0) : 0u;
+                        const uint32_t hi = (!TAIL || k + 2 * i + 1 < g.K) ? bload_u16(rr[p], R.b_off[c] + 4 * i + 2, 0) : 0u;
+                        st.bn[c][p][i] = lo | (hi << 16);
+                    }
+            }
+        }
+    } else {
+        // base at row k0; the row within the 4-row group goes in the scalar offset
+        const int64_t bytes = ((g.K - 1 - k0) * g.ldb + g.N) * 2;
+        const rsrc_t rr[3] = {make_rsrc(g.B0 + k0 * g.ldb, bytes), make_rsrc(g.B1 + k0 * g.ldb, bytes),
+                              make_rsrc(g.B2 + k0 * g.ldb, bytes)};
+        const uint32_t row_bytes = (uint32_t)(g.ldb * 2);
+#pragma unroll
+        for (int c = 0; c < C::B_PAIRS; ++c) {
+            const int64_t k = k0 + R.b_kg[2 * c] * 4;
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                uint32_t r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (TAIL && k + e >= g.K) {
+                        r[e] = 0u;
+                    } else if (BVEC) {
+                        r[e] = bload_u32(rr[p], R.b_off[c], e * row_bytes);
+                    } else {
+                        const uint32_t lo = bload_u16(rr[p], R.b_off[c], e * row_bytes);
+                        const uint32_t hi = R.b_second_ok[c] ? bload_u16(rr[p], R.b_off[c] + 2, e * row_bytes) : 0u;
+                        r[e] = lo | (hi << 16);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    st.bk[c][p][0][i] = __builtin_amdgcn_perm(r[2 * i + 1], r[2 * i], 0x05040100u);  // column n
+                    st.bk[c][p][1][i] = __builtin_amdgcn_perm(r[2 * i + 1], r[2 * i], 0x07060302u);  // column n+1
+                }
+            }
+        }
+    }
+}
+
+template <class C, int BSRC>
+__device__ __forceinline__ void store_stage(const Stage<C, BSRC> &st, const Roles<C, BSRC> &R, uint16_t *buf)
+{
+    uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        split8_packed(st.a[c], p0, p1, p2);
+        st_lds16(buf + 0 * C::TILE + R.a_lds[c], p0);
+        st_lds16(buf + 1 * C::TILE + R.a_lds[c], p1);
+        st_lds16(buf + 2 * C::TILE + R.a_lds[c], p2);
+    }
+    if constexpr (BSRC == B_FP32) {
+#pragma unroll
+        for (int c = 0; c < C::B_CHUNKS; ++c) {
+            split8_packed(st.b[c], p0, p1, p2);
+            st_lds16(buf + 0 * C::TILE + R.b_lds[c], p0);
+            st_lds16(buf + 1 * C::TILE + R.b_lds[c], p1);
+            st_lds16(buf + 2 * C::TILE + R.b_lds[c], p2);
+        }
+    } else if constexpr (BSRC == B_PLANES_NK) {
+#pragma unroll
+        for (int c = 0; c < C::B_CHUNKS; ++c)
+#pragma unroll
+            for (int p = 0; p < 3; ++p) st_lds16(buf + p * C::TILE + R.b_lds[c], st.bn[c][p]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < C::B_PAIRS; ++c)
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                st_lds8(buf + p * C::TILE + R.b_lds[2 * c], st.bk[c][p][0]);
+                st_lds8(buf + p * C::TILE + R.b_lds[2 * c + 1], st.bk[c][p][1]);
+            }
+    }
+}
+
 // ---------------------------------------------------------------- kernel
 
-template <int NB, bool AVEC, int BSRC>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16x9_kernel(GemmArgs g)
+template <class C, int NB, bool AVEC, int BSRC, bool BVEC>
+__global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * TILE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * C::TILE];
 
     int tm, tn;
     tile_of_block(g.tiles_m, g.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-
-    // Loader roles.  A: wave w stages rows 16w..16w+15; lane -> (row, 8-wide k group).
-    const int a_row = wave * 16 + (lane & 15), a_kg = lane >> 4;
-    // B: thread -> (column, 8-wide k group).
-    const int b_col = tid & (BN - 1), b_kg = tid >> 7;
-    const int a_off = a_row * KP + a_kg * 8;
-    const int b_off = (BM + b_col) * KP + b_kg * 8;
-
-    const float *arow = g.A + lmin(m0 + a_row, g.M - 1) * g.lda;
-    const int64_t bj = lmin(n0 + b_col, g.N - 1);
-    const float *bcol = (BSRC == B_FP32) ? g.B + bj : nullptr;
-    const uint16_t *bc0 = (BSRC == B_PLANES) ? g.B0 + bj : nullptr;
-    const uint16_t *bc1 = (BSRC == B_PLANES) ? g.B1 + bj : nullptr;
-    const uint16_t *bc2 = (BSRC == B_PLANES) ? g.B2 + bj : nullptr;
-
-    // Compute roles: wave (wm, wn) owns rows wm*64.., columns wn*32..
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
 
-    f32x16_t acc[MI][NB];
+    Roles<C, BSRC> R;
+    make_roles<C, BSRC, BVEC>(R, g, m0, n0);
+
+    f32x16_t acc[C::MI][C::NI][NB];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-        for (int s = 0; s < NB; ++s) acc[i][s] = f32x16_t{};
+        for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int s = 0; s < NB; ++s) acc[i][j][s] = f32x16_t{};
 
     const int64_t nk = (g.K + BK - 1) / BK;
     const bool k_ragged = (g.K % BK) != 0;
 
-    Stage<BSRC> st;
-    if (nk == 1 && k_ragged)
-        load_stage<AVEC, BSRC, true>(st, g, arow, bcol, bc0, bc1, bc2, a_kg * 8, b_kg * 8);
-    else
-        load_stage<AVEC, BSRC, false>(st, g, arow, bcol, bc0, bc1, bc2, a_kg * 8, b_kg * 8);
-    store_stage<BSRC>(st, lds, a_off, b_off);
+    Stage<C, BSRC> st;
+    if (nk == 1 && k_ragged) load_stage<C, BSRC, AVEC, BVEC, true>(st, R, g, m0, n0, 0);
+    else load_stage<C, BSRC, AVEC, BVEC, false>(st, R, g, m0, n0, 0);
+    store_stage<C, BSRC>(st, R, lds);
     __syncthreads();
 
     for (int64_t kt = 0; kt < nk; ++kt) {
-        uint16_t *cur = lds + (kt & 1) * 3 * TILE_ELEMS;
-        uint16_t *nxt = lds + ((kt + 1) & 1) * 3 * TILE_ELEMS;
+        const uint16_t *cur = lds + (kt & 1) * 3 * C::TILE;
+        uint16_t *nxt = lds + ((kt + 1) & 1) * 3 * C::TILE;
         const bool have_next = kt + 1 < nk;
         if (have_next) {
-            const int64_t k0 = (kt + 1) * BK;
-            if (kt + 2 == nk && k_ragged)
-                load_stage<AVEC, BSRC, true>(st, g, arow, bcol, bc0, bc1, bc2, k0 + a_kg * 8, k0 + b_kg * 8);
-            else
-                load_stage<AVEC, BSRC, false>(st, g, arow, bcol, bc0, bc1, bc2, k0 + a_kg * 8, k0 + b_kg * 8);
+            if (kt + 2 == nk && k_ragged) load_stage<C, BSRC, AVEC, BVEC, true>(st, R, g, m0, n0, (kt + 1) * BK);
+            else load_stage<C, BSRC, AVEC, BVEC, false>(st, R, g, m0, n0, (kt + 1) * BK);
         }
 
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 16) {
-            bf16x8_t af[MI][3], bfr[NI][3];
+            bf16x8_t af[C::MI][3], bfr[C::NI][3];
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    af[i][c] = ld_frag(cur + c * TILE_ELEMS + (wm * WTM + i * 32 + frag_row) * KP + kk + frag_k);
+                for (int i = 0; i < C::MI; ++i)
+                    af[i][c] = ld_frag(cur + c * C::TILE + (wm * C::WTM + i * 32 + frag_row) * KP + kk + frag_k);
 #pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    bfr[j][c] = ld_frag(cur + c * TILE_ELEMS + (BM + wn * WTN + j * 32 + frag_row) * KP + kk + frag_k);
+                for (int j = 0; j < C::NI; ++j)
+                    bfr[j][c] = ld_frag(cur + c * C::TILE + (C::BM + wn * C::WTN + j * 32 + frag_row) * KP + kk +
+                                        frag_k);
             }
 #pragma unroll
             for (int p = 0; p < 3; ++p)
@@ -239,32 +420,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16x9_kernel(GemmArgs g)
                 for (int q = 0; q < 3; ++q) {
                     if (p + q < NB) {
 #pragma unroll
-                        for (int i = 0; i < MI; ++i)
-                            acc[i][p + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][p], bfr[0][q],
-                                                                                     acc[i][p + q], 0, 0, 0);
+                        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+                            for (int j = 0; j < C::NI; ++j)
+                                acc[i][j][p + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    af[i][p], bfr[j][q], acc[i][j][p + q], 0, 0, 0);
                     }
                 }
         }
 
-        if (have_next) store_stage<BSRC>(st, nxt, a_off, b_off);
+        if (have_next) store_stage<C, BSRC>(st, R, nxt);
         __syncthreads();
     }
 
     // Epilogue: recombine the bands smallest first and store.
-    const int col = (int)(n0 + wn * WTN + (lane & 31));
-    const bool col_ok = col < g.N;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int j = 0; j < C::NI; ++j) {
+        const int64_t col = n0 + wn * C::WTN + j * 32 + (lane & 31);
+        const bool col_ok = col < g.N;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            float v = 0.0f;
-            if constexpr (NB >= 5) v = 0x1p-32f * acc[i][4][r];
-            if constexpr (NB >= 4) v = __builtin_fmaf(acc[i][3][r], 0x1p-24f, v);
-            if constexpr (NB >= 3) v = __builtin_fmaf(acc[i][2][r], 0x1p-16f, v);
-            if constexpr (NB >= 2) v = __builtin_fmaf(acc[i][1][r], 0x1p-8f, v);
-            v = v + acc[i][0][r];
-            if (col_ok && row < g.M) g.C[row * g.ldc + col] = v;
+        for (int i = 0; i < C::MI; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * C::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                float v = 0.0f;
+                if constexpr (NB >= 5) v = 0x1p-32f * acc[i][j][4][r];
+                if constexpr (NB >= 4) v = __builtin_fmaf(acc[i][j][3][r], 0x1p-24f, v);
+                if constexpr (NB >= 3) v = __builtin_fmaf(acc[i][j][2][r], 0x1p-16f, v);
+                if constexpr (NB >= 2) v = __builtin_fmaf(acc[i][j][1][r], 0x1p-8f, v);
+                v = v + acc[i][j][0][r];
+                if (col_ok && row < g.M) g.C[row * g.ldc + col] = v;
+            }
         }
     }
 }
@@ -291,37 +477,54 @@ hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, int num_cus,
 
 // ---------------------------------------------------------------- dispatch
 
-template <int NB, int BSRC>
-static void launch_nb(const GemmArgs &g, bool avec, dim3 grid, hipStream_t stream)
+template <class C, int NB, int BSRC>
+static void launch_cfg(const GemmArgs &g, bool avec, bool bvec, hipStream_t stream)
 {
-    if (avec)
-        hipLaunchKernelGGL((gemm_bf16x9_kernel<NB, true, BSRC>), grid, dim3(NTHREADS), 0, stream, g);
-    else
-        hipLaunchKernelGGL((gemm_bf16x9_kernel<NB, false, BSRC>), grid, dim3(NTHREADS), 0, stream, g);
+    const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n)), block(C::NT);
+    if (avec) {
+        if (bvec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, true>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, false>), grid, block, 0, stream, g);
+    } else {
+        if (bvec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, true>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, false>), grid, block, 0, stream, g);
+    }
 }
 
-template <int BSRC>
-static void launch_bsrc(const GemmArgs &g, int nbands, bool avec, dim3 grid, hipStream_t stream)
+template <class C, int BSRC>
+static void launch_nb(const GemmArgs &g, int nbands, bool avec, bool bvec, hipStream_t stream)
 {
     switch (nbands) {
-    case 1: launch_nb<1, BSRC>(g, avec, grid, stream); break;
-    case 2: launch_nb<2, BSRC>(g, avec, grid, stream); break;
-    case 3: launch_nb<3, BSRC>(g, avec, grid, stream); break;
-    case 4: launch_nb<4, BSRC>(g, avec, grid, stream); break;
-    default: launch_nb<5, BSRC>(g, avec, grid, stream); break;
+    case 1: launch_cfg<C, 1, BSRC>(g, avec, bvec, stream); break;
+    case 2: launch_cfg<C, 2, BSRC>(g, avec, bvec, stream); break;
+    case 3: launch_cfg<C, 3, BSRC>(g, avec, bvec, stream); break;
+    case 4: launch_cfg<C, 4, BSRC>(g, avec, bvec, stream); break;
+    default: launch_cfg<C, 5, BSRC>(g, avec, bvec, stream); break;
     }
+}
+
+template <class C>
+static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream)
+{
+    GemmArgs g = args;
+    g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
+    g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
+    const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0);
+    bool bvec = false;
+    if (bsrc == B_PLANES_NK)
+        bvec = aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && (g.ldb % 8 == 0);
+    else if (bsrc == B_PLANES_KN)
+        bvec = aligned(g.B0, 4) && aligned(g.B1, 4) && aligned(g.B2, 4) && (g.ldb % 2 == 0) && (g.N % 2 == 0);
+    switch (bsrc) {
+    case B_FP32: launch_nb<C, B_FP32>(g, nbands, avec, false, stream); break;
+    case B_PLANES_NK: launch_nb<C, B_PLANES_NK>(g, nbands, avec, bvec, stream); break;
+    default: launch_nb<C, B_PLANES_KN>(g, nbands, avec, bvec, stream); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream)
 {
-    GemmArgs g = args;
-    g.tiles_m = (int)((g.M + BM - 1) / BM);
-    g.tiles_n = (int)((g.N + BN - 1) / BN);
-    const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n));
-    const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0);
-    if (bsrc == B_FP32) launch_bsrc<B_FP32>(g, nbands, avec, grid, stream);
-    else launch_bsrc<B_PLANES>(g, nbands, avec, grid, stream);
-    return hipGetLastError();
+    return launch_with<Cfg8>(args, nbands, bsrc, stream);
 }
 
 }  // namespace sgemm_emu_dev

@@ -9,7 +9,11 @@ namespace sgemm_emu_dev {
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // B operand source of the GEMM kernel.
-enum BSource { B_FP32 = 0, B_PLANES = 1 };
+enum BSource {
+    B_FP32 = 0,        // FP32 K x N, split inside the GEMM
+    B_PLANES_KN = 1,   // three BF16 planes, K x N row-major
+    B_PLANES_NK = 2    // three BF16 planes, N x K row-major (B transposed, k contiguous)
+};
 
 struct GemmArgs {
     int64_t M, N, K;
@@ -23,6 +27,7 @@ struct GemmArgs {
     float *C;
     int64_t ldc;
     int tiles_m, tiles_n;
+    int variant;             // kernel configuration (0: 8 waves 64x32, 1: 4 waves 64x64)
 };
 
 hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,

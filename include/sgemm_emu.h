@@ -40,6 +40,8 @@
  *   Float pointers must be 4-byte aligned, BF16 plane pointers 2-byte aligned.
  *   16-byte aligned A with lda % 4 == 0 takes the vector-load path; any other
  *   layout takes a scalar-load path with the same arithmetic.
+ *   Leading dimensions are limited to 8,388,544 elements (32-bit offsets
+ *   inside a 128-row tile); larger ones give SGEMM_EMU_EINVAL.
  *   M == 0 or N == 0: nothing is done.  K == 0: C is set to zero.
  *   C must not overlap A or B (not checked).
  *   Column-major callers compute C^T = B^T A^T by swapping the operands.
@@ -91,16 +93,26 @@ int sgemm_emu(int64_t M, int64_t N, int64_t K,
               float *C, int64_t ldc,
               int nbands, sgemm_emu_stream_t stream);
 
+/* Layouts of pre-split B planes (sgemm_emu_presplit_b). */
+enum sgemm_emu_b_layout {
+    SGEMM_EMU_B_KN = 0,  /* planes are K x N row-major: B0[k*ldb + j], as split_f32_bf16x3(B) gives */
+    SGEMM_EMU_B_NK = 1   /* planes are N x K row-major: B0[j*ldb + k], as split_f32_bf16x3(B^T) gives,
+                            e.g. from a linear layer's weight stored [out_features][in_features] */
+};
+
 /*
  * sgemm_emu_presplit_b -- as sgemm_emu, with B already split into its three
  * BF16 component planes by split_f32_bf16x3 (for weights split once and reused,
- * as the linear layers of an interatomic potential do).  B0, B1, B2 are K x N
- * row-major uint16 BF16 bit patterns with leading dimension ldb >= max(1, N).
- * A is split inside the kernel.  The result equals sgemm_emu on the FP32 B.
+ * as the linear layers of an interatomic potential do).  B0, B1, B2 are uint16
+ * BF16 bit patterns in the layout given by b_layout, with leading dimension
+ * ldb >= max(1, N) for SGEMM_EMU_B_KN and ldb >= max(1, K) for SGEMM_EMU_B_NK.
+ * A is split inside the kernel.  The result equals sgemm_emu on the FP32 B
+ * bit for bit.  An unknown b_layout gives SGEMM_EMU_EINVAL.
  */
 int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
                          const float *A, int64_t lda,
                          const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb,
+                         int b_layout,
                          float *C, int64_t ldc,
                          int nbands, sgemm_emu_stream_t stream);
 

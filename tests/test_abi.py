@@ -72,13 +72,15 @@ def test_sgemm_validation_before_any_hip_call(L, args, status):
 @pytest.mark.parametrize("nbands", [0, 6, -3])
 def test_bad_nbands(L, nbands):
     assert L.sgemm_emu(4, 4, 4, P, 4, P, 4, P, 4, nbands, None) == -1
-    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, P, P, 4, P, 4, nbands, None) == -1
+    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, P, P, 4, 0, P, 4, nbands, None) == -1
 
 
 def test_presplit_validation(L):
-    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, 0, P, 4, P, 4, 5, None) == -2
-    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P + 1, P, P, 4, P, 4, 5, None) == -1
-    assert L.sgemm_emu_presplit_b(4, 8, 4, P, 4, P, P, P, 7, P, 8, 5, None) == -1
+    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, 0, P, 4, 0, P, 4, 5, None) == -2
+    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P + 1, P, P, 4, 0, P, 4, 5, None) == -1
+    assert L.sgemm_emu_presplit_b(4, 8, 4, P, 4, P, P, P, 7, 0, P, 8, 5, None) == -1   # K x N: ldb < N
+    assert L.sgemm_emu_presplit_b(4, 8, 6, P, 6, P, P, P, 5, 1, P, 8, 5, None) == -1   # N x K: ldb < K
+    assert L.sgemm_emu_presplit_b(4, 8, 4, P, 4, P, P, P, 8, 2, P, 8, 5, None) == -1   # unknown layout
 
 
 def test_split_validation(L):

@@ -28,7 +28,7 @@ def gpu_gemm(fe, Ad, Bd, M, N, K, nbands=5, presplit=False):
     if presplit:
         planes = [torch.empty((K, N), dtype=torch.int16, device="cuda") for _ in range(3)]
         fe.split_f32_bf16x3(K, N, Bd, N, *planes, N)
-        fe.sgemm_emu_presplit_b(M, N, K, Ad, K, *planes, N, Cd, N, nbands)
+        fe.sgemm_emu_presplit_b(M, N, K, Ad, K, *planes, N, fe.SGEMM_EMU_B_KN, Cd, N, nbands)
     elif nbands == 5:
         fe.sgemm_bf16x9(M, N, K, Ad, K, Bd, N, Cd, N)
     else:

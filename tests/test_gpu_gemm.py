@@ -44,7 +44,12 @@ def run(fe, A, B, nbands=5, entry="fused", ldc_pad=0, a_offset=0):
     if entry == "presplit":
         planes = [torch.empty(max(K * N, 1), dtype=torch.int16, device="cuda") for _ in range(3)]
         fe.split_f32_bf16x3(K, N, Bd, max(N, 1), *planes, max(N, 1))
-        fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, max(N, 1), Cd, max(ldc, 1), nbands)
+        fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, max(N, 1), fe.SGEMM_EMU_B_KN, Cd, max(ldc, 1), nbands)
+    elif entry == "presplit_t":
+        Bt = dev(np.ascontiguousarray(B.T))
+        planes = [torch.empty(max(K * N, 1), dtype=torch.int16, device="cuda") for _ in range(3)]
+        fe.split_f32_bf16x3(N, K, Bt, max(K, 1), *planes, max(K, 1))
+        fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, max(K, 1), fe.SGEMM_EMU_B_NK, Cd, max(ldc, 1), nbands)
     elif nbands == 5 and entry == "fused":
         fe.sgemm_bf16x9(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1))
     else:
@@ -60,7 +65,7 @@ SHAPES = [(1, 1, 1), (7, 13, 5), (128, 128, 32), (129, 130, 33), (64, 300, 17), 
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("entry", ["fused", "presplit"])
+@pytest.mark.parametrize("entry", ["fused", "presplit", "presplit_t"])
 def test_random_shapes_within_bound(fe, shape, entry):
     M, N, K = shape
     g = _rng(M * 7919 + N * 31 + K)
@@ -75,8 +80,9 @@ def test_presplit_equals_fused_bitwise(fe):
     A = g.standard_normal((200, 150)).astype(np.float32)
     B = g.standard_normal((150, 190)).astype(np.float32)
     for nb in (1, 3, 5):
-        assert np.array_equal(run(fe, A, B, nb, "fused").view(np.uint32),
-                              run(fe, A, B, nb, "presplit").view(np.uint32))
+        ref = run(fe, A, B, nb, "fused").view(np.uint32)
+        assert np.array_equal(ref, run(fe, A, B, nb, "presplit").view(np.uint32))
+        assert np.array_equal(ref, run(fe, A, B, nb, "presplit_t").view(np.uint32))
 
 
 def test_unaligned_a_and_padded_c(fe):
@@ -97,7 +103,7 @@ def _full24(g, shape):
     return (s * np.ldexp(m.astype(np.float64), g.integers(-20, 20, size=shape) - 23)).astype(np.float32)
 
 
-@pytest.mark.parametrize("entry", ["fused", "presplit"])
+@pytest.mark.parametrize("entry", ["fused", "presplit", "presplit_t"])
 def test_identity_and_scaled_permutation_exact(fe, entry):
     g = _rng(7)
     n = 160
