@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip torch.matmul / fused-B context timings")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="for HBM counter runs: two steps, then one plain 512 MiB device copy whose "
+                        "FETCH/WRITE counts calibrate the counters; prints no JSON line")
     return p.parse_args()
 
 
@@ -75,29 +78,43 @@ def main():
     Hd = torch.from_numpy(H).to(dev)
     W1d = torch.from_numpy(W1).to(dev)
     W2d = torch.from_numpy(W2).to(dev)
+    # The weights as a linear layer stores them, [out_features][in_features].
+    W1t = W1d.t().contiguous()
+    W2t = W2d.t().contiguous()
     C1 = torch.empty((M, F), dtype=torch.float32, device=dev)
     C2 = torch.empty((M, D), dtype=torch.float32, device=dev)
-    P1 = [torch.empty((D, F), dtype=torch.int16, device=dev) for _ in range(3)]
-    P2 = [torch.empty((F, D), dtype=torch.int16, device=dev) for _ in range(3)]
+    P1 = [torch.empty((F, D), dtype=torch.int16, device=dev) for _ in range(3)]
+    P2 = [torch.empty((D, F), dtype=torch.int16, device=dev) for _ in range(3)]
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
     ev = []
 
     def step(record):
-        fe.split_f32_bf16x3(D, F, W1d, F, *P1, F, sp)
-        fe.split_f32_bf16x3(F, D, W2d, D, *P2, D, sp)
+        fe.split_f32_bf16x3(F, D, W1t, D, *P1, D, sp)
+        fe.split_f32_bf16x3(D, F, W2t, F, *P2, F, sp)
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record(stream)
-        fe.sgemm_emu_presplit_b(M, F, D, Xd, D, *P1, F, fe.SGEMM_EMU_B_KN, C1, F, 5, sp)
+        fe.sgemm_emu_presplit_b(M, F, D, Xd, D, *P1, D, fe.SGEMM_EMU_B_NK, C1, F, 5, sp)
         if record:
             e[1].record(stream)
             e[2].record(stream)
-        fe.sgemm_emu_presplit_b(M, D, F, Hd, F, *P2, D, fe.SGEMM_EMU_B_KN, C2, D, 5, sp)
+        fe.sgemm_emu_presplit_b(M, D, F, Hd, F, *P2, F, fe.SGEMM_EMU_B_NK, C2, D, 5, sp)
         if record:
             e[3].record(stream)
             ev.append(e)
+
+    if args.traffic_probe:
+        for _ in range(2):
+            step(False)
+        src = torch.empty(128 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)          # the calibration kernel: reads and writes exactly 512 MiB
+        torch.cuda.synchronize()
+        log("traffic probe done: 2 steps, then a 536870912-byte copy")
+        return
 
     for _ in range(args.warmup):
         step(False)
@@ -152,8 +169,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "pet_large: X[552960x256] @ W1[256x1024] and H[552960x1024] @ W2[1024x256] "
-                        "(17280 atoms x 32 tokens), weights split once per step, all nine products",
-            "M": M, "d": D, "ffn": F, "nbands": 5, "entry": "split_f32_bf16x3 + sgemm_emu_presplit_b",
+                        "(17280 atoms x 32 tokens), weights held [out][in] and split once per step, "
+                        "all nine products",
+            "M": M, "d": D, "ffn": F, "nbands": 5,
+            "entry": "split_f32_bf16x3 + sgemm_emu_presplit_b(SGEMM_EMU_B_NK)",
         },
         "pct_bf16_peak_9products": round(100.0 * value * 9 / MI355X_BF16_DENSE_TFLOPS, 2),
         "pct_fp32_vector_peak": round(100.0 * value / MI355X_FP32_VECTOR_TFLOPS, 2),
@@ -165,7 +184,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
             "traffic": None,
-            "kernel": "gemm_bf16x9_kernel<5, A vector loads, B planes>",
+            "kernel": "gemm_bf16x9_kernel<Cfg<2,4,64,32,sched>, 5 bands, A vector loads, N x K planes>",
             "flops_per_launch": bf16_flops_per_launch,
         },
         "cpu_baseline": cpu,

@@ -84,15 +84,6 @@ int current_device(int *num_cus)
 
 int launched(hipError_t e) { return e == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_ELAUNCH; }
 
-// Kernel configuration; SGEMM_EMU_KERNEL_VARIANT selects another one for measurement.
-int kernel_variant()
-{
-    static const int v = [] {
-        const char *e = getenv("SGEMM_EMU_KERNEL_VARIANT");
-        return e ? atoi(e) : 0;
-    }();
-    return v;
-}
 
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
@@ -124,7 +115,6 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     if (K == 0) return launched(launch_zero(M, N, C, ldc, num_cus, stream));
 
     GemmArgs g{};
-    g.variant = kernel_variant();
     g.M = M; g.N = N; g.K = K;
     g.A = A; g.lda = lda;
     g.B = B; g.B0 = B0; g.B1 = B1; g.B2 = B2; g.ldb = ldb;

@@ -45,8 +45,10 @@ constexpr int KP = BK + 8;          // LDS row pitch in BF16 elements (80 bytes)
 constexpr int KG = BK / 8;          // 8-wide k groups per row
 constexpr int GROUP_M = 8;
 
-template <int WAVES_M_, int WAVES_N_, int WTM_, int WTN_>
+template <int WAVES_M_, int WAVES_N_, int WTM_, int WTN_, bool SCHED_ = false, int VALU_PER_MFMA_ = 4>
 struct Cfg {
+    static constexpr bool SCHED = SCHED_;     // explicit MFMA / LDS / VALU interleaving
+    static constexpr int VALU_PER_MFMA = VALU_PER_MFMA_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int NT = 64 * WAVES;
@@ -64,8 +66,8 @@ struct Cfg {
     static_assert(NT % 16 == 0 && (BM % 16) == 0 && (BN % 16) == 0, "loader mapping");
 };
 
-using Cfg8 = Cfg<2, 4, 64, 32>;     // 8 waves, 2 per SIMD, 128 x 128 tile
-using Cfg4 = Cfg<2, 2, 64, 64>;     // 4 waves, 1 per SIMD, 128 x 128 tile
+using Cfg8 = Cfg<2, 4, 64, 32>;              // 8 waves, 2 per SIMD, 128 x 128 tile
+using Cfg8S = Cfg<2, 4, 64, 32, true, 4>;    // same, staging interleaved with the MFMAs
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -227,89 +229,83 @@ __device__ __forceinline__ void make_roles(Roles<C, BSRC> &R, const GemmArgs &g,
     }
 }
 
-// Load the K step starting at k0 into registers.
-template <class C, int BSRC, bool AVEC, bool BVEC, bool TAIL>
+// Load the K step starting at k0 into registers.  Every load is in bounds of
+// its descriptor; elements with k >= K are fixed up by mask_stage:
+//   * A and N x K planes run along k inside a row: past K they read the rest
+//     of the row (or zero past the descriptor's end), so they are masked;
+//   * FP32 B and K x N planes run along k across rows: the row offset is part
+//     of the range-checked vector offset, so rows past K read as zero.
+template <class C, int BSRC, bool AVEC, bool BVEC>
 __device__ __forceinline__ void load_stage(Stage<C, BSRC> &st, const Roles<C, BSRC> &R, const GemmArgs &g,
                                            int64_t m0, int64_t n0, int64_t k0)
 {
-    // A: base at (m0, k0); covers the tile's rows.
+    // A: base at (m0, k0); the descriptor ends at element (last row, K-1).
     {
         const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
         const rsrc_t ra = make_rsrc(g.A + m0 * g.lda + k0, ((rows - 1) * g.lda + (g.K - k0)) * 4);
 #pragma unroll
         for (int c = 0; c < C::A_CHUNKS; ++c) {
-            const int64_t k = k0 + R.a_kg[c] * 8;
             float(&x)[8] = st.a[c];
-            if (AVEC && (!TAIL || k + 8 <= g.K)) {
+            if (AVEC) {
                 const u32x4_t v0 = bload_u32x4(ra, R.a_off[c], 0);
                 const u32x4_t v1 = bload_u32x4(ra, R.a_off[c] + 16, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { x[e] = __uint_as_float(v0[e]); x[4 + e] = __uint_as_float(v1[e]); }
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (!TAIL || k + e < g.K) ? bload_f32(ra, R.a_off[c] + 4 * e, 0) : 0.0f;
+                for (int e = 0; e < 8; ++e) x[e] = bload_f32(ra, R.a_off[c] + 4 * e, 0);
             }
         }
     }
     if constexpr (BSRC == B_FP32) {
-        // base at row k0; the row within the 8-row group goes in the scalar offset
+        // base at row k0; the descriptor ends at element (K-1, N-1)
         const rsrc_t rb = make_rsrc(g.B + k0 * g.ldb, ((g.K - 1 - k0) * g.ldb + g.N) * 4);
         const uint32_t row_bytes = (uint32_t)(g.ldb * 4);
 #pragma unroll
-        for (int c = 0; c < C::B_CHUNKS; ++c) {
-            const int64_t k = k0 + R.b_kg[c] * 8;
+        for (int c = 0; c < C::B_CHUNKS; ++c)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                st.b[c][e] = (!TAIL || k + e < g.K) ? bload_f32(rb, R.b_off[c], e * row_bytes) : 0.0f;
-        }
+            for (int e = 0; e < 8; ++e) st.b[c][e] = bload_f32(rb, R.b_off[c] + e * row_bytes, 0);
     } else if constexpr (BSRC == B_PLANES_NK) {
-        // base at (n0, k0); k past K is masked per element
+        // base at (n0, k0); the descriptor ends at element (last column, K-1)
         const int64_t cols = lmin((int64_t)C::BN, g.N - n0);
         const int64_t bytes = ((cols - 1) * g.ldb + (g.K - k0)) * 2;
         const int64_t base = n0 * g.ldb + k0;
-        const rsrc_t r0 = make_rsrc(g.B0 + base, bytes), r1 = make_rsrc(g.B1 + base, bytes),
-                     r2 = make_rsrc(g.B2 + base, bytes);
+        const rsrc_t rr[3] = {make_rsrc(g.B0 + base, bytes), make_rsrc(g.B1 + base, bytes),
+                              make_rsrc(g.B2 + base, bytes)};
 #pragma unroll
-        for (int c = 0; c < C::B_CHUNKS; ++c) {
-            const int64_t k = k0 + R.b_kg[c] * 8;
-            if (BVEC && (!TAIL || k + 8 <= g.K)) {
-                const u32x4_t v0 = bload_u32x4(r0, R.b_off[c], 0), v1 = bload_u32x4(r1, R.b_off[c], 0),
-                              v2 = bload_u32x4(r2, R.b_off[c], 0);
+        for (int c = 0; c < C::B_CHUNKS; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { st.bn[c][0][i] = v0[i]; st.bn[c][1][i] = v1[i]; st.bn[c][2][i] = v2[i]; }
-            } else {
-                const rsrc_t rr[3] = {r0, r1, r2};
+            for (int p = 0; p < 3; ++p) {
+                if (BVEC) {
+                    const u32x4_t v = bload_u32x4(rr[p], R.b_off[c], 0);
 #pragma unroll
-                for (int p = 0; p < 3; ++p)
+                    for (int i = 0; i < 4; ++i) st.bn[c][p][i] = v[i];
+                } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t lo = (!TAIL || k + 2 * i < g.K) ? bload_u16(rr[p], R.b_off[c] + 4 * i, 0) : 0u;
-                        const uint32_t hi = (!TAIL || k + 2 * i + 1 < g.K) ? bload_u16(rr[p], R.b_off[c] + 4 * i + 2, 0) : 0u;
-                        st.bn[c][p][i] = lo | (hi << 16);
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        st.bn[c][p][i] = bload_u16(rr[p], R.b_off[c] + 4 * i, 0) |
+                                         (bload_u16(rr[p], R.b_off[c] + 4 * i + 2, 0) << 16);
+                }
             }
-        }
     } else {
-        // base at row k0; the row within the 4-row group goes in the scalar offset
+        // base at row k0; the descriptor ends at element (K-1, N-1)
         const int64_t bytes = ((g.K - 1 - k0) * g.ldb + g.N) * 2;
         const rsrc_t rr[3] = {make_rsrc(g.B0 + k0 * g.ldb, bytes), make_rsrc(g.B1 + k0 * g.ldb, bytes),
                               make_rsrc(g.B2 + k0 * g.ldb, bytes)};
         const uint32_t row_bytes = (uint32_t)(g.ldb * 2);
 #pragma unroll
         for (int c = 0; c < C::B_PAIRS; ++c) {
-            const int64_t k = k0 + R.b_kg[2 * c] * 4;
 #pragma unroll
             for (int p = 0; p < 3; ++p) {
                 uint32_t r[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (TAIL && k + e >= g.K) {
-                        r[e] = 0u;
-                    } else if (BVEC) {
-                        r[e] = bload_u32(rr[p], R.b_off[c], e * row_bytes);
+                    const uint32_t off = R.b_off[c] + e * row_bytes;
+                    if (BVEC) {
+                        r[e] = bload_u32(rr[p], off, 0);
                     } else {
-                        const uint32_t lo = bload_u16(rr[p], R.b_off[c], e * row_bytes);
-                        const uint32_t hi = R.b_second_ok[c] ? bload_u16(rr[p], R.b_off[c] + 2, e * row_bytes) : 0u;
+                        const uint32_t lo = bload_u16(rr[p], off, 0);
+                        const uint32_t hi = R.b_second_ok[c] ? bload_u16(rr[p], off + 2, 0) : 0u;
                         r[e] = lo | (hi << 16);
                     }
                 }
@@ -323,13 +319,39 @@ __device__ __forceinline__ void load_stage(Stage<C, BSRC> &st, const Roles<C, BS
     }
 }
 
+// Zero the staged elements whose k is >= K (only the last K step can have any).
 template <class C, int BSRC>
-__device__ __forceinline__ void store_stage(const Stage<C, BSRC> &st, const Roles<C, BSRC> &R, uint16_t *buf)
+__device__ __forceinline__ void mask_stage(Stage<C, BSRC> &st, const Roles<C, BSRC> &R, int64_t k0, int64_t K)
+{
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (k0 + R.a_kg[c] * 8 + e >= K) st.a[c][e] = 0.0f;
+    if constexpr (BSRC == B_PLANES_NK) {
+#pragma unroll
+        for (int c = 0; c < C::B_CHUNKS; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t k = k0 + R.b_kg[c] * 8 + 2 * i;
+                const uint32_t keep = (k >= K) ? 0u : (k + 1 >= K) ? 0x0000FFFFu : 0xFFFFFFFFu;
+#pragma unroll
+                for (int p = 0; p < 3; ++p) st.bn[c][p][i] &= keep;
+            }
+    }
+}
+
+// Split the staged FP32 values and write the component tiles to LDS.  The
+// split assumes finite inputs; the return value tells the caller whether this
+// lane met an Inf or NaN and must run restage_special afterwards.
+template <class C, int BSRC>
+__device__ __forceinline__ bool store_stage(const Stage<C, BSRC> &st, const Roles<C, BSRC> &R, uint16_t *buf)
 {
     uint32_t p0[4], p1[4], p2[4];
+    bool special = false;
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
-        split8_packed(st.a[c], p0, p1, p2);
+        special |= split8_packed_finite(st.a[c], p0, p1, p2);
         st_lds16(buf + 0 * C::TILE + R.a_lds[c], p0);
         st_lds16(buf + 1 * C::TILE + R.a_lds[c], p1);
         st_lds16(buf + 2 * C::TILE + R.a_lds[c], p2);
@@ -337,7 +359,7 @@ __device__ __forceinline__ void store_stage(const Stage<C, BSRC> &st, const Role
     if constexpr (BSRC == B_FP32) {
 #pragma unroll
         for (int c = 0; c < C::B_CHUNKS; ++c) {
-            split8_packed(st.b[c], p0, p1, p2);
+            special |= split8_packed_finite(st.b[c], p0, p1, p2);
             st_lds16(buf + 0 * C::TILE + R.b_lds[c], p0);
             st_lds16(buf + 1 * C::TILE + R.b_lds[c], p1);
             st_lds16(buf + 2 * C::TILE + R.b_lds[c], p2);
@@ -356,9 +378,131 @@ __device__ __forceinline__ void store_stage(const Stage<C, BSRC> &st, const Role
                 st_lds8(buf + p * C::TILE + R.b_lds[2 * c + 1], st.bk[c][p][1]);
             }
     }
+    return special;
+}
+
+// Rare path for a lane whose staged values included Inf or NaN: reload the
+// same K step and rewrite its FP32-sourced component tiles with the full
+// special-value split.  Runs before the barrier that publishes the tile.
+template <class C, int BSRC, bool AVEC, bool BVEC>
+__device__ __forceinline__ void restage_special(const Roles<C, BSRC> &R, const GemmArgs &g, int64_t m0, int64_t n0,
+                                             int64_t k0, uint16_t *buf)
+{
+    Stage<C, BSRC> st;
+    load_stage<C, BSRC, AVEC, BVEC>(st, R, g, m0, n0, k0);
+    if (k0 + BK > g.K) mask_stage<C, BSRC>(st, R, k0, g.K);
+    uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        split8_packed(st.a[c], p0, p1, p2);
+        st_lds16(buf + 0 * C::TILE + R.a_lds[c], p0);
+        st_lds16(buf + 1 * C::TILE + R.a_lds[c], p1);
+        st_lds16(buf + 2 * C::TILE + R.a_lds[c], p2);
+    }
+    if constexpr (BSRC == B_FP32) {
+#pragma unroll
+        for (int c = 0; c < C::B_CHUNKS; ++c) {
+            split8_packed(st.b[c], p0, p1, p2);
+            st_lds16(buf + 0 * C::TILE + R.b_lds[c], p0);
+            st_lds16(buf + 1 * C::TILE + R.b_lds[c], p1);
+            st_lds16(buf + 2 * C::TILE + R.b_lds[c], p2);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- kernel
+
+template <class C, int NB>
+struct Acc {
+    f32x16_t v[C::MI][C::NI][NB];
+};
+
+template <class C>
+struct Frags {
+    bf16x8_t a[C::MI][3], b[C::NI][3];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(Frags<C> &f, const uint16_t *cur, int kk, int wm, int wn, int lane)
+{
+    const int frag_row = lane & 31, frag_k = kk + (lane >> 5) * 8;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+            f.a[i][c] = ld_frag(cur + c * C::TILE + (wm * C::WTM + i * 32 + frag_row) * KP + frag_k);
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+            f.b[j][c] = ld_frag(cur + c * C::TILE + (C::BM + wn * C::WTN + j * 32 + frag_row) * KP + frag_k);
+    }
+}
+
+// The nine (or fewer) band products of one 16-wide k slice.
+template <class C, int NB>
+__device__ __forceinline__ void mfma_slice(Acc<C, NB> &acc, const Frags<C> &f)
+{
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            if (p + q < NB) {
+#pragma unroll
+                for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::NI; ++j)
+                        acc.v[i][j][p + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i][p], f.b[j][q],
+                                                                                     acc.v[i][j][p + q], 0, 0, 0);
+            }
+        }
+}
+
+constexpr int products(int nb) { return nb >= 5 ? 9 : nb == 4 ? 8 : nb == 3 ? 6 : nb == 2 ? 3 : 1; }
+
+// Global load instructions one thread issues per K step (see load_stage).
+template <class C, int BSRC, bool AVEC, bool BVEC>
+constexpr int global_loads_per_stage()
+{
+    const int a = C::A_CHUNKS * (AVEC ? 2 : 8);
+    const int b = BSRC == B_FP32 ? C::B_CHUNKS * 8
+                : BSRC == B_PLANES_NK ? C::B_CHUNKS * 3 * (BVEC ? 1 : 8)
+                : C::B_PAIRS * 3 * 4 * (BVEC ? 1 : 2);
+    return a + b;
+}
+
+// One K step that also stages the next one.  Source order keeps the live
+// ranges short (loads, slice 0, slice 1, split + LDS writes); with C::SCHED
+// the scheduling groups below then pull the fragment reads of slice 1 under
+// the MFMAs of slice 0, and the split arithmetic and LDS writes of the next
+// step under the MFMAs of slice 1, so the matrix cores keep running while the
+// next tile is staged.  The body is a single basic block.
+template <class C, int NB, bool AVEC, int BSRC, bool BVEC, bool RAGGED>
+__device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC> &st, const Roles<C, BSRC> &R,
+                                                  const GemmArgs &g, int64_t m0, int64_t n0, int64_t k_next,
+                                                  const uint16_t *cur, uint16_t *nxt, int wm, int wn, int lane)
+{
+    load_stage<C, BSRC, AVEC, BVEC>(st, R, g, m0, n0, k_next);
+    if constexpr (RAGGED) mask_stage<C, BSRC>(st, R, k_next, g.K);
+    Frags<C> f;
+    read_frags<C>(f, cur, 0, wm, wn, lane);
+    mfma_slice<C, NB>(acc, f);
+    read_frags<C>(f, cur, 16, wm, wn, lane);
+    mfma_slice<C, NB>(acc, f);
+    const bool special = store_stage<C, BSRC>(st, R, nxt);
+    if constexpr (C::SCHED) {
+        constexpr int NM = products(NB) * C::MI * C::NI;      // MFMAs per slice
+        constexpr int NR = 3 * (C::MI + C::NI);                // fragment reads per slice
+        constexpr int NLOAD = global_loads_per_stage<C, BSRC, AVEC, BVEC>();
+        constexpr int NVALU = (BSRC == B_FP32) ? 2 * C::VALU_PER_MFMA : C::VALU_PER_MFMA;
+        __builtin_amdgcn_sched_group_barrier(0x020, NLOAD, 0);  // next step's global loads first
+        (void)NR;
+#pragma unroll
+        for (int i = 0; i < 2 * NM; ++i) {                      // MFMAs with the split in between
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i >= NM / 2) __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);
+        }
+    }
+    if (__builtin_expect(special, 0)) restage_special<C, BSRC, AVEC, BVEC>(R, g, m0, n0, k_next, nxt);
+}
 
 template <class C, int NB, bool AVEC, int BSRC, bool BVEC>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
@@ -370,67 +514,52 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
 
     Roles<C, BSRC> R;
     make_roles<C, BSRC, BVEC>(R, g, m0, n0);
 
-    f32x16_t acc[C::MI][C::NI][NB];
+    Acc<C, NB> acc;
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
         for (int j = 0; j < C::NI; ++j)
 #pragma unroll
-            for (int s = 0; s < NB; ++s) acc[i][j][s] = f32x16_t{};
+            for (int s = 0; s < NB; ++s) acc.v[i][j][s] = f32x16_t{};
 
     const int64_t nk = (g.K + BK - 1) / BK;
-    const bool k_ragged = (g.K % BK) != 0;
 
     Stage<C, BSRC> st;
-    if (nk == 1 && k_ragged) load_stage<C, BSRC, AVEC, BVEC, true>(st, R, g, m0, n0, 0);
-    else load_stage<C, BSRC, AVEC, BVEC, false>(st, R, g, m0, n0, 0);
-    store_stage<C, BSRC>(st, R, lds);
+    load_stage<C, BSRC, AVEC, BVEC>(st, R, g, m0, n0, 0);
+    if (BK > g.K) mask_stage<C, BSRC>(st, R, 0, g.K);
+    if (store_stage<C, BSRC>(st, R, lds)) restage_special<C, BSRC, AVEC, BVEC>(R, g, m0, n0, 0, lds);
     __syncthreads();
 
-    for (int64_t kt = 0; kt < nk; ++kt) {
+    // Steady state: every step but the last stages its successor.  Inside the
+    // loop the successor is a full K step; a ragged last step is staged by
+    // the one step after the loop, which masks k >= K.
+    const int64_t nfull = g.K / BK;
+    int64_t kt = 0;
+    for (; kt + 2 <= nfull; ++kt) {
         const uint16_t *cur = lds + (kt & 1) * 3 * C::TILE;
         uint16_t *nxt = lds + ((kt + 1) & 1) * 3 * C::TILE;
-        const bool have_next = kt + 1 < nk;
-        if (have_next) {
-            if (kt + 2 == nk && k_ragged) load_stage<C, BSRC, AVEC, BVEC, true>(st, R, g, m0, n0, (kt + 1) * BK);
-            else load_stage<C, BSRC, AVEC, BVEC, false>(st, R, g, m0, n0, (kt + 1) * BK);
-        }
-
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            bf16x8_t af[C::MI][3], bfr[C::NI][3];
-#pragma unroll
-            for (int c = 0; c < 3; ++c) {
-#pragma unroll
-                for (int i = 0; i < C::MI; ++i)
-                    af[i][c] = ld_frag(cur + c * C::TILE + (wm * C::WTM + i * 32 + frag_row) * KP + kk + frag_k);
-#pragma unroll
-                for (int j = 0; j < C::NI; ++j)
-                    bfr[j][c] = ld_frag(cur + c * C::TILE + (C::BM + wn * C::WTN + j * 32 + frag_row) * KP + kk +
-                                        frag_k);
-            }
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-#pragma unroll
-                for (int q = 0; q < 3; ++q) {
-                    if (p + q < NB) {
-#pragma unroll
-                        for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-                            for (int j = 0; j < C::NI; ++j)
-                                acc[i][j][p + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                    af[i][p], bfr[j][q], acc[i][j][p + q], 0, 0, 0);
-                    }
-                }
-        }
-
-        if (have_next) store_stage<C, BSRC>(st, R, nxt);
+        step_staging_next<C, NB, AVEC, BSRC, BVEC, false>(acc, st, R, g, m0, n0, (kt + 1) * BK, cur, nxt, wm, wn,
+                                                         lane);
         __syncthreads();
+    }
+    if (kt + 1 < nk) {
+        const uint16_t *cur = lds + (kt & 1) * 3 * C::TILE;
+        uint16_t *nxt = lds + ((kt + 1) & 1) * 3 * C::TILE;
+        step_staging_next<C, NB, AVEC, BSRC, BVEC, true>(acc, st, R, g, m0, n0, (kt + 1) * BK, cur, nxt, wm, wn,
+                                                        lane);
+        __syncthreads();
+    }
+    {
+        const uint16_t *cur = lds + ((nk - 1) & 1) * 3 * C::TILE;
+        Frags<C> f;
+        read_frags<C>(f, cur, 0, wm, wn, lane);
+        mfma_slice<C, NB>(acc, f);
+        read_frags<C>(f, cur, 16, wm, wn, lane);
+        mfma_slice<C, NB>(acc, f);
     }
 
     // Epilogue: recombine the bands smallest first and store.
@@ -444,11 +573,11 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm * C::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 float v = 0.0f;
-                if constexpr (NB >= 5) v = 0x1p-32f * acc[i][j][4][r];
-                if constexpr (NB >= 4) v = __builtin_fmaf(acc[i][j][3][r], 0x1p-24f, v);
-                if constexpr (NB >= 3) v = __builtin_fmaf(acc[i][j][2][r], 0x1p-16f, v);
-                if constexpr (NB >= 2) v = __builtin_fmaf(acc[i][j][1][r], 0x1p-8f, v);
-                v = v + acc[i][j][0][r];
+                if constexpr (NB >= 5) v = 0x1p-32f * acc.v[i][j][4][r];
+                if constexpr (NB >= 4) v = __builtin_fmaf(acc.v[i][j][3][r], 0x1p-24f, v);
+                if constexpr (NB >= 3) v = __builtin_fmaf(acc.v[i][j][2][r], 0x1p-16f, v);
+                if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
+                v = v + acc.v[i][j][0][r];
                 if (col_ok && row < g.M) g.C[row * g.ldc + col] = v;
             }
         }
@@ -508,10 +637,13 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
     GemmArgs g = args;
     g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
     g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
-    const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0);
+    // 128-bit loads along k need every 4 (A) or 8 (N x K planes) elements to
+    // lie entirely below or entirely above K, so that no vector load straddles
+    // the end of its descriptor's range.
+    const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0) && (g.K % 4 == 0);
     bool bvec = false;
     if (bsrc == B_PLANES_NK)
-        bvec = aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && (g.ldb % 8 == 0);
+        bvec = aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && (g.ldb % 8 == 0) && (g.K % 8 == 0);
     else if (bsrc == B_PLANES_KN)
         bvec = aligned(g.B0, 4) && aligned(g.B1, 4) && aligned(g.B2, 4) && (g.ldb % 2 == 0) && (g.N % 2 == 0);
     switch (bsrc) {
@@ -522,9 +654,13 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
     return hipGetLastError();
 }
 
+// Configuration per B source, chosen by measurement on MI355X: the explicit
+// MFMA / split interleaving pays off where the kernel splits FP32 B or copies
+// N x K planes; with K x N planes the compiler's own schedule is faster.
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream)
 {
-    return launch_with<Cfg8>(args, nbands, bsrc, stream);
+    if (bsrc == B_PLANES_KN) return launch_with<Cfg8>(args, nbands, bsrc, stream);
+    return launch_with<Cfg8S>(args, nbands, bsrc, stream);
 }
 
 }  // namespace sgemm_emu_dev

@@ -27,7 +27,6 @@ struct GemmArgs {
     float *C;
     int64_t ldc;
     int tiles_m, tiles_n;
-    int variant;             // kernel configuration (0: 8 waves 64x32, 1: 4 waves 64x64)
 };
 
 hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,

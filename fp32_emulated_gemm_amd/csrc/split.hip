@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void split_vec8_kernel(
         f32x4_t v1 = __builtin_nontemporal_load(src + 1);
         float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         uint32_t p0[4], p1[4], p2[4];
-        split8_packed(x, p0, p1, p2);
+        if (split8_packed_finite(x, p0, p1, p2)) split8_packed(x, p0, p1, p2);
         const int64_t o = row * ldo + col;
         *reinterpret_cast<uint4 *>(X0 + o) = make_uint4(p0[0], p0[1], p0[2], p0[3]);
         *reinterpret_cast<uint4 *>(X1 + o) = make_uint4(p1[0], p1[1], p1[2], p1[3]);

@@ -53,21 +53,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo, uint32_t hi)
     return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
 }
 
-// Split 8 values and pack each component into 4 dwords (element e in half e%2
-// of dword e/2).
+// Split 8 values assumed finite and pack each component into 4 dwords
+// (element e in half e%2 of dword e/2).  Returns true if any input was Inf or
+// NaN, in which case the packed words are not the defined split and the
+// caller must redo the chunk with split8_packed.  Branch-free, so it can be
+// interleaved with other work.
+__device__ __forceinline__ bool split8_packed_finite(const float (&x)[8], uint32_t (&p0)[4],
+                                                     uint32_t (&p1)[4], uint32_t (&p2)[4])
+{
+    uint32_t c0[8], c1[8], c2[8];
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = split_finite(x[e], c0[e], c1[e], c2[e]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p0[i] = pack_bf16x2(c0[2 * i], c0[2 * i + 1]);
+        p1[i] = pack_bf16x2(c1[2 * i], c1[2 * i + 1]);
+        p2[i] = pack_bf16x2(c2[2 * i], c2[2 * i + 1]);
+    }
+    // Any non-finite input makes its t NaN, and NaN survives the sum; finite
+    // inputs can at worst overflow the sum to Inf (not NaN) or to Inf - Inf =
+    // NaN, which only sends a finite chunk down the exact slow path.
+    const float probe = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+    return probe != probe;
+}
+
+// Split 8 values of any class and pack each component into 4 dwords.
 __device__ __forceinline__ void split8_packed(const float (&x)[8], uint32_t (&p0)[4],
                                               uint32_t (&p1)[4], uint32_t (&p2)[4])
 {
     uint32_t c0[8], c1[8], c2[8];
-    bool special = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float t = split_finite(x[e], c0[e], c1[e], c2[e]);
-        special |= (t != t);
-    }
-    if (__builtin_expect(special, 0)) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) split_fix_special(x[e], c0[e], c1[e], c2[e]);
+        if (t != t) split_fix_special(x[e], c0[e], c1[e], c2[e]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -97,6 +97,36 @@ def test_unaligned_a_and_padded_c(fe):
     assert np.array_equal(C0.view(np.uint32), C1.view(np.uint32))
 
 
+@pytest.mark.parametrize("entry", ["fused", "presplit", "presplit_t"])
+@pytest.mark.parametrize("M,N,K,lda", [(70, 66, 45, 48), (129, 131, 61, 64), (40, 30, 5, 8)])
+def test_ragged_k_with_padded_lda(fe, entry, M, N, K, lda):
+    """K not a multiple of the 8-wide staging chunks with lda > K: the elements
+    past K in each row of A are other data and must not contribute."""
+    g = _rng(M + N + K)
+    Abuf = g.standard_normal((M, lda)).astype(np.float32) * 1e3     # junk past K
+    A = np.ascontiguousarray(Abuf[:, :K])
+    B = g.standard_normal((K, N)).astype(np.float32)
+    Ad = dev(Abuf)
+    Bd = dev(B)
+    Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    print(f"ragged K {entry} M={M} N={N} K={K} lda={lda}", flush=True, file=sys.stderr)
+    if entry == "fused":
+        fe.sgemm_bf16x9(M, N, K, Ad, lda, Bd, N, Cd, N)
+    elif entry == "presplit":
+        planes = [torch.empty(K * N, dtype=torch.int16, device="cuda") for _ in range(3)]
+        fe.split_f32_bf16x3(K, N, Bd, N, *planes, N)
+        fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, N, fe.SGEMM_EMU_B_KN, Cd, N, 5)
+    else:
+        ldt = K + 3
+        Bt = np.zeros((N, ldt), np.float32)
+        Bt[:, :K] = B.T
+        Bt[:, K:] = 7e3                                                   # junk past K in each plane row
+        planes = [torch.empty(N * ldt, dtype=torch.int16, device="cuda") for _ in range(3)]
+        fe.split_f32_bf16x3(N, ldt, dev(Bt), ldt, *planes, ldt)
+        fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, ldt, fe.SGEMM_EMU_B_NK, Cd, N, 5)
+    check_against_fp64(host(Cd), A, B, label=f"ragged {entry}")
+
+
 def _full24(g, shape):
     m = g.integers(1 << 23, 1 << 24, size=shape) | 1
     s = np.where(g.integers(0, 2, size=shape) == 1, -1.0, 1.0)
