@@ -108,12 +108,17 @@ def main():
     if args.traffic_probe:
         for _ in range(2):
             step(False)
-        src = torch.empty(128 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        # Calibration: a plain device copy of known size whose source is cold.
+        # The source is written first, then a 1 GiB fill evicts it from the
+        # 256 MB last-level cache, then the copy reads and writes 2 GiB.
+        src = torch.empty(512 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        evict = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(2.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)          # the calibration kernel: reads and writes exactly 512 MiB
+        dst.copy_(src)
         torch.cuda.synchronize()
-        log("traffic probe done: 2 steps, then a 536870912-byte copy")
+        log(f"traffic probe done: 2 steps, then a {src.numel() * 4}-byte copy "
+            f"(evict buffer {evict.numel() * 4} bytes)")
         return
 
     for _ in range(args.warmup):
