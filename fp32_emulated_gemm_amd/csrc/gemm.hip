@@ -112,10 +112,17 @@ __device__ __forceinline__ void chunk_rc(int q, int &row, int &kg)
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int RSRC_WORD3 = 0x00020000;   // raw, untyped buffer on gfx9-family GPUs
 
+// Descriptor of `bytes` bytes at `base`.  Callers pass wave-uniform values;
+// readfirstlane states that to the compiler, which otherwise may keep a
+// value in vector registers and wrap every load in a loop over lanes.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
 {
     const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, RSRC_WORD3);
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(n), RSRC_WORD3);
 }
 
 __device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off, uint32_t soff)
@@ -504,6 +511,32 @@ __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC
     if (__builtin_expect(special, 0)) restage_special<C, BSRC, AVEC, BVEC>(R, g, m0, n0, k_next, nxt);
 }
 
+template <class C, int NB>
+__device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const GemmArgs &g, int64_t m0, int64_t n0, int wm,
+                                        int wn, int lane)
+{
+    // recombine the bands smallest first and store
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) {
+        const int64_t col = n0 + wn * C::WTN + j * 32 + (lane & 31);
+        const bool col_ok = col < g.N;
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * C::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                float v = 0.0f;
+                if constexpr (NB >= 5) v = 0x1p-32f * acc.v[i][j][4][r];
+                if constexpr (NB >= 4) v = __builtin_fmaf(acc.v[i][j][3][r], 0x1p-24f, v);
+                if constexpr (NB >= 3) v = __builtin_fmaf(acc.v[i][j][2][r], 0x1p-16f, v);
+                if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
+                v = v + acc.v[i][j][0][r];
+                if (col_ok && row < g.M) g.C[row * g.ldc + col] = v;
+            }
+        }
+    }
+}
+
 template <class C, int NB, bool AVEC, int BSRC, bool BVEC>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
 {
@@ -562,26 +595,234 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
         mfma_slice<C, NB>(acc, f);
     }
 
-    // Epilogue: recombine the bands smallest first and store.
+    store_c<C, NB>(acc, g, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------- N x K planes through LDS DMA
+//
+// Specialisation for pre-split B in the N x K layout with K a multiple of
+// 2 BK and 16-byte aligned planes (the layout of a linear layer's [out][in]
+// weight).  B never passes through registers: each K step's three plane
+// tiles are copied global -> LDS by 16-byte buffer loads with LDS
+// destination (lane l lands at base + 16 l), two steps ahead, into a ring of
+// three LDS buffers.  B tiles are unpadded (64-byte rows) with the 16-byte
+// slot of k group kg of row r stored at slot kg ^ ((r >> 2) & 3), which keeps
+// the fragment reads of 16 consecutive rows on 16 distinct bank groups.
+// A keeps the register path but with two register sets, also two steps
+// ahead, so the split of step kt+1 (interleaved with the MFMAs of step kt)
+// never waits for a load issued in the same step.
+
+constexpr int B_DMA_TILE = 128 * BK;   // BF16 elements of one plane tile (BN = 128 rows x 32 k)
+
+template <class C>
+struct DmaLayout {
+    static constexpr int A_TILE = C::BM * KP;                    // one padded A component tile
+    static constexpr int A_BYTES = 2 * 3 * A_TILE * 2;           // two buffers
+    static constexpr int B_BYTES = 3 * 3 * B_DMA_TILE * 2;       // three buffers
+    static constexpr int TOTAL = A_BYTES + B_BYTES;
+    static_assert(C::BN == 128 && C::WAVES == 8, "one plane tile = one 1 KB DMA per wave");
+};
+
+__device__ __forceinline__ int bslot(int row, int kg) { return kg ^ ((row >> 2) & 3); }
+
+template <class C>
+__device__ __forceinline__ void dma_b_stage(const GemmArgs &g, int64_t n0, int64_t k0, uint16_t *bbuf, int wave,
+                                            int lane)
+{
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    // wave w copies rows 16w .. 16w+15 of each plane tile; lane -> (row, slot)
+    const int row = wave * 16 + (lane >> 2), slot = lane & 3, kg = bslot(row, slot);
+    const int64_t cols = lmin((int64_t)C::BN, g.N - n0);
+    const int64_t n = lmin((int64_t)row, cols - 1);
+    const int64_t bytes = ((cols - 1) * g.ldb + (g.K - k0)) * 2;
+    const int64_t base = n0 * g.ldb + k0;
+    const uint32_t off = (uint32_t)((n * g.ldb + kg * 8) * 2);
+    const uint16_t *planes[3] = {g.B0, g.B1, g.B2};
 #pragma unroll
-    for (int j = 0; j < C::NI; ++j) {
-        const int64_t col = n0 + wn * C::WTN + j * 32 + (lane & 31);
-        const bool col_ok = col < g.N;
+    for (int p = 0; p < 3; ++p) {
+        const rsrc_t r = make_rsrc(planes[p] + base, bytes);
+        uint16_t *dst = bbuf + p * B_DMA_TILE + wave * 16 * BK;    // wave-uniform 1 KB block
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)off, 0, 0, 0);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void read_frags_dma(Frags<C> &f, const uint16_t *abuf, const uint16_t *bbuf, int kk,
+                                               int wm, int wn, int lane)
+{
+    const int frag_row = lane & 31, kg = (kk >> 3) + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < C::MI; ++i) {
+    for (int c = 0; c < 3; ++c) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * C::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                float v = 0.0f;
-                if constexpr (NB >= 5) v = 0x1p-32f * acc.v[i][j][4][r];
-                if constexpr (NB >= 4) v = __builtin_fmaf(acc.v[i][j][3][r], 0x1p-24f, v);
-                if constexpr (NB >= 3) v = __builtin_fmaf(acc.v[i][j][2][r], 0x1p-16f, v);
-                if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
-                v = v + acc.v[i][j][0][r];
-                if (col_ok && row < g.M) g.C[row * g.ldc + col] = v;
-            }
+        for (int i = 0; i < C::MI; ++i)
+            f.a[i][c] = ld_frag(abuf + c * DmaLayout<C>::A_TILE + (wm * C::WTM + i * 32 + frag_row) * KP + kg * 8);
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) {
+            const int row = wn * C::WTN + j * 32 + frag_row;
+            f.b[j][c] = ld_frag(bbuf + c * B_DMA_TILE + row * BK + bslot(row, kg) * 8);
         }
     }
+}
+
+template <class C, bool AVEC>
+__device__ __forceinline__ void load_a_stage(float (&a)[C::A_CHUNKS][8], const uint32_t (&a_off)[C::A_CHUNKS],
+                                             const GemmArgs &g, int64_t m0, int64_t k0)
+{
+    const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
+    const rsrc_t ra = make_rsrc(g.A + m0 * g.lda + k0, ((rows - 1) * g.lda + (g.K - k0)) * 4);
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        if (AVEC) {
+            const u32x4_t v0 = bload_u32x4(ra, a_off[c], 0);
+            const u32x4_t v1 = bload_u32x4(ra, a_off[c] + 16, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { a[c][e] = __uint_as_float(v0[e]); a[c][4 + e] = __uint_as_float(v1[e]); }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[c][e] = bload_f32(ra, a_off[c] + 4 * e, 0);
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ bool store_a_stage(const float (&a)[C::A_CHUNKS][8], const int (&a_lds)[C::A_CHUNKS],
+                                              uint16_t *abuf)
+{
+    uint32_t p0[4], p1[4], p2[4];
+    bool special = false;
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        special |= split8_packed_finite(a[c], p0, p1, p2);
+        st_lds16(abuf + 0 * DmaLayout<C>::A_TILE + a_lds[c], p0);
+        st_lds16(abuf + 1 * DmaLayout<C>::A_TILE + a_lds[c], p1);
+        st_lds16(abuf + 2 * DmaLayout<C>::A_TILE + a_lds[c], p2);
+    }
+    return special;
+}
+
+template <class C, bool AVEC>
+__device__ __forceinline__ void restage_a_special(const uint32_t (&a_off)[C::A_CHUNKS], const int (&a_lds)[C::A_CHUNKS],
+                                                  const GemmArgs &g, int64_t m0, int64_t k0, uint16_t *abuf)
+{
+    float a[C::A_CHUNKS][8];
+    load_a_stage<C, AVEC>(a, a_off, g, m0, k0);
+    uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        split8_packed(a[c], p0, p1, p2);
+        st_lds16(abuf + 0 * DmaLayout<C>::A_TILE + a_lds[c], p0);
+        st_lds16(abuf + 1 * DmaLayout<C>::A_TILE + a_lds[c], p1);
+        st_lds16(abuf + 2 * DmaLayout<C>::A_TILE + a_lds[c], p2);
+    }
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (they complete in issue order), leaving the other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One K step of the DMA pipeline: issue the B copy and the A loads of step
+// kt+2, run the MFMAs of step kt, split the A of step kt+1 (held in
+// `a_split`, loaded one step earlier) into the other A buffer, then make sure
+// step kt+1's B copy has landed.  Steps past the end of K are harmless: their
+// descriptors end at the operands' last elements, so they read zeros or data
+// nobody consumes.
+template <class C, int NB, bool AVEC>
+__device__ __forceinline__ void dma_step(Acc<C, NB> &acc, float (&a_load)[C::A_CHUNKS][8],
+                                         const float (&a_split)[C::A_CHUNKS][8], const uint32_t (&a_off)[C::A_CHUNKS],
+                                         const int (&a_lds)[C::A_CHUNKS], const GemmArgs &g, int64_t m0,
+                                         int64_t n0, int64_t kt, uint16_t *lds, int wave, int wm, int wn, int lane)
+{
+    uint16_t *const a_base = lds;
+    uint16_t *const b_base = lds + DmaLayout<C>::A_BYTES / 2;
+    const uint16_t *abuf = a_base + (kt & 1) * 3 * DmaLayout<C>::A_TILE;
+    const uint16_t *bbuf = b_base + (kt % 3) * 3 * B_DMA_TILE;
+    dma_b_stage<C>(g, n0, (kt + 2) * BK, b_base + ((kt + 2) % 3) * 3 * B_DMA_TILE, wave, lane);
+    load_a_stage<C, AVEC>(a_load, a_off, g, m0, (kt + 2) * BK);
+    Frags<C> f;
+    read_frags_dma<C>(f, abuf, bbuf, 0, wm, wn, lane);
+    mfma_slice<C, NB>(acc, f);
+    read_frags_dma<C>(f, abuf, bbuf, 16, wm, wn, lane);
+    mfma_slice<C, NB>(acc, f);
+    const bool special = store_a_stage<C>(a_split, a_lds, a_base + ((kt + 1) & 1) * 3 * DmaLayout<C>::A_TILE);
+    if constexpr (C::SCHED) {
+        // a_split arrived during the previous step, so its split can run under
+        // all of this step's MFMAs; the copies and loads of step kt+2 go first.
+        constexpr int NM = products(NB) * C::MI * C::NI;
+#pragma unroll
+        for (int i = 0; i < 2 * NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+    }
+    if (__builtin_expect(special, 0))
+        restage_a_special<C, AVEC>(a_off, a_lds, g, m0, (kt + 1) * BK,
+                                   a_base + ((kt + 1) & 1) * 3 * DmaLayout<C>::A_TILE);
+    // step kt+1's B tile must have landed before the barrier; only step kt+2's
+    // three copies and A loads may still be in flight (they complete in order)
+    wait_vmem_at_most<3 + C::A_CHUNKS * (AVEC ? 2 : 8)>();
+}
+
+template <class C, int NB, bool AVEC>
+__global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[DmaLayout<C>::TOTAL / 2];
+
+    int tm, tn;
+    tile_of_block(g.tiles_m, g.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+
+    uint32_t a_off[C::A_CHUNKS];
+    int a_lds[C::A_CHUNKS];
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        int row, kg;
+        chunk_rc(c * C::NT + threadIdx.x, row, kg);
+        const int64_t r = lmin(m0 + row, g.M - 1) - m0;
+        a_off[c] = (uint32_t)((r * g.lda + kg * 8) * 4);
+        a_lds[c] = row * KP + kg * 8;
+    }
+
+    Acc<C, NB> acc;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int s = 0; s < NB; ++s) acc.v[i][j][s] = f32x16_t{};
+
+    const int64_t nk = g.K / BK;                 // K is a multiple of 2 BK on this path
+    uint16_t *const a_base = lds;
+    uint16_t *const b_base = lds + DmaLayout<C>::A_BYTES / 2;
+    float a_next[C::A_CHUNKS][8], a_cur[C::A_CHUNKS][8];
+
+    // Prologue: steps 0 and 1 in flight (step 1 may lie past K), step 0 staged.
+    dma_b_stage<C>(g, n0, 0, b_base, wave, lane);
+    load_a_stage<C, AVEC>(a_cur, a_off, g, m0, 0);
+    dma_b_stage<C>(g, n0, BK, b_base + 3 * B_DMA_TILE, wave, lane);
+    load_a_stage<C, AVEC>(a_next, a_off, g, m0, BK);
+    if (store_a_stage<C>(a_cur, a_lds, a_base)) restage_a_special<C, AVEC>(a_off, a_lds, g, m0, 0, a_base);
+    wait_vmem_at_most<3 + C::A_CHUNKS * (AVEC ? 2 : 8)>();
+    __syncthreads();
+
+    // Two steps per trip keep the register sets static: an even step splits
+    // a_next (its successor) and loads a_cur (two ahead); an odd step the
+    // reverse.  The step count is even on this path.
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+        dma_step<C, NB, AVEC>(acc, a_cur, a_next, a_off, a_lds, g, m0, n0, kt, lds, wave, wm, wn, lane);
+        __syncthreads();
+        dma_step<C, NB, AVEC>(acc, a_next, a_cur, a_off, a_lds, g, m0, n0, kt + 1, lds, wave, wm, wn, lane);
+        __syncthreads();
+    }
+    wait_vmem_at_most<0>();      // drain the copies issued past the end of K
+
+    store_c<C, NB>(acc, g, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------- K == 0
@@ -631,6 +872,31 @@ static void launch_nb(const GemmArgs &g, int nbands, bool avec, bool bvec, hipSt
     }
 }
 
+template <class C, int NB>
+static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n)), block(C::NT);
+    if (avec) hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, true>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, false>), grid, block, 0, stream, g);
+}
+
+template <class C>
+static hipError_t launch_dma(const GemmArgs &args, int nbands, hipStream_t stream)
+{
+    GemmArgs g = args;
+    g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
+    g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
+    const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0);
+    switch (nbands) {
+    case 1: launch_dma_nb<C, 1>(g, avec, stream); break;
+    case 2: launch_dma_nb<C, 2>(g, avec, stream); break;
+    case 3: launch_dma_nb<C, 3>(g, avec, stream); break;
+    case 4: launch_dma_nb<C, 4>(g, avec, stream); break;
+    default: launch_dma_nb<C, 5>(g, avec, stream); break;
+    }
+    return hipGetLastError();
+}
+
 template <class C>
 static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream)
 {
@@ -660,6 +926,9 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream)
 {
     if (bsrc == B_PLANES_KN) return launch_with<Cfg8>(args, nbands, bsrc, stream);
+    if (bsrc == B_PLANES_NK && args.K % (2 * BK) == 0 && args.ldb % 8 == 0 && aligned(args.B0, 16) &&
+        aligned(args.B1, 16) && aligned(args.B2, 16))
+        return launch_dma<Cfg8S>(args, nbands, stream);
     return launch_with<Cfg8S>(args, nbands, bsrc, stream);
 }
 

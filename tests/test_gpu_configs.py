@@ -23,9 +23,15 @@ def log(msg):
     print(msg, flush=True, file=sys.stderr)
 
 
-def gpu_gemm(fe, Ad, Bd, M, N, K, nbands=5, presplit=False):
+def gpu_gemm(fe, Ad, Bd, M, N, K, nbands=5, presplit=False, weight_nk=None):
+    """presplit=True: planes of B (K x N); weight_nk: B^T as a [N][K] weight, split
+    into N x K planes (the benchmark's configuration)."""
     Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    if presplit:
+    if weight_nk is not None:
+        planes = [torch.empty((N, K), dtype=torch.int16, device="cuda") for _ in range(3)]
+        fe.split_f32_bf16x3(N, K, weight_nk, K, *planes, K)
+        fe.sgemm_emu_presplit_b(M, N, K, Ad, K, *planes, K, fe.SGEMM_EMU_B_NK, Cd, N, nbands)
+    elif presplit:
         planes = [torch.empty((K, N), dtype=torch.int16, device="cuda") for _ in range(3)]
         fe.split_f32_bf16x3(K, N, Bd, N, *planes, N)
         fe.sgemm_emu_presplit_b(M, N, K, Ad, K, *planes, N, fe.SGEMM_EMU_B_KN, Cd, N, nbands)
@@ -75,21 +81,24 @@ def test_square4096_sampled(fe, orc):
     rows = sample_rows(4096, 48, 3)
     check_against_fp64(C[rows], A, B, rows=rows, label="square4096")
     assert np.isfinite(C).all()
+    Ct = host(gpu_gemm(fe, dev(A), None, 4096, 4096, 4096, weight_nk=dev(np.ascontiguousarray(B.T))))
+    assert np.array_equal(C.view(np.uint32), Ct.view(np.uint32))
 
 
 def test_pet_large_sampled(fe, orc):
-    """The benchmark's configuration: weights pre-split, activations split in the GEMM."""
+    """The benchmark's configuration: weights held [out][in], split once into N x K
+    planes; activations split inside the GEMM."""
     w = workloads.pet_large()
     X, W1, W2, H = w["X"], w["W1"], w["W2"], w["H"]
     M = X.shape[0]
     log("pet_large GEMM1")
-    C1 = host(gpu_gemm(fe, dev(X), dev(W1), M, 1024, 256, presplit=True))
+    C1 = host(gpu_gemm(fe, dev(X), None, M, 1024, 256, weight_nk=dev(np.ascontiguousarray(W1.T))))
     rows = sample_rows(M, 96, 4)
     check_against_fp64(C1[rows], X, W1, rows=rows, label="pet_large GEMM1")
     assert np.isfinite(C1).all()
     del C1
     log("pet_large GEMM2")
-    C2 = host(gpu_gemm(fe, dev(H), dev(W2), M, 256, 1024, presplit=True))
+    C2 = host(gpu_gemm(fe, dev(H), None, M, 256, 1024, weight_nk=dev(np.ascontiguousarray(W2.T))))
     check_against_fp64(C2[rows], H, W2, rows=rows, label="pet_large GEMM2")
     assert np.isfinite(C2).all()
 

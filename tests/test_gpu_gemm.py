@@ -75,6 +75,44 @@ def test_random_shapes_within_bound(fe, shape, entry):
     check_against_fp64(C, A, B, label=f"{entry} {shape}")
 
 
+DMA_SHAPES = [(129, 130, 64), (300, 257, 128), (64, 300, 256), (513, 384, 192), (1000, 1030, 1024)]
+
+
+@pytest.mark.parametrize("shape", DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_nk_planes_dma_path_within_bound(fe, shape):
+    """N x K planes with K a multiple of 64: B copied to LDS by DMA, two steps ahead."""
+    M, N, K = shape
+    g = _rng(M * 31 + N * 7 + K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="presplit_t")
+    check_against_fp64(C, A, B, label=f"nk dma {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
+
+
+@pytest.mark.parametrize("nbands", [1, 2, 3, 4, 5])
+def test_nk_planes_dma_path_padded_ldb_and_bands(fe, orc, nbands):
+    """Plane rows padded (ldb > K) on the DMA path, every band count, against the
+    register path and the oracle's truncated-band value."""
+    M, N, K, ldt = 200, 140, 128, 136
+    g = _rng(77 + nbands)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    Bt = np.zeros((N, ldt), np.float32)
+    Bt[:, :K] = B.T
+    Bt[:, K:] = np.inf                                    # padding must never be read
+    planes = [torch.empty(N * ldt, dtype=torch.int16, device="cuda") for _ in range(3)]
+    fe.split_f32_bf16x3(N, ldt, dev(Bt), ldt, *planes, ldt)
+    Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    print(f"nk dma padded nbands={nbands}", flush=True, file=sys.stderr)
+    fe.sgemm_emu_presplit_b(M, N, K, dev(A), K, *planes, ldt, fe.SGEMM_EMU_B_NK, Cd, N, nbands)
+    C = host(Cd).astype(np.float64)
+    T = orc.gemm_trunc_f64(A, B, nbands)
+    _, G = orc.gemm_f64(A, B)
+    assert np.all(np.abs(C - T) <= 2 * K * 2.0 ** -24 * G)
+    assert np.array_equal(C.astype(np.float32).view(np.uint32), run(fe, A, B, nbands, "fused").view(np.uint32))
+
+
 def test_presplit_equals_fused_bitwise(fe):
     g = _rng(5)
     A = g.standard_normal((200, 150)).astype(np.float32)
@@ -161,7 +199,8 @@ def test_smallest_band_first_case(fe):
                                           (1 << 9, 1 << 13, 1, 16), (1 << 19, 1 << 20, 0, 4),
                                           (1 << 23, 1 << 24, 0, 2), (1 << 23, 1 << 24, 2, 5)])
 @pytest.mark.parametrize("nbands", [5, 4, 3, 2, 1])
-def test_exact_class_bitwise_vs_oracle(fe, orc, lo, hi, emax, K, nbands):
+@pytest.mark.parametrize("entry", ["fused", "presplit_t"])
+def test_exact_class_bitwise_vs_oracle(fe, orc, lo, hi, emax, K, nbands, entry):
     """On elements whose band sums are exact in any order, GPU == oracle emulation."""
     g = _rng(lo + K + emax)
     M, N = 40, 36
@@ -174,7 +213,7 @@ def test_exact_class_bitwise_vs_oracle(fe, orc, lo, hi, emax, K, nbands):
     A, B = draw((M, K)), draw((K, N))
     mask = exact_class_mask(A, B)
     assert mask.mean() > 0.3
-    C = run(fe, A, B, nbands)
+    C = run(fe, A, B, nbands, entry)
     E = orc.gemm_emu(A, B, nbands)
     assert np.array_equal(C.view(np.uint32)[mask], E.view(np.uint32)[mask])
 
