@@ -189,7 +189,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
             "traffic": None,
-            "kernel": "gemm_bf16x9_kernel<Cfg<2,4,64,32,sched>, 5 bands, A vector loads, N x K planes>",
+            "kernel": "gemm_bf16x9_dma_kernel<Cfg<2,4,64,32,sched>, 5 bands>: N x K planes copied to LDS by DMA, A split in-kernel",
             "flops_per_launch": bf16_flops_per_launch,
         },
         "cpu_baseline": cpu,

@@ -3,8 +3,11 @@
 //
 // Every argument is checked before the first HIP call, so an invalid call
 // returns an error status without touching the GPU (and works on machines
-// without one).  The library allocates no device memory and keeps no state
-// besides a per-device cache of "is this a gfx950" and its CU count.
+// without one).  The library keeps no state besides a per-device cache of
+// "is this a gfx950", its CU count and a memory pool.  The only device memory it
+// allocates is the stream-ordered workspace for pre-splitting FP32 B
+// (hipMallocFromPoolAsync / hipFreeAsync on the caller's stream, from the
+// library's own pool, which keeps freed blocks for reuse).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -20,6 +23,10 @@ using namespace sgemm_emu_dev;
 namespace {
 
 constexpr int64_t kMaxBytes = INT64_MAX / 8;
+// sgemm_bf16x9 / sgemm_emu pre-split FP32 B into a workspace from this many rows of A on
+// (B is then split once instead of once per 128-row tile row), up to this B size.
+constexpr int64_t kPresplitMinRows = 1024;
+constexpr uint64_t kPresplitMaxElems = (uint64_t)1 << 28;
 // Largest leading dimension (elements) whose 128-row tile span fits 32-bit byte offsets.
 constexpr int64_t kMaxTileLd = ((int64_t)1 << 32) / (128 * 4) - 64;
 
@@ -52,6 +59,8 @@ int check_dims(int64_t M, int64_t N, int64_t K)
 struct DeviceInfo {
     int checked = 0;   // 0 unknown, 1 gfx950, -1 other
     int num_cus = 0;
+    int pool_state = 0;           // 0 not tried, 1 created, -1 unavailable
+    hipMemPool_t pool = nullptr;  // workspace pool, kept until the process ends
 };
 
 constexpr int kMaxDevices = 64;
@@ -59,7 +68,7 @@ DeviceInfo g_devices[kMaxDevices];
 std::mutex g_mutex;
 
 // Current device if it is a gfx950, with its CU count; SGEMM_EMU_EARCH otherwise.
-int current_device(int *num_cus)
+int current_device(int *num_cus, int *device = nullptr)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
@@ -79,7 +88,40 @@ int current_device(int *num_cus)
     }
     if (d.checked != 1) return SGEMM_EMU_EARCH;
     *num_cus = d.num_cus;
+    if (device) *device = dev;
     return SGEMM_EMU_OK;
+}
+
+// The library's own stream-ordered memory pool on device `dev` (created on first
+// use), or nullptr if pools are unavailable.  Its release threshold is
+// unlimited, so freed workspace stays reserved for the next call instead of
+// going back to the driver at each synchronisation.
+hipMemPool_t workspace_pool(int dev)
+{
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceInfo &d = g_devices[dev];
+    if (d.pool_state == 0) {
+        d.pool_state = -1;
+        int supported = 0;
+        if (hipDeviceGetAttribute(&supported, hipDeviceAttributeMemoryPoolsSupported, dev) == hipSuccess &&
+            supported) {
+            hipMemPoolProps props;
+            memset(&props, 0, sizeof(props));
+            props.allocType = hipMemAllocationTypePinned;
+            props.handleTypes = hipMemHandleTypeNone;
+            props.location.type = hipMemLocationTypeDevice;
+            props.location.id = dev;
+            hipMemPool_t pool = nullptr;
+            if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+                uint64_t keep = UINT64_MAX;
+                (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+                d.pool = pool;
+                d.pool_state = 1;
+            }
+        }
+        (void)hipGetLastError();
+    }
+    return d.pool;
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_ELAUNCH; }
@@ -110,8 +152,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     if (lda > kMaxTileLd || ldb > kMaxTileLd) return SGEMM_EMU_EINVAL;
     if (M == 0 || N == 0) return SGEMM_EMU_OK;
 
-    int num_cus = 0;
-    if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
+    int num_cus = 0, dev = 0;
+    if ((rc = current_device(&num_cus, &dev)) != SGEMM_EMU_OK) return rc;
     if (K == 0) return launched(launch_zero(M, N, C, ldc, num_cus, stream));
 
     GemmArgs g{};
@@ -119,6 +161,32 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     g.A = A; g.lda = lda;
     g.B = B; g.B0 = B0; g.B1 = B1; g.B2 = B2; g.ldb = ldb;
     g.C = C; g.ldc = ldc;
+    g.num_cus = num_cus;
+
+    // FP32 B with many tile rows: split B once into N x K planes in a
+    // stream-ordered workspace and run the LDS-DMA kernel, instead of splitting
+    // B again in every tile row.  Same split, same products, same order of
+    // MFMA accumulation, so the result is bitwise identical.
+    hipMemPool_t pool = nullptr;
+    if (bsrc == B_FP32 && K % 64 == 0 && M >= kPresplitMinRows && (uint64_t)K * (uint64_t)N <= kPresplitMaxElems &&
+        (pool = workspace_pool(dev)) != nullptr) {
+        const int64_t ldo = K;
+        const size_t plane = (size_t)N * (size_t)ldo * sizeof(uint16_t);
+        const size_t plane_pad = (plane + 255) & ~(size_t)255;
+        void *ws = nullptr;
+        if (hipMallocFromPoolAsync(&ws, 3 * plane_pad, pool, stream) == hipSuccess && ws != nullptr) {
+            uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
+                     *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
+            hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, ldo, num_cus, stream);
+            if (e == hipSuccess) {
+                g.B0 = P0; g.B1 = P1; g.B2 = P2; g.ldb = ldo;
+                e = launch_gemm(g, nbands, B_PLANES_NK, stream);
+            }
+            const hipError_t f = hipFreeAsync(ws, stream);
+            return launched(e == hipSuccess ? f : e);
+        }
+        (void)hipGetLastError();   // no workspace: fall through to the in-kernel split
+    }
     return launched(launch_gemm(g, nbands, bsrc, stream));
 }
 

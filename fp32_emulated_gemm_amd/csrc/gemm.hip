@@ -72,11 +72,13 @@ using Cfg8S = Cfg<2, 4, 64, 32, true, 4>;    // same, staging interleaved with t
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// Block index -> (tile_m, tile_n), XCD-contiguous and grouped by tile-rows.
-__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int &tm, int &tn)
+// Tile index v in [0, T) -> (tile_m, tile_n).  Consecutive v are dealt
+// round-robin to the 8 XCDs, so v is remapped to give each XCD a contiguous
+// run of tiles, and tiles run in groups of 8 tile-rows so concurrent tiles
+// share A and B panels in the XCD's L2.
+__device__ __forceinline__ void tile_of_index(int v, int T, int tiles_m, int tiles_n, int &tm, int &tn)
 {
-    const int G = (int)gridDim.x, b = (int)blockIdx.x;
-    const int per = G >> 3, extra = G & 7, xcd = b & 7, idx = b >> 3;
+    const int per = T >> 3, extra = T & 7, xcd = v & 7, idx = v >> 3;
     const int t = xcd * per + imin(xcd, extra) + idx;
     const int group_size = GROUP_M * tiles_n;
     const int group = t / group_size;
@@ -85,6 +87,12 @@ __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int &tm,
     const int in = t - group * group_size;
     tm = first_m + in % gm;
     tn = in / gm;
+}
+
+// One tile per workgroup: the block index is the tile index.
+__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    tile_of_index((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, tm, tn);
 }
 
 // Chunk q of a tile side with `rows` rows (A: rows of A, B: columns of B) ->
@@ -725,30 +733,51 @@ __device__ __forceinline__ void wait_vmem_at_most()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// One K step of the DMA pipeline: issue the B copy and the A loads of step
-// kt+2, run the MFMAs of step kt, split the A of step kt+1 (held in
-// `a_split`, loaded one step earlier) into the other A buffer, then make sure
-// step kt+1's B copy has landed.  Steps past the end of K are harmless: their
+// Per-thread byte offsets of the A chunks of the tile starting at row m0
+// (rows past M re-read row M-1; their results are not stored).
+template <class C>
+__device__ __forceinline__ void a_offsets(uint32_t (&a_off)[C::A_CHUNKS], const GemmArgs &g, int64_t m0)
+{
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        int row, kg;
+        chunk_rc(c * C::NT + threadIdx.x, row, kg);
+        const int64_t r = lmin(m0 + row, g.M - 1) - m0;
+        a_off[c] = (uint32_t)((r * g.lda + kg * 8) * 4);
+    }
+}
+
+// Where a K step's operands come from: tile origin, first k, and this
+// thread's A offsets for that tile.
+template <class C>
+struct StepSrc {
+    int64_t m0, n0, k0;
+    uint32_t a_off[C::A_CHUNKS];
+};
+
+// One K step of the DMA pipeline: issue the B copy and the A loads of the
+// step two ahead (`ld`, possibly the next tile's first steps), run the MFMAs
+// of the current step from `abuf` / `bbuf`, split the A of the next step (held
+// in `a_split`, loaded one step earlier; `sp` says where it came from, for
+// the rare special-value path) into `abuf_next`, then make sure the next
+// step's B copy has landed.  Steps past the end of K are harmless: their
 // descriptors end at the operands' last elements, so they read zeros or data
 // nobody consumes.
 template <class C, int NB, bool AVEC>
 __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, float (&a_load)[C::A_CHUNKS][8],
-                                         const float (&a_split)[C::A_CHUNKS][8], const uint32_t (&a_off)[C::A_CHUNKS],
-                                         const int (&a_lds)[C::A_CHUNKS], const GemmArgs &g, int64_t m0,
-                                         int64_t n0, int64_t kt, uint16_t *lds, int wave, int wm, int wn, int lane)
+                                         const float (&a_split)[C::A_CHUNKS][8], const StepSrc<C> &ld,
+                                         const StepSrc<C> &sp, const int (&a_lds)[C::A_CHUNKS],
+                                         const GemmArgs &g, const uint16_t *abuf, const uint16_t *bbuf,
+                                         uint16_t *abuf_next, uint16_t *bbuf_ld, int wave, int wm, int wn, int lane)
 {
-    uint16_t *const a_base = lds;
-    uint16_t *const b_base = lds + DmaLayout<C>::A_BYTES / 2;
-    const uint16_t *abuf = a_base + (kt & 1) * 3 * DmaLayout<C>::A_TILE;
-    const uint16_t *bbuf = b_base + (kt % 3) * 3 * B_DMA_TILE;
-    dma_b_stage<C>(g, n0, (kt + 2) * BK, b_base + ((kt + 2) % 3) * 3 * B_DMA_TILE, wave, lane);
-    load_a_stage<C, AVEC>(a_load, a_off, g, m0, (kt + 2) * BK);
+    dma_b_stage<C>(g, ld.n0, ld.k0, bbuf_ld, wave, lane);
+    load_a_stage<C, AVEC>(a_load, ld.a_off, g, ld.m0, ld.k0);
     Frags<C> f;
     read_frags_dma<C>(f, abuf, bbuf, 0, wm, wn, lane);
     mfma_slice<C, NB>(acc, f);
     read_frags_dma<C>(f, abuf, bbuf, 16, wm, wn, lane);
     mfma_slice<C, NB>(acc, f);
-    const bool special = store_a_stage<C>(a_split, a_lds, a_base + ((kt + 1) & 1) * 3 * DmaLayout<C>::A_TILE);
+    const bool special = store_a_stage<C>(a_split, a_lds, abuf_next);
     if constexpr (C::SCHED) {
         // a_split arrived during the previous step, so its split can run under
         // all of this step's MFMAs; the copies and loads of step kt+2 go first.
@@ -759,34 +788,47 @@ __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, float (&a_load)[C::A_C
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
     }
-    if (__builtin_expect(special, 0))
-        restage_a_special<C, AVEC>(a_off, a_lds, g, m0, (kt + 1) * BK,
-                                   a_base + ((kt + 1) & 1) * 3 * DmaLayout<C>::A_TILE);
-    // step kt+1's B tile must have landed before the barrier; only step kt+2's
-    // three copies and A loads may still be in flight (they complete in order)
+    if (__builtin_expect(special, 0)) restage_a_special<C, AVEC>(sp.a_off, a_lds, g, sp.m0, sp.k0, abuf_next);
+    // the next step's B tile must have landed before the barrier; only the
+    // three copies and A loads just issued may still be in flight (loads
+    // complete in order)
     wait_vmem_at_most<3 + C::A_CHUNKS * (AVEC ? 2 : 8)>();
 }
 
+// Persistent: one workgroup per CU walks tiles v = blockIdx.x, + gridDim.x, ...
+// The last two K steps of a tile already load the next tile's first two, and
+// the last one splits the next tile's first A step, so a tile's start costs
+// no load latency and its C stores drain while the next tile computes.
 template <class C, int NB, bool AVEC>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[DmaLayout<C>::TOTAL / 2];
+    uint16_t *const a_base = lds;
+    uint16_t *const b_base = lds + DmaLayout<C>::A_BYTES / 2;
+    constexpr int A_BUF = 3 * DmaLayout<C>::A_TILE, B_BUF = 3 * B_DMA_TILE;
 
-    int tm, tn;
-    tile_of_block(g.tiles_m, g.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int T = g.tiles_m * g.tiles_n, G = (int)gridDim.x;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int64_t nk = g.K / BK;                 // K is a multiple of 2 BK on this path
 
-    uint32_t a_off[C::A_CHUNKS];
     int a_lds[C::A_CHUNKS];
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
         int row, kg;
         chunk_rc(c * C::NT + threadIdx.x, row, kg);
-        const int64_t r = lmin(m0 + row, g.M - 1) - m0;
-        a_off[c] = (uint32_t)((r * g.lda + kg * 8) * 4);
         a_lds[c] = row * KP + kg * 8;
+    }
+
+    int v = (int)blockIdx.x;
+    StepSrc<C> cur;                              // the tile being computed, k0 unused
+    {
+        int tm, tn;
+        tile_of_index(v, T, g.tiles_m, g.tiles_n, tm, tn);
+        cur.m0 = (int64_t)tm * C::BM;
+        cur.n0 = (int64_t)tn * C::BN;
+        cur.k0 = 0;
+        a_offsets<C>(cur.a_off, g, cur.m0);
     }
 
     Acc<C, NB> acc;
@@ -797,32 +839,73 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 #pragma unroll
             for (int s = 0; s < NB; ++s) acc.v[i][j][s] = f32x16_t{};
 
-    const int64_t nk = g.K / BK;                 // K is a multiple of 2 BK on this path
-    uint16_t *const a_base = lds;
-    uint16_t *const b_base = lds + DmaLayout<C>::A_BYTES / 2;
     float a_next[C::A_CHUNKS][8], a_cur[C::A_CHUNKS][8];
 
-    // Prologue: steps 0 and 1 in flight (step 1 may lie past K), step 0 staged.
-    dma_b_stage<C>(g, n0, 0, b_base, wave, lane);
-    load_a_stage<C, AVEC>(a_cur, a_off, g, m0, 0);
-    dma_b_stage<C>(g, n0, BK, b_base + 3 * B_DMA_TILE, wave, lane);
-    load_a_stage<C, AVEC>(a_next, a_off, g, m0, BK);
-    if (store_a_stage<C>(a_cur, a_lds, a_base)) restage_a_special<C, AVEC>(a_off, a_lds, g, m0, 0, a_base);
+    // Prologue: steps 0 and 1 of the first tile in flight, step 0 staged.
+    dma_b_stage<C>(g, cur.n0, 0, b_base, wave, lane);
+    load_a_stage<C, AVEC>(a_cur, cur.a_off, g, cur.m0, 0);
+    dma_b_stage<C>(g, cur.n0, BK, b_base + B_BUF, wave, lane);
+    load_a_stage<C, AVEC>(a_next, cur.a_off, g, cur.m0, BK);
+    if (store_a_stage<C>(a_cur, a_lds, a_base)) restage_a_special<C, AVEC>(cur.a_off, a_lds, g, cur.m0, 0, a_base);
     wait_vmem_at_most<3 + C::A_CHUNKS * (AVEC ? 2 : 8)>();
     __syncthreads();
 
-    // Two steps per trip keep the register sets static: an even step splits
-    // a_next (its successor) and loads a_cur (two ahead); an odd step the
-    // reverse.  The step count is even on this path.
-    for (int64_t kt = 0; kt < nk; kt += 2) {
-        dma_step<C, NB, AVEC>(acc, a_cur, a_next, a_off, a_lds, g, m0, n0, kt, lds, wave, wm, wn, lane);
-        __syncthreads();
-        dma_step<C, NB, AVEC>(acc, a_next, a_cur, a_off, a_lds, g, m0, n0, kt + 1, lds, wave, wm, wn, lane);
-        __syncthreads();
+    int bs = 0;                                  // B ring slot of the current step
+    for (;;) {
+        // The next tile, or (none left) the current one again, whose steps
+        // past K then serve as harmless dummy loads.
+        const int64_t vn = (int64_t)v + G;
+        const bool has_next = vn < T;
+        StepSrc<C> nxt = cur;
+        if (has_next) {
+            int tm, tn;
+            tile_of_index((int)vn, T, g.tiles_m, g.tiles_n, tm, tn);
+            nxt.m0 = (int64_t)tm * C::BM;
+            nxt.n0 = (int64_t)tn * C::BN;
+            a_offsets<C>(nxt.a_off, g, nxt.m0);
+        }
+
+        // Two steps per trip keep the register sets static: an even step
+        // splits a_next (its successor) and loads a_cur (two ahead); an odd
+        // step the reverse.  The step count is even on this path, so A
+        // buffer parity follows kt.
+        for (int64_t kt = 0; kt < nk; kt += 2) {
+            const bool last = kt + 2 >= nk;
+            const bool roll = last && has_next;
+            StepSrc<C> ld = roll ? nxt : cur;
+            ld.k0 = roll ? 0 : (kt + 2) * BK;
+            StepSrc<C> sp = cur;
+            sp.k0 = (kt + 1) * BK;
+            const int b1 = bs == 2 ? 0 : bs + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+            dma_step<C, NB, AVEC>(acc, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
+                                  a_base + A_BUF, b_base + b2 * B_BUF, wave, wm, wn, lane);
+            __syncthreads();
+
+            ld.k0 += BK;
+            if (last) {
+                sp = nxt;
+                sp.k0 = has_next ? 0 : nk * BK;
+            } else {
+                sp.k0 += BK;
+            }
+            dma_step<C, NB, AVEC>(acc, a_next, a_cur, ld, sp, a_lds, g, a_base + A_BUF, b_base + b1 * B_BUF,
+                                  a_base, b_base + bs * B_BUF, wave, wm, wn, lane);
+            __syncthreads();
+            bs = b2;
+        }
+
+        store_c<C, NB>(acc, g, cur.m0, cur.n0, wm, wn, lane);
+        if (!has_next) break;
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+                for (int s = 0; s < NB; ++s) acc.v[i][j][s] = f32x16_t{};
+        v = (int)vn;
+        cur = nxt;
     }
     wait_vmem_at_most<0>();      // drain the copies issued past the end of K
-
-    store_c<C, NB>(acc, g, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------- K == 0
@@ -875,7 +958,11 @@ static void launch_nb(const GemmArgs &g, int nbands, bool avec, bool bvec, hipSt
 template <class C, int NB>
 static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n)), block(C::NT);
+    // One resident workgroup per CU (LDS-limited); a multiple of 8 keeps each
+    // workgroup on one XCD for all of its tiles.
+    const int64_t tiles = (int64_t)g.tiles_m * g.tiles_n;
+    int64_t slots = (int64_t)(g.num_cus > 8 ? g.num_cus & ~7 : 8);
+    const dim3 grid((unsigned)(tiles < slots ? tiles : slots)), block(C::NT);
     if (avec) hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, true>), grid, block, 0, stream, g);
     else hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, false>), grid, block, 0, stream, g);
 }
@@ -923,11 +1010,15 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
 // Configuration per B source, chosen by measurement on MI355X: the explicit
 // MFMA / split interleaving pays off where the kernel splits FP32 B or copies
 // N x K planes; with K x N planes the compiler's own schedule is faster.
+bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const void *B2)
+{
+    return K % (2 * BK) == 0 && ldb % 8 == 0 && aligned(B0, 16) && aligned(B1, 16) && aligned(B2, 16);
+}
+
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream)
 {
     if (bsrc == B_PLANES_KN) return launch_with<Cfg8>(args, nbands, bsrc, stream);
-    if (bsrc == B_PLANES_NK && args.K % (2 * BK) == 0 && args.ldb % 8 == 0 && aligned(args.B0, 16) &&
-        aligned(args.B1, 16) && aligned(args.B2, 16))
+    if (bsrc == B_PLANES_NK && gemm_uses_dma(args.K, args.ldb, args.B0, args.B1, args.B2))
         return launch_dma<Cfg8S>(args, nbands, stream);
     return launch_with<Cfg8S>(args, nbands, bsrc, stream);
 }

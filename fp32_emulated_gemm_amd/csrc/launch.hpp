@@ -27,12 +27,19 @@ struct GemmArgs {
     float *C;
     int64_t ldc;
     int tiles_m, tiles_n;
+    int num_cus;             // compute units of the device (persistent grids)
 };
 
 hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
                         uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream);
 
+hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                                  uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream);
+
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream);
+
+// True when launch_gemm takes the LDS-DMA kernel for N x K planes of this shape.
+bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const void *B2);
 
 hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, int num_cus, hipStream_t stream);
 

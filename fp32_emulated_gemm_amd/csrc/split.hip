@@ -55,6 +55,67 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(
     }
 }
 
+// Split with transposition: X is rows x cols (ldx), the planes are cols x rows
+// (leading dimension ldo); turns an FP32 K x N operand into N x K planes.
+// One workgroup per 64 x 64 tile of X.  The tile goes through LDS: read along
+// X's rows (each wave reads 256 contiguous bytes per row), then each thread
+// takes 8 consecutive rows of one column, splits them, and writes one 16-byte
+// run of each plane row; eight neighbouring lanes cover 128 contiguous bytes.
+// The LDS row pitch of 65 floats makes both the row-wise writes and the
+// column-wise reads free of bank conflicts.
+// Requires rows % 8 == 0, ldo % 8 == 0 and 16-byte aligned planes.
+constexpr int kTT = 64;
+
+__global__ __launch_bounds__(256) void split_transpose_kernel(
+    const float *__restrict__ X, int64_t ldx, uint16_t *__restrict__ X0, uint16_t *__restrict__ X1,
+    uint16_t *__restrict__ X2, int64_t ldo, int64_t rows, int64_t cols, int64_t tiles_c)
+{
+    __shared__ float tile[kTT][kTT + 1];
+    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTT;
+    const int64_t c0 = (int64_t)(blockIdx.x % tiles_c) * kTT;
+    const int tid = threadIdx.x;
+    const int c = tid & (kTT - 1);
+    const bool col_in = c0 + c < cols;
+#pragma unroll
+    for (int i = 0; i < kTT / 4; ++i) {
+        const int r = (tid >> 6) + 4 * i;
+        float v = 0.0f;
+        if (col_in && r0 + r < rows) v = X[(r0 + r) * ldx + c0 + c];
+        tile[r][c] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int u = tid + 256 * j;
+        const int kg = u & 7, n = u >> 3;
+        if (c0 + n >= cols || r0 + 8 * kg >= rows) continue;  // rows % 8 == 0: groups are whole
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = tile[8 * kg + e][n];
+        uint32_t p0[4], p1[4], p2[4];
+        if (split8_packed_finite(x, p0, p1, p2)) split8_packed(x, p0, p1, p2);
+        const int64_t o = (c0 + n) * ldo + r0 + 8 * kg;
+        *reinterpret_cast<uint4 *>(X0 + o) = make_uint4(p0[0], p0[1], p0[2], p0[3]);
+        *reinterpret_cast<uint4 *>(X1 + o) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
+        *reinterpret_cast<uint4 *>(X2 + o) = make_uint4(p2[0], p2[1], p2[2], p2[3]);
+    }
+}
+
+hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                                  uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream)
+{
+    (void)num_cus;
+    if (rows % 8 != 0 || ldo % 8 != 0 || ldo < rows || !aligned(X0, 16) || !aligned(X1, 16) ||
+        !aligned(X2, 16))
+        return hipErrorInvalidValue;
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t tiles_c = (cols + kTT - 1) / kTT, tiles_r = (rows + kTT - 1) / kTT;
+    if (tiles_r > (int64_t)0x7FFFFFFF / tiles_c) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(split_transpose_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, stream, X,
+                       ldx, X0, X1, X2, ldo, rows, cols, tiles_c);
+    return hipGetLastError();
+}
+
 hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
                         uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream)
 {

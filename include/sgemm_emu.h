@@ -31,12 +31,20 @@
  *   Matrices are row-major.  A is M x K with A[i*lda + k]; B is K x N with
  *   B[k*ldb + j]; C is M x N with C[i*ldc + j].  C := A * B (no alpha, beta).
  *   All matrix pointers are DEVICE pointers on the current HIP device.  The
- *   caller owns every buffer; the library keeps no per-call state.
+ *   caller owns every buffer; the library keeps no per-call state beyond the
+ *   stream-ordered workspace described below.
  *   `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *   asynchronously; faults inside kernels surface at the caller's next
  *   synchronisation, as in BLAS libraries.
  *   Arguments are validated before any HIP call; on an error status nothing
  *   has been enqueued.
+ *   Device memory: sgemm_bf16x9 and sgemm_emu with M >= 1024, K % 64 == 0 and
+ *   K * N <= 2^28 split B once into a temporary N x K set of BF16 planes
+ *   (6 K N bytes) taken stream-ordered (hipMallocFromPoolAsync, hipFreeAsync on
+ *   `stream`) from a memory pool the library creates per device and keeps
+ *   until the process ends, with freed blocks held for reuse.  If that
+ *   allocation fails they split B inside the GEMM kernel instead; the result
+ *   is bitwise the same either way.  No other call allocates device memory.
  *   Float pointers must be 4-byte aligned, BF16 plane pointers 2-byte aligned.
  *   16-byte aligned A with lda % 4 == 0 takes the vector-load path; any other
  *   layout takes a scalar-load path with the same arithmetic.

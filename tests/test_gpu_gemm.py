@@ -113,6 +113,92 @@ def test_nk_planes_dma_path_padded_ldb_and_bands(fe, orc, nbands):
     assert np.array_equal(C.astype(np.float32).view(np.uint32), run(fe, A, B, nbands, "fused").view(np.uint32))
 
 
+def _fused_in_row_blocks(fe, A, B, nbands, rows=1000):
+    """A B from the in-kernel split of FP32 B: row blocks below the size at which
+    sgemm_bf16x9 / sgemm_emu switch to splitting B once into a workspace.  Rows of
+    C do not depend on the other rows, so the blocks stack to the full product."""
+    return np.concatenate([run(fe, A[i:i + rows], B, nbands, "fused") for i in range(0, A.shape[0], rows)])
+
+
+WS_SHAPES = [(1024, 130, 64), (1100, 257, 128), (1500, 1000, 512), (2048, 64, 192)]
+
+
+@pytest.mark.parametrize("shape", WS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp32_b_workspace_path(fe, shape):
+    """FP32 B with at least 1024 rows of A and K % 64 == 0: B is split once into N x K
+    planes in a workspace.  Same result, bit for bit, as the in-kernel split and as
+    the caller-split N x K planes."""
+    M, N, K = shape
+    g = _rng(M + 3 * N + 11 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="fused")
+    check_against_fp64(C, A, B, label=f"workspace {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
+    assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, 5).view(np.uint32))
+
+
+@pytest.mark.parametrize("nbands", [1, 2, 3, 4])
+def test_fp32_b_workspace_path_bands(fe, nbands):
+    M, N, K = 1030, 200, 128
+    g = _rng(900 + nbands)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, nbands, "fused")
+    assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, nbands).view(np.uint32))
+
+
+def test_fp32_b_workspace_path_special_values(fe):
+    """Inf, NaN, subnormals and zeros in B take the transposing split's exact path."""
+    M, N, K = 1024, 96, 128
+    g = _rng(4242)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    B[3, 5] = np.inf
+    B[70, 17] = -np.inf
+    B[100, 40] = np.nan
+    B[9, 60] = np.float32(1e-40)
+    B[:, 80] = 0.0
+    C = run(fe, A, B, entry="fused")
+    R = _fused_in_row_blocks(fe, A, B, 5)
+    assert np.array_equal(np.isnan(C), np.isnan(R))
+    fin = ~np.isnan(R)
+    assert np.array_equal(C[fin].view(np.uint32), R[fin].view(np.uint32))
+
+
+PERSIST_SHAPES = [(4100, 1100, 128), (8200, 1030, 64), (4096, 2048, 256)]
+
+
+@pytest.mark.parametrize("shape", PERSIST_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dma_path_several_tiles_per_workgroup(fe, shape):
+    """More tiles than resident workgroups: each workgroup walks several tiles and
+    loads the next tile's first K steps during the current tile's last ones."""
+    M, N, K = shape
+    g = _rng(M + 5 * N + 17 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="presplit_t")
+    check_against_fp64(C, A, B, label=f"persistent {shape}")
+    assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, 5).view(np.uint32))
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
+
+
+def test_dma_path_special_values_in_next_tile_first_step(fe):
+    """Inf and NaN in A at k < 32 of tiles that are not a workgroup's first: their
+    first K step is split at the end of the previous tile, on the rare exact path."""
+    M, N, K = 8200, 1030, 64
+    g = _rng(31337)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    for r, k, v in [(300 * 128 // 9 + 5, 3, np.inf), (5000, 0, -np.inf), (7777, 31, np.nan), (8199, 7, np.inf)]:
+        A[r, k] = v
+    C = run(fe, A, B, entry="presplit_t")
+    R = _fused_in_row_blocks(fe, A, B, 5)
+    assert np.array_equal(np.isnan(C), np.isnan(R))
+    fin = ~np.isnan(R)
+    assert np.array_equal(C[fin].view(np.uint32), R[fin].view(np.uint32))
+
+
 def test_presplit_equals_fused_bitwise(fe):
     g = _rng(5)
     A = g.standard_normal((200, 150)).astype(np.float32)
