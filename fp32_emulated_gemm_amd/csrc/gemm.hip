@@ -45,10 +45,12 @@ constexpr int KP = BK + 8;          // LDS row pitch in BF16 elements (80 bytes)
 constexpr int KG = BK / 8;          // 8-wide k groups per row
 constexpr int GROUP_M = 8;
 
-template <int WAVES_M_, int WAVES_N_, int WTM_, int WTN_, bool SCHED_ = false, int VALU_PER_MFMA_ = 4>
+template <int WAVES_M_, int WAVES_N_, int WTM_, int WTN_, bool SCHED_ = false, int VALU_PER_MFMA_ = 4,
+          int DMA_TAIL_ = 6>
 struct Cfg {
     static constexpr bool SCHED = SCHED_;     // explicit MFMA / LDS / VALU interleaving
     static constexpr int VALU_PER_MFMA = VALU_PER_MFMA_;
+    static constexpr int DMA_TAIL = DMA_TAIL_; // MFMAs of a DMA step left to cover the next fragment reads
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int NT = 64 * WAVES;
@@ -68,6 +70,7 @@ struct Cfg {
 
 using Cfg8 = Cfg<2, 4, 64, 32>;              // 8 waves, 2 per SIMD, 128 x 128 tile
 using Cfg8S = Cfg<2, 4, 64, 32, true, 4>;    // same, staging interleaved with the MFMAs
+using Cfg4D = Cfg<2, 2, 64, 64, true, 2, 12>; // 4 waves, 1 per SIMD, 128 x 128 tile (DMA kernel)
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -628,8 +631,27 @@ struct DmaLayout {
     static constexpr int A_BYTES = 2 * 3 * A_TILE * 2;           // two buffers
     static constexpr int B_BYTES = 3 * 3 * B_DMA_TILE * 2;       // three buffers
     static constexpr int TOTAL = A_BYTES + B_BYTES;
-    static_assert(C::BN == 128 && C::WAVES == 8, "one plane tile = one 1 KB DMA per wave");
+    static constexpr int B_ROWS_PER_WAVE = 128 / C::WAVES;       // plane-tile rows one wave copies
+    static constexpr int B_COPIES = B_ROWS_PER_WAVE / 16;        // 1 KB copies per plane and wave
+    static_assert(C::BN == 128 && B_ROWS_PER_WAVE % 16 == 0, "plane tile rows split into 16-row copies");
 };
+
+// Vector-memory operations one thread issues per K step of the DMA pipeline.
+template <class C, bool AVEC>
+constexpr int dma_vmem_per_step()
+{
+    return 3 * DmaLayout<C>::B_COPIES + C::A_CHUNKS * (AVEC ? 2 : 8);
+}
+
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations,
+// then for the other waves.  Unlike __syncthreads() it does not wait for the
+// wave's outstanding LDS-DMA copies (the step that follows issued them for
+// later use); callers wait for the copies they need with wait_vmem_at_most.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ int bslot(int row, int kg) { return kg ^ ((row >> 2) & 3); }
 
@@ -638,19 +660,28 @@ __device__ __forceinline__ void dma_b_stage(const GemmArgs &g, int64_t n0, int64
                                             int lane)
 {
     typedef __attribute__((address_space(3))) void lds_void_t;
-    // wave w copies rows 16w .. 16w+15 of each plane tile; lane -> (row, slot)
-    const int row = wave * 16 + (lane >> 2), slot = lane & 3, kg = bslot(row, slot);
+    constexpr int RPW = DmaLayout<C>::B_ROWS_PER_WAVE;
+    // wave w copies rows RPW w .. RPW w + RPW - 1 of each plane tile, 16 rows
+    // per copy; lane -> (row, slot)
     const int64_t cols = lmin((int64_t)C::BN, g.N - n0);
-    const int64_t n = lmin((int64_t)row, cols - 1);
     const int64_t bytes = ((cols - 1) * g.ldb + (g.K - k0)) * 2;
     const int64_t base = n0 * g.ldb + k0;
-    const uint32_t off = (uint32_t)((n * g.ldb + kg * 8) * 2);
+    uint32_t off[DmaLayout<C>::B_COPIES];
+#pragma unroll
+    for (int d = 0; d < DmaLayout<C>::B_COPIES; ++d) {
+        const int row = wave * RPW + d * 16 + (lane >> 2), kg = bslot(row, lane & 3);
+        const int64_t n = lmin((int64_t)row, cols - 1);
+        off[d] = (uint32_t)((n * g.ldb + kg * 8) * 2);
+    }
     const uint16_t *planes[3] = {g.B0, g.B1, g.B2};
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
         const rsrc_t r = make_rsrc(planes[p] + base, bytes);
-        uint16_t *dst = bbuf + p * B_DMA_TILE + wave * 16 * BK;    // wave-uniform 1 KB block
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)off, 0, 0, 0);
+#pragma unroll
+        for (int d = 0; d < DmaLayout<C>::B_COPIES; ++d) {
+            uint16_t *dst = bbuf + p * B_DMA_TILE + (wave * RPW + d * 16) * BK;   // wave-uniform 1 KB block
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)off[d], 0, 0, 0);
+        }
     }
 }
 
@@ -755,50 +786,80 @@ struct StepSrc {
     uint32_t a_off[C::A_CHUNKS];
 };
 
-// One K step of the DMA pipeline: issue the B copy and the A loads of the
-// step two ahead (`ld`, possibly the next tile's first steps), run the MFMAs
-// of the current step from `abuf` / `bbuf`, split the A of the next step (held
-// in `a_split`, loaded one step earlier; `sp` says where it came from, for
-// the rare special-value path) into `abuf_next`, then make sure the next
-// step's B copy has landed.  Steps past the end of K are harmless: their
-// descriptors end at the operands' last elements, so they read zeros or data
-// nobody consumes.
-template <class C, int NB, bool AVEC>
-__device__ __forceinline__ void dma_step(Acc<C, NB> &acc, float (&a_load)[C::A_CHUNKS][8],
-                                         const float (&a_split)[C::A_CHUNKS][8], const StepSrc<C> &ld,
-                                         const StepSrc<C> &sp, const int (&a_lds)[C::A_CHUNKS],
-                                         const GemmArgs &g, const uint16_t *abuf, const uint16_t *bbuf,
-                                         uint16_t *abuf_next, uint16_t *bbuf_ld, int wave, int wm, int wn, int lane)
+// MFMAs [FIRST, LAST) of one k slice, in the order of mfma_slice.
+template <class C, int NB, int FIRST, int LAST>
+__device__ __forceinline__ void mfma_slice_part(Acc<C, NB> &acc, const Frags<C> &f)
 {
+    int n = 0;
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            if (p + q < NB) {
+#pragma unroll
+                for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::NI; ++j) {
+                        if (n >= FIRST && n < LAST)
+                            acc.v[i][j][p + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                f.a[i][p], f.b[j][q], acc.v[i][j][p + q], 0, 0, 0);
+                        ++n;
+                    }
+            }
+        }
+}
+
+// One K step of the DMA pipeline.  On entry f0 holds the fragments of the
+// step's first k slice (read after the previous barrier).  The step issues
+// the B copy and the A loads of the step two ahead (`ld`, possibly the next
+// tile's), reads the second slice's fragments into f1, runs the first slice,
+// splits the A of the next step (`a_split`, loaded one step earlier; `sp`
+// says where it came from, for the rare special-value path) into `abuf_next`,
+// runs most of the second slice, waits for the next step's B copy, passes the
+// barrier, reads the next step's first-slice fragments into f0, and finishes
+// the second slice while those reads are in flight.  Steps past the end of K
+// are harmless: their descriptors end at the operands' last elements, so they
+// read zeros or data nobody consumes.
+template <class C, int NB, bool AVEC>
+__device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C> &f1,
+                                         float (&a_load)[C::A_CHUNKS][8], const float (&a_split)[C::A_CHUNKS][8],
+                                         const StepSrc<C> &ld, const StepSrc<C> &sp, const int (&a_lds)[C::A_CHUNKS],
+                                         const GemmArgs &g, const uint16_t *abuf, const uint16_t *bbuf,
+                                         uint16_t *abuf_next, const uint16_t *bbuf_next, uint16_t *bbuf_ld, int wave,
+                                         int wm, int wn, int lane)
+{
+    constexpr int NM = products(NB) * C::MI * C::NI;     // MFMAs per k slice
+    constexpr int TAIL = C::DMA_TAIL < NM ? C::DMA_TAIL : NM;
     dma_b_stage<C>(g, ld.n0, ld.k0, bbuf_ld, wave, lane);
     load_a_stage<C, AVEC>(a_load, ld.a_off, g, ld.m0, ld.k0);
-    Frags<C> f;
-    read_frags_dma<C>(f, abuf, bbuf, 0, wm, wn, lane);
-    mfma_slice<C, NB>(acc, f);
-    read_frags_dma<C>(f, abuf, bbuf, 16, wm, wn, lane);
-    mfma_slice<C, NB>(acc, f);
+    read_frags_dma<C>(f1, abuf, bbuf, 16, wm, wn, lane);
+    mfma_slice<C, NB>(acc, f0);
     const bool special = store_a_stage<C>(a_split, a_lds, abuf_next);
+    mfma_slice_part<C, NB, 0, NM - TAIL>(acc, f1);
     if constexpr (C::SCHED) {
-        // a_split arrived during the previous step, so its split can run under
-        // all of this step's MFMAs; the copies and loads of step kt+2 go first.
-        constexpr int NM = products(NB) * C::MI * C::NI;
+        // a_split arrived during the previous step, so its split and LDS
+        // writes can run under the MFMAs; the copies and loads go first.
 #pragma unroll
-        for (int i = 0; i < 2 * NM; ++i) {
+        for (int i = 0; i < 2 * NM - TAIL; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
     }
     if (__builtin_expect(special, 0)) restage_a_special<C, AVEC>(sp.a_off, a_lds, g, sp.m0, sp.k0, abuf_next);
-    // the next step's B tile must have landed before the barrier; only the
-    // three copies and A loads just issued may still be in flight (loads
-    // complete in order)
-    wait_vmem_at_most<3 + C::A_CHUNKS * (AVEC ? 2 : 8)>();
+    // The next step's B tile must have landed before the barrier; only the
+    // copies and A loads issued at the top of this step may still be in
+    // flight (vector-memory operations complete in order).
+    wait_vmem_at_most<dma_vmem_per_step<C, AVEC>()>();
+    lds_barrier();
+    read_frags_dma<C>(f0, abuf_next, bbuf_next, 0, wm, wn, lane);
+    mfma_slice_part<C, NB, NM - TAIL, NM>(acc, f1);
 }
 
 // Persistent: one workgroup per CU walks tiles v = blockIdx.x, + gridDim.x, ...
 // The last two K steps of a tile already load the next tile's first two, and
-// the last one splits the next tile's first A step, so a tile's start costs
-// no load latency and its C stores drain while the next tile computes.
+// the last one splits the next tile's first A step and reads its first
+// fragments, so a tile's start costs no load latency and its C stores drain
+// while the next tile computes.
 template <class C, int NB, bool AVEC>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 {
@@ -840,15 +901,18 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             for (int s = 0; s < NB; ++s) acc.v[i][j][s] = f32x16_t{};
 
     float a_next[C::A_CHUNKS][8], a_cur[C::A_CHUNKS][8];
+    Frags<C> f0, f1;
 
-    // Prologue: steps 0 and 1 of the first tile in flight, step 0 staged.
+    // Prologue: steps 0 and 1 of the first tile in flight, step 0 staged and
+    // its first-slice fragments read.
     dma_b_stage<C>(g, cur.n0, 0, b_base, wave, lane);
     load_a_stage<C, AVEC>(a_cur, cur.a_off, g, cur.m0, 0);
     dma_b_stage<C>(g, cur.n0, BK, b_base + B_BUF, wave, lane);
     load_a_stage<C, AVEC>(a_next, cur.a_off, g, cur.m0, BK);
     if (store_a_stage<C>(a_cur, a_lds, a_base)) restage_a_special<C, AVEC>(cur.a_off, a_lds, g, cur.m0, 0, a_base);
-    wait_vmem_at_most<3 + C::A_CHUNKS * (AVEC ? 2 : 8)>();
-    __syncthreads();
+    wait_vmem_at_most<dma_vmem_per_step<C, AVEC>()>();
+    lds_barrier();
+    read_frags_dma<C>(f0, a_base, b_base, 0, wm, wn, lane);
 
     int bs = 0;                                  // B ring slot of the current step
     for (;;) {
@@ -877,9 +941,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             StepSrc<C> sp = cur;
             sp.k0 = (kt + 1) * BK;
             const int b1 = bs == 2 ? 0 : bs + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-            dma_step<C, NB, AVEC>(acc, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
-                                  a_base + A_BUF, b_base + b2 * B_BUF, wave, wm, wn, lane);
-            __syncthreads();
+            dma_step<C, NB, AVEC>(acc, f0, f1, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
+                                  a_base + A_BUF, b_base + b1 * B_BUF, b_base + b2 * B_BUF, wave, wm, wn, lane);
 
             ld.k0 += BK;
             if (last) {
@@ -888,9 +951,9 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             } else {
                 sp.k0 += BK;
             }
-            dma_step<C, NB, AVEC>(acc, a_next, a_cur, ld, sp, a_lds, g, a_base + A_BUF, b_base + b1 * B_BUF,
-                                  a_base, b_base + bs * B_BUF, wave, wm, wn, lane);
-            __syncthreads();
+            dma_step<C, NB, AVEC>(acc, f0, f1, a_next, a_cur, ld, sp, a_lds, g, a_base + A_BUF,
+                                  b_base + b1 * B_BUF, a_base, b_base + b2 * B_BUF, b_base + bs * B_BUF, wave, wm,
+                                  wn, lane);
             bs = b2;
         }
 
