@@ -522,27 +522,41 @@ __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC
     if (__builtin_expect(special, 0)) restage_special<C, BSRC, AVEC, BVEC>(R, g, m0, n0, k_next, nxt);
 }
 
+// Recombine the bands smallest first and store the tile.  The stores are
+// raw buffer stores through a descriptor that starts at the tile's first row
+// and ends at element (last row of C inside the tile, N-1): rows past M fall
+// outside it and are dropped by the hardware range check, so only the
+// column test (fixed per lane) needs a branch.
 template <class C, int NB>
 __device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const GemmArgs &g, int64_t m0, int64_t n0, int wm,
                                         int wn, int lane)
 {
-    // recombine the bands smallest first and store
+    const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
+    const rsrc_t rc = make_rsrc(g.C + m0 * g.ldc, ((rows - 1) * g.ldc + g.N) * 4);
+    // 128 rows of C fit 32-bit byte offsets (leading dimensions are limited)
+    const uint32_t ldc4 = (uint32_t)g.ldc * 4u;
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
         const int64_t col = n0 + wn * C::WTN + j * 32 + (lane & 31);
-        const bool col_ok = col < g.N;
+        if (col < g.N) {
+            uint32_t lane_off = (uint32_t)col * 4u + (uint32_t)(wm * C::WTM + 4 * (lane >> 5)) * ldc4;
+            // Opaque to the optimiser: otherwise it reassociates the 32 row
+            // offsets below into tile-invariant values and keeps them all live.
+            asm volatile("" : "+v"(lane_off));
 #pragma unroll
-        for (int i = 0; i < C::MI; ++i) {
+            for (int i = 0; i < C::MI; ++i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * C::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                float v = 0.0f;
-                if constexpr (NB >= 5) v = 0x1p-32f * acc.v[i][j][4][r];
-                if constexpr (NB >= 4) v = __builtin_fmaf(acc.v[i][j][3][r], 0x1p-24f, v);
-                if constexpr (NB >= 3) v = __builtin_fmaf(acc.v[i][j][2][r], 0x1p-16f, v);
-                if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
-                v = v + acc.v[i][j][0][r];
-                if (col_ok && row < g.M) g.C[row * g.ldc + col] = v;
+                for (int r = 0; r < 16; ++r) {
+                    float v = 0.0f;
+                    if constexpr (NB >= 5) v = 0x1p-32f * acc.v[i][j][4][r];
+                    if constexpr (NB >= 4) v = __builtin_fmaf(acc.v[i][j][3][r], 0x1p-24f, v);
+                    if constexpr (NB >= 3) v = __builtin_fmaf(acc.v[i][j][2][r], 0x1p-16f, v);
+                    if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
+                    v = v + acc.v[i][j][0][r];
+                    const uint32_t row = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, (int)(lane_off + row * ldc4), 0,
+                                                          0);
+                }
             }
         }
     }
@@ -855,6 +869,21 @@ __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C>
     mfma_slice_part<C, NB, NM - TAIL, NM>(acc, f1);
 }
 
+// Clear the accumulators with MFMAs of zero operands: one instruction per 16
+// registers, on the matrix pipe that idles while the epilogue stores.
+template <class C, int NB>
+__device__ __forceinline__ void clear_acc(Acc<C, NB> &acc)
+{
+    const bf16x8_t z = {};
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int s = 0; s < NB; ++s)
+                acc.v[i][j][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16_t{}, 0, 0, 0);
+}
+
 // Persistent: one workgroup per CU walks tiles v = blockIdx.x, + gridDim.x, ...
 // The last two K steps of a tile already load the next tile's first two, and
 // the last one splits the next tile's first A step and reads its first
@@ -893,12 +922,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     }
 
     Acc<C, NB> acc;
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-            for (int s = 0; s < NB; ++s) acc.v[i][j][s] = f32x16_t{};
+    clear_acc<C, NB>(acc);
 
     float a_next[C::A_CHUNKS][8], a_cur[C::A_CHUNKS][8];
     Frags<C> f0, f1;
@@ -959,12 +983,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 
         store_c<C, NB>(acc, g, cur.m0, cur.n0, wm, wn, lane);
         if (!has_next) break;
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-            for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-                for (int s = 0; s < NB; ++s) acc.v[i][j][s] = f32x16_t{};
+        clear_acc<C, NB>(acc);
         v = (int)vn;
         cur = nxt;
     }
