@@ -31,6 +31,17 @@ MI355X_BF16_DENSE_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk/CU
 MI355X_FP32_VECTOR_TFLOPS = 157.3
 MI355X_HBM_GBS = 8000.0
 METRIC = "BF16x9 SGEMM effective FP32 TFLOP/s (2MNK/t) and % of bf16 MFMA peak"
+HERE = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
+
+# HBM traffic of the timed GEMM kernel per launch ([X@W1, H@W2], bytes), from two
+# rocprofv3 --pmc runs of `python3 bench.py --traffic-probe` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
+# the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
+# x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
+# source they were taken on; once gemm.hip has changed, roofline.traffic is null.
+GEMM_TRAFFIC = {"gemm_hip_sha256": "85d7f8019e45295fc8baa5933ef06ee2e598752231be22c8576c1a5ebefe752e",
+                "bytes_per_launch": [4024948997, 3853598442]}
 
 
 def log(msg):
@@ -144,6 +155,12 @@ def main():
     bf16_flops_per_launch = [18.0 * M * F * D, 18.0 * M * D * F]
     achieved = sum(bf16_flops_per_launch) / ((g1_ms + g2_ms) * 1e-3) / 1e12
     log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms); GEMM1 {g1_ms:.3f} ms, GEMM2 {g2_ms:.3f} ms")
+    # bytes each GEMM must move at least: A (FP32) + three BF16 planes of B + C (FP32)
+    algo_bytes = [4 * M * D + 6 * D * F + 4 * M * F, 4 * M * F + 6 * F * D + 4 * M * D]
+    traffic_per_launch = None
+    if GEMM_TRAFFIC["gemm_hip_sha256"] == source_sha256(GEMM_SOURCE):
+        traffic_per_launch = GEMM_TRAFFIC["bytes_per_launch"]
+    traffic = None if traffic_per_launch is None else sum(traffic_per_launch) / len(traffic_per_launch)
 
     # correctness spot check of the timed outputs against torch FP32 (sanity, not parity)
     ref1 = torch.matmul(Xd[:256], W1d)
@@ -188,7 +205,9 @@ def main():
             "peak": MI355X_BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_per_launch": traffic_per_launch,
+            "algorithmic_bytes_per_launch": algo_bytes,
             "kernel": "gemm_bf16x9_dma_kernel<Cfg<2,4,64,32,sched>, 5 bands>: N x K planes copied to LDS by DMA, A split in-kernel",
             "flops_per_launch": bf16_flops_per_launch,
         },
@@ -196,6 +215,12 @@ def main():
         "context": context,
     }
     print(json.dumps(out), flush=True)
+
+
+def source_sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def timed(fn, stream, reps):
