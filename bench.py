@@ -40,8 +40,8 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "85d7f8019e45295fc8baa5933ef06ee2e598752231be22c8576c1a5ebefe752e",
-                "bytes_per_launch": [4024948997, 3853598442]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "e1f341d1eebdbab615e360f537bb9ff095c08be170f5c2625c4c492dfc13ed03",
+                "bytes_per_launch": [2844960426, 3281705059]}
 
 
 def log(msg):

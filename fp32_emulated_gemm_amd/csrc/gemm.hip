@@ -43,7 +43,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int BK = 32;
 constexpr int KP = BK + 8;          // LDS row pitch in BF16 elements (80 bytes)
 constexpr int KG = BK / 8;          // 8-wide k groups per row
-constexpr int GROUP_M = 8;
 
 template <int WAVES_M_, int WAVES_N_, int WTM_, int WTN_, bool SCHED_ = false, int VALU_PER_MFMA_ = 4,
           int DMA_TAIL_ = 6>
@@ -77,25 +76,27 @@ __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a
 
 // Tile index v in [0, T) -> (tile_m, tile_n).  Consecutive v are dealt
 // round-robin to the 8 XCDs, so v is remapped to give each XCD a contiguous
-// run of tiles, and tiles run in groups of 8 tile-rows so concurrent tiles
-// share A and B panels in the XCD's L2.
-__device__ __forceinline__ void tile_of_index(int v, int T, int tiles_m, int tiles_n, int &tm, int &tn)
+// run of tiles, and tiles run in groups of group_m tile-rows (column-major
+// inside a group) so the tiles an XCD runs at once share A and B panels in
+// its L2.
+__device__ __forceinline__ void tile_of_index(int v, int T, int tiles_m, int tiles_n, int group_m, int &tm,
+                                              int &tn)
 {
     const int per = T >> 3, extra = T & 7, xcd = v & 7, idx = v >> 3;
     const int t = xcd * per + imin(xcd, extra) + idx;
-    const int group_size = GROUP_M * tiles_n;
+    const int group_size = group_m * tiles_n;
     const int group = t / group_size;
-    const int first_m = group * GROUP_M;
-    const int gm = imin(tiles_m - first_m, GROUP_M);
+    const int first_m = group * group_m;
+    const int gm = imin(tiles_m - first_m, group_m);
     const int in = t - group * group_size;
     tm = first_m + in % gm;
     tn = in / gm;
 }
 
 // One tile per workgroup: the block index is the tile index.
-__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int &tm, int &tn)
+__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
 {
-    tile_of_index((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_of_index((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
 }
 
 // Chunk q of a tile side with `rows` rows (A: rows of A, B: columns of B) ->
@@ -522,6 +523,10 @@ __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC
     if (__builtin_expect(special, 0)) restage_special<C, BSRC, AVEC, BVEC>(R, g, m0, n0, k_next, nxt);
 }
 
+// Cache policy of the C stores: non-temporal (streamed past L2), so the
+// output does not evict the A and B panels other tiles still read.
+constexpr int kStreamingStore = 2;
+
 // Recombine the bands smallest first and store the tile.  The stores are
 // raw buffer stores through a descriptor that starts at the tile's first row
 // and ends at element (last row of C inside the tile, N-1): rows past M fall
@@ -555,7 +560,7 @@ __device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const GemmArgs &g
                     v = v + acc.v[i][j][0][r];
                     const uint32_t row = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, (int)(lane_off + row * ldc4), 0,
-                                                          0);
+                                                          kStreamingStore);
                 }
             }
         }
@@ -568,7 +573,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * C::TILE];
 
     int tm, tn;
-    tile_of_block(g.tiles_m, g.tiles_n, tm, tn);
+    tile_of_block(g.tiles_m, g.tiles_n, g.group_m, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -914,7 +919,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     StepSrc<C> cur;                              // the tile being computed, k0 unused
     {
         int tm, tn;
-        tile_of_index(v, T, g.tiles_m, g.tiles_n, tm, tn);
+        tile_of_index(v, T, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
         cur.m0 = (int64_t)tm * C::BM;
         cur.n0 = (int64_t)tn * C::BN;
         cur.k0 = 0;
@@ -947,7 +952,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
         StepSrc<C> nxt = cur;
         if (has_next) {
             int tm, tn;
-            tile_of_index((int)vn, T, g.tiles_m, g.tiles_n, tm, tn);
+            tile_of_index((int)vn, T, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
             nxt.m0 = (int64_t)tm * C::BM;
             nxt.n0 = (int64_t)tn * C::BN;
             a_offsets<C>(nxt.a_off, g, nxt.m0);
@@ -1012,6 +1017,17 @@ hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, int num_cus,
 
 // ---------------------------------------------------------------- dispatch
 
+// Tile-rows per group.  An XCD runs about num_cus / 8 consecutive tiles at
+// once.  A narrow tile grid (at least 4 whole tile-rows in that window) runs
+// row by row (groups of one row), so the column tiles that read an A row
+// panel are neighbours and run together; wider grids use groups of 8 rows,
+// which share both A and B panels.
+static int group_rows(int tiles_n, int num_cus)
+{
+    const int per_xcd = num_cus >= 8 ? num_cus / 8 : 1;
+    return tiles_n * 4 <= per_xcd ? 1 : 8;
+}
+
 template <class C, int NB, int BSRC>
 static void launch_cfg(const GemmArgs &g, bool avec, bool bvec, hipStream_t stream)
 {
@@ -1055,6 +1071,7 @@ static hipError_t launch_dma(const GemmArgs &args, int nbands, hipStream_t strea
     GemmArgs g = args;
     g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
     g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
+    g.group_m = group_rows(g.tiles_n, g.num_cus);
     const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0);
     switch (nbands) {
     case 1: launch_dma_nb<C, 1>(g, avec, stream); break;
@@ -1072,6 +1089,7 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
     GemmArgs g = args;
     g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
     g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
+    g.group_m = group_rows(g.tiles_n, g.num_cus);
     // 128-bit loads along k need every 4 (A) or 8 (N x K planes) elements to
     // lie entirely below or entirely above K, so that no vector load straddles
     // the end of its descriptor's range.

@@ -27,6 +27,7 @@ struct GemmArgs {
     float *C;
     int64_t ldc;
     int tiles_m, tiles_n;
+    int group_m;             // tile-rows per group of the tile order
     int num_cus;             // compute units of the device (persistent grids)
 };
 
