@@ -225,7 +225,8 @@ def source_sha256(path):
 
 def timed(fn, stream, reps):
     import torch
-    fn()
+    for _ in range(3):
+        fn()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -249,6 +250,15 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     res["sgemm_bf16x9_X@W1_tflops"] = round(fl / t / 1e9, 2)
     t = timed(lambda: fe.sgemm_bf16x9(M, D, F, Hd, F, W2d, D, C2, D, sp), stream, 5)
     res["sgemm_bf16x9_H@W2_tflops"] = round(fl / t / 1e9, 2)
+    # the linear layer built on the same planes: forward with bias, and the input
+    # gradient dX = dY W1 (W1's N x K planes read as K x N)
+    W1t_planes = fe.split(W1d.t().contiguous())
+    bias1 = torch.zeros(F, dtype=torch.float32, device=Xd.device)
+    t = timed(lambda: fe.sgemm_emu_linear(M, F, D, Xd, D, *W1t_planes, D, bias1, C1, F, 5, sp), stream, 5)
+    res["linear_fwd_X@W1^T+b_tflops"] = round(fl / t / 1e9, 2)
+    t = timed(lambda: fe.sgemm_emu_presplit_b(M, D, F, C1, F, *W1t_planes, D, fe.SGEMM_EMU_B_KN, C2, D, 5, sp),
+              stream, 5)
+    res["linear_dX=dY@W1_tflops"] = round(fl / t / 1e9, 2)
     n = 4096
     g = torch.Generator(device="cuda").manual_seed(1)
     A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1

@@ -527,14 +527,27 @@ __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC
 // output does not evict the A and B panels other tiles still read.
 constexpr int kStreamingStore = 2;
 
-// Recombine the bands smallest first and store the tile.  The stores are
+// Recombine the bands smallest first, add the bias (if any) and store the tile.  The stores are
 // raw buffer stores through a descriptor that starts at the tile's first row
 // and ends at element (last row of C inside the tile, N-1): rows past M fall
 // outside it and are dropped by the hardware range check, so only the
 // column test (fixed per lane) needs a branch.
+// Bias of each of this lane's output columns, -0 where there is none (x + (-0)
+// is x for every x, including -0 and NaN).  Loaded well before the epilogue
+// so its latency never stalls the stores.
+template <class C>
+__device__ __forceinline__ void load_bias(float (&bv)[C::NI], const GemmArgs &g, int64_t n0, int wn, int lane)
+{
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) {
+        const int64_t col = n0 + wn * C::WTN + j * 32 + (lane & 31);
+        bv[j] = (g.bias && col < g.N) ? g.bias[col] : -0.0f;
+    }
+}
+
 template <class C, int NB>
-__device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const GemmArgs &g, int64_t m0, int64_t n0, int wm,
-                                        int wn, int lane)
+__device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const float (&bv)[C::NI], const GemmArgs &g,
+                                        int64_t m0, int64_t n0, int wm, int wn, int lane)
 {
     const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
     const rsrc_t rc = make_rsrc(g.C + m0 * g.ldc, ((rows - 1) * g.ldc + g.N) * 4);
@@ -544,6 +557,7 @@ __device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const GemmArgs &g
     for (int j = 0; j < C::NI; ++j) {
         const int64_t col = n0 + wn * C::WTN + j * 32 + (lane & 31);
         if (col < g.N) {
+            const float bval = bv[j];
             uint32_t lane_off = (uint32_t)col * 4u + (uint32_t)(wm * C::WTM + 4 * (lane >> 5)) * ldc4;
             // Opaque to the optimiser: otherwise it reassociates the 32 row
             // offsets below into tile-invariant values and keeps them all live.
@@ -558,6 +572,7 @@ __device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const GemmArgs &g
                     if constexpr (NB >= 3) v = __builtin_fmaf(acc.v[i][j][2][r], 0x1p-16f, v);
                     if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
                     v = v + acc.v[i][j][0][r];
+                    v = v + bval;
                     const uint32_t row = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, (int)(lane_off + row * ldc4), 0,
                                                           kStreamingStore);
@@ -580,6 +595,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
 
     Roles<C, BSRC> R;
     make_roles<C, BSRC, BVEC>(R, g, m0, n0);
+    float bias[C::NI];
+    load_bias<C>(bias, g, n0, wn, lane);
 
     Acc<C, NB> acc;
 #pragma unroll
@@ -625,7 +642,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
         mfma_slice<C, NB>(acc, f);
     }
 
-    store_c<C, NB>(acc, g, m0, n0, wm, wn, lane);
+    store_c<C, NB>(acc, bias, g, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------- N x K planes through LDS DMA
@@ -945,6 +962,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 
     int bs = 0;                                  // B ring slot of the current step
     for (;;) {
+        float bias[C::NI];                       // issued now, needed by the tile's epilogue
+        load_bias<C>(bias, g, cur.n0, wn, lane);
         // The next tile, or (none left) the current one again, whose steps
         // past K then serve as harmless dummy loads.
         const int64_t vn = (int64_t)v + G;
@@ -986,7 +1005,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             bs = b2;
         }
 
-        store_c<C, NB>(acc, g, cur.m0, cur.n0, wm, wn, lane);
+        store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
         if (!has_next) break;
         clear_acc<C, NB>(acc);
         v = (int)vn;
@@ -997,21 +1016,23 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 
 // ---------------------------------------------------------------- K == 0
 
-__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ C, int64_t ldc, int64_t M, int64_t N)
+__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ C, int64_t ldc, int64_t M, int64_t N,
+                                                   const float *__restrict__ bias)
 {
     const int64_t total = M * N;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-        const int64_t r = e / N;
-        C[r * ldc + (e - r * N)] = 0.0f;
+        const int64_t r = e / N, c = e - r * N;
+        C[r * ldc + c] = bias ? 0.0f + bias[c] : 0.0f;
     }
 }
 
-hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, int num_cus, hipStream_t stream)
+hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, const float *bias, int num_cus,
+                       hipStream_t stream)
 {
     int64_t blocks = (M * N + 255) / 256;
     if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, ldc, M, N);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, ldc, M, N, bias);
     return hipGetLastError();
 }
 

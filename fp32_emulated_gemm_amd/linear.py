@@ -1,0 +1,108 @@
+"""Linear layer on the BF16x9 emulated SGEMM (a thin torch op over the C ABI).
+
+The pages use the emulation as a drop-in for the FP32 matrix multiplication of
+the linear layers of an interatomic potential, keeping the trained weights and
+layer shapes (NVIDIA Technical Blog, "Unlocking Tensor Core Performance for
+Machine Learning Interatomic Potentials", section "TF32x3 on NVIDIA Ampere
+GPUs"; discuss.pytorch.kr summary, section "PyTorch에서 직접 써 보려면").
+Forces are gradients of the energy with respect to the inputs, so the layer
+provides the forward product and the input gradient, both emulated:
+
+    forward   Y  = X W^T + b      sgemm_emu_linear (W's planes as N x K)
+    backward  dX = dY W           sgemm_emu_presplit_b (the same planes as K x N)
+
+The weight [out_features][in_features] is split into its three BF16 planes
+once and reused until the weight tensor changes.  Parameter gradients (dW, db)
+are not provided: the layer is for fixed weights, its parameters are created
+with requires_grad=False, and a backward pass that would need them raises.
+"""
+import torch
+
+from . import SGEMM_EMU_B_KN, sgemm_emu_linear, sgemm_emu_presplit_b, split
+
+
+class WeightPlanes:
+    """The three BF16 planes of a [out][in] weight, re-split when the weight changes."""
+
+    def __init__(self):
+        self._key = None
+        self.planes = None
+
+    def get(self, weight):
+        key = (weight.data_ptr(), weight._version, tuple(weight.shape), weight.device)
+        if key != self._key:
+            self.planes = split(weight.detach().contiguous())
+            self._key = key
+        return self.planes
+
+
+class _LinearFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x2d, weight, bias, planes, nbands):
+        M, K = x2d.shape
+        N = weight.shape[0]
+        y = torch.empty((M, N), dtype=torch.float32, device=x2d.device)
+        sgemm_emu_linear(M, N, K, x2d, max(K, 1), planes[0], planes[1], planes[2], max(K, 1), bias, y,
+                         max(N, 1), nbands)
+        ctx.planes = planes
+        ctx.nbands = nbands
+        ctx.shape = (M, N, K)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        if ctx.needs_input_grad[1] or ctx.needs_input_grad[2]:
+            raise RuntimeError("fp32_emulated_gemm_amd.linear provides the input gradient only; "
+                               "set requires_grad=False on the weight and bias")
+        M, N, K = ctx.shape
+        p0, p1, p2 = ctx.planes
+        dy = dy.contiguous()
+        dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
+        sgemm_emu_presplit_b(M, K, N, dy, max(N, 1), p0, p1, p2, max(K, 1), SGEMM_EMU_B_KN, dx, max(K, 1),
+                             ctx.nbands)
+        return dx, None, None, None, None
+
+
+def linear(x, weight, bias=None, nbands=5, planes=None):
+    """Y = x W^T + b on the emulated GEMM, for float32 CUDA tensors x[..., in],
+    weight[out, in], bias[out].  `planes` (from `split(weight)`) skips the split."""
+    if x.dtype != torch.float32 or weight.dtype != torch.float32:
+        raise TypeError("linear expects float32 tensors")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (weight.shape[0],)):
+        raise ValueError("bias must be float32 of shape [out_features]")
+    if planes is None:
+        planes = split(weight.detach().contiguous())
+    lead = x.shape[:-1]
+    x2d = x.reshape(-1, x.shape[-1]).contiguous()
+    b = None if bias is None else bias.contiguous()
+    y = _LinearFn.apply(x2d, weight, b, planes, nbands)
+    return y.reshape(*lead, weight.shape[0])
+
+
+class Linear(torch.nn.Module):
+    """Drop-in for torch.nn.Linear (fixed weights) running on the emulated GEMM."""
+
+    def __init__(self, in_features, out_features, bias=True, nbands=5, device=None):
+        super().__init__()
+        self.in_features, self.out_features, self.nbands = in_features, out_features, nbands
+        self.weight = torch.nn.Parameter(torch.empty((out_features, in_features), device=device),
+                                         requires_grad=False)
+        self.bias = (torch.nn.Parameter(torch.zeros(out_features, device=device), requires_grad=False)
+                     if bias else None)
+        self._planes = WeightPlanes()
+
+    @classmethod
+    def from_linear(cls, layer, nbands=5):
+        m = cls(layer.in_features, layer.out_features, layer.bias is not None, nbands, layer.weight.device)
+        with torch.no_grad():
+            m.weight.copy_(layer.weight)
+            if layer.bias is not None:
+                m.bias.copy_(layer.bias)
+        return m
+
+    def forward(self, x):
+        return linear(x, self.weight, self.bias, self.nbands, self._planes.get(self.weight))
+
+    def extra_repr(self):
+        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+                f"bias={self.bias is not None}, nbands={self.nbands}")

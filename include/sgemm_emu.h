@@ -50,7 +50,8 @@
  *   layout takes a scalar-load path with the same arithmetic.
  *   Leading dimensions are limited to 8,388,544 elements (32-bit offsets
  *   inside a 128-row tile); larger ones give SGEMM_EMU_EINVAL.
- *   M == 0 or N == 0: nothing is done.  K == 0: C is set to zero.
+ *   M == 0 or N == 0: nothing is done.  K == 0: C is set to zero (plus the
+ *   bias, for sgemm_emu_linear).
  *   C must not overlap A or B (not checked).
  *   Column-major callers compute C^T = B^T A^T by swapping the operands.
  */
@@ -123,6 +124,30 @@ int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
                          int b_layout,
                          float *C, int64_t ldc,
                          int nbands, sgemm_emu_stream_t stream);
+
+/*
+ * sgemm_emu_linear -- the forward pass of a linear layer, Y = X W^T + bias, with
+ * the weight held as a linear layer stores it, W[out_features][in_features],
+ * and given as its three BF16 planes (split_f32_bf16x3 of W, split once and
+ * reused).  The pages use the emulation as a drop-in for the FP32 matrix
+ * multiplication inside such layers with the trained weights and shapes kept
+ * (NVIDIA blog, section "TF32x3 on NVIDIA Ampere GPUs"; discuss.pytorch.kr
+ * summary, section "PyTorch에서 직접 써 보려면").
+ *   X: M x K FP32 (ldx >= max(1, K)); W0, W1, W2: N x K planes (ldw >= max(1, K));
+ *   bias: N FP32 values or NULL; Y: M x N FP32 (ldy >= max(1, N)), written.
+ * Y[i][j] = fl32(C[i][j] + bias[j]) where C is sgemm_emu_presplit_b(...,
+ * SGEMM_EMU_B_NK, ...) on the same arguments: one FP32 rounding after the band
+ * recombination.  With bias == NULL, Y equals C bit for bit.  The input
+ * gradient dX = dY W of the same layer is sgemm_emu_presplit_b(M, K, N, dY, ldy,
+ * W0, W1, W2, ldw, SGEMM_EMU_B_KN, dX, ldx, nbands): the N x K planes of W are
+ * the K x N planes of the backward product.
+ */
+int sgemm_emu_linear(int64_t M, int64_t N, int64_t K,
+                     const float *X, int64_t ldx,
+                     const uint16_t *W0, const uint16_t *W1, const uint16_t *W2, int64_t ldw,
+                     const float *bias,
+                     float *Y, int64_t ldy,
+                     int nbands, sgemm_emu_stream_t stream);
 
 /*
  * split_f32_bf16x3 -- the split alone, as its own kernel: for every element of
