@@ -252,11 +252,16 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     res["sgemm_bf16x9_H@W2_tflops"] = round(fl / t / 1e9, 2)
     # the linear layer built on the same planes: forward with bias, and the input
     # gradient dX = dY W1 (W1's N x K planes read as K x N)
-    W1t_planes = fe.split(W1d.t().contiguous())
+    W1t_ = W1d.t().contiguous()                      # [out][in]
+    W1t_planes = fe.split(W1t_)
     bias1 = torch.zeros(F, dtype=torch.float32, device=Xd.device)
     t = timed(lambda: fe.sgemm_emu_linear(M, F, D, Xd, D, *W1t_planes, D, bias1, C1, F, 5, sp), stream, 5)
     res["linear_fwd_X@W1^T+b_tflops"] = round(fl / t / 1e9, 2)
     t = timed(lambda: fe.sgemm_emu_presplit_b(M, D, F, C1, F, *W1t_planes, D, fe.SGEMM_EMU_B_KN, C2, D, 5, sp),
+              stream, 5)
+    res["linear_dX=dY@W1_kn_planes_tflops"] = round(fl / t / 1e9, 2)
+    W1_planes = fe.split_t(W1t_)                    # planes of (W1t_)^T: N x K for dY W1t_
+    t = timed(lambda: fe.sgemm_emu_presplit_b(M, D, F, C1, F, *W1_planes, F, fe.SGEMM_EMU_B_NK, C2, D, 5, sp),
               stream, 5)
     res["linear_dX=dY@W1_tflops"] = round(fl / t / 1e9, 2)
     n = 4096

@@ -9,6 +9,7 @@ memory and streams only.  The functions keep the C names and argument order:
     sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nbands, stream=None)
     sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, Y, ldy, nbands, stream=None)
     split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
+    split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     sgemm_emu_products(nbands), sgemm_emu_strerror(status), sgemm_emu_version()
 
 Matrix arguments may be torch tensors (their data pointer is passed; they must
@@ -39,7 +40,7 @@ SGEMM_EMU_B_KN = 0   # pre-split planes K x N (split of B)
 SGEMM_EMU_B_NK = 1   # pre-split planes N x K (split of B^T, e.g. a weight stored [out][in])
 
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "sgemm_emu_linear", "split_f32_bf16x3",
-           "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
+           "split_f32_bf16x3_transposed", "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
 
 
 class SgemmEmuError(RuntimeError):
@@ -64,13 +65,14 @@ def lib():
         L.sgemm_emu_presplit_b.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, ci, vp, i64, ci, vp]
         L.sgemm_emu_linear.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp, i64, ci, vp]
         L.split_f32_bf16x3.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
+        L.split_f32_bf16x3_transposed.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.sgemm_emu_products.argtypes = [ci]
         L.sgemm_emu_strerror.argtypes = [ci]
         L.sgemm_emu_strerror.restype = ctypes.c_char_p
         L.sgemm_emu_version.argtypes = []
         L.sgemm_emu_version.restype = ctypes.c_char_p
         for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "sgemm_emu_linear", "split_f32_bf16x3",
-                  "sgemm_emu_products"):
+                  "split_f32_bf16x3_transposed", "sgemm_emu_products"):
             getattr(L, n).restype = ci
         _LIB = L
     return _LIB
@@ -135,6 +137,11 @@ def split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):
                                       _stream(stream)), "split_f32_bf16x3")
 
 
+def split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):
+    return _ok(lib().split_f32_bf16x3_transposed(rows, cols, _addr(X), ldx, _addr(X0), _addr(X1), _addr(X2), ldo,
+                                                 _stream(stream)), "split_f32_bf16x3_transposed")
+
+
 def sgemm_emu_products(nbands):
     return lib().sgemm_emu_products(nbands)
 
@@ -175,6 +182,14 @@ def split(X, stream=None):
     rows, cols = X.shape
     outs = [torch.empty((rows, cols), dtype=torch.int16, device=X.device) for _ in range(3)]
     split_f32_bf16x3(rows, cols, X, _ld(X), outs[0], outs[1], outs[2], max(cols, 1), stream)
+    return tuple(outs)
+
+
+def split_t(X, stream=None):
+    """The components of X^T (cols x rows) as three int16 tensors, from X directly."""
+    rows, cols = X.shape
+    outs = [torch.empty((cols, rows), dtype=torch.int16, device=X.device) for _ in range(3)]
+    split_f32_bf16x3_transposed(rows, cols, X, _ld(X), outs[0], outs[1], outs[2], max(rows, 1), stream)
     return tuple(outs)
 
 

@@ -242,6 +242,21 @@ int split_f32_bf16x3(int64_t rows, int64_t cols, const float *X, int64_t ldx, ui
     return launched(launch_split(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, (hipStream_t)stream));
 }
 
+int split_f32_bf16x3_transposed(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                                uint16_t *X1, uint16_t *X2, int64_t ldo, sgemm_emu_stream_t stream)
+{
+    int rc;
+    if (rows < 0 || cols < 0) return SGEMM_EMU_EINVAL;
+    if ((rc = check_matrix(rows, cols, X, ldx, 4)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(cols, rows, X0, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(cols, rows, X1, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(cols, rows, X2, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if (rows == 0 || cols == 0) return SGEMM_EMU_OK;
+    int num_cus = 0;
+    if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
+    return launched(launch_split_transpose(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, (hipStream_t)stream));
+}
+
 int sgemm_emu_products(int nbands)
 {
     static const int products[6] = {-1, 1, 3, 6, 8, 9};

@@ -35,6 +35,9 @@ __global__ __launch_bounds__(256) void split_vec8_kernel(
     }
 }
 
+// One element per thread (any layout).  TRANSPOSE writes the planes of X^T:
+// element (row, col) lands at col * ldo + row.
+template <bool TRANSPOSE>
 __global__ __launch_bounds__(256) void split_scalar_kernel(
     const float *__restrict__ X, int64_t ldx, uint16_t *__restrict__ X0, uint16_t *__restrict__ X1,
     uint16_t *__restrict__ X2, int64_t ldo, int64_t rows, int64_t cols)
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(
         uint32_t c0, c1, c2;
         float t = split_finite(x, c0, c1, c2);
         if (t != t) split_fix_special(x, c0, c1, c2);
-        const int64_t o = row * ldo + col;
+        const int64_t o = TRANSPOSE ? col * ldo + row : row * ldo + col;
         X0[o] = (uint16_t)(c0 >> 16);
         X1[o] = (uint16_t)(c1 >> 16);
         X2[o] = (uint16_t)(c2 >> 16);
@@ -63,7 +66,8 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(
 // run of each plane row; eight neighbouring lanes cover 128 contiguous bytes.
 // The LDS row pitch of 65 floats makes both the row-wise writes and the
 // column-wise reads free of bank conflicts.
-// Requires rows % 8 == 0, ldo % 8 == 0 and 16-byte aligned planes.
+// Requires rows % 8 == 0, ldo % 8 == 0 and 16-byte aligned planes; other
+// layouts take split_scalar_kernel<true>.
 constexpr int kTT = 64;
 
 __global__ __launch_bounds__(256) void split_transpose_kernel(
@@ -104,11 +108,15 @@ __global__ __launch_bounds__(256) void split_transpose_kernel(
 hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
                                   uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream)
 {
-    (void)num_cus;
-    if (rows % 8 != 0 || ldo % 8 != 0 || ldo < rows || !aligned(X0, 16) || !aligned(X1, 16) ||
-        !aligned(X2, 16))
-        return hipErrorInvalidValue;
     if (rows == 0 || cols == 0) return hipSuccess;
+    if (rows % 8 != 0 || ldo % 8 != 0 || !aligned(X0, 16) || !aligned(X1, 16) || !aligned(X2, 16)) {
+        const int threads = 256;
+        int64_t blocks = (rows * cols + threads - 1) / threads;
+        if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
+        hipLaunchKernelGGL(split_scalar_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, stream, X, ldx,
+                           X0, X1, X2, ldo, rows, cols);
+        return hipGetLastError();
+    }
     const int64_t tiles_c = (cols + kTT - 1) / kTT, tiles_r = (rows + kTT - 1) / kTT;
     if (tiles_r > (int64_t)0x7FFFFFFF / tiles_c) return hipErrorInvalidValue;
     hipLaunchKernelGGL(split_transpose_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, stream, X,
@@ -142,7 +150,7 @@ hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx,
         const int64_t total = rows * cols;
         int64_t blocks = (total + threads - 1) / threads;
         if (blocks > max_blocks) blocks = max_blocks;
-        hipLaunchKernelGGL(split_scalar_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, X, ldx,
+        hipLaunchKernelGGL(split_scalar_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, stream, X, ldx,
                            X0, X1, X2, ldo, rows, cols);
     }
     return hipGetLastError();

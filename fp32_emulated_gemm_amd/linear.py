@@ -8,21 +8,29 @@ GPUs"; discuss.pytorch.kr summary, section "PyTorch에서 직접 써 보려면")
 Forces are gradients of the energy with respect to the inputs, so the layer
 provides the forward product and the input gradient, both emulated:
 
-    forward   Y  = X W^T + b      sgemm_emu_linear (W's planes as N x K)
-    backward  dX = dY W           sgemm_emu_presplit_b (the same planes as K x N)
+    forward   Y  = X W^T + b      sgemm_emu_linear (W's planes, N x K)
+    backward  dX = dY W           sgemm_emu_presplit_b (the planes of W^T, N x K)
 
-The weight [out_features][in_features] is split into its three BF16 planes
-once and reused until the weight tensor changes.  Parameter gradients (dW, db)
+The weight [out_features][in_features] is split once into the planes of W and
+of W^T (the N x K layout is the one the GEMM copies straight into LDS for both
+products) and reused until the weight tensor changes.  Parameter gradients (dW, db)
 are not provided: the layer is for fixed weights, its parameters are created
 with requires_grad=False, and a backward pass that would need them raises.
 """
 import torch
 
-from . import SGEMM_EMU_B_KN, sgemm_emu_linear, sgemm_emu_presplit_b, split
+from . import SGEMM_EMU_B_NK, sgemm_emu_linear, sgemm_emu_presplit_b, split, split_t
+
+
+def split_weight(weight):
+    """(planes of W [out][in], planes of W^T [in][out]) for the forward product
+    and the input gradient."""
+    w = weight.detach().contiguous()
+    return split(w), split_t(w)
 
 
 class WeightPlanes:
-    """The three BF16 planes of a [out][in] weight, re-split when the weight changes."""
+    """split_weight of a [out][in] weight, redone when the weight changes."""
 
     def __init__(self):
         self._key = None
@@ -31,7 +39,7 @@ class WeightPlanes:
     def get(self, weight):
         key = (weight.data_ptr(), weight._version, tuple(weight.shape), weight.device)
         if key != self._key:
-            self.planes = split(weight.detach().contiguous())
+            self.planes = split_weight(weight)
             self._key = key
         return self.planes
 
@@ -42,9 +50,9 @@ class _LinearFn(torch.autograd.Function):
         M, K = x2d.shape
         N = weight.shape[0]
         y = torch.empty((M, N), dtype=torch.float32, device=x2d.device)
-        sgemm_emu_linear(M, N, K, x2d, max(K, 1), planes[0], planes[1], planes[2], max(K, 1), bias, y,
-                         max(N, 1), nbands)
-        ctx.planes = planes
+        w0, w1, w2 = planes[0]
+        sgemm_emu_linear(M, N, K, x2d, max(K, 1), w0, w1, w2, max(K, 1), bias, y, max(N, 1), nbands)
+        ctx.planes = planes[1]
         ctx.nbands = nbands
         ctx.shape = (M, N, K)
         return y
@@ -55,23 +63,23 @@ class _LinearFn(torch.autograd.Function):
             raise RuntimeError("fp32_emulated_gemm_amd.linear provides the input gradient only; "
                                "set requires_grad=False on the weight and bias")
         M, N, K = ctx.shape
-        p0, p1, p2 = ctx.planes
+        t0, t1, t2 = ctx.planes             # W^T: K x N of the backward product dY[M x N] W[N x K]
         dy = dy.contiguous()
         dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
-        sgemm_emu_presplit_b(M, K, N, dy, max(N, 1), p0, p1, p2, max(K, 1), SGEMM_EMU_B_KN, dx, max(K, 1),
+        sgemm_emu_presplit_b(M, K, N, dy, max(N, 1), t0, t1, t2, max(N, 1), SGEMM_EMU_B_NK, dx, max(K, 1),
                              ctx.nbands)
         return dx, None, None, None, None
 
 
 def linear(x, weight, bias=None, nbands=5, planes=None):
     """Y = x W^T + b on the emulated GEMM, for float32 CUDA tensors x[..., in],
-    weight[out, in], bias[out].  `planes` (from `split(weight)`) skips the split."""
+    weight[out, in], bias[out].  `planes` (from `split_weight(weight)`) skips the split."""
     if x.dtype != torch.float32 or weight.dtype != torch.float32:
         raise TypeError("linear expects float32 tensors")
     if bias is not None and (bias.dtype != torch.float32 or bias.shape != (weight.shape[0],)):
         raise ValueError("bias must be float32 of shape [out_features]")
     if planes is None:
-        planes = split(weight.detach().contiguous())
+        planes = split_weight(weight)
     lead = x.shape[:-1]
     x2d = x.reshape(-1, x.shape[-1]).contiguous()
     b = None if bias is None else bias.contiguous()

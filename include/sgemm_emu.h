@@ -140,7 +140,8 @@ int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
  * recombination.  With bias == NULL, Y equals C bit for bit.  The input
  * gradient dX = dY W of the same layer is sgemm_emu_presplit_b(M, K, N, dY, ldy,
  * W0, W1, W2, ldw, SGEMM_EMU_B_KN, dX, ldx, nbands): the N x K planes of W are
- * the K x N planes of the backward product.
+ * the K x N planes of the backward product.  Faster, with the same bits: the
+ * planes of W^T (split_f32_bf16x3_transposed of W) with SGEMM_EMU_B_NK.
  */
 int sgemm_emu_linear(int64_t M, int64_t N, int64_t K,
                      const float *X, int64_t ldx,
@@ -159,6 +160,20 @@ int split_f32_bf16x3(int64_t rows, int64_t cols,
                      const float *X, int64_t ldx,
                      uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo,
                      sgemm_emu_stream_t stream);
+
+/*
+ * split_f32_bf16x3_transposed -- the same split, written transposed: for the
+ * rows x cols FP32 matrix X (ldx >= max(1, cols)), X0, X1, X2 receive the
+ * components of X^T, a cols x rows matrix (leading dimension ldo >= max(1, rows)):
+ * element X[r][c] lands at X0[c*ldo + r].  Turns a K x N operand into N x K
+ * planes (SGEMM_EMU_B_NK), e.g. a linear layer's weight W [out][in] into the
+ * planes the input gradient dX = dY W reads fastest.  Bit-exact with
+ * split_f32_bf16x3 of the transposed matrix.
+ */
+int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
+                                const float *X, int64_t ldx,
+                                uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo,
+                                sgemm_emu_stream_t stream);
 
 /* Number of BF16 products evaluated for nbands (1, 3, 6, 8, 9), or -1 if invalid. */
 int sgemm_emu_products(int nbands);

@@ -104,6 +104,15 @@ def test_split_validation(L):
     assert L.split_f32_bf16x3(0, 4, 0, 4, 0, 0, 0, 4, None) == 0
 
 
+def test_split_transposed_validation(L):
+    # X is rows x cols (ldx >= cols); the planes are cols x rows (ldo >= rows)
+    assert L.split_f32_bf16x3_transposed(-1, 4, P, 4, P, P, P, 4, None) == -1
+    assert L.split_f32_bf16x3_transposed(6, 4, P, 3, P, P, P, 6, None) == -1
+    assert L.split_f32_bf16x3_transposed(6, 4, P, 4, P, P, P, 5, None) == -1
+    assert L.split_f32_bf16x3_transposed(6, 4, P, 4, P, 0, P, 6, None) == -2
+    assert L.split_f32_bf16x3_transposed(0, 4, 0, 4, 0, 0, 0, 1, None) == 0
+
+
 def test_valid_call_without_gpu_reports_arch(L):
     import torch
     if torch.cuda.is_available():

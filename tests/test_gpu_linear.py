@@ -99,6 +99,26 @@ def test_input_gradient_within_bound(fe, shape):
     check_against_fp64(host(dX), dY, W, label=f"dX {shape}")
 
 
+@pytest.mark.parametrize("shape", [(1100, 256, 1024), (300, 130, 64), (77, 1000, 96)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_input_gradient_transposed_planes_bitwise(fe, shape):
+    """dX = dY W from the planes of W^T (N x K, split_f32_bf16x3_transposed of W)
+    equals the K x N reading of W's own planes bit for bit."""
+    M, N, K = shape              # layer: in = K, out = N
+    g = _rng(3 * M + N + K)
+    W = g.standard_normal((N, K)).astype(np.float32)
+    dY = g.standard_normal((M, N)).astype(np.float32)
+    Wd, dYd = dev(W), dev(dY)
+    P = fe.split(Wd)
+    T = fe.split_t(Wd)
+    a = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    b = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    print(f"linear bwd planes M={M} N={N} K={K}", flush=True, file=sys.stderr)
+    fe.sgemm_emu_presplit_b(M, K, N, dYd, N, *P, K, fe.SGEMM_EMU_B_KN, a, K, 5)
+    fe.sgemm_emu_presplit_b(M, K, N, dYd, N, *T, N, fe.SGEMM_EMU_B_NK, b, K, 5)
+    assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+
+
 def test_torch_op_forward_and_input_gradient(fe, orc):
     from fp32_emulated_gemm_amd.linear import linear
     g = _rng(77)

@@ -63,3 +63,29 @@ def test_split_layouts(fe, orc, rows, cols, ldx, ldo, offset):
 
 def test_split_empty_is_noop(fe):
     fe.split_f32_bf16x3(0, 16, None, 16, None, None, None, 16)
+
+
+@pytest.mark.parametrize("rows,cols,ldx,ldo", [
+    (64, 64, 64, 64),           # one LDS tile
+    (256, 1024, 1024, 256),     # a [out][in] weight, tiled kernel
+    (1024, 257, 260, 1032),     # ragged columns, padded leading dimensions
+    (130, 70, 70, 130),         # rows not a multiple of 8: scalar kernel
+    (24, 5, 7, 40),
+])
+def test_split_transposed_bit_exact(fe, orc, rows, cols, ldx, ldo):
+    """split_f32_bf16x3_transposed(X) == the oracle's split of X^T, including
+    Inf, NaN, zeros and subnormals; padding of the planes untouched."""
+    g = np.random.Generator(np.random.Philox(key=rows * 7 + cols))
+    X = (g.standard_normal((rows, ldx)) * 2.0 ** g.integers(-60, 60, (rows, ldx))).astype(np.float32)
+    specials = [np.inf, -np.inf, np.nan, 0.0, -0.0, np.float32(1e-41), np.float32(-3e-39)]
+    for s, v in enumerate(specials):
+        X[(s * 5) % rows, (s * 3) % cols] = v
+    print(f"split transposed {rows}x{cols} ldx={ldx} ldo={ldo}", flush=True, file=sys.stderr)
+    planes = [torch.full((cols * ldo,), -1, dtype=torch.int16, device="cuda") for _ in range(3)]
+    fe.split_f32_bf16x3_transposed(rows, cols, torch.from_numpy(X).cuda(), ldx, *planes, ldo)
+    got = [p.reshape(cols, ldo) for p in _planes_host(planes)]
+    want = orc.split(np.ascontiguousarray(X[:, :cols].T))
+    for c in range(3):
+        assert np.array_equal(got[c][:, :rows], want[c])
+        if ldo > rows:
+            assert np.all(got[c][:, rows:] == 0xFFFF)
