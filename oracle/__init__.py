@@ -19,7 +19,7 @@ Functions:
   sgemm_naive_f32(A, B)   -> C, sequential FP32 accumulation (CPU baseline)
   gemm_emu(A, B, nbands)  -> C, scalar band emulation ([NVB] Fig. 1 caption)
   gemm_trunc_f64(A, B, b) -> T_b, the FP64 value of the kept products
-  gelu_f64_to_f32(x)      -> fp32(GELU(x)) with erf
+  gelu_f64_to_f32(x)      -> fp32(x Phi(x)), exact GELU (erfc form) in double
 """
 import ctypes
 import os
@@ -173,7 +173,7 @@ def gemm_trunc_f64(A, B, nbands=5, rows=None):
 
 
 def gelu_f64_to_f32(x):
-    """fp32(0.5 x (1 + erf(x / sqrt 2))) evaluated in double."""
+    """fp32(x Phi(x)) = fp32(0.5 x erfc(-x / sqrt 2)), evaluated in double."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     y = np.empty(x.shape, dtype=np.float32)
     if x.size:

@@ -278,17 +278,20 @@ int orc_gemm_trunc_f64(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
 }
 
 /*
- * GELU with the error function, y = fp32_RNE(0.5 x (1 + erf(x / sqrt 2))), taken
- * in double.  Used only to build the hidden activations between the two
- * linear layers of the small PET-like workload (the pages name no activation;
- * the workload does).
+ * GELU in its exact form, y = fp32_RNE(x Phi(x)) with Phi the standard normal
+ * CDF, taken in double.  Phi(x) = (1 + erf(x / sqrt 2)) / 2 = erfc(-x / sqrt 2) / 2;
+ * the erfc expression is used because 1 + erf(.) cancels for negative x
+ * (it is exactly 0 in double below x = -8.3, where x Phi(x) is still a normal
+ * FP32 number).  Builds the hidden activations between the two linear layers
+ * of the small PET-like workload, and is the reference of the fused GELU
+ * epilogue (the pages name no activation; the workload does).
  */
 int orc_gelu_f64_to_f32(int64_t n, const double *x, float *y)
 {
     if (n < 0) return ORC_EINVAL;
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i)
-        y[i] = (float)(0.5 * x[i] * (1.0 + erf(x[i] / sqrt(2.0))));
+        y[i] = (float)(0.5 * x[i] * erfc(-x[i] / sqrt(2.0)));
     return ORC_OK;
 }
 
