@@ -255,8 +255,11 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     W1t_ = W1d.t().contiguous()                      # [out][in]
     W1t_planes = fe.split(W1t_)
     bias1 = torch.zeros(F, dtype=torch.float32, device=Xd.device)
-    t = timed(lambda: fe.sgemm_emu_linear(M, F, D, Xd, D, *W1t_planes, D, bias1, C1, F, 5, sp), stream, 5)
+    t = timed(lambda: fe.sgemm_emu_linear(M, F, D, Xd, D, *W1t_planes, D, bias1, fe.SGEMM_EMU_ACT_NONE, C1, F, 5, sp), stream, 5)
     res["linear_fwd_X@W1^T+b_tflops"] = round(fl / t / 1e9, 2)
+    t = timed(lambda: fe.sgemm_emu_linear(M, F, D, Xd, D, *W1t_planes, D, bias1, fe.SGEMM_EMU_ACT_GELU, C1, F, 5,
+                                          sp), stream, 5)
+    res["linear_fwd_gelu(X@W1^T+b)_tflops"] = round(fl / t / 1e9, 2)
     t = timed(lambda: fe.sgemm_emu_presplit_b(M, D, F, C1, F, *W1t_planes, D, fe.SGEMM_EMU_B_KN, C2, D, 5, sp),
               stream, 5)
     res["linear_dX=dY@W1_kn_planes_tflops"] = round(fl / t / 1e9, 2)

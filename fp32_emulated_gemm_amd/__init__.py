@@ -7,7 +7,7 @@ memory and streams only.  The functions keep the C names and argument order:
     sgemm_bf16x9(M, N, K, A, lda, B, ldb, C, ldc, stream=None)
     sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream=None)
     sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nbands, stream=None)
-    sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, Y, ldy, nbands, stream=None)
+    sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, activation, Y, ldy, nbands, stream=None)
     split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     sgemm_emu_products(nbands), sgemm_emu_strerror(status), sgemm_emu_version()
@@ -38,6 +38,8 @@ SGEMM_EMU_EARCH = -3
 SGEMM_EMU_ELAUNCH = -4
 SGEMM_EMU_B_KN = 0   # pre-split planes K x N (split of B)
 SGEMM_EMU_B_NK = 1   # pre-split planes N x K (split of B^T, e.g. a weight stored [out][in])
+SGEMM_EMU_ACT_NONE = 0
+SGEMM_EMU_ACT_GELU = 1  # GELU, exact (erf) form
 
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "sgemm_emu_linear", "split_f32_bf16x3",
            "split_f32_bf16x3_transposed", "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
@@ -63,7 +65,7 @@ def lib():
         L.sgemm_bf16x9.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.sgemm_emu.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp]
         L.sgemm_emu_presplit_b.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, ci, vp, i64, ci, vp]
-        L.sgemm_emu_linear.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp, i64, ci, vp]
+        L.sgemm_emu_linear.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, ci, vp, i64, ci, vp]
         L.split_f32_bf16x3.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.split_f32_bf16x3_transposed.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.sgemm_emu_products.argtypes = [ci]
@@ -127,9 +129,9 @@ def sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nba
                "sgemm_emu_presplit_b")
 
 
-def sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, Y, ldy, nbands, stream=None):
+def sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, activation, Y, ldy, nbands, stream=None):
     return _ok(lib().sgemm_emu_linear(M, N, K, _addr(X), ldx, _addr(W0), _addr(W1), _addr(W2), ldw, _addr(bias),
-                                      _addr(Y), ldy, nbands, _stream(stream)), "sgemm_emu_linear")
+                                      activation, _addr(Y), ldy, nbands, _stream(stream)), "sgemm_emu_linear")
 
 
 def split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):

@@ -129,7 +129,8 @@ int launched(hipError_t e) { return e == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_E
 
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
-                int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr)
+                int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
+                int act = SGEMM_EMU_ACT_NONE)
 {
     int rc;
     if ((rc = check_dims(M, N, K)) != SGEMM_EMU_OK) return rc;
@@ -149,13 +150,14 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     }
     if ((rc = check_matrix(M, N, C, ldc, 4)) != SGEMM_EMU_OK) return rc;
     if (((uintptr_t)bias % 4) != 0) return SGEMM_EMU_EINVAL;
+    if (act != SGEMM_EMU_ACT_NONE && act != SGEMM_EMU_ACT_GELU) return SGEMM_EMU_EINVAL;
     // The kernels address one K step of a 128 x 128 tile with 32-bit byte offsets.
     if (lda > kMaxTileLd || ldb > kMaxTileLd) return SGEMM_EMU_EINVAL;
     if (M == 0 || N == 0) return SGEMM_EMU_OK;
 
     int num_cus = 0, dev = 0;
     if ((rc = current_device(&num_cus, &dev)) != SGEMM_EMU_OK) return rc;
-    if (K == 0) return launched(launch_zero(M, N, C, ldc, bias, num_cus, stream));
+    if (K == 0) return launched(launch_zero(M, N, C, ldc, bias, act, num_cus, stream));
 
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
@@ -163,6 +165,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     g.B = B; g.B0 = B0; g.B1 = B1; g.B2 = B2; g.ldb = ldb;
     g.C = C; g.ldc = ldc;
     g.bias = bias;
+    g.act = act;
     g.num_cus = num_cus;
 
     // FP32 B with many tile rows: split B once into N x K planes in a
@@ -220,11 +223,11 @@ int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K, const float *A, int64_
 }
 
 int sgemm_emu_linear(int64_t M, int64_t N, int64_t K, const float *X, int64_t ldx, const uint16_t *W0,
-                     const uint16_t *W1, const uint16_t *W2, int64_t ldw, const float *bias, float *Y, int64_t ldy,
-                     int nbands, sgemm_emu_stream_t stream)
+                     const uint16_t *W1, const uint16_t *W2, int64_t ldw, const float *bias, int activation,
+                     float *Y, int64_t ldy, int nbands, sgemm_emu_stream_t stream)
 {
     return gemm_common(M, N, K, X, ldx, nullptr, W0, W1, W2, ldw, Y, ldy, nbands, B_PLANES_NK,
-                       (hipStream_t)stream, bias);
+                       (hipStream_t)stream, bias, activation);
 }
 
 int split_f32_bf16x3(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0, uint16_t *X1,

@@ -523,11 +523,20 @@ __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC
     if (__builtin_expect(special, 0)) restage_special<C, BSRC, AVEC, BVEC>(R, g, m0, n0, k_next, nxt);
 }
 
+// GELU in its exact form, 0.5 z (1 + erf(z / sqrt(2))), evaluated as
+// 0.5 z erfc(-z / sqrt(2)): the same function, without the cancellation of
+// 1 + erf(.) for negative z, so the relative error stays a few ulp.
+__device__ __forceinline__ float gelu_erf(float z)
+{
+    return (0.5f * z) * erfcf(z * -0.70710678118654752f);
+}
+
 // Cache policy of the C stores: non-temporal (streamed past L2), so the
 // output does not evict the A and B panels other tiles still read.
 constexpr int kStreamingStore = 2;
 
-// Recombine the bands smallest first, add the bias (if any) and store the tile.  The stores are
+// Recombine the bands smallest first, add the bias (if any), apply the
+// activation (if any) and store the tile.  The stores are
 // raw buffer stores through a descriptor that starts at the tile's first row
 // and ends at element (last row of C inside the tile, N-1): rows past M fall
 // outside it and are dropped by the hardware range check, so only the
@@ -545,9 +554,9 @@ __device__ __forceinline__ void load_bias(float (&bv)[C::NI], const GemmArgs &g,
     }
 }
 
-template <class C, int NB>
-__device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const float (&bv)[C::NI], const GemmArgs &g,
-                                        int64_t m0, int64_t n0, int wm, int wn, int lane)
+template <class C, int NB, int ACT>
+__device__ __forceinline__ void store_c_act(const Acc<C, NB> &acc, const float (&bv)[C::NI], const GemmArgs &g,
+                                            int64_t m0, int64_t n0, int wm, int wn, int lane)
 {
     const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
     const rsrc_t rc = make_rsrc(g.C + m0 * g.ldc, ((rows - 1) * g.ldc + g.N) * 4);
@@ -573,6 +582,7 @@ __device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const float (&bv)
                     if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
                     v = v + acc.v[i][j][0][r];
                     v = v + bval;
+                    if constexpr (ACT == 1) v = gelu_erf(v);
                     const uint32_t row = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, (int)(lane_off + row * ldc4), 0,
                                                           kStreamingStore);
@@ -580,6 +590,16 @@ __device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const float (&bv)
             }
         }
     }
+}
+
+// The epilogue with the activation chosen once per tile (a straight-line body
+// per activation, rather than a test per element).
+template <class C, int NB>
+__device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const float (&bv)[C::NI], const GemmArgs &g,
+                                        int64_t m0, int64_t n0, int wm, int wn, int lane)
+{
+    if (g.act == 1) store_c_act<C, NB, 1>(acc, bv, g, m0, n0, wm, wn, lane);
+    else store_c_act<C, NB, 0>(acc, bv, g, m0, n0, wm, wn, lane);
 }
 
 template <class C, int NB, bool AVEC, int BSRC, bool BVEC>
@@ -1017,22 +1037,24 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 // ---------------------------------------------------------------- K == 0
 
 __global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ C, int64_t ldc, int64_t M, int64_t N,
-                                                   const float *__restrict__ bias)
+                                                   const float *__restrict__ bias, int act)
 {
     const int64_t total = M * N;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
         const int64_t r = e / N, c = e - r * N;
-        C[r * ldc + c] = bias ? 0.0f + bias[c] : 0.0f;
+        float v = bias ? 0.0f + bias[c] : 0.0f;
+        if (act == 1) v = gelu_erf(v);
+        C[r * ldc + c] = v;
     }
 }
 
-hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, const float *bias, int num_cus,
+hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, const float *bias, int act, int num_cus,
                        hipStream_t stream)
 {
     int64_t blocks = (M * N + 255) / 256;
     if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, ldc, M, N, bias);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, ldc, M, N, bias, act);
     return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct GemmArgs {
     float *C;
     int64_t ldc;
     const float *bias;       // N values added to every row of C, or null
+    int act;                 // activation applied last: 0 none, 1 GELU (erf form)
     int tiles_m, tiles_n;
     int group_m;             // tile-rows per group of the tile order
     int num_cus;             // compute units of the device (persistent grids)
@@ -43,8 +44,8 @@ hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream
 // True when launch_gemm takes the LDS-DMA kernel for N x K planes of this shape.
 bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const void *B2);
 
-// C := 0 (K == 0), plus bias[j] in column j when bias is not null.
-hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, const float *bias, int num_cus,
+// C := act(0 + bias[j]) (K == 0); without bias and activation C := 0.
+hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, const float *bias, int act, int num_cus,
                        hipStream_t stream);
 
 }  // namespace sgemm_emu_dev

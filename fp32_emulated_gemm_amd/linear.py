@@ -19,7 +19,10 @@ with requires_grad=False, and a backward pass that would need them raises.
 """
 import torch
 
-from . import SGEMM_EMU_B_NK, sgemm_emu_linear, sgemm_emu_presplit_b, split, split_t
+from . import (SGEMM_EMU_ACT_GELU, SGEMM_EMU_ACT_NONE, SGEMM_EMU_B_NK, sgemm_emu_linear, sgemm_emu_presplit_b, split,
+               split_t)
+
+_ACTIVATIONS = {None: SGEMM_EMU_ACT_NONE, "gelu": SGEMM_EMU_ACT_GELU}
 
 
 def split_weight(weight):
@@ -46,12 +49,12 @@ class WeightPlanes:
 
 class _LinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x2d, weight, bias, planes, nbands):
+    def forward(ctx, x2d, weight, bias, planes, nbands, act):
         M, K = x2d.shape
         N = weight.shape[0]
         y = torch.empty((M, N), dtype=torch.float32, device=x2d.device)
         w0, w1, w2 = planes[0]
-        sgemm_emu_linear(M, N, K, x2d, max(K, 1), w0, w1, w2, max(K, 1), bias, y, max(N, 1), nbands)
+        sgemm_emu_linear(M, N, K, x2d, max(K, 1), w0, w1, w2, max(K, 1), bias, act, y, max(N, 1), nbands)
         ctx.planes = planes[1]
         ctx.nbands = nbands
         ctx.shape = (M, N, K)
@@ -68,14 +71,21 @@ class _LinearFn(torch.autograd.Function):
         dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
         sgemm_emu_presplit_b(M, K, N, dy, max(N, 1), t0, t1, t2, max(N, 1), SGEMM_EMU_B_NK, dx, max(K, 1),
                              ctx.nbands)
-        return dx, None, None, None, None
+        return dx, None, None, None, None, None
 
 
-def linear(x, weight, bias=None, nbands=5, planes=None):
-    """Y = x W^T + b on the emulated GEMM, for float32 CUDA tensors x[..., in],
-    weight[out, in], bias[out].  `planes` (from `split_weight(weight)`) skips the split."""
+def linear(x, weight, bias=None, nbands=5, planes=None, activation=None):
+    """Y = act(x W^T + b) on the emulated GEMM, for float32 CUDA tensors x[..., in],
+    weight[out, in], bias[out]; activation None or "gelu" (exact erf form, fused
+    into the GEMM's epilogue, forward only).  `planes` (from
+    `split_weight(weight)`) skips the split."""
     if x.dtype != torch.float32 or weight.dtype != torch.float32:
         raise TypeError("linear expects float32 tensors")
+    if activation not in _ACTIVATIONS:
+        raise ValueError(f"unknown activation {activation!r}")
+    act = _ACTIVATIONS[activation]
+    if act != SGEMM_EMU_ACT_NONE and torch.is_grad_enabled() and x.requires_grad:
+        raise NotImplementedError("the fused activation runs forward only; apply it separately to differentiate")
     if bias is not None and (bias.dtype != torch.float32 or bias.shape != (weight.shape[0],)):
         raise ValueError("bias must be float32 of shape [out_features]")
     if planes is None:
@@ -83,16 +93,17 @@ def linear(x, weight, bias=None, nbands=5, planes=None):
     lead = x.shape[:-1]
     x2d = x.reshape(-1, x.shape[-1]).contiguous()
     b = None if bias is None else bias.contiguous()
-    y = _LinearFn.apply(x2d, weight, b, planes, nbands)
+    y = _LinearFn.apply(x2d, weight, b, planes, nbands, act)
     return y.reshape(*lead, weight.shape[0])
 
 
 class Linear(torch.nn.Module):
     """Drop-in for torch.nn.Linear (fixed weights) running on the emulated GEMM."""
 
-    def __init__(self, in_features, out_features, bias=True, nbands=5, device=None):
+    def __init__(self, in_features, out_features, bias=True, nbands=5, device=None, activation=None):
         super().__init__()
         self.in_features, self.out_features, self.nbands = in_features, out_features, nbands
+        self.activation = activation
         self.weight = torch.nn.Parameter(torch.empty((out_features, in_features), device=device),
                                          requires_grad=False)
         self.bias = (torch.nn.Parameter(torch.zeros(out_features, device=device), requires_grad=False)
@@ -109,8 +120,8 @@ class Linear(torch.nn.Module):
         return m
 
     def forward(self, x):
-        return linear(x, self.weight, self.bias, self.nbands, self._planes.get(self.weight))
+        return linear(x, self.weight, self.bias, self.nbands, self._planes.get(self.weight), self.activation)
 
     def extra_repr(self):
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
-                f"bias={self.bias is not None}, nbands={self.nbands}")
+                f"bias={self.bias is not None}, nbands={self.nbands}, activation={self.activation}")

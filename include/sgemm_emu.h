@@ -125,8 +125,14 @@ int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
                          float *C, int64_t ldc,
                          int nbands, sgemm_emu_stream_t stream);
 
+/* Activation applied by sgemm_emu_linear after the bias. */
+enum sgemm_emu_activation {
+    SGEMM_EMU_ACT_NONE = 0,
+    SGEMM_EMU_ACT_GELU = 1   /* GELU, exact (erf) form: 0.5 z (1 + erf(z / sqrt(2))) */
+};
+
 /*
- * sgemm_emu_linear -- the forward pass of a linear layer, Y = X W^T + bias, with
+ * sgemm_emu_linear -- the forward pass of a linear layer, Y = act(X W^T + bias), with
  * the weight held as a linear layer stores it, W[out_features][in_features],
  * and given as its three BF16 planes (split_f32_bf16x3 of W, split once and
  * reused).  The pages use the emulation as a drop-in for the FP32 matrix
@@ -134,10 +140,14 @@ int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
  * (NVIDIA blog, section "TF32x3 on NVIDIA Ampere GPUs"; discuss.pytorch.kr
  * summary, section "PyTorch에서 직접 써 보려면").
  *   X: M x K FP32 (ldx >= max(1, K)); W0, W1, W2: N x K planes (ldw >= max(1, K));
- *   bias: N FP32 values or NULL; Y: M x N FP32 (ldy >= max(1, N)), written.
- * Y[i][j] = fl32(C[i][j] + bias[j]) where C is sgemm_emu_presplit_b(...,
+ *   bias: N FP32 values or NULL; activation: SGEMM_EMU_ACT_NONE or
+ *   SGEMM_EMU_ACT_GELU (anything else gives SGEMM_EMU_EINVAL);
+ *   Y: M x N FP32 (ldy >= max(1, N)), written.
+ * Z[i][j] = fl32(C[i][j] + bias[j]) where C is sgemm_emu_presplit_b(...,
  * SGEMM_EMU_B_NK, ...) on the same arguments: one FP32 rounding after the band
- * recombination.  With bias == NULL, Y equals C bit for bit.  The input
+ * recombination.  With bias == NULL, Z equals C bit for bit.  Y = Z without an
+ * activation; with SGEMM_EMU_ACT_GELU, Y = GELU(Z) in FP32 (erfc-based, a few
+ * ulp from the correctly rounded value, fused into the GEMM's epilogue).  The input
  * gradient dX = dY W of the same layer is sgemm_emu_presplit_b(M, K, N, dY, ldy,
  * W0, W1, W2, ldw, SGEMM_EMU_B_KN, dX, ldx, nbands): the N x K planes of W are
  * the K x N planes of the backward product.  Faster, with the same bits: the
@@ -146,7 +156,7 @@ int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
 int sgemm_emu_linear(int64_t M, int64_t N, int64_t K,
                      const float *X, int64_t ldx,
                      const uint16_t *W0, const uint16_t *W1, const uint16_t *W2, int64_t ldw,
-                     const float *bias,
+                     const float *bias, int activation,
                      float *Y, int64_t ldy,
                      int nbands, sgemm_emu_stream_t stream);
 

@@ -84,16 +84,18 @@ def test_presplit_validation(L):
 
 
 def test_linear_validation(L):
-    # sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, Y, ldy, nbands, stream); W is N x K
-    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 5, None, P, 8, 5, None) == -1    # ldw < K
-    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, 0, 6, None, P, 8, 5, None) == -2    # null plane
-    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, P + 2, P, 8, 5, None) == -1   # misaligned bias
-    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, None, P, 7, 5, None) == -1    # ldy < N
-    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, P, P, 8, 0, None) == -1       # nbands
-    assert L.sgemm_emu_linear(0, 8, 6, 0, 6, P, P, P, 6, P, 0, 8, 5, None) == 0        # empty
+    # sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, act, Y, ldy, nbands, stream); W is N x K
+    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 5, None, 0, P, 8, 5, None) == -1    # ldw < K
+    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, 0, 6, None, 0, P, 8, 5, None) == -2    # null plane
+    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, P + 2, 0, P, 8, 5, None) == -1   # misaligned bias
+    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, None, 0, P, 7, 5, None) == -1    # ldy < N
+    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, P, 0, P, 8, 0, None) == -1       # nbands
+    assert L.sgemm_emu_linear(0, 8, 6, 0, 6, P, P, P, 6, P, 0, 0, 8, 5, None) == 0        # empty
+    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, P, 2, P, 8, 5, None) == -1       # activation
+    assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, P, -1, P, 8, 5, None) == -1
     import torch
     if not torch.cuda.is_available():
-        assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, P, P, 8, 5, None) == -3
+        assert L.sgemm_emu_linear(4, 8, 6, P, 6, P, P, P, 6, P, 0, P, 8, 5, None) == -3
 
 
 def test_split_validation(L):

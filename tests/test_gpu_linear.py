@@ -30,15 +30,26 @@ def _planes(fe, W):
     return fe.split(dev(W))
 
 
-def _forward(fe, X, W, b, nbands=5):
+def _forward(fe, X, W, b, nbands=5, act=0):
     M, K = X.shape
     N = W.shape[0]
-    print(f"linear fwd M={M} N={N} K={K} bias={b is not None} nbands={nbands}", flush=True, file=sys.stderr)
+    print(f"linear fwd M={M} N={N} K={K} bias={b is not None} nbands={nbands} act={act}", flush=True,
+          file=sys.stderr)
     P = _planes(fe, W)
     Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-    fe.sgemm_emu_linear(M, N, K, dev(X), max(K, 1), *P, max(K, 1), None if b is None else dev(b), Y, max(N, 1),
-                        nbands)
+    fe.sgemm_emu_linear(M, N, K, dev(X), max(K, 1), *P, max(K, 1), None if b is None else dev(b), act, Y,
+                        max(N, 1), nbands)
     return host(Y)
+
+
+def gelu_tolerance(z, e):
+    """Allowed |GELU_gpu - fp32(GELU(z))| at the exact pre-activation z, for an
+    FP32 erfc-form evaluation: the rounded argument z/sqrt 2 (2 ulp, amplified
+    by |d ln erfc(x)/dx| <= 2|x| + 1.2 in the tail, x = z/sqrt 2), the erfc
+    evaluation and the final product (16 ulp in all), the oracle's own rounding,
+    plus a floor for results below the normal range."""
+    x = np.abs(z) / np.sqrt(2.0)
+    return (16.0 + 4.0 * x * (x + 0.6)) * U * np.abs(e) + 2.0 ** -140
 
 
 LIN_SHAPES = [(1, 1, 1), (37, 70, 33), (300, 257, 128), (1000, 1030, 256), (2048, 1024, 256), (129, 64, 100)]
@@ -82,6 +93,39 @@ def test_forward_bands_and_k_zero(fe, nbands):
     b[0] = -0.0
     Y = _forward(fe, np.zeros((9, 0), np.float32), np.zeros((40, 0), np.float32), b, nbands)
     assert np.array_equal(Y.view(np.uint32), np.broadcast_to((np.float32(0) + b), (9, 40)).view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(37, 70, 33), (300, 257, 128), (2048, 1024, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_forward_gelu_epilogue_vs_oracle(fe, orc, shape):
+    """Y = GELU(X W^T + b) fused in the epilogue against the oracle's exact GELU of
+    its FP64 pre-activation: the GEMM bound carried through GELU (slope <= 1.13)
+    plus the evaluation tolerance."""
+    M, N, K = shape
+    g = _rng(M * 5 + N * 3 + K)
+    X = g.standard_normal((M, K)).astype(np.float32)
+    W = (g.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    b = (2.0 * g.standard_normal(N)).astype(np.float32)
+    Y = _forward(fe, X, W, b, act=fe.SGEMM_EMU_ACT_GELU).astype(np.float64)
+    Z, G = orc.gemm_f64(X, np.ascontiguousarray(W.T))
+    Z = Z + b.astype(np.float64)[None, :]
+    E = orc.gelu_f64_to_f32(Z).astype(np.float64)
+    e_gemm = 2.0 * K * U * G + 9.0 * K * FLOOR + U * np.abs(Z)
+    assert np.all(np.abs(Y - E) <= 1.13 * e_gemm + gelu_tolerance(Z, E))
+    assert (Z < -5).any() and (Z > 5).any()          # both tails exercised
+
+
+def test_gelu_epilogue_k_zero_and_extremes(fe, orc):
+    """K = 0: Y = GELU(0 + b); b spans the far negative tail, zeros and large values."""
+    b = np.array([-0.0, 0.0, -12.0, -9.0, -6.0, -3.0, -1.0, -1e-3, 1e-3, 1.0, 3.0, 10.0, 1e30, -1e30, 1e-40],
+                 np.float32)
+    Y = _forward(fe, np.zeros((3, 0), np.float32), np.zeros((b.size, 0), np.float32), b,
+                 act=fe.SGEMM_EMU_ACT_GELU).astype(np.float64)
+    z = (np.float32(0) + b).astype(np.float64)
+    E = orc.gelu_f64_to_f32(z).astype(np.float64)
+    fin = np.isfinite(E)
+    assert np.all(np.abs(Y[:, fin] - E[fin]) <= gelu_tolerance(z[fin], E[fin]))
+    assert np.all(Y[:, 13] == 0.0) and np.all(Y[:, 12] == np.float32(1e30))
 
 
 @pytest.mark.parametrize("shape", [(300, 257, 128), (1024, 256, 1024), (77, 1000, 96)],
@@ -136,6 +180,23 @@ def test_torch_op_forward_and_input_gradient(fe, orc):
     ref += b[None, :]
     assert np.all(np.abs(Y - ref) <= 2.0 * K * U * G + 9.0 * K * FLOOR + U * np.abs(ref))
     check_against_fp64(host(x.grad).reshape(-1, K), Gy.reshape(-1, N), W, label="torch op dX")
+
+
+def test_torch_op_gelu_forward_only(fe):
+    from fp32_emulated_gemm_amd.linear import Linear, linear
+    torch.manual_seed(1)
+    ref_layer = torch.nn.Linear(96, 40).cuda()
+    m = Linear.from_linear(ref_layer)
+    m.activation = "gelu"
+    x = torch.randn(300, 96, device="cuda")
+    with torch.no_grad():
+        y = m(x)
+        y_ref = torch.nn.functional.gelu(ref_layer(x))
+    assert torch.allclose(y, y_ref, rtol=1e-5, atol=1e-6)
+    with pytest.raises(NotImplementedError):
+        linear(x.requires_grad_(True), m.weight, m.bias, activation="gelu")
+    with pytest.raises(ValueError):
+        linear(x.detach(), m.weight, m.bias, activation="relu")
 
 
 def test_module_matches_nn_linear_and_refuses_parameter_grads(fe):
