@@ -10,6 +10,7 @@ memory and streams only.  The functions keep the C names and argument order:
     sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, activation, Y, ldy, nbands, stream=None)
     split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
+    sgemm_emu_split_k(M, N, K, nbands)
     sgemm_emu_products(nbands), sgemm_emu_strerror(status), sgemm_emu_version()
 
 Matrix arguments may be torch tensors (their data pointer is passed; they must
@@ -42,7 +43,8 @@ SGEMM_EMU_ACT_NONE = 0
 SGEMM_EMU_ACT_GELU = 1  # GELU, exact (erf) form
 
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "sgemm_emu_linear", "split_f32_bf16x3",
-           "split_f32_bf16x3_transposed", "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
+           "split_f32_bf16x3_transposed", "sgemm_emu_split_k", "sgemm_emu_products", "sgemm_emu_strerror",
+           "sgemm_emu_version")
 
 
 class SgemmEmuError(RuntimeError):
@@ -68,13 +70,14 @@ def lib():
         L.sgemm_emu_linear.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, ci, vp, i64, ci, vp]
         L.split_f32_bf16x3.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.split_f32_bf16x3_transposed.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
+        L.sgemm_emu_split_k.argtypes = [i64, i64, i64, ci]
         L.sgemm_emu_products.argtypes = [ci]
         L.sgemm_emu_strerror.argtypes = [ci]
         L.sgemm_emu_strerror.restype = ctypes.c_char_p
         L.sgemm_emu_version.argtypes = []
         L.sgemm_emu_version.restype = ctypes.c_char_p
         for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "sgemm_emu_linear", "split_f32_bf16x3",
-                  "split_f32_bf16x3_transposed", "sgemm_emu_products"):
+                  "split_f32_bf16x3_transposed", "sgemm_emu_split_k", "sgemm_emu_products"):
             getattr(L, n).restype = ci
         _LIB = L
     return _LIB
@@ -142,6 +145,11 @@ def split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):
 def split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):
     return _ok(lib().split_f32_bf16x3_transposed(rows, cols, _addr(X), ldx, _addr(X0), _addr(X1), _addr(X2), ldo,
                                                  _stream(stream)), "split_f32_bf16x3_transposed")
+
+
+def sgemm_emu_split_k(M, N, K, nbands=5):
+    status = lib().sgemm_emu_split_k(M, N, K, nbands)
+    return _ok(status, "sgemm_emu_split_k") if status < 0 else status
 
 
 def sgemm_emu_products(nbands):

@@ -168,31 +168,64 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     g.act = act;
     g.num_cus = num_cus;
 
+    g.splits = 1;
+
     // FP32 B with many tile rows: split B once into N x K planes in a
     // stream-ordered workspace and run the LDS-DMA kernel, instead of splitting
     // B again in every tile row.  Same split, same products, same order of
     // MFMA accumulation, so the result is bitwise identical.
     hipMemPool_t pool = nullptr;
+    void *bws = nullptr;
     if (bsrc == B_FP32 && K % 64 == 0 && M >= kPresplitMinRows && (uint64_t)K * (uint64_t)N <= kPresplitMaxElems &&
         (pool = workspace_pool(dev)) != nullptr) {
         const int64_t ldo = K;
         const size_t plane = (size_t)N * (size_t)ldo * sizeof(uint16_t);
         const size_t plane_pad = (plane + 255) & ~(size_t)255;
-        void *ws = nullptr;
-        if (hipMallocFromPoolAsync(&ws, 3 * plane_pad, pool, stream) == hipSuccess && ws != nullptr) {
-            uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
-                     *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
-            hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, ldo, num_cus, stream);
-            if (e == hipSuccess) {
-                g.B0 = P0; g.B1 = P1; g.B2 = P2; g.ldb = ldo;
-                e = launch_gemm(g, nbands, B_PLANES_NK, stream);
+        if (hipMallocFromPoolAsync(&bws, 3 * plane_pad, pool, stream) == hipSuccess && bws != nullptr) {
+            uint16_t *P0 = (uint16_t *)bws, *P1 = (uint16_t *)((char *)bws + plane_pad),
+                     *P2 = (uint16_t *)((char *)bws + 2 * plane_pad);
+            const hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, ldo, num_cus, stream);
+            if (e != hipSuccess) {
+                (void)hipFreeAsync(bws, stream);
+                return launched(e);
             }
-            const hipError_t f = hipFreeAsync(ws, stream);
-            return launched(e == hipSuccess ? f : e);
+            g.B0 = P0; g.B1 = P1; g.B2 = P2; g.ldb = ldo;
+            bsrc = B_PLANES_NK;
+        } else {
+            bws = nullptr;
+            (void)hipGetLastError();   // no workspace: the GEMM splits B itself
         }
-        (void)hipGetLastError();   // no workspace: fall through to the in-kernel split
     }
-    return launched(launch_gemm(g, nbands, bsrc, stream));
+
+    // Grids that would leave CUs idle on the N x K DMA kernel are split along
+    // K: each (tile, K slice) recombines its own bands and writes the result to
+    // a pooled partial buffer; a reduction kernel adds the slices in order.
+    void *pws = nullptr;
+    if (bsrc == B_PLANES_NK && gemm_uses_dma(K, g.ldb, g.B0, g.B1, g.B2)) {
+        const int sl = gemm_split_count(M, N, K, nbands, num_cus);
+        if (sl > 1 && (pool != nullptr || (pool = workspace_pool(dev)) != nullptr)) {
+            const size_t bytes = (size_t)sl * (size_t)M * (size_t)N * sizeof(float);
+            if (hipMallocFromPoolAsync(&pws, bytes, pool, stream) == hipSuccess && pws != nullptr) {
+                g.splits = sl;
+                g.partials = (float *)pws;
+                g.ldp = N;
+            } else {
+                pws = nullptr;
+                (void)hipGetLastError();   // no buffer: one unit per tile
+            }
+        }
+    }
+
+    hipError_t e = launch_gemm(g, nbands, bsrc, stream);
+    if (pws != nullptr) {
+        const hipError_t f = hipFreeAsync(pws, stream);
+        if (e == hipSuccess) e = f;
+    }
+    if (bws != nullptr) {
+        const hipError_t f = hipFreeAsync(bws, stream);
+        if (e == hipSuccess) e = f;
+    }
+    return launched(e);
 }
 
 }  // namespace
@@ -258,6 +291,17 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols, const float *X, int6
     int num_cus = 0;
     if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
     return launched(launch_split_transpose(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, (hipStream_t)stream));
+}
+
+int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands)
+{
+    int rc;
+    if ((rc = check_dims(M, N, K)) != SGEMM_EMU_OK) return rc;
+    if (nbands < 1 || nbands > 5) return SGEMM_EMU_EINVAL;
+    int num_cus = 0;
+    if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
+    if (M == 0 || N == 0 || K == 0) return 1;
+    return gemm_split_count(M, N, K, nbands, num_cus);
 }
 
 int sgemm_emu_products(int nbands)

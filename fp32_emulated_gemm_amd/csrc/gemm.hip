@@ -554,14 +554,18 @@ __device__ __forceinline__ void load_bias(float (&bv)[C::NI], const GemmArgs &g,
     }
 }
 
+// ACT: 0 none, 1 GELU; ACT = -1 writes the recombined K-slice result `slice`
+// to the split-K partial buffer instead (no bias, no activation).
 template <class C, int NB, int ACT>
 __device__ __forceinline__ void store_c_act(const Acc<C, NB> &acc, const float (&bv)[C::NI], const GemmArgs &g,
-                                            int64_t m0, int64_t n0, int wm, int wn, int lane)
+                                            int64_t m0, int64_t n0, int wm, int wn, int lane, int slice = 0)
 {
     const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
-    const rsrc_t rc = make_rsrc(g.C + m0 * g.ldc, ((rows - 1) * g.ldc + g.N) * 4);
+    float *const dst = ACT < 0 ? g.partials + (int64_t)slice * g.M * g.ldp : g.C;
+    const int64_t ld = ACT < 0 ? g.ldp : g.ldc;
+    const rsrc_t rc = make_rsrc(dst + m0 * ld, ((rows - 1) * ld + g.N) * 4);
     // 128 rows of C fit 32-bit byte offsets (leading dimensions are limited)
-    const uint32_t ldc4 = (uint32_t)g.ldc * 4u;
+    const uint32_t ldc4 = (uint32_t)ld * 4u;
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
         const int64_t col = n0 + wn * C::WTN + j * 32 + (lane & 31);
@@ -581,7 +585,7 @@ __device__ __forceinline__ void store_c_act(const Acc<C, NB> &acc, const float (
                     if constexpr (NB >= 3) v = __builtin_fmaf(acc.v[i][j][2][r], 0x1p-16f, v);
                     if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
                     v = v + acc.v[i][j][0][r];
-                    v = v + bval;
+                    if constexpr (ACT >= 0) v = v + bval;
                     if constexpr (ACT == 1) v = gelu_erf(v);
                     const uint32_t row = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, (int)(lane_off + row * ldc4), 0,
@@ -839,6 +843,8 @@ __device__ __forceinline__ void a_offsets(uint32_t (&a_off)[C::A_CHUNKS], const 
 template <class C>
 struct StepSrc {
     int64_t m0, n0, k0;
+    int64_t kb;                  // first k of the work unit (its K slice)
+    int slice;                   // K slice of the work unit (split-K), 0 without split
     uint32_t a_off[C::A_CHUNKS];
 };
 
@@ -926,6 +932,22 @@ __device__ __forceinline__ void clear_acc(Acc<C, NB> &acc)
                 acc.v[i][j][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16_t{}, 0, 0, 0);
 }
 
+// Work unit v -> its tile, K slice and first k.  Without split-K a unit is a
+// tile; with S slices, unit v covers K slice v / T of tile v % T.
+template <class C>
+__device__ __forceinline__ void unit_src(StepSrc<C> &u, int v, int T, int64_t steps_per_unit, const GemmArgs &g)
+{
+    const int t = v % T, sl = v / T;
+    int tm, tn;
+    tile_of_index(t, T, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    u.m0 = (int64_t)tm * C::BM;
+    u.n0 = (int64_t)tn * C::BN;
+    u.slice = sl;
+    u.kb = (int64_t)sl * steps_per_unit * BK;
+    u.k0 = u.kb;
+    a_offsets<C>(u.a_off, g, u.m0);
+}
+
 // Persistent: one workgroup per CU walks tiles v = blockIdx.x, + gridDim.x, ...
 // The last two K steps of a tile already load the next tile's first two, and
 // the last one splits the next tile's first A step and reads its first
@@ -940,9 +962,11 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     constexpr int A_BUF = 3 * DmaLayout<C>::A_TILE, B_BUF = 3 * B_DMA_TILE;
 
     const int T = g.tiles_m * g.tiles_n, G = (int)gridDim.x;
+    const int units = T * g.splits;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int64_t nk = g.K / BK;                 // K is a multiple of 2 BK on this path
+    // K is a multiple of 2 BK on this path and each K slice an even number of steps
+    const int64_t nk = g.K / BK / g.splits;
 
     int a_lds[C::A_CHUNKS];
 #pragma unroll
@@ -953,15 +977,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     }
 
     int v = (int)blockIdx.x;
-    StepSrc<C> cur;                              // the tile being computed, k0 unused
-    {
-        int tm, tn;
-        tile_of_index(v, T, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-        cur.m0 = (int64_t)tm * C::BM;
-        cur.n0 = (int64_t)tn * C::BN;
-        cur.k0 = 0;
-        a_offsets<C>(cur.a_off, g, cur.m0);
-    }
+    StepSrc<C> cur;                              // the work unit being computed
+    unit_src<C>(cur, v, T, nk, g);
 
     Acc<C, NB> acc;
     clear_acc<C, NB>(acc);
@@ -971,11 +988,12 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 
     // Prologue: steps 0 and 1 of the first tile in flight, step 0 staged and
     // its first-slice fragments read.
-    dma_b_stage<C>(g, cur.n0, 0, b_base, wave, lane);
-    load_a_stage<C, AVEC>(a_cur, cur.a_off, g, cur.m0, 0);
-    dma_b_stage<C>(g, cur.n0, BK, b_base + B_BUF, wave, lane);
-    load_a_stage<C, AVEC>(a_next, cur.a_off, g, cur.m0, BK);
-    if (store_a_stage<C>(a_cur, a_lds, a_base)) restage_a_special<C, AVEC>(cur.a_off, a_lds, g, cur.m0, 0, a_base);
+    dma_b_stage<C>(g, cur.n0, cur.kb, b_base, wave, lane);
+    load_a_stage<C, AVEC>(a_cur, cur.a_off, g, cur.m0, cur.kb);
+    dma_b_stage<C>(g, cur.n0, cur.kb + BK, b_base + B_BUF, wave, lane);
+    load_a_stage<C, AVEC>(a_next, cur.a_off, g, cur.m0, cur.kb + BK);
+    if (store_a_stage<C>(a_cur, a_lds, a_base))
+        restage_a_special<C, AVEC>(cur.a_off, a_lds, g, cur.m0, cur.kb, a_base);
     wait_vmem_at_most<dma_vmem_per_step<C, AVEC>()>();
     lds_barrier();
     read_frags_dma<C>(f0, a_base, b_base, 0, wm, wn, lane);
@@ -984,18 +1002,12 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     for (;;) {
         float bias[C::NI];                       // issued now, needed by the tile's epilogue
         load_bias<C>(bias, g, cur.n0, wn, lane);
-        // The next tile, or (none left) the current one again, whose steps
-        // past K then serve as harmless dummy loads.
+        // The next unit, or (none left) the current one again, whose steps
+        // past its K slice then serve as harmless dummy loads.
         const int64_t vn = (int64_t)v + G;
-        const bool has_next = vn < T;
+        const bool has_next = vn < units;
         StepSrc<C> nxt = cur;
-        if (has_next) {
-            int tm, tn;
-            tile_of_index((int)vn, T, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-            nxt.m0 = (int64_t)tm * C::BM;
-            nxt.n0 = (int64_t)tn * C::BN;
-            a_offsets<C>(nxt.a_off, g, nxt.m0);
-        }
+        if (has_next) unit_src<C>(nxt, (int)vn, T, nk, g);
 
         // Two steps per trip keep the register sets static: an even step
         // splits a_next (its successor) and loads a_cur (two ahead); an odd
@@ -1005,9 +1017,9 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             const bool last = kt + 2 >= nk;
             const bool roll = last && has_next;
             StepSrc<C> ld = roll ? nxt : cur;
-            ld.k0 = roll ? 0 : (kt + 2) * BK;
+            ld.k0 = roll ? nxt.kb : cur.kb + (kt + 2) * BK;
             StepSrc<C> sp = cur;
-            sp.k0 = (kt + 1) * BK;
+            sp.k0 = cur.kb + (kt + 1) * BK;
             const int b1 = bs == 2 ? 0 : bs + 1, b2 = b1 == 2 ? 0 : b1 + 1;
             dma_step<C, NB, AVEC>(acc, f0, f1, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
                                   a_base + A_BUF, b_base + b1 * B_BUF, b_base + b2 * B_BUF, wave, wm, wn, lane);
@@ -1015,7 +1027,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             ld.k0 += BK;
             if (last) {
                 sp = nxt;
-                sp.k0 = has_next ? 0 : nk * BK;
+                sp.k0 = has_next ? nxt.kb : cur.kb + nk * BK;
             } else {
                 sp.k0 += BK;
             }
@@ -1025,13 +1037,50 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             bs = b2;
         }
 
-        store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
+        // Split-K: the slice's bands are recombined as usual and the result goes
+        // to the partial buffer; splitk_reduce_kernel adds the slices.
+        if (g.splits > 1) store_c_act<C, NB, -1>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane, cur.slice);
+        else store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
         if (!has_next) break;
         clear_acc<C, NB>(acc);
         v = (int)vn;
         cur = nxt;
     }
     wait_vmem_at_most<0>();      // drain the copies issued past the end of K
+}
+
+// ---------------------------------------------------------------- split-K reduction
+
+// C = act(sum over K slices of the slices' recombined results + bias), per
+// element, adding the slices in slice order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g)
+{
+    const int64_t total = g.M * g.N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t plane = g.M * g.ldp;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+        const int64_t r = e / g.N, c = e - r * g.N;
+        const float *p = g.partials + r * g.ldp + c;
+        float v = p[0];
+        for (int sl = 1; sl < g.splits; ++sl) v += p[(int64_t)sl * plane];
+        v = v + (g.bias ? g.bias[c] : -0.0f);
+        if (g.act == 1) v = gelu_erf(v);
+        g.C[r * g.ldc + c] = v;
+    }
+}
+
+int gemm_split_count(int64_t M, int64_t N, int64_t K, int nbands, int num_cus)
+{
+    (void)nbands;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t pairs = K / (2 * BK);
+    if (K % (2 * BK) != 0 || tiles * 4 >= (int64_t)num_cus * 3) return 1;   // 3/4 of the CUs busy already
+    int best = 1;
+    for (int sl = 2; sl <= 16; ++sl) {
+        if (tiles * sl > num_cus || pairs / sl < 4) break;     // one round, at least 8 K steps per slice
+        if (pairs % sl == 0) best = sl;
+    }
+    return best;
 }
 
 // ---------------------------------------------------------------- K == 0
@@ -1101,11 +1150,16 @@ static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
 {
     // One resident workgroup per CU (LDS-limited); a multiple of 8 keeps each
     // workgroup on one XCD for all of its tiles.
-    const int64_t tiles = (int64_t)g.tiles_m * g.tiles_n;
+    const int64_t units = (int64_t)g.tiles_m * g.tiles_n * g.splits;
     int64_t slots = (int64_t)(g.num_cus > 8 ? g.num_cus & ~7 : 8);
-    const dim3 grid((unsigned)(tiles < slots ? tiles : slots)), block(C::NT);
+    const dim3 grid((unsigned)(units < slots ? units : slots)), block(C::NT);
     if (avec) hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, true>), grid, block, 0, stream, g);
     else hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, false>), grid, block, 0, stream, g);
+    if (g.splits > 1) {
+        int64_t blocks = (g.M * g.N + 255) / 256;
+        if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g);
+    }
 }
 
 template <class C>

@@ -31,6 +31,9 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int group_m;             // tile-rows per group of the tile order
     int num_cus;             // compute units of the device (persistent grids)
+    int splits;              // K slices (split-K, N x K DMA kernel only); 1 = none
+    float *partials;         // splits planes of M x ldp floats, one recombined result per K slice
+    int64_t ldp;
 };
 
 hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
@@ -40,6 +43,10 @@ hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, in
                                   uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream);
+
+// K slices the N x K DMA kernel should use for this shape (1 = no split-K):
+// grids that leave a quarter of the CUs idle get split along K.
+int gemm_split_count(int64_t M, int64_t N, int64_t K, int nbands, int num_cus);
 
 // True when launch_gemm takes the LDS-DMA kernel for N x K planes of this shape.
 bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const void *B2);

@@ -44,7 +44,9 @@
  *   `stream`) from a memory pool the library creates per device and keeps
  *   until the process ends, with freed blocks held for reuse.  If that
  *   allocation fails they split B inside the GEMM kernel instead; the result
- *   is bitwise the same either way.  No other call allocates device memory.
+ *   is bitwise the same either way.  GEMMs on small tile grids also take a
+ *   pooled split-K buffer (see sgemm_emu_split_k).  No other device memory is
+ *   allocated.
  *   Float pointers must be 4-byte aligned, BF16 plane pointers 2-byte aligned.
  *   16-byte aligned A with lda % 4 == 0 takes the vector-load path; any other
  *   layout takes a scalar-load path with the same arithmetic.
@@ -184,6 +186,24 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
                                 const float *X, int64_t ldx,
                                 uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo,
                                 sgemm_emu_stream_t stream);
+
+/*
+ * sgemm_emu_split_k -- the number of K slices (split-K) the GEMM uses for an
+ * M x N x K product on the current device when it runs the N x K plane kernel
+ * (sgemm_emu_presplit_b with SGEMM_EMU_B_NK, sgemm_emu_linear, and
+ * sgemm_bf16x9 / sgemm_emu when they pre-split B; all need K % 64 == 0 and
+ * 16-byte aligned planes with ldb % 8 == 0).  1 means one pass over K per
+ * output tile.  With S > 1 slices (grids that would leave a quarter of the
+ * CUs idle), each (tile, slice) runs the method on its K range (five band
+ * sums, recombined smallest band first) and writes its FP32 result to a
+ * stream-ordered pooled buffer (S * M * N floats); a reduction kernel adds the
+ * S results in slice order, then the bias and activation.  Results differ in
+ * rounding from the one-pass order (still within the same error bound) and
+ * are deterministic for a given shape and device.  If the buffer cannot be
+ * allocated the GEMM runs one pass per tile.  Returns S >= 1, or a negative
+ * status (invalid sizes or nbands, no gfx950 device).
+ */
+int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands);
 
 /* Number of BF16 products evaluated for nbands (1, 3, 6, 8, 9), or -1 if invalid. */
 int sgemm_emu_products(int nbands);

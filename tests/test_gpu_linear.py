@@ -160,7 +160,27 @@ def test_input_gradient_transposed_planes_bitwise(fe, shape):
     print(f"linear bwd planes M={M} N={N} K={K}", flush=True, file=sys.stderr)
     fe.sgemm_emu_presplit_b(M, K, N, dYd, N, *P, K, fe.SGEMM_EMU_B_KN, a, K, 5)
     fe.sgemm_emu_presplit_b(M, K, N, dYd, N, *T, N, fe.SGEMM_EMU_B_NK, b, K, 5)
-    assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+    check_against_fp64(host(b), dY, W, label=f"dX planes of W^T {shape}")
+    if fe.sgemm_emu_split_k(M, K, N) == 1:          # else the N x K kernel adds slice by slice
+        assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+
+
+def test_forward_split_k_with_bias_and_gelu(fe, orc):
+    """A small grid (split-K): bias and GELU are applied by the reduction."""
+    M, N, K = 200, 140, 1024
+    assert fe.sgemm_emu_split_k(M, N, K) > 1
+    g = _rng(808)
+    X = g.standard_normal((M, K)).astype(np.float32)
+    W = (g.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    b = (2.0 * g.standard_normal(N)).astype(np.float32)
+    Z, G = orc.gemm_f64(X, np.ascontiguousarray(W.T))
+    Z = Z + b.astype(np.float64)[None, :]
+    e_gemm = 2.0 * K * U * G + 9.0 * K * FLOOR + U * np.abs(Z)
+    Y = _forward(fe, X, W, b).astype(np.float64)
+    assert np.all(np.abs(Y - Z) <= e_gemm)
+    Yg = _forward(fe, X, W, b, act=fe.SGEMM_EMU_ACT_GELU).astype(np.float64)
+    E = orc.gelu_f64_to_f32(Z).astype(np.float64)
+    assert np.all(np.abs(Yg - E) <= 1.13 * e_gemm + gelu_tolerance(Z, E))
 
 
 def test_torch_op_forward_and_input_gradient(fe, orc):
