@@ -13,8 +13,9 @@ pages cited in ``oracle.c``:
   [KR]  discuss.pytorch.kr summary of the same post.
 
 Functions:
-  split(X)                -> (X0, X1, X2) uint16 BF16 bit patterns
-                             ([KR] "Blackwell의 BF16x9", x = x0 + 2^-8 x1 + 2^-16 x2)
+  split(X, mode)          -> (X0, X1, X2) uint16 BF16 bit patterns
+                             ([KR] "Blackwell의 BF16x9", x = x0 + 2^-8 x1 + 2^-16 x2);
+                             mode SPLIT_RZ (the method's reading) or SPLIT_RNE (ablation)
   gemm_f64(A, B, rows)    -> (Cref, G) FP64 reference and sum |a*b|
   sgemm_naive_f32(A, B)   -> C, sequential FP32 accumulation (CPU baseline)
   gemm_emu(A, B, nbands)  -> C, scalar band emulation ([NVB] Fig. 1 caption)
@@ -31,6 +32,8 @@ from . import build as _build
 _LIB = None
 
 ORC_FLUSH_PRODUCT_SUBNORMALS = 1
+ORC_SPLIT_RNE = 2            # gemm_emu / gemm_trunc_f64 flag: round-to-nearest split
+SPLIT_RZ, SPLIT_RNE = 0, 1   # split modes
 
 _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
@@ -51,15 +54,19 @@ def lib():
                                     ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_uint16)]
         L.orc_split_one.restype = None
         L.orc_split.argtypes = [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64]
+        L.orc_split_mode.argtypes = [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64, ctypes.c_int]
+        L.orc_split_one_mode.argtypes = [ctypes.c_float, ctypes.c_int, ctypes.POINTER(ctypes.c_uint16),
+                                         ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_uint16)]
+        L.orc_split_one_mode.restype = None
         L.orc_gemm_f64.argtypes = [_i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
         L.orc_sgemm_naive_f32.argtypes = [_i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
         L.orc_gemm_emu.argtypes = [_i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                    ctypes.c_int, ctypes.c_int, _vp]
         L.orc_gemm_trunc_f64.argtypes = [_i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
-                                         ctypes.c_int]
+                                         ctypes.c_int, ctypes.c_int]
         L.orc_gelu_f64_to_f32.argtypes = [_i64, _vp, _vp]
         L.orc_num_threads.argtypes = []
-        for name in ("orc_split", "orc_gemm_f64", "orc_sgemm_naive_f32", "orc_gemm_emu",
+        for name in ("orc_split", "orc_split_mode", "orc_gemm_f64", "orc_sgemm_naive_f32", "orc_gemm_emu",
                      "orc_gemm_trunc_f64", "orc_gelu_f64_to_f32", "orc_num_threads"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
@@ -96,21 +103,24 @@ def num_threads() -> int:
     return lib().orc_num_threads()
 
 
-def split_one(x: float):
+def split_one(x: float, mode=SPLIT_RZ):
     """Split one FP32 value; returns the three BF16 bit patterns (x0, x1, x2)."""
     c = [ctypes.c_uint16() for _ in range(3)]
-    lib().orc_split_one(ctypes.c_float(x), *[ctypes.byref(v) for v in c])
+    if mode == SPLIT_RZ:
+        lib().orc_split_one(ctypes.c_float(x), *[ctypes.byref(v) for v in c])
+    else:
+        lib().orc_split_one_mode(ctypes.c_float(x), int(mode), *[ctypes.byref(v) for v in c])
     return tuple(v.value for v in c)
 
 
-def split(X):
+def split(X, mode=SPLIT_RZ):
     """Elementwise split of a float32 array of any shape into three uint16 arrays."""
     X = np.ascontiguousarray(X, dtype=np.float32)
     flat = X.reshape(1, -1) if X.size else X.reshape(0, 0)
     outs = [np.empty(flat.shape, dtype=np.uint16) for _ in range(3)]
     if flat.size:
-        _check(lib().orc_split(flat.shape[0], flat.shape[1], _ptr(flat), flat.shape[1],
-                               *[_ptr(o) for o in outs], flat.shape[1]), "split")
+        _check(lib().orc_split_mode(flat.shape[0], flat.shape[1], _ptr(flat), flat.shape[1],
+                                    *[_ptr(o) for o in outs], flat.shape[1], int(mode)), "split")
     return tuple(o.reshape(X.shape) for o in outs)
 
 
@@ -158,7 +168,7 @@ def gemm_emu(A, B, nbands=5, rows=None, flags=0, want_bands=False):
     return (C, S) if want_bands else C
 
 
-def gemm_trunc_f64(A, B, nbands=5, rows=None):
+def gemm_trunc_f64(A, B, nbands=5, rows=None, flags=0):
     """FP64 value of the kept products: sum over p+q < nbands of 2^-8(p+q) A_p B_q."""
     A, B = _mat(A), _mat(B)
     M, K = A.shape
@@ -168,7 +178,7 @@ def gemm_trunc_f64(A, B, nbands=5, rows=None):
     r, nr = _rows(rows, M)
     T = np.empty((nr, N), dtype=np.float64)
     _check(lib().orc_gemm_trunc_f64(nr, _ptr(r), N, K, _ptr(A), max(K, 1), _ptr(B), max(N, 1),
-                                    _ptr(T), max(N, 1), int(nbands)), "gemm_trunc_f64")
+                                    _ptr(T), max(N, 1), int(nbands), int(flags)), "gemm_trunc_f64")
     return T
 
 

@@ -25,7 +25,9 @@
  *     ([NVB] same section, the equation under Fig. 2; [KR] "Ampere의 TF32x3").
  *
  * Readings taken where the pages are silent (each listed in the design notes):
- *   - the split truncates (rounds toward zero) at each stage;
+ *   - the split truncates (rounds toward zero) at each stage; a
+ *     round-to-nearest-even split (never rounding to Inf) is kept as an
+ *     ablation (ORC_SPLIT_RNE);
  *   - components are stored scaled, the band weight 2^-8s is applied once per
  *     band when the bands are recombined;
  *   - one FP32 accumulator per band over the whole K range, recombined once;
@@ -50,6 +52,11 @@
 #define ORC_EINVAL (-1)
 #define ORC_ENOMEM (-2)
 
+/* Split rounding: truncation (the method's reading) or, for the rounding
+ * ablation, round to nearest even at each stage (never to Inf). */
+#define ORC_SPLIT_RZ_MODE 0
+#define ORC_SPLIT_RNE_MODE 1
+
 static uint32_t bits_of(float f) { uint32_t u; memcpy(&u, &f, sizeof u); return u; }
 static float float_of(uint32_t u) { float f; memcpy(&f, &u, sizeof f); return f; }
 
@@ -61,12 +68,31 @@ static float bf16_value(uint16_t h) { return float_of((uint32_t)h << 16); }
 static uint16_t trunc_bf16(float v) { return (uint16_t)(bits_of(v) >> 16); }
 
 /*
+ * Round a finite float to the nearest BF16, ties to the even mantissa.  The
+ * two candidates are its truncation and the next BF16 away from zero, chosen
+ * by comparing the two distances in double (both exact).  Above the largest
+ * finite BF16 the next step is Inf, infinitely far, so a finite value keeps
+ * its truncation there and the split never overflows.
+ */
+static uint16_t rne_bf16(float v)
+{
+    uint16_t lo = trunc_bf16(v);
+    uint16_t hi = (uint16_t)(lo + 1);                 /* one BF16 step further from zero */
+    double a = fabs((double)v);
+    double dl = a - fabs((double)bf16_value(lo));
+    double dh = fabs((double)bf16_value(hi)) - a;
+    if (dl < dh) return lo;
+    if (dh < dl) return hi;
+    return (lo & 1u) ? hi : lo;                       /* tie: even mantissa */
+}
+
+/*
  * Split of one FP32 value into three scaled BF16 components.
  * [KR] "Blackwell의 BF16x9": x = x0 + 2^-8 x1 + 2^-16 x2, 8 bits per piece.
  * Done in double so every step is visibly exact: x, x0 and 2^8 (x - x0) all
  * have at most 24 significant bits within a 53-bit double.
  */
-void orc_split_one(float x, uint16_t *c0, uint16_t *c1, uint16_t *c2)
+void orc_split_one_mode(float x, int mode, uint16_t *c0, uint16_t *c1, uint16_t *c2)
 {
     uint32_t u = bits_of(x);
     if ((u & 0x7F800000u) == 0x7F800000u) {          /* Inf or NaN */
@@ -75,11 +101,12 @@ void orc_split_one(float x, uint16_t *c0, uint16_t *c1, uint16_t *c2)
         *c0 = hi; *c1 = 0; *c2 = 0;
         return;
     }
-    uint16_t h0 = trunc_bf16(x);                        /* x0 = RZ_bf16(x) */
+    /* x0 = RZ_bf16(x), or RNE_bf16(x) for the round-to-nearest ablation */
+    uint16_t h0 = mode == ORC_SPLIT_RNE_MODE ? rne_bf16(x) : trunc_bf16(x);
     double r = (double)x - (double)bf16_value(h0);      /* exact remainder */
     double t = r * 256.0;                               /* 2^8 (x - x0) */
     float tf = (float)t;                                /* exact: <= 16 bits */
-    uint16_t h1 = trunc_bf16(tf);                       /* x1 = RZ_bf16(t) */
+    uint16_t h1 = mode == ORC_SPLIT_RNE_MODE ? rne_bf16(tf) : trunc_bf16(tf);
     double s = (t - (double)bf16_value(h1)) * 256.0;    /* x2 = 2^8 (t - x1) */
     float sf = (float)s;                                /* exact: <= 8 bits */
     uint16_t h2 = trunc_bf16(sf);
@@ -89,16 +116,28 @@ void orc_split_one(float x, uint16_t *c0, uint16_t *c1, uint16_t *c2)
     *c0 = h0; *c1 = h1; *c2 = h2;
 }
 
+void orc_split_one(float x, uint16_t *c0, uint16_t *c1, uint16_t *c2)
+{
+    orc_split_one_mode(x, ORC_SPLIT_RZ_MODE, c0, c1, c2);
+}
+
 /* Elementwise split of a rows x cols matrix with leading dimensions. */
-int orc_split(int64_t rows, int64_t cols, const float *X, int64_t ldx,
-              uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo)
+int orc_split_mode(int64_t rows, int64_t cols, const float *X, int64_t ldx,
+                   uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo, int mode)
 {
     if (rows < 0 || cols < 0 || ldx < cols || ldo < cols) return ORC_EINVAL;
+    if (mode != ORC_SPLIT_RZ_MODE && mode != ORC_SPLIT_RNE_MODE) return ORC_EINVAL;
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i)
         for (int64_t j = 0; j < cols; ++j)
-            orc_split_one(X[i * ldx + j], &X0[i * ldo + j], &X1[i * ldo + j], &X2[i * ldo + j]);
+            orc_split_one_mode(X[i * ldx + j], mode, &X0[i * ldo + j], &X1[i * ldo + j], &X2[i * ldo + j]);
     return ORC_OK;
+}
+
+int orc_split(int64_t rows, int64_t cols, const float *X, int64_t ldx,
+              uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo)
+{
+    return orc_split_mode(rows, cols, X, ldx, X0, X1, X2, ldo, ORC_SPLIT_RZ_MODE);
 }
 
 /* Row index helper: rows == NULL means "all rows 0..nrows-1". */
@@ -159,8 +198,9 @@ int orc_sgemm_naive_f32(int64_t nrows, const int64_t *rows, int64_t N, int64_t K
     return ORC_OK;
 }
 
-/* Flags of the scalar emulation (only used to model hardware behaviour). */
-#define ORC_FLUSH_PRODUCT_SUBNORMALS 1  /* product below 2^-126 becomes +-0 */
+/* Flags of the scalar emulation and the truncated-band value. */
+#define ORC_FLUSH_PRODUCT_SUBNORMALS 1  /* product below 2^-126 becomes +-0 (hardware model) */
+#define ORC_SPLIT_RNE 2                 /* split A and B with ORC_SPLIT_RNE_MODE */
 
 /*
  * Scalar band emulation of the BF16x9 GEMM.
@@ -186,6 +226,7 @@ int orc_gemm_emu(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
 {
     if (nrows < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return ORC_EINVAL;
     if (nbands < 1 || nbands > 5) return ORC_EINVAL;
+    const int smode = (flags & ORC_SPLIT_RNE) ? ORC_SPLIT_RNE_MODE : ORC_SPLIT_RZ_MODE;
 
     /* Step 1 for B: three component planes, each K x N, as FP32 values. */
     size_t plane = (size_t)K * (size_t)N;
@@ -195,7 +236,7 @@ int orc_gemm_emu(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
     for (int64_t k = 0; k < K; ++k)
         for (int64_t j = 0; j < N; ++j) {
             uint16_t h[3];
-            orc_split_one(B[k * ldb + j], &h[0], &h[1], &h[2]);
+            orc_split_one_mode(B[k * ldb + j], smode, &h[0], &h[1], &h[2]);
             for (int q = 0; q < 3; ++q) Bc[q * plane + (size_t)k * N + j] = bf16_value(h[q]);
         }
 
@@ -208,7 +249,7 @@ int orc_gemm_emu(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
         for (int64_t j = 0; j < 5 * N; ++j) S[j] = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
             uint16_t h[3];
-            orc_split_one(A[i * lda + k], &h[0], &h[1], &h[2]);       /* step 1 for A */
+            orc_split_one_mode(A[i * lda + k], smode, &h[0], &h[1], &h[2]);   /* step 1 for A */
             for (int p = 0; p < 3; ++p) {
                 float ap = bf16_value(h[p]);
                 for (int q = 0; q < 3; ++q) {
@@ -247,13 +288,15 @@ int orc_gemm_emu(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
  * double; the sum runs k ascending, then p ascending.  With nbands = 5 this is
  * the exact algebraic value of the nine-product sum; with nbands = 2 it is the
  * TF32x3 form hi*hi + hi*lo + lo*hi ([NVB] the equation under Fig. 2).
+ * flags: ORC_SPLIT_RNE selects the round-to-nearest split.
  */
 int orc_gemm_trunc_f64(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
                        const float *A, int64_t lda, const float *B, int64_t ldb,
-                       double *T, int64_t ldt, int nbands)
+                       double *T, int64_t ldt, int nbands, int flags)
 {
     if (nrows < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldt < N) return ORC_EINVAL;
     if (nbands < 1 || nbands > 5) return ORC_EINVAL;
+    const int smode = (flags & ORC_SPLIT_RNE) ? ORC_SPLIT_RNE_MODE : ORC_SPLIT_RZ_MODE;
     static const double weight[5] = {1.0, 0x1p-8, 0x1p-16, 0x1p-24, 0x1p-32};
     int rc = ORC_OK;
     #pragma omp parallel for schedule(dynamic, 1)
@@ -263,10 +306,10 @@ int orc_gemm_trunc_f64(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
         for (int64_t j = 0; j < N; ++j) t[j] = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             uint16_t a[3];
-            orc_split_one(A[i * lda + k], &a[0], &a[1], &a[2]);
+            orc_split_one_mode(A[i * lda + k], smode, &a[0], &a[1], &a[2]);
             for (int64_t j = 0; j < N; ++j) {
                 uint16_t b[3];
-                orc_split_one(B[k * ldb + j], &b[0], &b[1], &b[2]);
+                orc_split_one_mode(B[k * ldb + j], smode, &b[0], &b[1], &b[2]);
                 for (int p = 0; p < 3; ++p)
                     for (int q = 0; q < 3; ++q)
                         if (p + q < nbands)

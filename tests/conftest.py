@@ -34,6 +34,8 @@ def pins_lib():
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         L.pin_split_range.argtypes = [ctypes.c_uint64, i64, vp, vp, vp, ctypes.POINTER(ctypes.c_uint64)]
         L.pin_split_range.restype = i64
+        L.pin_split_rne_range.argtypes = [ctypes.c_uint64, i64, vp, vp, vp, ctypes.POINTER(ctypes.c_uint64)]
+        L.pin_split_rne_range.restype = i64
         L.pin_bf16_products.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(i64)]
         L.pin_bf16_products.restype = i64
         L.pin_band_algebra.argtypes = [i64] + [vp] * 8

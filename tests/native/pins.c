@@ -89,6 +89,73 @@ int64_t pin_split_range(uint64_t start, int64_t count, const uint16_t *x0,
 }
 
 /*
+ * Is h a round-to-nearest-even BF16 of the finite value v (a double holding a
+ * float, the split's remainder t, or x itself)?  The two BF16 magnitudes that
+ * bracket |v| are found by masking |v|'s FP32 pattern to its high half and
+ * stepping once away from zero; h must be the nearer one with v's sign, the
+ * one with an even last mantissa bit on a tie, and the lower one when the
+ * upper would be Inf (the split never rounds to Inf).  Zero v must give +-0.
+ */
+static int is_rne_bf16(double v, uint16_t h)
+{
+    float vf = (float)v;
+    if ((double)vf != v) return 0;                       /* v must be exactly a float */
+    uint32_t mag = u_of(fabsf(vf)) >> 16;                /* truncated magnitude */
+    uint16_t lo = (uint16_t)mag, hi = (uint16_t)(mag + 1);
+    double a = fabs(v);
+    uint16_t hm = h & 0x7FFF;
+    if (a == 0.0) return hm == 0;
+    if (hm != lo && hm != hi) return 0;
+    if (((h >> 15) != 0) != (v < 0.0)) return 0;         /* same sign as v */
+    if ((hi & 0x7F80) == 0x7F80) return hm == lo;        /* upper neighbour is Inf */
+    double dl = a - bf(lo), dh = bf(hi) - a;
+    if (dl < dh) return hm == lo;
+    if (dh < dl) return hm == hi;
+    return (hm & 1) == 0;                                /* tie: even mantissa */
+}
+
+/*
+ * Round-to-nearest split (the ablation's rounding), encodings start ..
+ * start+count-1: exact reconstruction, x0 a round-to-nearest-even BF16 of x,
+ * x1 of t = 2^8 (x - x0), finite components, special classes as for RZ.
+ */
+int64_t pin_split_rne_range(uint64_t start, int64_t count, const uint16_t *x0,
+                            const uint16_t *x1, const uint16_t *x2, uint64_t *first_bad)
+{
+    int64_t bad = 0;
+    uint64_t first = UINT64_MAX;
+    #pragma omp parallel for reduction(+:bad) schedule(static)
+    for (int64_t n = 0; n < count; ++n) {
+        uint32_t u = (uint32_t)(start + (uint64_t)n);
+        float x = f_of(u);
+        int ok = 1;
+        if (!isfinite(x)) {
+            float c0 = f_of((uint32_t)x0[n] << 16);
+            ok = x1[n] == 0 && x2[n] == 0 && (signbit(c0) != 0) == (signbit(x) != 0);
+            if (isnan(x)) ok = ok && isnan(c0) && (x0[n] & 0x0040);
+            else ok = ok && isinf(c0);
+        } else {
+            double X = (double)x;
+            double r = bf(x0[n]) + ldexp(bf(x1[n]), -8) + ldexp(bf(x2[n]), -16);
+            ok = ok && (r == X);
+            if (x == 0.0f) ok = ok && (x0[n] == (uint16_t)(u >> 16)) && x1[n] == 0 && x2[n] == 0;
+            else ok = ok && is_rne_bf16(X, x0[n]);
+            double t = ldexp(X - bf(x0[n]), 8);
+            if (t != 0.0) ok = ok && is_rne_bf16(t, x1[n]);
+            else ok = ok && x1[n] == 0;
+            ok = ok && isfinite(bf(x0[n])) && isfinite(bf(x1[n])) && isfinite(bf(x2[n]));
+        }
+        if (!ok) {
+            bad += 1;
+            #pragma omp critical
+            { if ((uint64_t)u < first) first = u; }
+        }
+    }
+    *first_bad = first;
+    return bad;
+}
+
+/*
  * BF16 x BF16 products are exact in FP32 when they stay in FP32's normal
  * range: 8 x 8 significant bits give at most 16.  Checks every ordered pair
  * (a, b) with a's pattern in [a_start, a_start + a_count) and every b.

@@ -334,3 +334,50 @@ def test_gelu_vs_tabulated_normal_cdf():
     xs = np.array([0.25, 0.5, 1.0, 2.0, 3.0])
     d = oracle.gelu_f64_to_f32(xs).astype(np.float64) - oracle.gelu_f64_to_f32(-xs).astype(np.float64)
     assert np.allclose(d, xs, rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------- round-to-nearest split (ablation)
+
+@pytest.mark.parametrize("nbands", [3, 4, 5])
+def test_emu_rne_identity_exact(orc, nbands):
+    """With the round-to-nearest split, A = I still gives C = B: the components
+    may carry opposite signs, but each partial sum of the recombination is a
+    prefix of x's own bits and exact."""
+    g = _rng(41)
+    X = _full24(g, (24, 24))
+    I = np.eye(24, dtype=np.float32)
+    C = orc.gemm_emu(I, X, nbands, flags=orc.ORC_SPLIT_RNE)
+    assert np.array_equal(C.view(np.uint32), X.view(np.uint32))
+
+
+def test_emu_rne_small_integers_exact(orc):
+    g = _rng(42)
+    A = g.integers(-1023, 1024, size=(20, 16)).astype(np.float32)
+    B = g.integers(-1023, 1024, size=(16, 12)).astype(np.float32)
+    C = orc.gemm_emu(A, B, 5, flags=orc.ORC_SPLIT_RNE)
+    assert np.array_equal(C, (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float32))
+
+
+def test_trunc_rne_nine_products_is_the_product(orc):
+    """All nine products of the round-to-nearest split sum to a b exactly, so the
+    FP64 truncated-band value with nbands = 5 matches the FP64 reference to
+    double rounding."""
+    g = _rng(43)
+    A = g.standard_normal((9, 40)).astype(np.float32)
+    B = g.standard_normal((40, 7)).astype(np.float32)
+    T = orc.gemm_trunc_f64(A, B, 5, flags=orc.ORC_SPLIT_RNE)
+    ref, G = orc.gemm_f64(A, B)
+    assert np.all(np.abs(T - ref) <= 64 * 2.0 ** -53 * G)
+
+
+def test_rne_split_halves_the_dropped_mass(orc):
+    """With three products (nbands = 2) the dropped terms start at 2^-16 x1 y1;
+    nearest rounding halves the largest possible |x1| and |x2|, so the RMS error
+    of the RNE ablation is well below RZ's (about a sixth here)."""
+    g = _rng(44)
+    A = g.standard_normal((32, 256)).astype(np.float32)
+    B = g.standard_normal((256, 32)).astype(np.float32)
+    ref, _ = orc.gemm_f64(A, B)
+    e_rz = orc.gemm_trunc_f64(A, B, 2) - ref
+    e_rne = orc.gemm_trunc_f64(A, B, 2, flags=orc.ORC_SPLIT_RNE) - ref
+    assert np.sqrt(np.mean(e_rne ** 2)) < 0.5 * np.sqrt(np.mean(e_rz ** 2))

@@ -15,14 +15,17 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
-FAST_PINS = ("test_split_golden or test_emu_identity or test_emu_recombination or "
+FAST_PINS = ("test_split_golden or test_split_rne_golden or test_emu_identity or test_emu_recombination or "
              "test_naive_f32 or test_gemm_f64_small_integers or test_gemm_f64_vs_numpy or "
              "test_emu_tolerance or test_emu_three_product or test_emu_band_drop or "
              "test_emu_small_integers or test_emu_special or test_gelu or test_emu_scaled_permutation")
 
 MUTANTS = {
-    "split_x0_round_nearest": ("uint16_t h0 = trunc_bf16(x);",
-                               "uint16_t h0 = (uint16_t)((bits_of(x) + 0x8000u) >> 16);"),
+    "split_x0_round_nearest": ("mode == ORC_SPLIT_RNE_MODE ? rne_bf16(x) : trunc_bf16(x);",
+                               "mode == ORC_SPLIT_RNE_MODE ? rne_bf16(x) : (uint16_t)((bits_of(x) + 0x8000u) >> 16);"),
+    "rne_ties_away": ("return (lo & 1u) ? hi : lo;", "return hi;"),
+    "rne_nearest_by_bits": ("if (dl < dh) return lo;", "if (bits_of(v) & 0x8000u) return hi; if (1) return lo;"),
+    "rne_x1_truncated": ("mode == ORC_SPLIT_RNE_MODE ? rne_bf16(tf) : trunc_bf16(tf);", "trunc_bf16(tf);"),
     "split_scale_2^7": ("double t = r * 256.0;", "double t = r * 128.0;"),
     "split_x2_unscaled": ("double s = (t - (double)bf16_value(h1)) * 256.0;",
                           "double s = (t - (double)bf16_value(h1)) * 1.0;"),
@@ -31,8 +34,8 @@ MUTANTS = {
     "emu_drop_a2b0": ("if (s >= nbands) continue;", "if (s >= nbands || (p == 2 && q == 0)) continue;"),
     "emu_band2_weight": ("acc = fmaf(S[2 * N + j], 0x1p-16f, acc);", "acc = fmaf(S[2 * N + j], 0x1p-15f, acc);"),
     "emu_sign_s0": ("C[r * ldc + j] = acc + S[j];", "C[r * ldc + j] = acc - S[j];"),
-    "emu_transposed_b": ("orc_split_one(B[k * ldb + j], &h[0], &h[1], &h[2]);",
-                         "orc_split_one(B[j * ldb + k], &h[0], &h[1], &h[2]);"),
+    "emu_transposed_b": ("orc_split_one_mode(B[k * ldb + j], smode, &h[0], &h[1], &h[2]);",
+                         "orc_split_one_mode(B[j * ldb + k], smode, &h[0], &h[1], &h[2]);"),
     "emu_largest_band_first": (
         "float acc = 0x1p-32f * S[4 * N + j];\n"
         "            acc = fmaf(S[3 * N + j], 0x1p-24f, acc);\n"

@@ -13,9 +13,9 @@ import pytest
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def _golden():
+def _golden(name="split_cases.txt"):
     rows = []
-    with open(os.path.join(HERE, "golden", "split_cases.txt")) as f:
+    with open(os.path.join(HERE, "golden", name)) as f:
         for line in f:
             if not line.strip() or line.startswith("#"):
                 continue
@@ -31,6 +31,28 @@ def test_split_golden(orc, case):
     c = orc.split(x)
     assert (int(c[0][0]), int(c[1][0]), int(c[2][0])) == (e0, e1, e2)
     assert orc.split_one(float(x[0])) == (e0, e1, e2) or np.isnan(x[0])
+
+
+@pytest.mark.parametrize("case", _golden("split_rne_cases.txt"), ids=lambda c: f"{c[0]:08X}")
+def test_split_rne_golden(orc, case):
+    """The round-to-nearest-even split (rounding ablation) on hand-derived cases."""
+    u, e0, e1, e2 = case
+    x = np.array([u], dtype=np.uint32).view(np.float32)
+    c = orc.split(x, orc.SPLIT_RNE)
+    assert (int(c[0][0]), int(c[1][0]), int(c[2][0])) == (e0, e1, e2)
+
+
+def test_split_rne_exhaustive_all_encodings(orc, pins):
+    """Every FP32 encoding through the round-to-nearest split: exact
+    reconstruction, nearest-even BF16 at both stages (never Inf), special classes."""
+    chunk = 1 << 26
+    first = ctypes.c_uint64()
+    for start in range(0, 1 << 32, chunk):
+        x = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        c0, c1, c2 = orc.split(x, orc.SPLIT_RNE)
+        bad = pins.pin_split_rne_range(start, chunk, c0.ctypes.data, c1.ctypes.data, c2.ctypes.data,
+                                       ctypes.byref(first))
+        assert bad == 0, f"{bad} encodings fail from {start:#x}; first {first.value:#010x}"
 
 
 def test_split_shapes_and_strides(orc):
