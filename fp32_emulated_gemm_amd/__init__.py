@@ -6,10 +6,12 @@ memory and streams only.  The functions keep the C names and argument order:
 
     sgemm_bf16x9(M, N, K, A, lda, B, ldb, C, ldc, stream=None)
     sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream=None)
+    sgemm_emu_ex(M, N, K, A, lda, B, ldb, C, ldc, nbands, flags, stream=None)
     sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nbands, stream=None)
     sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, activation, Y, ldy, nbands, stream=None)
     split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
+    split_f32_bf16x3_ex(rows, cols, X, ldx, X0, X1, X2, ldo, flags, stream=None)
     sgemm_emu_split_k(M, N, K, nbands)
     sgemm_emu_products(nbands), sgemm_emu_strerror(status), sgemm_emu_version()
 
@@ -41,10 +43,12 @@ SGEMM_EMU_B_KN = 0   # pre-split planes K x N (split of B)
 SGEMM_EMU_B_NK = 1   # pre-split planes N x K (split of B^T, e.g. a weight stored [out][in])
 SGEMM_EMU_ACT_NONE = 0
 SGEMM_EMU_ACT_GELU = 1  # GELU, exact (erf) form
+SGEMM_EMU_SPLIT_RNE = 1        # flag: round-to-nearest-even split (rounding ablation)
+SGEMM_EMU_SPLIT_TRANSPOSE = 2  # flag (split_f32_bf16x3_ex): planes of X^T
 
-EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "sgemm_emu_linear", "split_f32_bf16x3",
-           "split_f32_bf16x3_transposed", "sgemm_emu_split_k", "sgemm_emu_products", "sgemm_emu_strerror",
-           "sgemm_emu_version")
+EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_linear",
+           "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
+           "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
 
 
 class SgemmEmuError(RuntimeError):
@@ -66,18 +70,21 @@ def lib():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.sgemm_bf16x9.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         L.sgemm_emu.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+        L.sgemm_emu_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, vp]
         L.sgemm_emu_presplit_b.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, ci, vp, i64, ci, vp]
         L.sgemm_emu_linear.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, ci, vp, i64, ci, vp]
         L.split_f32_bf16x3.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.split_f32_bf16x3_transposed.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
+        L.split_f32_bf16x3_ex.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, ci, vp]
         L.sgemm_emu_split_k.argtypes = [i64, i64, i64, ci]
         L.sgemm_emu_products.argtypes = [ci]
         L.sgemm_emu_strerror.argtypes = [ci]
         L.sgemm_emu_strerror.restype = ctypes.c_char_p
         L.sgemm_emu_version.argtypes = []
         L.sgemm_emu_version.restype = ctypes.c_char_p
-        for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_presplit_b", "sgemm_emu_linear", "split_f32_bf16x3",
-                  "split_f32_bf16x3_transposed", "sgemm_emu_split_k", "sgemm_emu_products"):
+        for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_linear",
+                  "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
+                  "sgemm_emu_products"):
             getattr(L, n).restype = ci
         _LIB = L
     return _LIB
@@ -126,6 +133,11 @@ def sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream=None):
                "sgemm_emu")
 
 
+def sgemm_emu_ex(M, N, K, A, lda, B, ldb, C, ldc, nbands, flags, stream=None):
+    return _ok(lib().sgemm_emu_ex(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, nbands, flags,
+                                  _stream(stream)), "sgemm_emu_ex")
+
+
 def sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nbands, stream=None):
     return _ok(lib().sgemm_emu_presplit_b(M, N, K, _addr(A), lda, _addr(B0), _addr(B1), _addr(B2), ldb,
                                           b_layout, _addr(C), ldc, nbands, _stream(stream)),
@@ -145,6 +157,11 @@ def split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):
 def split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None):
     return _ok(lib().split_f32_bf16x3_transposed(rows, cols, _addr(X), ldx, _addr(X0), _addr(X1), _addr(X2), ldo,
                                                  _stream(stream)), "split_f32_bf16x3_transposed")
+
+
+def split_f32_bf16x3_ex(rows, cols, X, ldx, X0, X1, X2, ldo, flags, stream=None):
+    return _ok(lib().split_f32_bf16x3_ex(rows, cols, _addr(X), ldx, _addr(X0), _addr(X1), _addr(X2), ldo, flags,
+                                         _stream(stream)), "split_f32_bf16x3_ex")
 
 
 def sgemm_emu_split_k(M, N, K, nbands=5):

@@ -130,7 +130,7 @@ int launched(hipError_t e) { return e == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_E
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
                 int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
-                int act = SGEMM_EMU_ACT_NONE)
+                int act = SGEMM_EMU_ACT_NONE, bool rne = false)
 {
     int rc;
     if ((rc = check_dims(M, N, K)) != SGEMM_EMU_OK) return rc;
@@ -184,7 +184,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
         if (hipMallocFromPoolAsync(&bws, 3 * plane_pad, pool, stream) == hipSuccess && bws != nullptr) {
             uint16_t *P0 = (uint16_t *)bws, *P1 = (uint16_t *)((char *)bws + plane_pad),
                      *P2 = (uint16_t *)((char *)bws + 2 * plane_pad);
-            const hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, ldo, num_cus, stream);
+            const hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, ldo, num_cus, stream, rne);
             if (e != hipSuccess) {
                 (void)hipFreeAsync(bws, stream);
                 return launched(e);
@@ -216,7 +216,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
         }
     }
 
-    hipError_t e = launch_gemm(g, nbands, bsrc, stream);
+    hipError_t e = launch_gemm(g, nbands, bsrc, stream, rne);
     if (pws != nullptr) {
         const hipError_t f = hipFreeAsync(pws, stream);
         if (e == hipSuccess) e = f;
@@ -244,6 +244,14 @@ int sgemm_emu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
 {
     return gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32,
                        (hipStream_t)stream);
+}
+
+int sgemm_emu_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+                 float *C, int64_t ldc, int nbands, int flags, sgemm_emu_stream_t stream)
+{
+    if ((flags & ~SGEMM_EMU_SPLIT_RNE) != 0) return SGEMM_EMU_EINVAL;
+    return gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32,
+                       (hipStream_t)stream, nullptr, SGEMM_EMU_ACT_NONE, (flags & SGEMM_EMU_SPLIT_RNE) != 0);
 }
 
 int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const uint16_t *B0,
@@ -278,19 +286,31 @@ int split_f32_bf16x3(int64_t rows, int64_t cols, const float *X, int64_t ldx, ui
     return launched(launch_split(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, (hipStream_t)stream));
 }
 
-int split_f32_bf16x3_transposed(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
-                                uint16_t *X1, uint16_t *X2, int64_t ldo, sgemm_emu_stream_t stream)
+int split_f32_bf16x3_ex(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0, uint16_t *X1,
+                        uint16_t *X2, int64_t ldo, int flags, sgemm_emu_stream_t stream)
 {
     int rc;
+    if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_SPLIT_TRANSPOSE)) != 0) return SGEMM_EMU_EINVAL;
+    const bool rne = (flags & SGEMM_EMU_SPLIT_RNE) != 0, tr = (flags & SGEMM_EMU_SPLIT_TRANSPOSE) != 0;
+    // planes are rows x cols, or cols x rows when transposed
+    const int64_t pr = tr ? cols : rows, pc = tr ? rows : cols;
     if (rows < 0 || cols < 0) return SGEMM_EMU_EINVAL;
     if ((rc = check_matrix(rows, cols, X, ldx, 4)) != SGEMM_EMU_OK) return rc;
-    if ((rc = check_matrix(cols, rows, X0, ldo, 2)) != SGEMM_EMU_OK) return rc;
-    if ((rc = check_matrix(cols, rows, X1, ldo, 2)) != SGEMM_EMU_OK) return rc;
-    if ((rc = check_matrix(cols, rows, X2, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(pr, pc, X0, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(pr, pc, X1, ldo, 2)) != SGEMM_EMU_OK) return rc;
+    if ((rc = check_matrix(pr, pc, X2, ldo, 2)) != SGEMM_EMU_OK) return rc;
     if (rows == 0 || cols == 0) return SGEMM_EMU_OK;
     int num_cus = 0;
     if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
-    return launched(launch_split_transpose(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    return launched(tr ? launch_split_transpose(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, s, rne)
+                       : launch_split(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, s, rne));
+}
+
+int split_f32_bf16x3_transposed(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                                uint16_t *X1, uint16_t *X2, int64_t ldo, sgemm_emu_stream_t stream)
+{
+    return split_f32_bf16x3_ex(rows, cols, X, ldx, X0, X1, X2, ldo, SGEMM_EMU_SPLIT_TRANSPOSE, stream);
 }
 
 int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands)

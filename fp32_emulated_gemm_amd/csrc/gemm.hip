@@ -363,14 +363,14 @@ __device__ __forceinline__ void mask_stage(Stage<C, BSRC> &st, const Roles<C, BS
 // Split the staged FP32 values and write the component tiles to LDS.  The
 // split assumes finite inputs; the return value tells the caller whether this
 // lane met an Inf or NaN and must run restage_special afterwards.
-template <class C, int BSRC>
+template <class C, int BSRC, bool RNE>
 __device__ __forceinline__ bool store_stage(const Stage<C, BSRC> &st, const Roles<C, BSRC> &R, uint16_t *buf)
 {
     uint32_t p0[4], p1[4], p2[4];
     bool special = false;
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
-        special |= split8_packed_finite(st.a[c], p0, p1, p2);
+        special |= split8_packed_finite<RNE>(st.a[c], p0, p1, p2);
         st_lds16(buf + 0 * C::TILE + R.a_lds[c], p0);
         st_lds16(buf + 1 * C::TILE + R.a_lds[c], p1);
         st_lds16(buf + 2 * C::TILE + R.a_lds[c], p2);
@@ -378,7 +378,7 @@ __device__ __forceinline__ bool store_stage(const Stage<C, BSRC> &st, const Role
     if constexpr (BSRC == B_FP32) {
 #pragma unroll
         for (int c = 0; c < C::B_CHUNKS; ++c) {
-            special |= split8_packed_finite(st.b[c], p0, p1, p2);
+            special |= split8_packed_finite<RNE>(st.b[c], p0, p1, p2);
             st_lds16(buf + 0 * C::TILE + R.b_lds[c], p0);
             st_lds16(buf + 1 * C::TILE + R.b_lds[c], p1);
             st_lds16(buf + 2 * C::TILE + R.b_lds[c], p2);
@@ -403,7 +403,7 @@ __device__ __forceinline__ bool store_stage(const Stage<C, BSRC> &st, const Role
 // Rare path for a lane whose staged values included Inf or NaN: reload the
 // same K step and rewrite its FP32-sourced component tiles with the full
 // special-value split.  Runs before the barrier that publishes the tile.
-template <class C, int BSRC, bool AVEC, bool BVEC>
+template <class C, int BSRC, bool AVEC, bool BVEC, bool RNE>
 __device__ __forceinline__ void restage_special(const Roles<C, BSRC> &R, const GemmArgs &g, int64_t m0, int64_t n0,
                                              int64_t k0, uint16_t *buf)
 {
@@ -413,7 +413,7 @@ __device__ __forceinline__ void restage_special(const Roles<C, BSRC> &R, const G
     uint32_t p0[4], p1[4], p2[4];
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
-        split8_packed(st.a[c], p0, p1, p2);
+        split8_packed<RNE>(st.a[c], p0, p1, p2);
         st_lds16(buf + 0 * C::TILE + R.a_lds[c], p0);
         st_lds16(buf + 1 * C::TILE + R.a_lds[c], p1);
         st_lds16(buf + 2 * C::TILE + R.a_lds[c], p2);
@@ -421,7 +421,7 @@ __device__ __forceinline__ void restage_special(const Roles<C, BSRC> &R, const G
     if constexpr (BSRC == B_FP32) {
 #pragma unroll
         for (int c = 0; c < C::B_CHUNKS; ++c) {
-            split8_packed(st.b[c], p0, p1, p2);
+            split8_packed<RNE>(st.b[c], p0, p1, p2);
             st_lds16(buf + 0 * C::TILE + R.b_lds[c], p0);
             st_lds16(buf + 1 * C::TILE + R.b_lds[c], p1);
             st_lds16(buf + 2 * C::TILE + R.b_lds[c], p2);
@@ -494,7 +494,7 @@ constexpr int global_loads_per_stage()
 // the MFMAs of slice 0, and the split arithmetic and LDS writes of the next
 // step under the MFMAs of slice 1, so the matrix cores keep running while the
 // next tile is staged.  The body is a single basic block.
-template <class C, int NB, bool AVEC, int BSRC, bool BVEC, bool RAGGED>
+template <class C, int NB, bool AVEC, int BSRC, bool BVEC, bool RAGGED, bool RNE>
 __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC> &st, const Roles<C, BSRC> &R,
                                                   const GemmArgs &g, int64_t m0, int64_t n0, int64_t k_next,
                                                   const uint16_t *cur, uint16_t *nxt, int wm, int wn, int lane)
@@ -506,7 +506,7 @@ __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC
     mfma_slice<C, NB>(acc, f);
     read_frags<C>(f, cur, 16, wm, wn, lane);
     mfma_slice<C, NB>(acc, f);
-    const bool special = store_stage<C, BSRC>(st, R, nxt);
+    const bool special = store_stage<C, BSRC, RNE>(st, R, nxt);
     if constexpr (C::SCHED) {
         constexpr int NM = products(NB) * C::MI * C::NI;      // MFMAs per slice
         constexpr int NR = 3 * (C::MI + C::NI);                // fragment reads per slice
@@ -520,7 +520,7 @@ __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC
             if (i >= NM / 2) __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);
         }
     }
-    if (__builtin_expect(special, 0)) restage_special<C, BSRC, AVEC, BVEC>(R, g, m0, n0, k_next, nxt);
+    if (__builtin_expect(special, 0)) restage_special<C, BSRC, AVEC, BVEC, RNE>(R, g, m0, n0, k_next, nxt);
 }
 
 // GELU in its exact form, 0.5 z (1 + erf(z / sqrt(2))), evaluated as
@@ -606,7 +606,7 @@ __device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const float (&bv)
     else store_c_act<C, NB, 0>(acc, bv, g, m0, n0, wm, wn, lane);
 }
 
-template <class C, int NB, bool AVEC, int BSRC, bool BVEC>
+template <class C, int NB, bool AVEC, int BSRC, bool BVEC, bool RNE>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * C::TILE];
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
     Stage<C, BSRC> st;
     load_stage<C, BSRC, AVEC, BVEC>(st, R, g, m0, n0, 0);
     if (BK > g.K) mask_stage<C, BSRC>(st, R, 0, g.K);
-    if (store_stage<C, BSRC>(st, R, lds)) restage_special<C, BSRC, AVEC, BVEC>(R, g, m0, n0, 0, lds);
+    if (store_stage<C, BSRC, RNE>(st, R, lds)) restage_special<C, BSRC, AVEC, BVEC, RNE>(R, g, m0, n0, 0, lds);
     __syncthreads();
 
     // Steady state: every step but the last stages its successor.  Inside the
@@ -646,14 +646,14 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
     for (; kt + 2 <= nfull; ++kt) {
         const uint16_t *cur = lds + (kt & 1) * 3 * C::TILE;
         uint16_t *nxt = lds + ((kt + 1) & 1) * 3 * C::TILE;
-        step_staging_next<C, NB, AVEC, BSRC, BVEC, false>(acc, st, R, g, m0, n0, (kt + 1) * BK, cur, nxt, wm, wn,
+        step_staging_next<C, NB, AVEC, BSRC, BVEC, false, RNE>(acc, st, R, g, m0, n0, (kt + 1) * BK, cur, nxt, wm, wn,
                                                          lane);
         __syncthreads();
     }
     if (kt + 1 < nk) {
         const uint16_t *cur = lds + (kt & 1) * 3 * C::TILE;
         uint16_t *nxt = lds + ((kt + 1) & 1) * 3 * C::TILE;
-        step_staging_next<C, NB, AVEC, BSRC, BVEC, true>(acc, st, R, g, m0, n0, (kt + 1) * BK, cur, nxt, wm, wn,
+        step_staging_next<C, NB, AVEC, BSRC, BVEC, true, RNE>(acc, st, R, g, m0, n0, (kt + 1) * BK, cur, nxt, wm, wn,
                                                         lane);
         __syncthreads();
     }
@@ -783,7 +783,7 @@ __device__ __forceinline__ void load_a_stage(float (&a)[C::A_CHUNKS][8], const u
     }
 }
 
-template <class C>
+template <class C, bool RNE>
 __device__ __forceinline__ bool store_a_stage(const float (&a)[C::A_CHUNKS][8], const int (&a_lds)[C::A_CHUNKS],
                                               uint16_t *abuf)
 {
@@ -791,7 +791,7 @@ __device__ __forceinline__ bool store_a_stage(const float (&a)[C::A_CHUNKS][8], 
     bool special = false;
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
-        special |= split8_packed_finite(a[c], p0, p1, p2);
+        special |= split8_packed_finite<RNE>(a[c], p0, p1, p2);
         st_lds16(abuf + 0 * DmaLayout<C>::A_TILE + a_lds[c], p0);
         st_lds16(abuf + 1 * DmaLayout<C>::A_TILE + a_lds[c], p1);
         st_lds16(abuf + 2 * DmaLayout<C>::A_TILE + a_lds[c], p2);
@@ -799,7 +799,7 @@ __device__ __forceinline__ bool store_a_stage(const float (&a)[C::A_CHUNKS][8], 
     return special;
 }
 
-template <class C, bool AVEC>
+template <class C, bool AVEC, bool RNE>
 __device__ __forceinline__ void restage_a_special(const uint32_t (&a_off)[C::A_CHUNKS], const int (&a_lds)[C::A_CHUNKS],
                                                   const GemmArgs &g, int64_t m0, int64_t k0, uint16_t *abuf)
 {
@@ -808,7 +808,7 @@ __device__ __forceinline__ void restage_a_special(const uint32_t (&a_off)[C::A_C
     uint32_t p0[4], p1[4], p2[4];
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
-        split8_packed(a[c], p0, p1, p2);
+        split8_packed<RNE>(a[c], p0, p1, p2);
         st_lds16(abuf + 0 * DmaLayout<C>::A_TILE + a_lds[c], p0);
         st_lds16(abuf + 1 * DmaLayout<C>::A_TILE + a_lds[c], p1);
         st_lds16(abuf + 2 * DmaLayout<C>::A_TILE + a_lds[c], p2);
@@ -882,7 +882,7 @@ __device__ __forceinline__ void mfma_slice_part(Acc<C, NB> &acc, const Frags<C> 
 // the second slice while those reads are in flight.  Steps past the end of K
 // are harmless: their descriptors end at the operands' last elements, so they
 // read zeros or data nobody consumes.
-template <class C, int NB, bool AVEC>
+template <class C, int NB, bool AVEC, bool RNE>
 __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C> &f1,
                                          float (&a_load)[C::A_CHUNKS][8], const float (&a_split)[C::A_CHUNKS][8],
                                          const StepSrc<C> &ld, const StepSrc<C> &sp, const int (&a_lds)[C::A_CHUNKS],
@@ -896,7 +896,7 @@ __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C>
     load_a_stage<C, AVEC>(a_load, ld.a_off, g, ld.m0, ld.k0);
     read_frags_dma<C>(f1, abuf, bbuf, 16, wm, wn, lane);
     mfma_slice<C, NB>(acc, f0);
-    const bool special = store_a_stage<C>(a_split, a_lds, abuf_next);
+    const bool special = store_a_stage<C, RNE>(a_split, a_lds, abuf_next);
     mfma_slice_part<C, NB, 0, NM - TAIL>(acc, f1);
     if constexpr (C::SCHED) {
         // a_split arrived during the previous step, so its split and LDS
@@ -907,7 +907,7 @@ __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C>
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
     }
-    if (__builtin_expect(special, 0)) restage_a_special<C, AVEC>(sp.a_off, a_lds, g, sp.m0, sp.k0, abuf_next);
+    if (__builtin_expect(special, 0)) restage_a_special<C, AVEC, RNE>(sp.a_off, a_lds, g, sp.m0, sp.k0, abuf_next);
     // The next step's B tile must have landed before the barrier; only the
     // copies and A loads issued at the top of this step may still be in
     // flight (vector-memory operations complete in order).
@@ -953,7 +953,7 @@ __device__ __forceinline__ void unit_src(StepSrc<C> &u, int v, int T, int64_t st
 // the last one splits the next tile's first A step and reads its first
 // fragments, so a tile's start costs no load latency and its C stores drain
 // while the next tile computes.
-template <class C, int NB, bool AVEC>
+template <class C, int NB, bool AVEC, bool RNE>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[DmaLayout<C>::TOTAL / 2];
@@ -992,8 +992,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     load_a_stage<C, AVEC>(a_cur, cur.a_off, g, cur.m0, cur.kb);
     dma_b_stage<C>(g, cur.n0, cur.kb + BK, b_base + B_BUF, wave, lane);
     load_a_stage<C, AVEC>(a_next, cur.a_off, g, cur.m0, cur.kb + BK);
-    if (store_a_stage<C>(a_cur, a_lds, a_base))
-        restage_a_special<C, AVEC>(cur.a_off, a_lds, g, cur.m0, cur.kb, a_base);
+    if (store_a_stage<C, RNE>(a_cur, a_lds, a_base))
+        restage_a_special<C, AVEC, RNE>(cur.a_off, a_lds, g, cur.m0, cur.kb, a_base);
     wait_vmem_at_most<dma_vmem_per_step<C, AVEC>()>();
     lds_barrier();
     read_frags_dma<C>(f0, a_base, b_base, 0, wm, wn, lane);
@@ -1021,7 +1021,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             StepSrc<C> sp = cur;
             sp.k0 = cur.kb + (kt + 1) * BK;
             const int b1 = bs == 2 ? 0 : bs + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-            dma_step<C, NB, AVEC>(acc, f0, f1, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
+            dma_step<C, NB, AVEC, RNE>(acc, f0, f1, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
                                   a_base + A_BUF, b_base + b1 * B_BUF, b_base + b2 * B_BUF, wave, wm, wn, lane);
 
             ld.k0 += BK;
@@ -1031,7 +1031,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             } else {
                 sp.k0 += BK;
             }
-            dma_step<C, NB, AVEC>(acc, f0, f1, a_next, a_cur, ld, sp, a_lds, g, a_base + A_BUF,
+            dma_step<C, NB, AVEC, RNE>(acc, f0, f1, a_next, a_cur, ld, sp, a_lds, g, a_base + A_BUF,
                                   b_base + b1 * B_BUF, a_base, b_base + b2 * B_BUF, b_base + bs * B_BUF, wave, wm,
                                   wn, lane);
             bs = b2;
@@ -1120,32 +1120,36 @@ static int group_rows(int tiles_n, int num_cus)
     return tiles_n * 4 <= per_xcd ? 1 : 8;
 }
 
-template <class C, int NB, int BSRC>
+template <class C, int NB, int BSRC, bool RNE>
 static void launch_cfg(const GemmArgs &g, bool avec, bool bvec, hipStream_t stream)
 {
     const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n)), block(C::NT);
-    if (avec) {
-        if (bvec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, true>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, false>), grid, block, 0, stream, g);
+    if constexpr (BSRC == B_FP32) {
+        // FP32 B loads element by element; only A has a vector path
+        if (avec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, false, RNE>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, false, RNE>), grid, block, 0, stream, g);
+    } else if (avec) {
+        if (bvec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, true, RNE>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, false, RNE>), grid, block, 0, stream, g);
     } else {
-        if (bvec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, true>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, false>), grid, block, 0, stream, g);
+        if (bvec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, true, RNE>), grid, block, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, false, RNE>), grid, block, 0, stream, g);
     }
 }
 
-template <class C, int BSRC>
+template <class C, int BSRC, bool RNE = false>
 static void launch_nb(const GemmArgs &g, int nbands, bool avec, bool bvec, hipStream_t stream)
 {
     switch (nbands) {
-    case 1: launch_cfg<C, 1, BSRC>(g, avec, bvec, stream); break;
-    case 2: launch_cfg<C, 2, BSRC>(g, avec, bvec, stream); break;
-    case 3: launch_cfg<C, 3, BSRC>(g, avec, bvec, stream); break;
-    case 4: launch_cfg<C, 4, BSRC>(g, avec, bvec, stream); break;
-    default: launch_cfg<C, 5, BSRC>(g, avec, bvec, stream); break;
+    case 1: launch_cfg<C, 1, BSRC, RNE>(g, avec, bvec, stream); break;
+    case 2: launch_cfg<C, 2, BSRC, RNE>(g, avec, bvec, stream); break;
+    case 3: launch_cfg<C, 3, BSRC, RNE>(g, avec, bvec, stream); break;
+    case 4: launch_cfg<C, 4, BSRC, RNE>(g, avec, bvec, stream); break;
+    default: launch_cfg<C, 5, BSRC, RNE>(g, avec, bvec, stream); break;
     }
 }
 
-template <class C, int NB>
+template <class C, int NB, bool RNE>
 static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
 {
     // One resident workgroup per CU (LDS-limited); a multiple of 8 keeps each
@@ -1153,8 +1157,8 @@ static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
     const int64_t units = (int64_t)g.tiles_m * g.tiles_n * g.splits;
     int64_t slots = (int64_t)(g.num_cus > 8 ? g.num_cus & ~7 : 8);
     const dim3 grid((unsigned)(units < slots ? units : slots)), block(C::NT);
-    if (avec) hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, true>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, false>), grid, block, 0, stream, g);
+    if (avec) hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, true, RNE>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, false, RNE>), grid, block, 0, stream, g);
     if (g.splits > 1) {
         int64_t blocks = (g.M * g.N + 255) / 256;
         if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
@@ -1162,7 +1166,7 @@ static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
     }
 }
 
-template <class C>
+template <class C, bool RNE>
 static hipError_t launch_dma(const GemmArgs &args, int nbands, hipStream_t stream)
 {
     GemmArgs g = args;
@@ -1171,17 +1175,17 @@ static hipError_t launch_dma(const GemmArgs &args, int nbands, hipStream_t strea
     g.group_m = group_rows(g.tiles_n, g.num_cus);
     const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0);
     switch (nbands) {
-    case 1: launch_dma_nb<C, 1>(g, avec, stream); break;
-    case 2: launch_dma_nb<C, 2>(g, avec, stream); break;
-    case 3: launch_dma_nb<C, 3>(g, avec, stream); break;
-    case 4: launch_dma_nb<C, 4>(g, avec, stream); break;
-    default: launch_dma_nb<C, 5>(g, avec, stream); break;
+    case 1: launch_dma_nb<C, 1, RNE>(g, avec, stream); break;
+    case 2: launch_dma_nb<C, 2, RNE>(g, avec, stream); break;
+    case 3: launch_dma_nb<C, 3, RNE>(g, avec, stream); break;
+    case 4: launch_dma_nb<C, 4, RNE>(g, avec, stream); break;
+    default: launch_dma_nb<C, 5, RNE>(g, avec, stream); break;
     }
     return hipGetLastError();
 }
 
 template <class C>
-static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream)
+static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
 {
     GemmArgs g = args;
     g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
@@ -1196,6 +1200,11 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
         bvec = aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && (g.ldb % 8 == 0) && (g.K % 8 == 0);
     else if (bsrc == B_PLANES_KN)
         bvec = aligned(g.B0, 4) && aligned(g.B1, 4) && aligned(g.B2, 4) && (g.ldb % 2 == 0) && (g.N % 2 == 0);
+    if (rne) {
+        if (bsrc != B_FP32) return hipErrorInvalidValue;
+        launch_nb<C, B_FP32, true>(g, nbands, avec, false, stream);
+        return hipGetLastError();
+    }
     switch (bsrc) {
     case B_FP32: launch_nb<C, B_FP32>(g, nbands, avec, false, stream); break;
     case B_PLANES_NK: launch_nb<C, B_PLANES_NK>(g, nbands, avec, bvec, stream); break;
@@ -1212,12 +1221,12 @@ bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const
     return K % (2 * BK) == 0 && ldb % 8 == 0 && aligned(B0, 16) && aligned(B1, 16) && aligned(B2, 16);
 }
 
-hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream)
+hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
 {
-    if (bsrc == B_PLANES_KN) return launch_with<Cfg8>(args, nbands, bsrc, stream);
+    if (bsrc == B_PLANES_KN) return launch_with<Cfg8>(args, nbands, bsrc, stream, rne);
     if (bsrc == B_PLANES_NK && gemm_uses_dma(args.K, args.ldb, args.B0, args.B1, args.B2))
-        return launch_dma<Cfg8S>(args, nbands, stream);
-    return launch_with<Cfg8S>(args, nbands, bsrc, stream);
+        return rne ? launch_dma<Cfg8S, true>(args, nbands, stream) : launch_dma<Cfg8S, false>(args, nbands, stream);
+    return launch_with<Cfg8S>(args, nbands, bsrc, stream, rne);
 }
 
 }  // namespace sgemm_emu_dev

@@ -36,13 +36,18 @@ struct GemmArgs {
     int64_t ldp;
 };
 
+// rne: round each split stage to nearest even instead of truncating (ablation).
 hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
-                        uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream);
+                        uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream,
+                        bool rne = false);
 
 hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
-                                  uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream);
+                                  uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream,
+                                  bool rne = false);
 
-hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream);
+// rne: the in-kernel split of A (and of FP32 B) rounds to nearest even; only
+// B_FP32 and B_PLANES_NK (DMA kernel) support it.
+hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne = false);
 
 // K slices the N x K DMA kernel should use for this shape (1 = no split-K):
 // grids that leave a quarter of the CUs idle get split along K.

@@ -12,7 +12,7 @@ namespace sgemm_emu_dev {
 
 // Flat chunk index -> (row, chunk-in-row).  chunks_per_row = cols / 8.  FLAT:
 // one contiguous row, so no division is needed.
-template <bool FLAT>
+template <bool FLAT, bool RNE>
 __global__ __launch_bounds__(256) void split_vec8_kernel(
     const float *__restrict__ X, int64_t ldx, uint16_t *__restrict__ X0, uint16_t *__restrict__ X1,
     uint16_t *__restrict__ X2, int64_t ldo, int64_t chunks_per_row, int64_t total_chunks)
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void split_vec8_kernel(
         f32x4_t v1 = __builtin_nontemporal_load(src + 1);
         float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         uint32_t p0[4], p1[4], p2[4];
-        if (split8_packed_finite(x, p0, p1, p2)) split8_packed(x, p0, p1, p2);
+        if (split8_packed_finite<RNE>(x, p0, p1, p2)) split8_packed<RNE>(x, p0, p1, p2);
         const int64_t o = row * ldo + col;
         *reinterpret_cast<uint4 *>(X0 + o) = make_uint4(p0[0], p0[1], p0[2], p0[3]);
         *reinterpret_cast<uint4 *>(X1 + o) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void split_vec8_kernel(
 
 // One element per thread (any layout).  TRANSPOSE writes the planes of X^T:
 // element (row, col) lands at col * ldo + row.
-template <bool TRANSPOSE>
+template <bool TRANSPOSE, bool RNE>
 __global__ __launch_bounds__(256) void split_scalar_kernel(
     const float *__restrict__ X, int64_t ldx, uint16_t *__restrict__ X0, uint16_t *__restrict__ X1,
     uint16_t *__restrict__ X2, int64_t ldo, int64_t rows, int64_t cols)
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(
         const int64_t col = e - row * cols;
         float x = X[row * ldx + col];
         uint32_t c0, c1, c2;
-        float t = split_finite(x, c0, c1, c2);
+        float t = split_finite<RNE>(x, c0, c1, c2);
         if (t != t) split_fix_special(x, c0, c1, c2);
         const int64_t o = TRANSPOSE ? col * ldo + row : row * ldo + col;
         X0[o] = (uint16_t)(c0 >> 16);
@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(
 // layouts take split_scalar_kernel<true>.
 constexpr int kTT = 64;
 
+template <bool RNE>
 __global__ __launch_bounds__(256) void split_transpose_kernel(
     const float *__restrict__ X, int64_t ldx, uint16_t *__restrict__ X0, uint16_t *__restrict__ X1,
     uint16_t *__restrict__ X2, int64_t ldo, int64_t rows, int64_t cols, int64_t tiles_c)
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void split_transpose_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = tile[8 * kg + e][n];
         uint32_t p0[4], p1[4], p2[4];
-        if (split8_packed_finite(x, p0, p1, p2)) split8_packed(x, p0, p1, p2);
+        if (split8_packed_finite<RNE>(x, p0, p1, p2)) split8_packed<RNE>(x, p0, p1, p2);
         const int64_t o = (c0 + n) * ldo + r0 + 8 * kg;
         *reinterpret_cast<uint4 *>(X0 + o) = make_uint4(p0[0], p0[1], p0[2], p0[3]);
         *reinterpret_cast<uint4 *>(X1 + o) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
@@ -105,27 +106,36 @@ __global__ __launch_bounds__(256) void split_transpose_kernel(
     }
 }
 
-hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
-                                  uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream)
+template <bool RNE>
+static hipError_t split_transpose_with(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                                       uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream)
 {
     if (rows == 0 || cols == 0) return hipSuccess;
     if (rows % 8 != 0 || ldo % 8 != 0 || !aligned(X0, 16) || !aligned(X1, 16) || !aligned(X2, 16)) {
         const int threads = 256;
         int64_t blocks = (rows * cols + threads - 1) / threads;
         if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
-        hipLaunchKernelGGL(split_scalar_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, stream, X, ldx,
+        hipLaunchKernelGGL((split_scalar_kernel<true, RNE>), dim3((unsigned)blocks), dim3(threads), 0, stream, X, ldx,
                            X0, X1, X2, ldo, rows, cols);
         return hipGetLastError();
     }
     const int64_t tiles_c = (cols + kTT - 1) / kTT, tiles_r = (rows + kTT - 1) / kTT;
     if (tiles_r > (int64_t)0x7FFFFFFF / tiles_c) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(split_transpose_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, stream, X,
+    hipLaunchKernelGGL(split_transpose_kernel<RNE>, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, stream, X,
                        ldx, X0, X1, X2, ldo, rows, cols, tiles_c);
     return hipGetLastError();
 }
 
-hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
-                        uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream)
+hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                                  uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream, bool rne)
+{
+    return rne ? split_transpose_with<true>(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, stream)
+               : split_transpose_with<false>(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, stream);
+}
+
+template <bool RNE>
+static hipError_t split_with(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                             uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream)
 {
     const bool vec = (cols % 8 == 0) && (ldx % 4 == 0) && (ldo % 8 == 0) &&
                      aligned(X, 16) && aligned(X0, 16) && aligned(X1, 16) && aligned(X2, 16);
@@ -141,19 +151,26 @@ hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx,
         int64_t blocks = (total + threads - 1) / threads;
         if (blocks > max_blocks) blocks = max_blocks;
         if (r == 1)
-            hipLaunchKernelGGL(split_vec8_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+            hipLaunchKernelGGL((split_vec8_kernel<true, RNE>), dim3((unsigned)blocks), dim3(threads), 0, stream,
                                X, lx, X0, X1, X2, lo, chunks_per_row, total);
         else
-            hipLaunchKernelGGL(split_vec8_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+            hipLaunchKernelGGL((split_vec8_kernel<false, RNE>), dim3((unsigned)blocks), dim3(threads), 0, stream,
                                X, lx, X0, X1, X2, lo, chunks_per_row, total);
     } else {
         const int64_t total = rows * cols;
         int64_t blocks = (total + threads - 1) / threads;
         if (blocks > max_blocks) blocks = max_blocks;
-        hipLaunchKernelGGL(split_scalar_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, stream, X, ldx,
-                           X0, X1, X2, ldo, rows, cols);
+        hipLaunchKernelGGL((split_scalar_kernel<false, RNE>), dim3((unsigned)blocks), dim3(threads), 0, stream, X,
+                           ldx, X0, X1, X2, ldo, rows, cols);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
+                        uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream, bool rne)
+{
+    return rne ? split_with<true>(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, stream)
+               : split_with<false>(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, stream);
 }
 
 }  // namespace sgemm_emu_dev

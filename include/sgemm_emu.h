@@ -104,6 +104,29 @@ int sgemm_emu(int64_t M, int64_t N, int64_t K,
               float *C, int64_t ldc,
               int nbands, sgemm_emu_stream_t stream);
 
+/* Flags of sgemm_emu_ex and split_f32_bf16x3_ex. */
+enum sgemm_emu_flags {
+    SGEMM_EMU_SPLIT_RNE = 1,        /* rounding ablation: each split stage rounds to the nearest BF16,
+                                       ties to even, never to Inf (a finite value that would round to
+                                       Inf keeps its truncation), instead of truncating */
+    SGEMM_EMU_SPLIT_TRANSPOSE = 2   /* split_f32_bf16x3_ex only: write the planes of X^T */
+};
+
+/*
+ * sgemm_emu_ex -- sgemm_emu with flags (0 or SGEMM_EMU_SPLIT_RNE; anything else
+ * gives SGEMM_EMU_EINVAL).  With SGEMM_EMU_SPLIT_RNE both A and B are split
+ * with the round-to-nearest rule: with all nine products the result is the
+ * same emulated product up to FP32 rounding (both splits are exact); with
+ * fewer bands the dropped terms are about half as large and unsigned-biased
+ * errors disappear.  The pages leave the rounding of the split open; the
+ * library's default is truncation.
+ */
+int sgemm_emu_ex(int64_t M, int64_t N, int64_t K,
+                 const float *A, int64_t lda,
+                 const float *B, int64_t ldb,
+                 float *C, int64_t ldc,
+                 int nbands, int flags, sgemm_emu_stream_t stream);
+
 /* Layouts of pre-split B planes (sgemm_emu_presplit_b). */
 enum sgemm_emu_b_layout {
     SGEMM_EMU_B_KN = 0,  /* planes are K x N row-major: B0[k*ldb + j], as split_f32_bf16x3(B) gives */
@@ -172,6 +195,17 @@ int split_f32_bf16x3(int64_t rows, int64_t cols,
                      const float *X, int64_t ldx,
                      uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo,
                      sgemm_emu_stream_t stream);
+
+/*
+ * split_f32_bf16x3_ex -- split_f32_bf16x3 with flags: SGEMM_EMU_SPLIT_RNE
+ * (round-to-nearest split, see sgemm_emu_ex) and/or SGEMM_EMU_SPLIT_TRANSPOSE
+ * (planes of X^T, cols x rows with ldo >= max(1, rows), as
+ * split_f32_bf16x3_transposed).  Other flag bits give SGEMM_EMU_EINVAL.
+ */
+int split_f32_bf16x3_ex(int64_t rows, int64_t cols,
+                        const float *X, int64_t ldx,
+                        uint16_t *X0, uint16_t *X1, uint16_t *X2, int64_t ldo,
+                        int flags, sgemm_emu_stream_t stream);
 
 /*
  * split_f32_bf16x3_transposed -- the same split, written transposed: for the

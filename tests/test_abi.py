@@ -106,6 +106,16 @@ def test_split_validation(L):
     assert L.split_f32_bf16x3(0, 4, 0, 4, 0, 0, 0, 4, None) == 0
 
 
+def test_ex_entry_flags(L):
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 2, None) == -1     # unknown flag
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 0, 1, None) == -1     # nbands
+    assert L.sgemm_emu_ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 5, 1, None) == 0      # empty
+    assert L.split_f32_bf16x3_ex(4, 4, P, 4, P, P, P, 4, 4, None) == -1    # unknown flag
+    assert L.split_f32_bf16x3_ex(6, 4, P, 4, P, P, P, 5, 2, None) == -1    # transposed: ldo < rows
+    assert L.split_f32_bf16x3_ex(6, 4, P, 4, P, P, P, 3, 1, None) == -1    # plain: ldo < cols
+    assert L.split_f32_bf16x3_ex(0, 4, 0, 4, 0, 0, 0, 4, 3, None) == 0
+
+
 def test_split_transposed_validation(L):
     # X is rows x cols (ldx >= cols); the planes are cols x rows (ldo >= rows)
     assert L.split_f32_bf16x3_transposed(-1, 4, P, 4, P, P, P, 4, None) == -1

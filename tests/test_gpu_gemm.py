@@ -460,3 +460,51 @@ def test_matmul_helpers(fe):
     torch.cuda.synchronize()
     assert torch.equal(C, Cp)
     check_against_fp64(C.cpu().numpy(), A.cpu().numpy(), B.cpu().numpy(), label="matmul")
+
+
+
+# ---------------------------------------------------------------- round-to-nearest split (ablation)
+
+def _run_ex(fe, A, B, nbands, flags):
+    M, K = A.shape
+    N = B.shape[1]
+    print(f"gemm ex M={M} N={N} K={K} nbands={nbands} flags={flags}", flush=True, file=sys.stderr)
+    Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    fe.sgemm_emu_ex(M, N, K, dev(A), K, dev(B), N, Cd, N, nbands, flags)
+    return host(Cd)
+
+
+RNE_SHAPES = [(200, 150, 70), (300, 257, 128), (1100, 260, 256), (1024, 1024, 1024)]
+
+
+@pytest.mark.parametrize("shape", RNE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_rne_split_gemm_within_bound(fe, orc, shape):
+    """SGEMM_EMU_SPLIT_RNE through the in-kernel split (fallback kernel) and the
+    workspace split (plane kernel, split-K for the square case): within the
+    FP64 bound with nine products, and every band count within the accumulation
+    bound of the oracle's truncated-band value under the same split."""
+    M, N, K = shape
+    g = _rng(M + 2 * N + 3 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    rows = np.sort(g.choice(M, size=min(M, 64), replace=False))
+    C = _run_ex(fe, A, B, 5, fe.SGEMM_EMU_SPLIT_RNE)
+    check_against_fp64(C[rows], A, B, rows=rows, label=f"rne {shape}")
+    _, G = orc.gemm_f64(A, B, rows=rows)
+    for nb in (1, 2, 3, 4):
+        Cb = _run_ex(fe, A, B, nb, fe.SGEMM_EMU_SPLIT_RNE)[rows].astype(np.float64)
+        T = orc.gemm_trunc_f64(A, B, nb, rows=rows, flags=orc.ORC_SPLIT_RNE)
+        assert np.all(np.abs(Cb - T) <= 2 * K * 2.0 ** -24 * G), f"nbands={nb}"
+
+
+def test_rne_split_identity_exact_and_smaller_ablation_error(fe, orc):
+    g = _rng(71)
+    X = (g.standard_normal((64, 64)) * 2.0 ** g.integers(-20, 20, (64, 64))).astype(np.float32)
+    I = np.eye(64, dtype=np.float32)
+    assert np.array_equal(_run_ex(fe, I, X, 5, fe.SGEMM_EMU_SPLIT_RNE).view(np.uint32), X.view(np.uint32))
+    A = g.standard_normal((256, 512)).astype(np.float32)
+    B = g.standard_normal((512, 256)).astype(np.float32)
+    ref, _ = orc.gemm_f64(A, B)
+    e_rz = _run_ex(fe, A, B, 2, 0).astype(np.float64) - ref
+    e_rne = _run_ex(fe, A, B, 2, fe.SGEMM_EMU_SPLIT_RNE).astype(np.float64) - ref
+    assert np.sqrt(np.mean(e_rne ** 2)) < 0.5 * np.sqrt(np.mean(e_rz ** 2))

@@ -89,3 +89,44 @@ def test_split_transposed_bit_exact(fe, orc, rows, cols, ldx, ldo):
         assert np.array_equal(got[c][:, :rows], want[c])
         if ldo > rows:
             assert np.all(got[c][:, rows:] == 0xFFFF)
+
+
+def test_split_rne_all_encodings_bit_exact(fe, orc):
+    """The round-to-nearest split (SGEMM_EMU_SPLIT_RNE) on all 2^32 encodings."""
+    chunk = 1 << 28
+    for start in range(0, 1 << 32, chunk):
+        print(f"split rne chunk {start:#x}", flush=True, file=sys.stderr)
+        x = torch.arange(start, start + chunk, dtype=torch.int64, device="cuda").to(torch.int32).view(torch.float32)
+        planes = [torch.empty(chunk, dtype=torch.int16, device="cuda") for _ in range(3)]
+        fe.split_f32_bf16x3_ex(1, chunk, x, chunk, *planes, chunk, fe.SGEMM_EMU_SPLIT_RNE)
+        got = _planes_host(planes)
+        xh = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        want = orc.split(xh, orc.SPLIT_RNE)
+        for c in range(3):
+            if not np.array_equal(got[c], want[c]):
+                bad = np.nonzero(got[c] != want[c])[0][0]
+                raise AssertionError(f"rne component {c} differs at encoding {start + bad:#010x}: "
+                                     f"gpu {got[c][bad]:#06x} oracle {want[c][bad]:#06x}")
+        del x, planes
+
+
+@pytest.mark.parametrize("rows,cols,ldx,ldo,flags", [
+    (37, 53, 53, 53, 1),        # scalar kernel, RNE
+    (64, 256, 256, 256, 1),     # vector kernel, RNE
+    (256, 1024, 1024, 256, 3),  # transposed, tiled, RNE
+    (130, 70, 70, 130, 3),      # transposed, element-wise, RNE
+])
+def test_split_ex_layouts(fe, orc, rows, cols, ldx, ldo, flags):
+    g = np.random.Generator(np.random.Philox(key=rows * 3 + cols + flags))
+    X = (g.standard_normal((rows, ldx)) * 2.0 ** g.integers(-60, 60, (rows, ldx))).astype(np.float32)
+    X[1, 2] = np.float32(3.4028235e38)
+    tr = bool(flags & fe.SGEMM_EMU_SPLIT_TRANSPOSE)
+    prow, pcol = (cols, rows) if tr else (rows, cols)
+    planes = [torch.full((prow * ldo,), -1, dtype=torch.int16, device="cuda") for _ in range(3)]
+    print(f"split ex {rows}x{cols} flags={flags}", flush=True, file=sys.stderr)
+    fe.split_f32_bf16x3_ex(rows, cols, torch.from_numpy(X).cuda(), ldx, *planes, ldo, flags)
+    got = [p.reshape(prow, ldo)[:, :pcol] for p in _planes_host(planes)]
+    src = X[:, :cols].T if tr else X[:, :cols]
+    want = orc.split(np.ascontiguousarray(src), orc.SPLIT_RNE)
+    for c in range(3):
+        assert np.array_equal(got[c], want[c])
