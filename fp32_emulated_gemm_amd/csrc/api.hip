@@ -249,9 +249,26 @@ int sgemm_emu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
 int sgemm_emu_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
                  float *C, int64_t ldc, int nbands, int flags, sgemm_emu_stream_t stream)
 {
-    if ((flags & ~SGEMM_EMU_SPLIT_RNE) != 0) return SGEMM_EMU_EINVAL;
-    return gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32,
-                       (hipStream_t)stream, nullptr, SGEMM_EMU_ACT_NONE, (flags & SGEMM_EMU_SPLIT_RNE) != 0);
+    if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_IEEE_SPECIALS)) != 0) return SGEMM_EMU_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    int rc = gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32, s, nullptr,
+                         SGEMM_EMU_ACT_NONE, (flags & SGEMM_EMU_SPLIT_RNE) != 0);
+    if (rc != SGEMM_EMU_OK || !(flags & SGEMM_EMU_IEEE_SPECIALS) || M == 0 || N == 0 || K == 0) return rc;
+    // IEEE fix-up of the outputs touched by non-finite inputs (flags and a
+    // column list in a pooled stream-ordered buffer)
+    int num_cus = 0, dev = 0;
+    if ((rc = current_device(&num_cus, &dev)) != SGEMM_EMU_OK) return rc;
+    hipMemPool_t pool = workspace_pool(dev);
+    if (pool == nullptr) return SGEMM_EMU_ELAUNCH;
+    void *work = nullptr;
+    const size_t bytes = (size_t)(2 * (M + N) + 1) * sizeof(int);
+    if (hipMallocFromPoolAsync(&work, bytes, pool, s) != hipSuccess || work == nullptr) {
+        (void)hipGetLastError();
+        return SGEMM_EMU_ELAUNCH;
+    }
+    hipError_t e = launch_ieee_fixup(M, N, K, A, lda, B, ldb, C, ldc, (int *)work, num_cus, s);
+    const hipError_t f = hipFreeAsync(work, s);
+    return launched(e == hipSuccess ? f : e);
 }
 
 int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const uint16_t *B0,

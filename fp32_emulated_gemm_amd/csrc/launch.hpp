@@ -57,6 +57,11 @@ int gemm_split_count(int64_t M, int64_t N, int64_t K, int nbands, int num_cus);
 bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const void *B2);
 
 // C := act(0 + bias[j]) (K == 0); without bias and activation C := 0.
+// Recompute, as plain FP32 dot products, every output of C = A B whose row of
+// A or column of B holds an Inf or NaN.  work: 2 (M + N) + 1 ints.
+hipError_t launch_ieee_fixup(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                             int64_t ldb, float *C, int64_t ldc, int *work, int num_cus, hipStream_t stream);
+
 hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, const float *bias, int act, int num_cus,
                        hipStream_t stream);
 

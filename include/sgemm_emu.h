@@ -109,12 +109,18 @@ enum sgemm_emu_flags {
     SGEMM_EMU_SPLIT_RNE = 1,        /* rounding ablation: each split stage rounds to the nearest BF16,
                                        ties to even, never to Inf (a finite value that would round to
                                        Inf keeps its truncation), instead of truncating */
-    SGEMM_EMU_SPLIT_TRANSPOSE = 2   /* split_f32_bf16x3_ex only: write the planes of X^T */
+    SGEMM_EMU_SPLIT_TRANSPOSE = 2,  /* split_f32_bf16x3_ex only: write the planes of X^T */
+    SGEMM_EMU_IEEE_SPECIALS = 4     /* sgemm_emu_ex only: outputs whose row of A or column of B holds
+                                       an Inf or NaN are recomputed as plain FP32 dot products (k
+                                       ascending, product and sum rounded separately), so they follow
+                                       IEEE-754 FP32 (+-Inf where the emulation's Inf x 0 component
+                                       gives NaN); other outputs are unchanged.  Costs one more read
+                                       of A and B and a pooled (2 (M + N) + 1)-int buffer. */
 };
 
 /*
- * sgemm_emu_ex -- sgemm_emu with flags (0 or SGEMM_EMU_SPLIT_RNE; anything else
- * gives SGEMM_EMU_EINVAL).  With SGEMM_EMU_SPLIT_RNE both A and B are split
+ * sgemm_emu_ex -- sgemm_emu with flags (SGEMM_EMU_SPLIT_RNE and/or
+ * SGEMM_EMU_IEEE_SPECIALS; other bits give SGEMM_EMU_EINVAL).  With SGEMM_EMU_SPLIT_RNE both A and B are split
  * with the round-to-nearest rule: with all nine products the result is the
  * same emulated product up to FP32 rounding (both splits are exact); with
  * fewer bands the dropped terms are about half as large and unsigned-biased

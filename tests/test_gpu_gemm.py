@@ -508,3 +508,44 @@ def test_rne_split_identity_exact_and_smaller_ablation_error(fe, orc):
     e_rz = _run_ex(fe, A, B, 2, 0).astype(np.float64) - ref
     e_rne = _run_ex(fe, A, B, 2, fe.SGEMM_EMU_SPLIT_RNE).astype(np.float64) - ref
     assert np.sqrt(np.mean(e_rne ** 2)) < 0.5 * np.sqrt(np.mean(e_rz ** 2))
+
+
+# ---------------------------------------------------------------- IEEE fix-up of non-finite inputs
+
+@pytest.mark.parametrize("shape", [(48, 40, 70), (1030, 300, 128), (200, 140, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ieee_specials_fixup(fe, orc, shape):
+    """SGEMM_EMU_IEEE_SPECIALS: outputs whose row of A or column of B holds an Inf
+    or NaN equal the oracle's plain FP32 dot product bit for bit (+-Inf where the
+    emulation gives NaN); all other outputs equal the emulation's."""
+    M, N, K = shape
+    g = _rng(M + N + K + 5)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    B[3, :] = 1.0                          # components (1, 0, 0): Inf x 0 inside the emulation
+    A[2, 3] = np.inf                       # row 2: IEEE gives +-Inf, the emulation NaN
+    A[5, 3] = -np.inf
+    A[7, 9] = np.nan
+    B[10, N - 1] = np.inf                  # last column flagged
+    B[11, N // 2] = -np.inf
+    A[M - 1, 0] = np.nan                   # last row flagged
+    C_emu = _run_ex(fe, A, B, 5, 0)
+    C = _run_ex(fe, A, B, 5, fe.SGEMM_EMU_IEEE_SPECIALS)
+    rows = np.unique([2, 5, 7, M - 1])
+    cols = np.unique([N - 1, N // 2])
+    flagged = np.zeros((M, N), bool)
+    flagged[rows, :] = True
+    flagged[:, cols] = True
+    naive = orc.sgemm_naive_f32(A, B)
+    assert np.array_equal(C[flagged].view(np.uint32), naive[flagged].view(np.uint32))
+    assert np.array_equal(C[~flagged].view(np.uint32), C_emu[~flagged].view(np.uint32))
+    assert np.isinf(C[2, 0]) and np.isnan(C_emu[2, 0])      # the case the fix-up exists for
+    assert np.all(~np.isfinite(C[flagged]))
+
+
+def test_ieee_specials_fixup_finite_inputs_unchanged(fe):
+    g = _rng(99)
+    A = g.standard_normal((300, 200)).astype(np.float32)
+    B = g.standard_normal((200, 150)).astype(np.float32)
+    assert np.array_equal(_run_ex(fe, A, B, 5, fe.SGEMM_EMU_IEEE_SPECIALS).view(np.uint32),
+                          _run_ex(fe, A, B, 5, 0).view(np.uint32))
