@@ -68,7 +68,7 @@ struct Cfg {
 };
 
 using Cfg8 = Cfg<2, 4, 64, 32>;              // 8 waves, 2 per SIMD, 128 x 128 tile
-using Cfg8S = Cfg<2, 4, 64, 32, true, 4>;    // same, staging interleaved with the MFMAs
+using Cfg8S = Cfg<2, 4, 64, 32, true, 4, 4>; // same, staging interleaved with the MFMAs
 using Cfg4D = Cfg<2, 2, 64, 64, true, 2, 12>; // 4 waves, 1 per SIMD, 128 x 128 tile (DMA kernel)
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
@@ -904,7 +904,7 @@ __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C>
 #pragma unroll
         for (int i = 0; i < 2 * NM - TAIL; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
     }
     if (__builtin_expect(special, 0)) restage_a_special<C, AVEC, RNE>(sp.a_off, a_lds, g, sp.m0, sp.k0, abuf_next);
