@@ -160,7 +160,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     if (K == 0) return launched(launch_zero(M, N, C, ldc, bias, act, num_cus, stream));
 
     GemmArgs g{};
-    g.M = M; g.N = N; g.K = K;
+    g.M = M; g.N = N; g.K = K; g.ka = K;
     g.A = A; g.lda = lda;
     g.B = B; g.B0 = B0; g.B1 = B1; g.B2 = B2; g.ldb = ldb;
     g.C = C; g.ldc = ldc;
@@ -173,23 +173,28 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // FP32 B with many tile rows: split B once into N x K planes in a
     // stream-ordered workspace and run the LDS-DMA kernel, instead of splitting
     // B again in every tile row.  Same split, same products, same order of
-    // MFMA accumulation, so the result is bitwise identical.
+    // MFMA accumulation, so the result is bitwise identical (zero-padded K
+    // steps add zero products).
     hipMemPool_t pool = nullptr;
     void *bws = nullptr;
-    if (bsrc == B_FP32 && K % 64 == 0 && M >= kPresplitMinRows && (uint64_t)K * (uint64_t)N <= kPresplitMaxElems &&
-        (pool = workspace_pool(dev)) != nullptr) {
-        const int64_t ldo = K;
+    // A K that is not a multiple of 64 is padded in the planes (zeros) and
+    // the kernel masks A past its K.
+    const int64_t kpad = (K + 63) / 64 * 64;
+    if (bsrc == B_FP32 && M >= kPresplitMinRows && (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems &&
+        !(rne && kpad != K) && (pool = workspace_pool(dev)) != nullptr) {
+        const int64_t ldo = kpad;
         const size_t plane = (size_t)N * (size_t)ldo * sizeof(uint16_t);
         const size_t plane_pad = (plane + 255) & ~(size_t)255;
         if (hipMallocFromPoolAsync(&bws, 3 * plane_pad, pool, stream) == hipSuccess && bws != nullptr) {
             uint16_t *P0 = (uint16_t *)bws, *P1 = (uint16_t *)((char *)bws + plane_pad),
                      *P2 = (uint16_t *)((char *)bws + 2 * plane_pad);
-            const hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, ldo, num_cus, stream, rne);
+            const hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, ldo, num_cus, stream, rne, kpad);
             if (e != hipSuccess) {
                 (void)hipFreeAsync(bws, stream);
                 return launched(e);
             }
             g.B0 = P0; g.B1 = P1; g.B2 = P2; g.ldb = ldo;
+            g.K = kpad;
             bsrc = B_PLANES_NK;
         } else {
             bws = nullptr;
@@ -201,8 +206,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // K: each (tile, K slice) recombines its own bands and writes the result to
     // a pooled partial buffer; a reduction kernel adds the slices in order.
     void *pws = nullptr;
-    if (bsrc == B_PLANES_NK && gemm_uses_dma(K, g.ldb, g.B0, g.B1, g.B2)) {
-        const int sl = gemm_split_count(M, N, K, nbands, num_cus);
+    if (bsrc == B_PLANES_NK && gemm_uses_dma(g.K, g.ldb, g.B0, g.B1, g.B2)) {
+        const int sl = gemm_split_count(M, N, g.K, nbands, num_cus);
         if (sl > 1 && (pool != nullptr || (pool = workspace_pool(dev)) != nullptr)) {
             const size_t bytes = (size_t)sl * (size_t)M * (size_t)N * sizeof(float);
             if (hipMallocFromPoolAsync(&pws, bytes, pool, stream) == hipSuccess && pws != nullptr) {

@@ -768,7 +768,8 @@ __device__ __forceinline__ void load_a_stage(float (&a)[C::A_CHUNKS][8], const u
                                              const GemmArgs &g, int64_t m0, int64_t k0)
 {
     const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
-    const rsrc_t ra = make_rsrc(g.A + m0 * g.lda + k0, ((rows - 1) * g.lda + (g.K - k0)) * 4);
+    // A's own K (g.ka) bounds the descriptor; g.K may be the padded K of the B planes
+    const rsrc_t ra = make_rsrc(g.A + m0 * g.lda + k0, ((rows - 1) * g.lda + (g.ka - k0)) * 4);
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
         if (AVEC) {
@@ -783,15 +784,34 @@ __device__ __forceinline__ void load_a_stage(float (&a)[C::A_CHUNKS][8], const u
     }
 }
 
-template <class C, bool RNE>
+// Elements of the staged A at k >= K (the last K step of an operand whose K
+// is not a multiple of 2 BK, against zero-padded B planes) must be zero:
+// their loads read the next row's values.  kvalid = K - (the step's first k).
+template <class C, bool KTAIL>
+__device__ __forceinline__ void mask_a_tail(float (&x)[8], const float (&a)[8], int c, int64_t kvalid)
+{
+    if constexpr (KTAIL) {
+        int row, kg;
+        chunk_rc(c * C::NT + threadIdx.x, row, kg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (kg * 8 + e < kvalid) ? a[e] : 0.0f;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = a[e];
+    }
+}
+
+template <class C, bool RNE, bool KTAIL>
 __device__ __forceinline__ bool store_a_stage(const float (&a)[C::A_CHUNKS][8], const int (&a_lds)[C::A_CHUNKS],
-                                              uint16_t *abuf)
+                                              uint16_t *abuf, int64_t kvalid)
 {
     uint32_t p0[4], p1[4], p2[4];
     bool special = false;
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
-        special |= split8_packed_finite<RNE>(a[c], p0, p1, p2);
+        float x[8];
+        mask_a_tail<C, KTAIL>(x, a[c], c, kvalid);
+        special |= split8_packed_finite<RNE>(x, p0, p1, p2);
         st_lds16(abuf + 0 * DmaLayout<C>::A_TILE + a_lds[c], p0);
         st_lds16(abuf + 1 * DmaLayout<C>::A_TILE + a_lds[c], p1);
         st_lds16(abuf + 2 * DmaLayout<C>::A_TILE + a_lds[c], p2);
@@ -799,7 +819,7 @@ __device__ __forceinline__ bool store_a_stage(const float (&a)[C::A_CHUNKS][8], 
     return special;
 }
 
-template <class C, bool AVEC, bool RNE>
+template <class C, bool AVEC, bool RNE, bool KTAIL>
 __device__ __forceinline__ void restage_a_special(const uint32_t (&a_off)[C::A_CHUNKS], const int (&a_lds)[C::A_CHUNKS],
                                                   const GemmArgs &g, int64_t m0, int64_t k0, uint16_t *abuf)
 {
@@ -808,7 +828,9 @@ __device__ __forceinline__ void restage_a_special(const uint32_t (&a_off)[C::A_C
     uint32_t p0[4], p1[4], p2[4];
 #pragma unroll
     for (int c = 0; c < C::A_CHUNKS; ++c) {
-        split8_packed<RNE>(a[c], p0, p1, p2);
+        float x[8];
+        mask_a_tail<C, KTAIL>(x, a[c], c, g.ka - k0);
+        split8_packed<RNE>(x, p0, p1, p2);
         st_lds16(abuf + 0 * DmaLayout<C>::A_TILE + a_lds[c], p0);
         st_lds16(abuf + 1 * DmaLayout<C>::A_TILE + a_lds[c], p1);
         st_lds16(abuf + 2 * DmaLayout<C>::A_TILE + a_lds[c], p2);
@@ -882,7 +904,7 @@ __device__ __forceinline__ void mfma_slice_part(Acc<C, NB> &acc, const Frags<C> 
 // the second slice while those reads are in flight.  Steps past the end of K
 // are harmless: their descriptors end at the operands' last elements, so they
 // read zeros or data nobody consumes.
-template <class C, int NB, bool AVEC, bool RNE>
+template <class C, int NB, bool AVEC, bool RNE, bool KTAIL>
 __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C> &f1,
                                          float (&a_load)[C::A_CHUNKS][8], const float (&a_split)[C::A_CHUNKS][8],
                                          const StepSrc<C> &ld, const StepSrc<C> &sp, const int (&a_lds)[C::A_CHUNKS],
@@ -896,7 +918,7 @@ __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C>
     load_a_stage<C, AVEC>(a_load, ld.a_off, g, ld.m0, ld.k0);
     read_frags_dma<C>(f1, abuf, bbuf, 16, wm, wn, lane);
     mfma_slice<C, NB>(acc, f0);
-    const bool special = store_a_stage<C, RNE>(a_split, a_lds, abuf_next);
+    const bool special = store_a_stage<C, RNE, KTAIL>(a_split, a_lds, abuf_next, g.ka - sp.k0);
     mfma_slice_part<C, NB, 0, NM - TAIL>(acc, f1);
     if constexpr (C::SCHED) {
         // a_split arrived during the previous step, so its split and LDS
@@ -907,7 +929,8 @@ __device__ __forceinline__ void dma_step(Acc<C, NB> &acc, Frags<C> &f0, Frags<C>
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
     }
-    if (__builtin_expect(special, 0)) restage_a_special<C, AVEC, RNE>(sp.a_off, a_lds, g, sp.m0, sp.k0, abuf_next);
+    if (__builtin_expect(special, 0))
+        restage_a_special<C, AVEC, RNE, KTAIL>(sp.a_off, a_lds, g, sp.m0, sp.k0, abuf_next);
     // The next step's B tile must have landed before the barrier; only the
     // copies and A loads issued at the top of this step may still be in
     // flight (vector-memory operations complete in order).
@@ -953,7 +976,7 @@ __device__ __forceinline__ void unit_src(StepSrc<C> &u, int v, int T, int64_t st
 // the last one splits the next tile's first A step and reads its first
 // fragments, so a tile's start costs no load latency and its C stores drain
 // while the next tile computes.
-template <class C, int NB, bool AVEC, bool RNE>
+template <class C, int NB, bool AVEC, bool RNE, bool KTAIL>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[DmaLayout<C>::TOTAL / 2];
@@ -992,8 +1015,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     load_a_stage<C, AVEC>(a_cur, cur.a_off, g, cur.m0, cur.kb);
     dma_b_stage<C>(g, cur.n0, cur.kb + BK, b_base + B_BUF, wave, lane);
     load_a_stage<C, AVEC>(a_next, cur.a_off, g, cur.m0, cur.kb + BK);
-    if (store_a_stage<C, RNE>(a_cur, a_lds, a_base))
-        restage_a_special<C, AVEC, RNE>(cur.a_off, a_lds, g, cur.m0, cur.kb, a_base);
+    if (store_a_stage<C, RNE, KTAIL>(a_cur, a_lds, a_base, g.ka - cur.kb))
+        restage_a_special<C, AVEC, RNE, KTAIL>(cur.a_off, a_lds, g, cur.m0, cur.kb, a_base);
     wait_vmem_at_most<dma_vmem_per_step<C, AVEC>()>();
     lds_barrier();
     read_frags_dma<C>(f0, a_base, b_base, 0, wm, wn, lane);
@@ -1021,7 +1044,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             StepSrc<C> sp = cur;
             sp.k0 = cur.kb + (kt + 1) * BK;
             const int b1 = bs == 2 ? 0 : bs + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-            dma_step<C, NB, AVEC, RNE>(acc, f0, f1, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
+            dma_step<C, NB, AVEC, RNE, KTAIL>(acc, f0, f1, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
                                   a_base + A_BUF, b_base + b1 * B_BUF, b_base + b2 * B_BUF, wave, wm, wn, lane);
 
             ld.k0 += BK;
@@ -1031,7 +1054,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             } else {
                 sp.k0 += BK;
             }
-            dma_step<C, NB, AVEC, RNE>(acc, f0, f1, a_next, a_cur, ld, sp, a_lds, g, a_base + A_BUF,
+            dma_step<C, NB, AVEC, RNE, KTAIL>(acc, f0, f1, a_next, a_cur, ld, sp, a_lds, g, a_base + A_BUF,
                                   b_base + b1 * B_BUF, a_base, b_base + b2 * B_BUF, b_base + bs * B_BUF, wave, wm,
                                   wn, lane);
             bs = b2;
@@ -1149,7 +1172,7 @@ static void launch_nb(const GemmArgs &g, int nbands, bool avec, bool bvec, hipSt
     }
 }
 
-template <class C, int NB, bool RNE>
+template <class C, int NB, bool RNE, bool KTAIL>
 static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
 {
     // One resident workgroup per CU (LDS-limited); a multiple of 8 keeps each
@@ -1157,8 +1180,8 @@ static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
     const int64_t units = (int64_t)g.tiles_m * g.tiles_n * g.splits;
     int64_t slots = (int64_t)(g.num_cus > 8 ? g.num_cus & ~7 : 8);
     const dim3 grid((unsigned)(units < slots ? units : slots)), block(C::NT);
-    if (avec) hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, true, RNE>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, false, RNE>), grid, block, 0, stream, g);
+    if (avec) hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, true, RNE, KTAIL>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, false, RNE, KTAIL>), grid, block, 0, stream, g);
     if (g.splits > 1) {
         int64_t blocks = (g.M * g.N + 255) / 256;
         if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
@@ -1166,20 +1189,21 @@ static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
     }
 }
 
-template <class C, bool RNE>
+template <class C, bool RNE, bool KTAIL>
 static hipError_t launch_dma(const GemmArgs &args, int nbands, hipStream_t stream)
 {
     GemmArgs g = args;
     g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
     g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
     g.group_m = group_rows(g.tiles_n, g.num_cus);
-    const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0);
+    // no 128-bit A load may straddle the end of A's rows (see launch_with)
+    const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0) && (g.ka % 4 == 0);
     switch (nbands) {
-    case 1: launch_dma_nb<C, 1, RNE>(g, avec, stream); break;
-    case 2: launch_dma_nb<C, 2, RNE>(g, avec, stream); break;
-    case 3: launch_dma_nb<C, 3, RNE>(g, avec, stream); break;
-    case 4: launch_dma_nb<C, 4, RNE>(g, avec, stream); break;
-    default: launch_dma_nb<C, 5, RNE>(g, avec, stream); break;
+    case 1: launch_dma_nb<C, 1, RNE, KTAIL>(g, avec, stream); break;
+    case 2: launch_dma_nb<C, 2, RNE, KTAIL>(g, avec, stream); break;
+    case 3: launch_dma_nb<C, 3, RNE, KTAIL>(g, avec, stream); break;
+    case 4: launch_dma_nb<C, 4, RNE, KTAIL>(g, avec, stream); break;
+    default: launch_dma_nb<C, 5, RNE, KTAIL>(g, avec, stream); break;
     }
     return hipGetLastError();
 }
@@ -1224,8 +1248,15 @@ bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
 {
     if (bsrc == B_PLANES_KN) return launch_with<Cfg8>(args, nbands, bsrc, stream, rne);
-    if (bsrc == B_PLANES_NK && gemm_uses_dma(args.K, args.ldb, args.B0, args.B1, args.B2))
-        return rne ? launch_dma<Cfg8S, true>(args, nbands, stream) : launch_dma<Cfg8S, false>(args, nbands, stream);
+    if (bsrc == B_PLANES_NK && gemm_uses_dma(args.K, args.ldb, args.B0, args.B1, args.B2)) {
+        // A K tail (only with B planes zero-padded to the kernel's K) masks A past its K
+        if (args.ka != args.K) {
+            if (rne) return hipErrorInvalidValue;
+            return launch_dma<Cfg8S, false, true>(args, nbands, stream);
+        }
+        return rne ? launch_dma<Cfg8S, true, false>(args, nbands, stream)
+                   : launch_dma<Cfg8S, false, false>(args, nbands, stream);
+    }
     return launch_with<Cfg8S>(args, nbands, bsrc, stream, rne);
 }
 

@@ -17,6 +17,7 @@ enum BSource {
 
 struct GemmArgs {
     int64_t M, N, K;
+    int64_t ka;              // K of A (== K, or less when the B planes are zero-padded to K)
     const float *A;
     int64_t lda;
     const float *B;          // B_FP32
@@ -41,9 +42,11 @@ hipError_t launch_split(int64_t rows, int64_t cols, const float *X, int64_t ldx,
                         uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream,
                         bool rne = false);
 
+// rows_out >= rows (0: rows): output columns rows .. rows_out-1 of the planes
+// are written as zeros (a K extent padded for the plane kernel).
 hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
                                   uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream,
-                                  bool rne = false);
+                                  bool rne = false, int64_t rows_out = 0);
 
 // rne: the in-kernel split of A (and of FP32 B) rounds to nearest even; only
 // B_FP32 and B_PLANES_NK (DMA kernel) support it.

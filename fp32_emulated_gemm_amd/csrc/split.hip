@@ -73,8 +73,9 @@ constexpr int kTT = 64;
 template <bool RNE>
 __global__ __launch_bounds__(256) void split_transpose_kernel(
     const float *__restrict__ X, int64_t ldx, uint16_t *__restrict__ X0, uint16_t *__restrict__ X1,
-    uint16_t *__restrict__ X2, int64_t ldo, int64_t rows, int64_t cols, int64_t tiles_c)
+    uint16_t *__restrict__ X2, int64_t ldo, int64_t rows_in, int64_t rows, int64_t cols, int64_t tiles_c)
 {
+    // rows_in <= rows: X rows past rows_in read as zero (a zero-padded K extent)
     __shared__ float tile[kTT][kTT + 1];
     const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTT;
     const int64_t c0 = (int64_t)(blockIdx.x % tiles_c) * kTT;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void split_transpose_kernel(
     for (int i = 0; i < kTT / 4; ++i) {
         const int r = (tid >> 6) + 4 * i;
         float v = 0.0f;
-        if (col_in && r0 + r < rows) v = X[(r0 + r) * ldx + c0 + c];
+        if (col_in && r0 + r < rows_in) v = X[(r0 + r) * ldx + c0 + c];
         tile[r][c] = v;
     }
     __syncthreads();
@@ -108,10 +109,14 @@ __global__ __launch_bounds__(256) void split_transpose_kernel(
 
 template <bool RNE>
 static hipError_t split_transpose_with(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
-                                       uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream)
+                                       uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream,
+                                       int64_t rows_out)
 {
+    const int64_t rows_in = rows;
+    if (rows_out > rows) rows = rows_out;
     if (rows == 0 || cols == 0) return hipSuccess;
     if (rows % 8 != 0 || ldo % 8 != 0 || !aligned(X0, 16) || !aligned(X1, 16) || !aligned(X2, 16)) {
+        if (rows != rows_in) return hipErrorInvalidValue;   // zero padding needs the tiled kernel
         const int threads = 256;
         int64_t blocks = (rows * cols + threads - 1) / threads;
         if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
@@ -122,15 +127,16 @@ static hipError_t split_transpose_with(int64_t rows, int64_t cols, const float *
     const int64_t tiles_c = (cols + kTT - 1) / kTT, tiles_r = (rows + kTT - 1) / kTT;
     if (tiles_r > (int64_t)0x7FFFFFFF / tiles_c) return hipErrorInvalidValue;
     hipLaunchKernelGGL(split_transpose_kernel<RNE>, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, stream, X,
-                       ldx, X0, X1, X2, ldo, rows, cols, tiles_c);
+                       ldx, X0, X1, X2, ldo, rows_in, rows, cols, tiles_c);
     return hipGetLastError();
 }
 
 hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
-                                  uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream, bool rne)
+                                  uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream, bool rne,
+                                  int64_t rows_out)
 {
-    return rne ? split_transpose_with<true>(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, stream)
-               : split_transpose_with<false>(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, stream);
+    return rne ? split_transpose_with<true>(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, stream, rows_out)
+               : split_transpose_with<false>(rows, cols, X, ldx, X0, X1, X2, ldo, num_cus, stream, rows_out);
 }
 
 template <bool RNE>

@@ -38,9 +38,9 @@
  *   synchronisation, as in BLAS libraries.
  *   Arguments are validated before any HIP call; on an error status nothing
  *   has been enqueued.
- *   Device memory: sgemm_bf16x9 and sgemm_emu with M >= 1024, K % 64 == 0 and
- *   K * N <= 2^28 split B once into a temporary N x K set of BF16 planes
- *   (6 K N bytes) taken stream-ordered (hipMallocFromPoolAsync, hipFreeAsync on
+ *   Device memory: sgemm_bf16x9 and sgemm_emu with M >= 1024 and K' * N <= 2^28
+ *   (K' = K rounded up to a multiple of 64) split B once into a temporary
+ *   N x K' set of BF16 planes, zero past K (6 K' N bytes), taken stream-ordered (hipMallocFromPoolAsync, hipFreeAsync on
  *   `stream`) from a memory pool the library creates per device and keeps
  *   until the process ends, with freed blocks held for reuse.  If that
  *   allocation fails they split B inside the GEMM kernel instead; the result
@@ -230,9 +230,9 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
 /*
  * sgemm_emu_split_k -- the number of K slices (split-K) the GEMM uses for an
  * M x N x K product on the current device when it runs the N x K plane kernel
- * (sgemm_emu_presplit_b with SGEMM_EMU_B_NK, sgemm_emu_linear, and
- * sgemm_bf16x9 / sgemm_emu when they pre-split B; all need K % 64 == 0 and
- * 16-byte aligned planes with ldb % 8 == 0).  1 means one pass over K per
+ * (sgemm_emu_presplit_b with SGEMM_EMU_B_NK and sgemm_emu_linear, which need
+ * K % 64 == 0 and 16-byte aligned planes with ldb % 8 == 0; sgemm_bf16x9 /
+ * sgemm_emu when they pre-split B, with K rounded up to a multiple of 64).  1 means one pass over K per
  * output tile.  With S > 1 slices (grids that would leave a quarter of the
  * CUs idle), each (tile, slice) runs the method on its K range (five band
  * sums, recombined smallest band first) and writes its FP32 result to a

@@ -128,22 +128,26 @@ def _fused_in_row_blocks(fe, A, B, nbands, rows=1000):
     return np.concatenate([run(fe, A[i:i + rows], B, nbands, "fused") for i in range(0, A.shape[0], rows)])
 
 
-WS_SHAPES = [(1024, 130, 64), (1100, 257, 128), (1500, 1000, 512), (2048, 64, 192)]
+WS_SHAPES = [(1024, 130, 64), (1100, 257, 128), (1500, 1000, 512), (2048, 64, 192),
+             (1100, 257, 100), (1024, 130, 33), (1030, 300, 90), (2048, 200, 1000)]   # ragged K: padded planes
 
 
 @pytest.mark.parametrize("shape", WS_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_fp32_b_workspace_path(fe, shape):
-    """FP32 B with at least 1024 rows of A and K % 64 == 0: B is split once into N x K
-    planes in a workspace.  Same result, bit for bit, as the in-kernel split and as
-    the caller-split N x K planes."""
+    """FP32 B with at least 1024 rows of A: B is split once into N x K planes in a
+    workspace (zero-padded to a multiple of 64 in K; the kernel masks A past K).
+    Same result, bit for bit, as the in-kernel split and as the caller-split
+    N x K planes (without split-K)."""
     M, N, K = shape
     g = _rng(M + 3 * N + 11 * K)
     A = g.standard_normal((M, K)).astype(np.float32)
     B = g.standard_normal((K, N)).astype(np.float32)
     C = run(fe, A, B, entry="fused")
     check_against_fp64(C, A, B, label=f"workspace {shape}")
-    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
-    if fe.sgemm_emu_split_k(M, N, K) == 1:
+    kpad = (K + 63) // 64 * 64
+    if K == kpad or fe.sgemm_emu_split_k(M, N, kpad) == 1:
+        assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
+    if fe.sgemm_emu_split_k(M, N, kpad) == 1:
         assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, 5).view(np.uint32))
 
 
@@ -155,6 +159,24 @@ def test_fp32_b_workspace_path_bands(fe, nbands):
     B = g.standard_normal((K, N)).astype(np.float32)
     C = run(fe, A, B, nbands, "fused")
     assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, nbands).view(np.uint32))
+
+
+def test_fp32_b_workspace_ragged_k_masks_a_tail(fe):
+    """Ragged K through the padded planes: A's values past K (the next row's
+    first elements, here Inf and NaN) must not reach the products."""
+    M, N, K = 1024, 96, 100
+    g = _rng(515)
+    buf = g.standard_normal(M * K + 64).astype(np.float32)
+    A = buf[: M * K].reshape(M, K).copy()
+    A[1:, :28] = np.where(g.random((M - 1, 28)) < 0.5, np.inf, np.nan)   # row i+1's head follows row i's tail
+    A[0, :] = 1.0
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="fused")
+    R = _fused_in_row_blocks(fe, A, B, 5)
+    assert np.array_equal(np.isnan(C), np.isnan(R)) and np.array_equal(np.isinf(C), np.isinf(R))
+    assert np.all(np.isfinite(C[0]))
+    fin = np.isfinite(R)
+    assert np.array_equal(C[fin].view(np.uint32), R[fin].view(np.uint32))
 
 
 def test_fp32_b_workspace_path_special_values(fe):
