@@ -8,27 +8,40 @@
 // p + q share one of five band accumulators; the bands are recombined with
 // weights 2^-8s, smallest band first.
 //
-// Kernel structure (one workgroup per BM x BN tile of C):
-//   * The waves form a WAVES_M x WAVES_N grid; each wave owns a WTM x WTN
-//     sub-tile made of 32 x 32 MFMA blocks, each with NB band accumulators of
-//     16 FP32 registers per lane (v_mfma_f32_32x32x16_bf16).
-//   * K advances in steps of BK = 32.  Threads load their share of the next
-//     step's A and B into registers one step ahead, split FP32 values in
-//     registers, and write the three BF16 component tiles into LDS,
-//     k-contiguous for both operands (B is transposed on the way in).  LDS is
-//     double-buffered, so one barrier per step separates producers from
-//     consumers.
-//   * B sources: FP32 K x N (split in the kernel), BF16 planes K x N (pairs of
-//     columns transposed with byte permutes), or BF16 planes N x K (already
-//     k-contiguous: copied to LDS as is).
-//   * LDS rows are 32 BF16 plus 8 BF16 of padding (80 bytes): the 128-bit
-//     fragment reads of 16 consecutive rows then touch 64 distinct banks.
-//   * Tile order: workgroups are dealt round-robin to the 8 XCDs, so the
-//     block index is remapped to give each XCD a contiguous run of tiles, and
-//     tiles run in groups of 8 tile-rows so concurrent tiles share A and B
-//     panels in the XCD's L2.
-//   * Epilogue: per output, acc = 2^-32 S4; acc = fma(S3, 2^-24, acc);
-//     acc = fma(S2, 2^-16, acc); acc = fma(S1, 2^-8, acc); C = acc + S0.
+// Two kernels share the tile, band and epilogue code:
+//
+// gemm_bf16x9_dma_kernel -- the main kernel, for B given as BF16 planes N x K
+// (a linear layer's [out][in] weight, or FP32 B split once into a workspace)
+// with K a multiple of 2 BK:
+//   * persistent: one workgroup of 8 waves per CU walks 128 x 128 output
+//     tiles (or, for small grids, (tile, K slice) units: split-K);
+//   * each wave owns 64 x 32 of the tile: two 32 x 32 MFMA blocks, each with
+//     NB band accumulators of 16 FP32 registers per lane
+//     (v_mfma_f32_32x32x16_bf16);
+//   * K advances in steps of BK = 32; the B planes of a step are copied
+//     global -> LDS by buffer loads with LDS destination, two steps ahead,
+//     into a ring of three buffers; A is loaded into registers two steps
+//     ahead and split one step ahead, interleaved with the MFMAs;
+//   * one LDS-only barrier per step; the next step's first fragments are read
+//     right after it while the step's last MFMAs run;
+//   * a tile's last two steps already load the next tile's first two.
+//
+// gemm_bf16x9_kernel -- the general kernel (FP32 B split in the kernel, K x N
+// planes, N x K planes with any K or layout): one workgroup per tile, A and B
+// staged through registers and split there, double-buffered LDS with one
+// barrier per step, the K tail masked.
+//
+// Common to both:
+//   * LDS A rows are 32 BF16 plus 8 BF16 of padding (80 bytes): the 128-bit
+//     fragment reads of 16 consecutive rows then touch 64 distinct banks
+//     (the DMA kernel's B rows are unpadded and XOR-swizzled instead);
+//   * tile order: workgroups are dealt round-robin to the 8 XCDs, so the
+//     tile index is remapped to give each XCD a contiguous run of tiles, in
+//     groups of tile-rows so that concurrent tiles share A and B panels in the
+//     XCD's L2;
+//   * epilogue: per output, acc = 2^-32 S4; acc = fma(S3, 2^-24, acc);
+//     acc = fma(S2, 2^-16, acc); acc = fma(S1, 2^-8, acc); C = acc + S0
+//     (then the bias and the activation of the linear entry point).
 // Edges: rows of A beyond M and columns of B beyond N are clamped to valid
 // memory (their results are never stored); k beyond K is zero-filled.
 #include "split_device.hpp"
@@ -69,7 +82,6 @@ struct Cfg {
 
 using Cfg8 = Cfg<2, 4, 64, 32>;              // 8 waves, 2 per SIMD, 128 x 128 tile
 using Cfg8S = Cfg<2, 4, 64, 32, true, 4, 4>; // same, staging interleaved with the MFMAs
-using Cfg4D = Cfg<2, 2, 64, 64, true, 2, 12>; // 4 waves, 1 per SIMD, 128 x 128 tile (DMA kernel)
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -1237,14 +1249,14 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
     return hipGetLastError();
 }
 
-// Configuration per B source, chosen by measurement on MI355X: the explicit
-// MFMA / split interleaving pays off where the kernel splits FP32 B or copies
-// N x K planes; with K x N planes the compiler's own schedule is faster.
 bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const void *B2)
 {
     return K % (2 * BK) == 0 && ldb % 8 == 0 && aligned(B0, 16) && aligned(B1, 16) && aligned(B2, 16);
 }
 
+// Configuration per B source, chosen by measurement on MI355X: the explicit
+// MFMA / split interleaving pays off where the kernel splits FP32 B or copies
+// N x K planes; with K x N planes the compiler's own schedule is faster.
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
 {
     if (bsrc == B_PLANES_KN) return launch_with<Cfg8>(args, nbands, bsrc, stream, rne);
