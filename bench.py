@@ -40,8 +40,19 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "e1f341d1eebdbab615e360f537bb9ff095c08be170f5c2625c4c492dfc13ed03",
-                "bytes_per_launch": [2844960426, 3281705059]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "4660bddbf60e1203ce6da771e0f385694664370e3ce89bcef7af4e3b49cea320",
+                "bytes_per_launch": [2843993344, 3264154752]}
+
+# MFMA activity of the same launches, from one rocprofv3 --pmc run of the same
+# probe (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE).
+# busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs): the
+# share of the kernel's active cycles in which a SIMD's matrix pipe was busy
+# (one 32x32x16 BF16 MFMA keeps it busy 32 cycles).  GRBM_GUI_ACTIVE per XCD
+# divided by the kernel's own time in this run gives the shader clock the chip
+# held under the load; roofline.frac = busy x clock / 2.4 GHz.
+GEMM_MFMA_PMC = {"gemm_hip_sha256": GEMM_TRAFFIC["gemm_hip_sha256"],
+                 "mfma_busy": [0.6396, 0.7160],
+                 "active_cycles_per_xcd": [3903776, 3478247]}
 
 
 def log(msg):
@@ -57,8 +68,8 @@ def parse():
     p.add_argument("--no-context", action="store_true", help="skip torch.matmul / fused-B context timings")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--traffic-probe", action="store_true",
-                   help="for HBM counter runs: two steps, then one plain 512 MiB device copy whose "
-                        "FETCH/WRITE counts calibrate the counters; prints no JSON line")
+                   help="for HBM counter runs: two steps, one split of X, then one plain 2 GiB device copy "
+                        "whose FETCH/WRITE counts calibrate the counters; prints no JSON line")
     return p.parse_args()
 
 
@@ -119,6 +130,11 @@ def main():
     if args.traffic_probe:
         for _ in range(2):
             step(False)
+        # the standalone split kernel on X (552960 x 256): 4 + 6 bytes per element
+        Xp = [torch.empty((M, D), dtype=torch.int16, device=dev) for _ in range(3)]
+        fe.split_f32_bf16x3(M, D, Xd, D, *Xp, D, sp)
+        torch.cuda.synchronize()
+        del Xp
         # Calibration: a plain device copy of known size whose source is cold.
         # The source is written first, then a 1 GiB fill evicts it from the
         # 256 MB last-level cache, then the copy reads and writes 2 GiB.
@@ -161,6 +177,10 @@ def main():
     if GEMM_TRAFFIC["gemm_hip_sha256"] == source_sha256(GEMM_SOURCE):
         traffic_per_launch = GEMM_TRAFFIC["bytes_per_launch"]
     traffic = None if traffic_per_launch is None else sum(traffic_per_launch) / len(traffic_per_launch)
+    mfma_busy = sclk = None
+    if GEMM_MFMA_PMC["gemm_hip_sha256"] == source_sha256(GEMM_SOURCE):
+        mfma_busy = GEMM_MFMA_PMC["mfma_busy"]
+        sclk = [round(c / (t * 1e-3) / 1e9, 3) for c, t in zip(GEMM_MFMA_PMC["active_cycles_per_xcd"], (g1_ms, g2_ms))]
 
     # correctness spot check of the timed outputs against torch FP32 (sanity, not parity)
     ref1 = torch.matmul(Xd[:256], W1d)
@@ -210,6 +230,8 @@ def main():
             "algorithmic_bytes_per_launch": algo_bytes,
             "kernel": "gemm_bf16x9_dma_kernel<Cfg<2,4,64,32,sched>, 5 bands>: N x K planes copied to LDS by DMA, A split in-kernel",
             "flops_per_launch": bf16_flops_per_launch,
+            "mfma_busy_per_launch_pmc": mfma_busy,
+            "sclk_ghz_under_load": sclk,
         },
         "cpu_baseline": cpu,
         "context": context,
@@ -267,6 +289,18 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     t = timed(lambda: fe.sgemm_emu_presplit_b(M, D, F, C1, F, *W1_planes, F, fe.SGEMM_EMU_B_NK, C2, D, 5, sp),
               stream, 5)
     res["linear_dX=dY@W1_tflops"] = round(fl / t / 1e9, 2)
+    # band-drop / product-count ablations on X @ W1 (bf16 work scales with the product count)
+    for nb in (4, 3, 2, 1):
+        t = timed(lambda: fe.sgemm_emu_presplit_b(M, F, D, Xd, D, *W1t_planes, D, fe.SGEMM_EMU_B_NK, C1, F, nb,
+                                                  sp), stream, 5)
+        res[f"ablation_X@W1_nbands{nb}_{fe.sgemm_emu_products(nb)}products_tflops"] = round(fl / t / 1e9, 2)
+    # the standalone split kernel on X (552960 x 256): 4 bytes read + 6 written per element
+    Xp = [torch.empty((M, D), dtype=torch.int16, device=Xd.device) for _ in range(3)]
+    t = timed(lambda: fe.split_f32_bf16x3(M, D, Xd, D, *Xp, D, sp), stream, 10)
+    res["split_X_ms"] = round(t, 4)
+    res["split_X_GBps"] = round(10.0 * M * D / t / 1e6, 1)
+    res["split_X_frac_of_8TBps"] = round(10.0 * M * D / t / 1e6 / MI355X_HBM_GBS, 3)
+    del Xp
     n = 4096
     g = torch.Generator(device="cuda").manual_seed(1)
     A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
@@ -276,6 +310,16 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     res["sgemm_bf16x9_4096^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
     t = timed(lambda: torch.matmul(A, B, out=C), stream, 10)
     res["torch_fp32_4096^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
+    # speed-up over the platform's own FP32 GEMM on the same shapes, next to the
+    # ratios the pages quote for other hardware (context only)
+    res["speedup_vs_torch_fp32"] = {
+        "X@W1": round(res["sgemm_bf16x9_X@W1_tflops"] / res["torch_fp32_X@W1_tflops"], 3),
+        "H@W2": round(res["sgemm_bf16x9_H@W2_tflops"] / res["torch_fp32_H@W2_tflops"], 3),
+        "4096^3": round(res["sgemm_bf16x9_4096^3_tflops"] / res["torch_fp32_4096^3_tflops"], 3),
+    }
+    res["pages_quoted_speedups_other_hardware"] = {
+        "BF16x9_vs_FP32_B300_large_PET_GEMMs": "2.2-2.5x", "BF16x9_vs_FP32_B300_4096^3": "2.41x",
+        "TF32x3_vs_FP32_A100_PET_GEMMs": "1.7-1.9x"}
     log(f"context: {res}")
     return res
 
