@@ -300,7 +300,35 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     res["split_X_ms"] = round(t, 4)
     res["split_X_GBps"] = round(10.0 * M * D / t / 1e6, 1)
     res["split_X_frac_of_8TBps"] = round(10.0 * M * D / t / 1e6 / MI355X_HBM_GBS, 3)
-    del Xp
+    # what a plain device copy of the same bytes reaches on this GPU (8 B per element
+    # of X moved), the practical ceiling for an HBM-bound stream
+    Xc = torch.empty_like(Xd)
+    t = timed(lambda: Xc.copy_(Xd), stream, 10)
+    res["copy_X_GBps"] = round(8.0 * M * D / t / 1e6, 1)
+    res["split_X_vs_copy"] = round(res["split_X_GBps"] / res["copy_X_GBps"], 3)
+    del Xp, Xc
+    q = 4096
+    Q = torch.rand((q, q), device="cuda") * 2 - 1
+    Qp = [torch.empty((q, q), dtype=torch.int16, device="cuda") for _ in range(3)]
+    t = timed(lambda: fe.split_f32_bf16x3(q, q, Q, q, *Qp, q, sp), stream, 20)
+    res["split_4096^2_GBps"] = round(10.0 * q * q / t / 1e6, 1)
+    del Q, Qp
+    # the small shapes: 256^3 and the PET GEMMs of a 192-atom system (6144 rows)
+    for name, (m, nn, k) in (("256^3", (256, 256, 256)), ("6144x1024x256", (6144, 1024, 256)),
+                             ("6144x256x1024", (6144, 256, 1024))):
+        A = torch.randn((m, k), device="cuda")
+        B = torch.randn((k, nn), device="cuda") / k ** 0.5
+        C = torch.empty((m, nn), device="cuda")
+        Bt_planes = fe.split(B.t().contiguous())
+        fs = 2.0 * m * nn * k
+        t = timed(lambda: fe.sgemm_bf16x9(m, nn, k, A, k, B, nn, C, nn, sp), stream, 20)
+        res[f"sgemm_bf16x9_{name}_tflops"] = round(fs / t / 1e9, 2)
+        t = timed(lambda: fe.sgemm_emu_presplit_b(m, nn, k, A, k, *Bt_planes, k, fe.SGEMM_EMU_B_NK, C, nn, 5, sp),
+                  stream, 20)
+        res[f"presplit_nk_{name}_tflops"] = round(fs / t / 1e9, 2)
+        t = timed(lambda: torch.matmul(A, B, out=C), stream, 20)
+        res[f"torch_fp32_{name}_tflops"] = round(fs / t / 1e9, 2)
+        del A, B, C, Bt_planes
     n = 4096
     g = torch.Generator(device="cuda").manual_seed(1)
     A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
@@ -310,12 +338,25 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     res["sgemm_bf16x9_4096^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
     t = timed(lambda: torch.matmul(A, B, out=C), stream, 10)
     res["torch_fp32_4096^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
+    del A, B, C
+    n = 8192
+    A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+    B = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+    C = torch.empty((n, n), device="cuda")
+    t = timed(lambda: fe.sgemm_bf16x9(n, n, n, A, n, B, n, C, n, sp), stream, 5)
+    res["sgemm_bf16x9_8192^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
+    t = timed(lambda: torch.matmul(A, B, out=C), stream, 5)
+    res["torch_fp32_8192^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
+    del A, B, C
     # speed-up over the platform's own FP32 GEMM on the same shapes, next to the
     # ratios the pages quote for other hardware (context only)
     res["speedup_vs_torch_fp32"] = {
         "X@W1": round(res["sgemm_bf16x9_X@W1_tflops"] / res["torch_fp32_X@W1_tflops"], 3),
         "H@W2": round(res["sgemm_bf16x9_H@W2_tflops"] / res["torch_fp32_H@W2_tflops"], 3),
         "4096^3": round(res["sgemm_bf16x9_4096^3_tflops"] / res["torch_fp32_4096^3_tflops"], 3),
+        "8192^3": round(res["sgemm_bf16x9_8192^3_tflops"] / res["torch_fp32_8192^3_tflops"], 3),
+        "6144x1024x256": round(res["sgemm_bf16x9_6144x1024x256_tflops"] / res["torch_fp32_6144x1024x256_tflops"], 3),
+        "6144x256x1024": round(res["sgemm_bf16x9_6144x256x1024_tflops"] / res["torch_fp32_6144x256x1024_tflops"], 3),
     }
     res["pages_quoted_speedups_other_hardware"] = {
         "BF16x9_vs_FP32_B300_large_PET_GEMMs": "2.2-2.5x", "BF16x9_vs_FP32_B300_4096^3": "2.41x",

@@ -4,10 +4,12 @@
 // Every argument is checked before the first HIP call, so an invalid call
 // returns an error status without touching the GPU (and works on machines
 // without one).  The library keeps no state besides a per-device cache of
-// "is this a gfx950", its CU count and a memory pool.  The only device memory it
-// allocates is the stream-ordered workspace for pre-splitting FP32 B
-// (hipMallocFromPoolAsync / hipFreeAsync on the caller's stream, from the
-// library's own pool, which keeps freed blocks for reuse).
+// "is this a gfx950", its CU count, a memory pool and a per-stream workspace
+// table.  The only device memory it allocates is stream-ordered workspace: the
+// planes of a pre-split FP32 B and the partial sums of a K-split GEMM (one
+// grow-only block per stream, kept for the stream's later calls), and the
+// flags of the IEEE fix-up (hipMallocFromPoolAsync / hipFreeAsync on the
+// caller's stream, from the library's own pool).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -126,6 +128,123 @@ hipMemPool_t workspace_pool(int dev)
 
 int launched(hipError_t e) { return e == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_ELAUNCH; }
 
+// ---------------------------------------------------------------- per-stream workspace
+// A pooled allocate / free pair costs the host about as much as a small GEMM
+// takes on the GPU.  So each stream keeps one grow-only workspace block that
+// every later call on that stream reuses; stream order keeps the uses apart.
+// A block is tagged with its stream's handle and with an event recorded after
+// its last use.  A call first makes its stream wait for that event: this
+// covers a stream destroyed with work pending whose handle comes back, and
+// lets a full table hand a slot to a new stream (freeing or reusing the old
+// block in stream order).
+// The device's table lock is held from the lookup until the call's last
+// launch, so calls from several host threads on one stream cannot interleave
+// their kernels.  A stream being captured into a graph takes a per-call block
+// from the pool instead, so the graph owns its memory.
+struct StreamWs {
+    bool used = false;
+    uintptr_t key = 0;           // the stream handle
+    void *ptr = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;   // recorded on the stream after the last call that used ptr
+    bool recorded = false;
+    uint64_t tick = 0;           // last use, for eviction
+};
+
+constexpr int kStreamSlots = 8;
+
+struct DeviceWs {
+    std::mutex mutex;
+    StreamWs slot[kStreamSlots];
+    uint64_t clock = 0;
+};
+
+DeviceWs g_ws[kMaxDevices];
+
+// Lease on a workspace for one call; release() after the call's last launch.
+struct WsLease {
+    std::unique_lock<std::mutex> lock;
+    StreamWs *entry = nullptr;
+    void *pooled = nullptr;      // per-call block (graph capture), freed at release
+    hipStream_t stream = nullptr;
+
+    void release()
+    {
+        if (entry != nullptr) entry->recorded = hipEventRecord(entry->done, stream) == hipSuccess;
+        if (pooled != nullptr) (void)hipFreeAsync(pooled, stream);
+        entry = nullptr;
+        pooled = nullptr;
+        if (lock.owns_lock()) lock.unlock();
+    }
+    ~WsLease() { release(); }
+};
+
+// A workspace of at least `bytes` for `stream`, or nullptr if none can be had
+// (the caller then runs without one).
+void *acquire_workspace(int dev, hipStream_t stream, size_t bytes, WsLease &L)
+{
+    L.stream = stream;
+    hipMemPool_t pool = workspace_pool(dev);
+    if (pool == nullptr) return nullptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        void *p = nullptr;
+        if (hipMallocFromPoolAsync(&p, bytes, pool, stream) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        L.pooled = p;
+        return p;
+    }
+    DeviceWs &D = g_ws[dev];
+    L.lock = std::unique_lock<std::mutex>(D.mutex);
+    StreamWs *e = nullptr;
+    for (StreamWs &x : D.slot)
+        if (x.used && x.key == (uintptr_t)stream) { e = &x; break; }
+    if (e == nullptr) {
+        for (StreamWs &x : D.slot)
+            if (!x.used) { e = &x; break; }
+        if (e == nullptr) {                       // table full: take the least recently used slot
+            e = &D.slot[0];
+            for (StreamWs &x : D.slot)
+                if (x.tick < e->tick) e = &x;
+        }
+        if (e->done == nullptr && hipEventCreateWithFlags(&e->done, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            e->done = nullptr;
+            L.lock.unlock();
+            return nullptr;
+        }
+        e->used = true;
+        e->key = (uintptr_t)stream;
+    }
+    // after the last use of this block, whichever stream made it
+    if (e->recorded && hipStreamWaitEvent(stream, e->done, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        L.lock.unlock();
+        return nullptr;
+    }
+    if (e->bytes < bytes) {
+        if (e->ptr != nullptr) (void)hipFreeAsync(e->ptr, stream);
+        e->ptr = nullptr;
+        e->bytes = 0;
+        const size_t grain = (size_t)2 << 20;
+        const size_t want = (bytes + grain - 1) / grain * grain;
+        void *p = nullptr;
+        if (hipMallocFromPoolAsync(&p, want, pool, stream) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            L.lock.unlock();
+            return nullptr;
+        }
+        e->ptr = p;
+        e->bytes = want;
+    }
+    e->tick = ++D.clock;
+    L.entry = e;
+    return e->ptr;
+}
+
 
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
@@ -174,62 +293,43 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // stream-ordered workspace and run the LDS-DMA kernel, instead of splitting
     // B again in every tile row.  Same split, same products, same order of
     // MFMA accumulation, so the result is bitwise identical (zero-padded K
-    // steps add zero products).
-    hipMemPool_t pool = nullptr;
-    void *bws = nullptr;
-    // A K that is not a multiple of 64 is padded in the planes (zeros) and
-    // the kernel masks A past its K.
+    // steps add zero products).  A K that is not a multiple of 64 is padded in
+    // the planes (zeros) and the kernel masks A past its K.
     const int64_t kpad = (K + 63) / 64 * 64;
-    if (bsrc == B_FP32 && M >= kPresplitMinRows && (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems &&
-        !(rne && kpad != K) && (pool = workspace_pool(dev)) != nullptr) {
-        const int64_t ldo = kpad;
-        const size_t plane = (size_t)N * (size_t)ldo * sizeof(uint16_t);
-        const size_t plane_pad = (plane + 255) & ~(size_t)255;
-        if (hipMallocFromPoolAsync(&bws, 3 * plane_pad, pool, stream) == hipSuccess && bws != nullptr) {
-            uint16_t *P0 = (uint16_t *)bws, *P1 = (uint16_t *)((char *)bws + plane_pad),
-                     *P2 = (uint16_t *)((char *)bws + 2 * plane_pad);
-            const hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, ldo, num_cus, stream, rne, kpad);
-            if (e != hipSuccess) {
-                (void)hipFreeAsync(bws, stream);
-                return launched(e);
-            }
-            g.B0 = P0; g.B1 = P1; g.B2 = P2; g.ldb = ldo;
-            g.K = kpad;
-            bsrc = B_PLANES_NK;
-        } else {
-            bws = nullptr;
-            (void)hipGetLastError();   // no workspace: the GEMM splits B itself
-        }
-    }
+    const bool presplit = bsrc == B_FP32 && M >= kPresplitMinRows &&
+                          (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !(rne && kpad != K);
+    const size_t plane = presplit ? (size_t)N * (size_t)kpad * sizeof(uint16_t) : 0;
+    const size_t plane_pad = (plane + 255) & ~(size_t)255;
 
     // Grids that would leave CUs idle on the N x K DMA kernel are split along
     // K: each (tile, K slice) recombines its own bands and writes the result to
-    // a pooled partial buffer; a reduction kernel adds the slices in order.
-    void *pws = nullptr;
-    if (bsrc == B_PLANES_NK && gemm_uses_dma(g.K, g.ldb, g.B0, g.B1, g.B2)) {
-        const int sl = gemm_split_count(M, N, g.K, nbands, num_cus);
-        if (sl > 1 && (pool != nullptr || (pool = workspace_pool(dev)) != nullptr)) {
-            const size_t bytes = (size_t)sl * (size_t)M * (size_t)N * sizeof(float);
-            if (hipMallocFromPoolAsync(&pws, bytes, pool, stream) == hipSuccess && pws != nullptr) {
-                g.splits = sl;
-                g.partials = (float *)pws;
-                g.ldp = N;
-            } else {
-                pws = nullptr;
-                (void)hipGetLastError();   // no buffer: one unit per tile
-            }
-        }
+    // a partial buffer; a reduction kernel adds the slices in order.
+    const bool dma = presplit || (bsrc == B_PLANES_NK && gemm_uses_dma(K, ldb, B0, B1, B2));
+    const int sl = dma ? gemm_split_count(M, N, presplit ? kpad : K, nbands, num_cus) : 1;
+    const size_t part_bytes = sl > 1 ? (size_t)sl * (size_t)M * (size_t)N * sizeof(float) : 0;
+
+    // One workspace per call holds the planes and the partials; without one
+    // the GEMM splits B itself and runs one unit per tile.
+    WsLease lease;
+    void *ws = nullptr;
+    if (plane_pad + part_bytes > 0) ws = acquire_workspace(dev, stream, 3 * plane_pad + part_bytes, lease);
+    if (ws != nullptr && presplit) {
+        uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
+                 *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
+        const hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, kpad, num_cus, stream, rne, kpad);
+        if (e != hipSuccess) return launched(e);
+        g.B0 = P0; g.B1 = P1; g.B2 = P2; g.ldb = kpad;
+        g.K = kpad;
+        bsrc = B_PLANES_NK;
+    }
+    if (ws != nullptr && sl > 1) {
+        g.splits = sl;
+        g.partials = (float *)((char *)ws + 3 * plane_pad);
+        g.ldp = N;
     }
 
-    hipError_t e = launch_gemm(g, nbands, bsrc, stream, rne);
-    if (pws != nullptr) {
-        const hipError_t f = hipFreeAsync(pws, stream);
-        if (e == hipSuccess) e = f;
-    }
-    if (bws != nullptr) {
-        const hipError_t f = hipFreeAsync(bws, stream);
-        if (e == hipSuccess) e = f;
-    }
+    const hipError_t e = launch_gemm(g, nbands, bsrc, stream, rne);
+    lease.release();
     return launched(e);
 }
 

@@ -40,13 +40,15 @@
  *   has been enqueued.
  *   Device memory: sgemm_bf16x9 and sgemm_emu with M >= 1024 and K' * N <= 2^28
  *   (K' = K rounded up to a multiple of 64) split B once into a temporary
- *   N x K' set of BF16 planes, zero past K (6 K' N bytes), taken stream-ordered (hipMallocFromPoolAsync, hipFreeAsync on
- *   `stream`) from a memory pool the library creates per device and keeps
- *   until the process ends, with freed blocks held for reuse.  If that
- *   allocation fails they split B inside the GEMM kernel instead; the result
- *   is bitwise the same either way.  GEMMs on small tile grids also take a
- *   pooled split-K buffer (see sgemm_emu_split_k).  No other device memory is
- *   allocated.
+ *   N x K' set of BF16 planes, zero past K (6 K' N bytes).  GEMMs on small
+ *   tile grids also need a split-K buffer (see sgemm_emu_split_k).  Both come
+ *   from one block per call, taken stream-ordered (hipMallocFromPoolAsync,
+ *   hipFreeAsync on `stream`) from a memory pool the library creates per
+ *   device and keeps until the process ends, with freed blocks held for
+ *   reuse.  If that allocation fails the GEMM splits B inside its kernel
+ *   (bitwise the same result) and runs one pass over K per tile (the
+ *   one-pass rounding order of sgemm_emu_split_k's S = 1).  No other device
+ *   memory is allocated (sgemm_emu_ex's IEEE fix-up aside, documented there).
  *   Float pointers must be 4-byte aligned, BF16 plane pointers 2-byte aligned.
  *   16-byte aligned A with lda % 4 == 0 takes the vector-load path; any other
  *   layout takes a scalar-load path with the same arithmetic.
@@ -232,8 +234,8 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
  * M x N x K product on the current device when it runs the N x K plane kernel
  * (sgemm_emu_presplit_b with SGEMM_EMU_B_NK and sgemm_emu_linear, which need
  * K % 64 == 0 and 16-byte aligned planes with ldb % 8 == 0; sgemm_bf16x9 /
- * sgemm_emu when they pre-split B, with K rounded up to a multiple of 64).  1 means one pass over K per
- * output tile.  With S > 1 slices (grids that would leave a quarter of the
+ * sgemm_emu when they pre-split B, with K rounded up to a multiple of 64).
+ * 1 means one pass over K per output tile.  With S > 1 slices (grids that would leave a quarter of the
  * CUs idle), each (tile, slice) runs the method on its K range (five band
  * sums, recombined smallest band first) and writes its FP32 result to a
  * stream-ordered pooled buffer (S * M * N floats); a reduction kernel adds the

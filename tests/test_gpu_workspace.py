@@ -1,0 +1,161 @@
+"""The per-stream workspace of the GEMM entry points.
+
+Calls that need device workspace (FP32 B split once into planes, split-K
+partial sums) reuse one block per stream.  These tests make such calls on
+several streams without host synchronisation in between, on more streams than
+the library's table holds, with growing and shrinking sizes on one stream, and
+from two host threads on one stream.  Every result must equal, bit for bit,
+the same call made alone with the device idle (the kernels are deterministic),
+and the references themselves are checked against the FP64 bound.
+"""
+import sys
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import check_against_fp64, dev, host
+
+pytestmark = pytest.mark.gpu
+
+# (M, N, K, entry): "fused" = sgemm_bf16x9 on FP32 B; "nk" = caller-split N x K planes
+CASES = [
+    (1024, 130, 64, "fused"),      # B planes in the workspace
+    (6144, 256, 1024, "fused"),    # planes and split-K partials in one block
+    (2048, 1000, 512, "fused"),    # a larger plane set
+    (129, 130, 1024, "nk"),        # split-K partials only
+    (1100, 257, 100, "fused"),     # ragged K: zero-padded planes
+]
+
+
+@pytest.fixture(scope="module")
+def fe():
+    import fp32_emulated_gemm_amd as fe
+    return fe
+
+
+class Problem:
+    def __init__(self, fe, case, seed):
+        M, N, K, entry = case
+        self.case = case
+        g = np.random.Generator(np.random.Philox(key=seed))
+        self.A_h = g.standard_normal((M, K)).astype(np.float32)
+        self.B_h = g.standard_normal((K, N)).astype(np.float32)
+        self.A = dev(self.A_h)
+        self.B = dev(self.B_h)
+        self.planes = None
+        if entry == "nk":
+            Bt = dev(np.ascontiguousarray(self.B_h.T))
+            self.planes = [torch.empty(N * K, dtype=torch.int16, device="cuda") for _ in range(3)]
+            fe.split_f32_bf16x3(N, K, Bt, K, *self.planes, K)
+
+    def launch(self, fe, C, stream):
+        M, N, K, entry = self.case
+        if entry == "fused":
+            fe.sgemm_bf16x9(M, N, K, self.A, K, self.B, N, C, N, stream)
+        else:
+            fe.sgemm_emu_presplit_b(M, N, K, self.A, K, *self.planes, K, fe.SGEMM_EMU_B_NK, C, N, 5, stream)
+
+    def out(self):
+        M, N = self.case[0], self.case[1]
+        return torch.full((M * N,), float("nan"), dtype=torch.float32, device="cuda")
+
+    def result(self, C):
+        M, N = self.case[0], self.case[1]
+        return host(C).reshape(M, N)
+
+
+@pytest.fixture(scope="module")
+def problems(fe):
+    probs = [Problem(fe, c, 7000 + i) for i, c in enumerate(CASES)]
+    refs = []
+    for p in probs:
+        print(f"workspace reference {p.case}", flush=True, file=sys.stderr)
+        C = p.out()
+        torch.cuda.synchronize()
+        p.launch(fe, C, None)
+        torch.cuda.synchronize()
+        R = p.result(C)
+        check_against_fp64(R, p.A_h, p.B_h, label=f"workspace reference {p.case}")
+        refs.append(R)
+    return probs, refs
+
+
+def _same(R, C, what):
+    assert np.array_equal(R.view(np.uint32), C.view(np.uint32)), what
+
+
+def _run_schedule(fe, problems, schedule):
+    """schedule: list of (problem index, stream).  Launch all, synchronise once,
+    compare each output with its reference."""
+    probs, refs = problems
+    outs = [probs[i].out() for i, _ in schedule]
+    torch.cuda.synchronize()
+    for (i, s), C in zip(schedule, outs):
+        probs[i].launch(fe, C, s)
+    torch.cuda.synchronize()
+    for n, ((i, s), C) in enumerate(zip(schedule, outs)):
+        _same(refs[i], probs[i].result(C), f"call {n}: case {probs[i].case}")
+
+
+def test_interleaved_streams(fe, problems):
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    n = len(problems[0])
+    schedule = [(i, streams[(i + rep) % 3]) for rep in range(3) for i in range(n)]
+    print("workspace: interleaved on 3 streams", flush=True, file=sys.stderr)
+    _run_schedule(fe, problems, schedule)
+
+
+def test_more_streams_than_slots(fe, problems):
+    """Eleven streams cycle through the table (eight slots): blocks of streams
+    that dropped out are handed over after their last use."""
+    streams = [torch.cuda.Stream() for _ in range(11)]
+    n = len(problems[0])
+    schedule = [(k % n, streams[k % 11]) for k in range(33)]
+    print("workspace: 11 streams", flush=True, file=sys.stderr)
+    _run_schedule(fe, problems, schedule)
+
+
+def test_grow_and_shrink_on_one_stream(fe, problems):
+    s = torch.cuda.Stream()
+    order = [0, 2, 0, 1, 4, 2, 3, 0]   # small, large, small, planes + partials, ragged, large, partials, small
+    print("workspace: one stream, changing sizes", flush=True, file=sys.stderr)
+    _run_schedule(fe, problems, [(i, s) for i in order])
+
+
+def test_default_stream_between_others(fe, problems):
+    s = torch.cuda.Stream()
+    schedule = [(1, None), (1, s), (2, None), (0, s), (1, None)]
+    print("workspace: default stream and one other", flush=True, file=sys.stderr)
+    _run_schedule(fe, problems, schedule)
+
+
+def test_two_host_threads_on_one_stream(fe, problems):
+    """Two threads enqueue on the same stream at once; each call holds the
+    table's lock until its last launch, so their kernels never interleave."""
+    probs, refs = problems
+    s = torch.cuda.Stream()
+    plan = {0: [1, 0, 2, 1, 4, 1], 1: [2, 1, 1, 0, 1, 4]}
+    outs = {t: [probs[i].out() for i in plan[t]] for t in plan}
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            for i, C in zip(plan[t], outs[t]):
+                probs[i].launch(fe, C, s)
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    print("workspace: two threads, one stream", flush=True, file=sys.stderr)
+    threads = [threading.Thread(target=worker, args=(t,)) for t in plan]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in plan:
+        for n, (i, C) in enumerate(zip(plan[t], outs[t])):
+            _same(refs[i], probs[i].result(C), f"thread {t} call {n}: case {probs[i].case}")
