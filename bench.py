@@ -188,6 +188,8 @@ def main():
     if not rel < 1e-5:
         raise SystemExit(f"bench: output check failed (relative error {rel:.3g})")
 
+    probe = mfma_probe(torch, stream)
+
     context = None
     if not args.no_context:
         context = context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp)
@@ -232,6 +234,8 @@ def main():
             "flops_per_launch": bf16_flops_per_launch,
             "mfma_busy_per_launch_pmc": mfma_busy,
             "sclk_ghz_under_load": sclk,
+            "probe_mfma_only_tflops": probe,
+            "frac_of_probe_random_operands": round(achieved / probe["random_operands"], 4),
         },
         "cpu_baseline": cpu,
         "context": context,
@@ -258,6 +262,34 @@ def timed(fn, stream, reps):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
+
+
+def mfma_probe(torch, stream):
+    """The practical ceiling of the GEMM's instruction: BF16 TFLOP/s of a kernel
+    that only issues v_mfma_f32_32x32x16_bf16 (one workgroup of 8 waves per CU,
+    four independent accumulators), on random and on constant operand bits."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(HERE, "fp32_emulated_gemm_amd", "libsgemm_probe.so"))
+    L.sgemm_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.sgemm_probe_mfma.restype = ctypes.c_int
+    L.sgemm_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.sgemm_probe_mfma_flops.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4000                                  # ~2-3 ms per launch
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    flops = L.sgemm_probe_mfma_flops(cus, iters)
+    res = {}
+    for name, rnd in (("random_operands", 1), ("constant_operands", 0)):
+        def call():
+            rc = L.sgemm_probe_mfma(cus, iters, rnd, out.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise SystemExit(f"bench: MFMA probe failed with status {rc}")
+        t = timed(call, stream, 5)
+        res[name] = round(flops / t / 1e9, 1)
+    if not bool(torch.isfinite(out).all()):
+        raise SystemExit("bench: MFMA probe produced non-finite sums")
+    log(f"MFMA-only probe: {res} TFLOP/s BF16 (nominal {MI355X_BF16_DENSE_TFLOPS})")
+    return res
 
 
 def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):

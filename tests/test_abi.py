@@ -132,3 +132,20 @@ def test_valid_call_without_gpu_reports_arch(L):
         pytest.skip("a GPU is present")
     assert L.sgemm_bf16x9(4, 4, 4, P, 4, P, 4, P, 4, None) == -3
     assert L.split_f32_bf16x3(4, 4, P, 4, P, P, P, 4, None) == -3
+
+
+def test_probe_library_loads_and_validates():
+    """The benchmark's MFMA probe library (not part of the GEMM ABI): it loads,
+    exports its two functions, counts flops as documented, and rejects bad
+    arguments before any HIP call."""
+    import fp32_emulated_gemm_amd  # noqa: F401  (binds the HIP runtime torch loaded)
+    P = ctypes.CDLL(os.path.join(ROOT, "fp32_emulated_gemm_amd", "libsgemm_probe.so"))
+    P.sgemm_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.sgemm_probe_mfma.restype = ctypes.c_int
+    P.sgemm_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    P.sgemm_probe_mfma_flops.restype = ctypes.c_double
+    # 8 waves x 16 MFMAs x 32768 flops per iteration and workgroup
+    assert P.sgemm_probe_mfma_flops(3, 5) == 3 * 8 * 5 * 16 * 32768
+    assert P.sgemm_probe_mfma(0, 5, 1, None, None) == -1
+    assert P.sgemm_probe_mfma(1, 0, 1, None, None) == -1
+    assert P.sgemm_probe_mfma(1, 5, 1, None, None) == -1
