@@ -29,6 +29,12 @@ constexpr int64_t kMaxBytes = INT64_MAX / 8;
 // (B is then split once instead of once per 128-row tile row), up to this B size.
 constexpr int64_t kPresplitMinRows = 1024;
 constexpr uint64_t kPresplitMaxElems = (uint64_t)1 << 28;
+// ... and by default only where it pays: a separate split launch and the
+// workspace cost a few microseconds, the in-kernel split of B a few percent of
+// the GEMM; the in-kernel path also has no split-K.  Measured on MI355X: the
+// in-kernel split wins at 6144x1024x256 (85 vs 74 TFLOP/s) and
+// 16384x256x1024 (125 vs 116), loses at 2048^3 (114 vs 123) and above.
+constexpr double kPresplitMinFlops = 1.2e10;
 // Largest leading dimension (elements) whose 128-row tile span fits 32-bit byte offsets.
 constexpr int64_t kMaxTileLd = ((int64_t)1 << 32) / (128 * 4) - 64;
 
@@ -249,7 +255,7 @@ void *acquire_workspace(int dev, hipStream_t stream, size_t bytes, WsLease &L)
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
                 int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
-                int act = SGEMM_EMU_ACT_NONE, bool rne = false)
+                int act = SGEMM_EMU_ACT_NONE, bool rne = false, bool force_presplit = false)
 {
     int rc;
     if ((rc = check_dims(M, N, K)) != SGEMM_EMU_OK) return rc;
@@ -297,7 +303,9 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // the planes (zeros) and the kernel masks A past its K.
     const int64_t kpad = (K + 63) / 64 * 64;
     const bool presplit = bsrc == B_FP32 && M >= kPresplitMinRows &&
-                          (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !(rne && kpad != K);
+                          (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !(rne && kpad != K) &&
+                          (force_presplit || gemm_split_count(M, N, kpad, nbands, num_cus) > 1 ||
+                           2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
     const size_t plane = presplit ? (size_t)N * (size_t)kpad * sizeof(uint16_t) : 0;
     const size_t plane_pad = (plane + 255) & ~(size_t)255;
 
@@ -354,10 +362,12 @@ int sgemm_emu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
 int sgemm_emu_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
                  float *C, int64_t ldc, int nbands, int flags, sgemm_emu_stream_t stream)
 {
-    if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_IEEE_SPECIALS)) != 0) return SGEMM_EMU_EINVAL;
+    if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_IEEE_SPECIALS | SGEMM_EMU_PRESPLIT_B)) != 0)
+        return SGEMM_EMU_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     int rc = gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32, s, nullptr,
-                         SGEMM_EMU_ACT_NONE, (flags & SGEMM_EMU_SPLIT_RNE) != 0);
+                         SGEMM_EMU_ACT_NONE, (flags & SGEMM_EMU_SPLIT_RNE) != 0,
+                         (flags & SGEMM_EMU_PRESPLIT_B) != 0);
     if (rc != SGEMM_EMU_OK || !(flags & SGEMM_EMU_IEEE_SPECIALS) || M == 0 || N == 0 || K == 0) return rc;
     // IEEE fix-up of the outputs touched by non-finite inputs (flags and a
     // column list in a pooled stream-ordered buffer)

@@ -39,16 +39,26 @@
  *   Arguments are validated before any HIP call; on an error status nothing
  *   has been enqueued.
  *   Device memory: sgemm_bf16x9 and sgemm_emu with M >= 1024 and K' * N <= 2^28
- *   (K' = K rounded up to a multiple of 64) split B once into a temporary
- *   N x K' set of BF16 planes, zero past K (6 K' N bytes).  GEMMs on small
- *   tile grids also need a split-K buffer (see sgemm_emu_split_k).  Both come
- *   from one block per call, taken stream-ordered (hipMallocFromPoolAsync,
- *   hipFreeAsync on `stream`) from a memory pool the library creates per
- *   device and keeps until the process ends, with freed blocks held for
- *   reuse.  If that allocation fails the GEMM splits B inside its kernel
- *   (bitwise the same result) and runs one pass over K per tile (the
- *   one-pass rounding order of sgemm_emu_split_k's S = 1).  No other device
- *   memory is allocated (sgemm_emu_ex's IEEE fix-up aside, documented there).
+ *   (K' = K rounded up to a multiple of 64) split B once into an N x K' set
+ *   of BF16 planes, zero past K (6 K' N bytes), where that is faster than
+ *   splitting B inside the GEMM kernel: when the tile grid is small enough
+ *   for split-K, or when 2 M N K >= 1.2e10 (sgemm_emu_ex's
+ *   SGEMM_EMU_PRESPLIT_B asks for it whenever M and K' N allow).  Both ways
+ *   give bitwise the same result.  GEMMs on small tile grids also need a
+ *   split-K buffer (see sgemm_emu_split_k).  Both live in one grow-only
+ *   workspace block per stream, which the stream's later calls reuse (stream
+ *   order keeps them apart; an event recorded after each use orders the next
+ *   user of the block, and calls from several host threads on one stream
+ *   enqueue one after the other).  A device keeps such blocks for up to 8
+ *   streams; a ninth stream takes over the least recently used block.  The
+ *   blocks come from a memory pool the library creates per device
+ *   (hipMallocFromPoolAsync on the calling stream) and stay allocated until
+ *   the process ends.  A stream being captured into a graph gets a block of
+ *   its own per call instead (freed with hipFreeAsync in the graph).  If no
+ *   workspace can be had the GEMM splits B inside its kernel (bitwise the
+ *   same result) and runs one pass over K per tile (the one-pass rounding
+ *   order of sgemm_emu_split_k's S = 1).  No other device memory is
+ *   allocated (sgemm_emu_ex's IEEE fix-up aside, documented there).
  *   Float pointers must be 4-byte aligned, BF16 plane pointers 2-byte aligned.
  *   16-byte aligned A with lda % 4 == 0 takes the vector-load path; any other
  *   layout takes a scalar-load path with the same arithmetic.
@@ -112,17 +122,21 @@ enum sgemm_emu_flags {
                                        ties to even, never to Inf (a finite value that would round to
                                        Inf keeps its truncation), instead of truncating */
     SGEMM_EMU_SPLIT_TRANSPOSE = 2,  /* split_f32_bf16x3_ex only: write the planes of X^T */
-    SGEMM_EMU_IEEE_SPECIALS = 4     /* sgemm_emu_ex only: outputs whose row of A or column of B holds
+    SGEMM_EMU_IEEE_SPECIALS = 4,    /* sgemm_emu_ex only: outputs whose row of A or column of B holds
                                        an Inf or NaN are recomputed as plain FP32 dot products (k
                                        ascending, product and sum rounded separately), so they follow
                                        IEEE-754 FP32 (+-Inf where the emulation's Inf x 0 component
                                        gives NaN); other outputs are unchanged.  Costs one more read
                                        of A and B and a pooled (2 (M + N) + 1)-int buffer. */
+    SGEMM_EMU_PRESPLIT_B = 8        /* sgemm_emu_ex only: split FP32 B once into workspace planes
+                                       whenever M >= 1024 and K' N <= 2^28, not only where the default
+                                       expects it to be faster (same result, bitwise) */
 };
 
 /*
- * sgemm_emu_ex -- sgemm_emu with flags (SGEMM_EMU_SPLIT_RNE and/or
- * SGEMM_EMU_IEEE_SPECIALS; other bits give SGEMM_EMU_EINVAL).  With SGEMM_EMU_SPLIT_RNE both A and B are split
+ * sgemm_emu_ex -- sgemm_emu with flags (SGEMM_EMU_SPLIT_RNE,
+ * SGEMM_EMU_IEEE_SPECIALS, SGEMM_EMU_PRESPLIT_B; other bits give
+ * SGEMM_EMU_EINVAL).  With SGEMM_EMU_SPLIT_RNE both A and B are split
  * with the round-to-nearest rule: with all nine products the result is the
  * same emulated product up to FP32 rounding (both splits are exact); with
  * fewer bands the dropped terms are about half as large and unsigned-biased

@@ -50,6 +50,8 @@ def run(fe, A, B, nbands=5, entry="fused", ldc_pad=0, a_offset=0):
         planes = [torch.empty(max(K * N, 1), dtype=torch.int16, device="cuda") for _ in range(3)]
         fe.split_f32_bf16x3(N, K, Bt, max(K, 1), *planes, max(K, 1))
         fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, max(K, 1), fe.SGEMM_EMU_B_NK, Cd, max(ldc, 1), nbands)
+    elif entry == "fused_ws":
+        fe.sgemm_emu_ex(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1), nbands, fe.SGEMM_EMU_PRESPLIT_B)
     elif nbands == 5 and entry == "fused":
         fe.sgemm_bf16x9(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1))
     else:
@@ -134,16 +136,18 @@ WS_SHAPES = [(1024, 130, 64), (1100, 257, 128), (1500, 1000, 512), (2048, 64, 19
 
 @pytest.mark.parametrize("shape", WS_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_fp32_b_workspace_path(fe, shape):
-    """FP32 B with at least 1024 rows of A: B is split once into N x K planes in a
-    workspace (zero-padded to a multiple of 64 in K; the kernel masks A past K).
-    Same result, bit for bit, as the in-kernel split and as the caller-split
-    N x K planes (without split-K)."""
+    """FP32 B with at least 1024 rows of A, pre-split on request: B is split once
+    into N x K planes in a workspace (zero-padded to a multiple of 64 in K; the
+    kernel masks A past K).  Same result, bit for bit, as sgemm_bf16x9's own
+    choice, as the in-kernel split and as the caller-split N x K planes
+    (without split-K)."""
     M, N, K = shape
     g = _rng(M + 3 * N + 11 * K)
     A = g.standard_normal((M, K)).astype(np.float32)
     B = g.standard_normal((K, N)).astype(np.float32)
-    C = run(fe, A, B, entry="fused")
+    C = run(fe, A, B, entry="fused_ws")
     check_against_fp64(C, A, B, label=f"workspace {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
     kpad = (K + 63) // 64 * 64
     if K == kpad or fe.sgemm_emu_split_k(M, N, kpad) == 1:
         assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
@@ -157,7 +161,7 @@ def test_fp32_b_workspace_path_bands(fe, nbands):
     g = _rng(900 + nbands)
     A = g.standard_normal((M, K)).astype(np.float32)
     B = g.standard_normal((K, N)).astype(np.float32)
-    C = run(fe, A, B, nbands, "fused")
+    C = run(fe, A, B, nbands, "fused_ws")
     assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, nbands).view(np.uint32))
 
 
@@ -171,7 +175,7 @@ def test_fp32_b_workspace_ragged_k_masks_a_tail(fe):
     A[1:, :28] = np.where(g.random((M - 1, 28)) < 0.5, np.inf, np.nan)   # row i+1's head follows row i's tail
     A[0, :] = 1.0
     B = g.standard_normal((K, N)).astype(np.float32)
-    C = run(fe, A, B, entry="fused")
+    C = run(fe, A, B, entry="fused_ws")
     R = _fused_in_row_blocks(fe, A, B, 5)
     assert np.array_equal(np.isnan(C), np.isnan(R)) and np.array_equal(np.isinf(C), np.isinf(R))
     assert np.all(np.isfinite(C[0]))
@@ -190,7 +194,7 @@ def test_fp32_b_workspace_path_special_values(fe):
     B[100, 40] = np.nan
     B[9, 60] = np.float32(1e-40)
     B[:, 80] = 0.0
-    C = run(fe, A, B, entry="fused")
+    C = run(fe, A, B, entry="fused_ws")
     R = _fused_in_row_blocks(fe, A, B, 5)
     assert np.array_equal(np.isnan(C), np.isnan(R))
     fin = ~np.isnan(R)

@@ -19,13 +19,14 @@ from gpu_util import check_against_fp64, dev, host
 
 pytestmark = pytest.mark.gpu
 
-# (M, N, K, entry): "fused" = sgemm_bf16x9 on FP32 B; "nk" = caller-split N x K planes
+# (M, N, K, entry): "ws" = sgemm_emu_ex on FP32 B with SGEMM_EMU_PRESPLIT_B (B split
+# into workspace planes); "fused" = sgemm_bf16x9's own choice; "nk" = caller-split planes
 CASES = [
-    (1024, 130, 64, "fused"),      # B planes in the workspace
-    (6144, 256, 1024, "fused"),    # planes and split-K partials in one block
-    (2048, 1000, 512, "fused"),    # a larger plane set
+    (1024, 130, 64, "ws"),         # B planes in the workspace
+    (6144, 256, 1024, "fused"),    # planes and split-K partials in one block (its own choice)
+    (2048, 1000, 512, "ws"),       # a larger plane set
     (129, 130, 1024, "nk"),        # split-K partials only
-    (1100, 257, 100, "fused"),     # ragged K: zero-padded planes
+    (1100, 257, 100, "ws"),        # ragged K: zero-padded planes
 ]
 
 
@@ -54,6 +55,8 @@ class Problem:
         M, N, K, entry = self.case
         if entry == "fused":
             fe.sgemm_bf16x9(M, N, K, self.A, K, self.B, N, C, N, stream)
+        elif entry == "ws":
+            fe.sgemm_emu_ex(M, N, K, self.A, K, self.B, N, C, N, 5, fe.SGEMM_EMU_PRESPLIT_B, stream)
         else:
             fe.sgemm_emu_presplit_b(M, N, K, self.A, K, *self.planes, K, fe.SGEMM_EMU_B_NK, C, N, 5, stream)
 
