@@ -150,3 +150,12 @@ def test_probe_library_loads_and_validates():
     assert P.sgemm_probe_mfma(0, 5, 1, None, None) == -1
     assert P.sgemm_probe_mfma(1, 0, 1, None, None) == -1
     assert P.sgemm_probe_mfma(1, 5, 1, None, None) == -1
+
+
+def test_leading_dimension_limit(L):
+    """lda / ldb up to 8,388,544 elements (a 128-row tile span in 32-bit byte
+    offsets); one more is rejected before any HIP call."""
+    top = (1 << 32) // (128 * 4) - 64
+    assert L.sgemm_bf16x9(4, 4, 4, P, top + 1, P, 4, P, 4, None) == -1
+    assert L.sgemm_bf16x9(4, 4, 4, P, 4, P, top + 1, P, 4, None) == -1
+    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, P, P, top + 1, 1, P, 4, 5, None) == -1
