@@ -521,6 +521,13 @@ def test_rne_split_gemm_within_bound(fe, orc, shape):
         Cb = _run_ex(fe, A, B, nb, fe.SGEMM_EMU_SPLIT_RNE)[rows].astype(np.float64)
         T = orc.gemm_trunc_f64(A, B, nb, rows=rows, flags=orc.ORC_SPLIT_RNE)
         assert np.all(np.abs(Cb - T) <= 2 * K * 2.0 ** -24 * G), f"nbands={nb}"
+    if M >= 1024:
+        # the RNE split of B into workspace planes (transposing split kernel)
+        W = _run_ex(fe, A, B, 5, fe.SGEMM_EMU_SPLIT_RNE | fe.SGEMM_EMU_PRESPLIT_B)
+        if fe.sgemm_emu_split_k(M, N, K) == 1:
+            assert np.array_equal(W.view(np.uint32), C.view(np.uint32))
+        else:
+            check_against_fp64(W[rows], A, B, rows=rows, label=f"rne workspace {shape}")
 
 
 def test_rne_split_identity_exact_and_smaller_ablation_error(fe, orc):
