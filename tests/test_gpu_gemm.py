@@ -582,3 +582,20 @@ def test_ieee_specials_fixup_finite_inputs_unchanged(fe):
     B = g.standard_normal((200, 150)).astype(np.float32)
     assert np.array_equal(_run_ex(fe, A, B, 5, fe.SGEMM_EMU_IEEE_SPECIALS).view(np.uint32),
                           _run_ex(fe, A, B, 5, 0).view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(2048, 2048, 2048), (6144, 1024, 256)], ids=lambda s: "x".join(map(str, s)))
+def test_presplit_rule_is_invisible(fe, shape):
+    """sgemm_bf16x9 splits FP32 B into workspace planes only where that is faster
+    (2048^3: yes; 6144x1024x256: no).  Either way the result equals, bit for bit,
+    the forced workspace path and the in-kernel split (row blocks below the
+    workspace threshold)."""
+    M, N, K = shape
+    g = _rng(M + N + K + 5)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="fused")
+    rows = np.sort(g.choice(M, size=32, replace=False))
+    check_against_fp64(C[rows], A, B, rows=rows, label=f"pre-split rule {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_ws").view(np.uint32))
+    assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, 5).view(np.uint32))
