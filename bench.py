@@ -113,10 +113,12 @@ def main():
     ev = []
 
     def step(record):
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e[4].record(stream)
         fe.split_f32_bf16x3(F, D, W1t, D, *P1, D, sp)
         fe.split_f32_bf16x3(D, F, W2t, F, *P2, F, sp)
         if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record(stream)
         fe.sgemm_emu_presplit_b(M, F, D, Xd, D, *P1, D, fe.SGEMM_EMU_B_NK, C1, F, 5, sp)
         if record:
@@ -166,6 +168,7 @@ def main():
     value = flops_eff / (ms_step * 1e-3) / 1e12
     g1 = [e[0].elapsed_time(e[1]) for e in ev]
     g2 = [e[2].elapsed_time(e[3]) for e in ev]
+    wsplit = [e[4].elapsed_time(e[0]) for e in ev]        # both weight splits of a step
     g1_ms, g2_ms = float(np.mean(g1)), float(np.mean(g2))
     # roofline of the GEMM kernel: nine BF16 products per FP32 multiply-add pair
     bf16_flops_per_launch = [18.0 * M * F * D, 18.0 * M * D * F]
@@ -221,6 +224,9 @@ def main():
         "pct_bf16_peak_9products": round(100.0 * value * 9 / MI355X_BF16_DENSE_TFLOPS, 2),
         "pct_fp32_vector_peak": round(100.0 * value / MI355X_FP32_VECTOR_TFLOPS, 2),
         "gemm_ms": {"X@W1": round(g1_ms, 4), "H@W2": round(g2_ms, 4)},
+        "gemm_ms_per_launch": {name: {"median": round(float(np.median(v)), 4), "min": round(float(np.min(v)), 4),
+                                      "max": round(float(np.max(v)), 4)} for name, v in (("X@W1", g1), ("H@W2", g2))},
+        "weight_split_ms_per_step": round(float(np.mean(wsplit)), 4),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
