@@ -410,22 +410,34 @@ def cpu_baseline(X, W1, H, W2, target_s):
     M = X.shape[0]
     flops_per_row = 2.0 * (W1.shape[0] * W1.shape[1] + W2.shape[0] * W2.shape[1])
 
-    def run(nrows):
+    def run(nrows, fn=oracle.sgemm_naive_f32):
         rows = np.linspace(0, M - 1, nrows).astype(np.int64)
         t = time.perf_counter()
-        oracle.sgemm_naive_f32(X, W1, rows=rows)
-        oracle.sgemm_naive_f32(H, W2, rows=rows)
+        fn(X, W1, rows=rows)
+        fn(H, W2, rows=rows)
         return time.perf_counter() - t
 
-    probe_rows = 256
-    tp = run(probe_rows)
-    nrows = int(min(M, max(probe_rows, probe_rows * target_s / max(tp, 1e-6))))
+    def sized(fn, seconds):
+        probe_rows = 128
+        tp = run(probe_rows, fn)
+        return int(min(M, max(probe_rows, probe_rows * seconds / max(tp, 1e-6))))
+
+    nrows = sized(oracle.sgemm_naive_f32, target_s)
     t = run(nrows)
     val = flops_per_row * nrows / t / 1e12
     log(f"cpu baseline: {nrows} rows in {t:.2f} s on {oracle.num_threads()} threads")
+    # beside it, the oracle's other two products on smaller samples (same rate unit)
+    others = {}
+    for name, fn in (("fp64_reference", lambda A, B, rows: oracle.gemm_f64(A, B, rows=rows, want_g=False)),
+                     ("band_emulation_9_products", oracle.gemm_emu)):
+        n = sized(fn, target_s / 4)
+        tt = run(n, fn)
+        others[name] = {"value": round(flops_per_row * n / tt / 1e12, 5), "rows": n, "seconds": round(tt, 2)}
+    log(f"cpu oracle, other products: {others}")
     return {"value": round(val, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"naive FP32 SGEMM (oracle) on {nrows} of {M} rows of X@W1 and H@W2, "
-                      f"{t:.1f} s; value = 2*rows*(256*1024+1024*256)/t"}
+                      f"{t:.1f} s; value = 2*rows*(256*1024+1024*256)/t",
+            "other_oracle_products": others}
 
 
 if __name__ == "__main__":
