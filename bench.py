@@ -376,6 +376,9 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     res["sgemm_bf16x9_4096^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
     t = timed(lambda: torch.matmul(A, B, out=C), stream, 10)
     res["torch_fp32_4096^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
+    for nb in (4, 3, 2):
+        t = timed(lambda: fe.sgemm_emu(n, n, n, A, n, B, n, C, n, nb, sp), stream, 10)
+        res[f"ablation_4096^3_nbands{nb}_{fe.sgemm_emu_products(nb)}products_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
     del A, B, C
     n = 8192
     A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
@@ -386,6 +389,17 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     t = timed(lambda: torch.matmul(A, B, out=C), stream, 5)
     res["torch_fp32_8192^3_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
     del A, B, C
+    # the accuracy-stress workload (scales 2^-20..2^20, near-cancelling rows,
+    # subnormals) at 8192^3, all nine products and the band-drop ablations
+    import workloads
+    w = workloads.stress8192()
+    A = torch.from_numpy(w["A"]).to("cuda")
+    B = torch.from_numpy(w["B"]).to("cuda")
+    C = torch.empty((n, n), device="cuda")
+    for nb in (5, 4, 3, 2):
+        t = timed(lambda: fe.sgemm_emu(n, n, n, A, n, B, n, C, n, nb, sp), stream, 5)
+        res[f"stress8192_nbands{nb}_{fe.sgemm_emu_products(nb)}products_tflops"] = round(2.0 * n ** 3 / t / 1e9, 2)
+    del A, B, C, w
     # speed-up over the platform's own FP32 GEMM on the same shapes, next to the
     # ratios the pages quote for other hardware (context only)
     res["speedup_vs_torch_fp32"] = {
