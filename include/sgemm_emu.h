@@ -58,7 +58,10 @@
  *   workspace can be had the GEMM splits B inside its kernel (bitwise the
  *   same result) and runs one pass over K per tile (the one-pass rounding
  *   order of sgemm_emu_split_k's S = 1).  No other device memory is
- *   allocated (sgemm_emu_ex's IEEE fix-up aside, documented there).
+ *   allocated (sgemm_emu_ex's IEEE fix-up aside, documented there).  The
+ *   pool, the blocks and their events belong to the device's primary
+ *   context: after hipDeviceReset the library must not be called again in
+ *   that process.
  *   Float pointers must be 4-byte aligned, BF16 plane pointers 2-byte aligned.
  *   16-byte aligned A with lda % 4 == 0 takes the vector-load path; any other
  *   layout takes a scalar-load path with the same arithmetic.
