@@ -316,8 +316,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     const int sl = dma ? gemm_split_count(M, N, presplit ? kpad : K, nbands, num_cus) : 1;
     const size_t part_bytes = sl > 1 ? (size_t)sl * (size_t)M * (size_t)N * sizeof(float) : 0;
 
-    // One workspace per call holds the planes and the partials; without one
-    // the GEMM splits B itself and runs one unit per tile.
+    // The stream's workspace block holds the planes and the partials; without
+    // one the GEMM splits B itself and runs one unit per tile.
     WsLease lease;
     void *ws = nullptr;
     if (plane_pad + part_bytes > 0) ws = acquire_workspace(dev, stream, 3 * plane_pad + part_bytes, lease);

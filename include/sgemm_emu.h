@@ -252,14 +252,15 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
  * (sgemm_emu_presplit_b with SGEMM_EMU_B_NK and sgemm_emu_linear, which need
  * K % 64 == 0 and 16-byte aligned planes with ldb % 8 == 0; sgemm_bf16x9 /
  * sgemm_emu when they pre-split B, with K rounded up to a multiple of 64).
- * 1 means one pass over K per output tile.  With S > 1 slices (grids that would leave a quarter of the
- * CUs idle), each (tile, slice) runs the method on its K range (five band
- * sums, recombined smallest band first) and writes its FP32 result to a
- * stream-ordered pooled buffer (S * M * N floats); a reduction kernel adds the
+ * 1 means one pass over K per output tile.  With S > 1 slices (grids that
+ * would leave a quarter of the CUs idle), each (tile, slice) runs the method
+ * on its K range (five band sums, recombined smallest band first) and writes
+ * its FP32 result to the stream's workspace (S * M * N floats, see the
+ * device-memory conventions above); a reduction kernel adds the
  * S results in slice order, then the bias and activation.  Results differ in
  * rounding from the one-pass order (still within the same error bound) and
- * are deterministic for a given shape and device.  If the buffer cannot be
- * allocated the GEMM runs one pass per tile.  Returns S >= 1, or a negative
+ * are deterministic for a given shape and device.  If no workspace can be
+ * had the GEMM runs one pass per tile.  Returns S >= 1, or a negative
  * status (invalid sizes or nbands, no gfx950 device).
  */
 int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands);
