@@ -125,3 +125,30 @@ class Linear(torch.nn.Module):
     def extra_repr(self):
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
                 f"bias={self.bias is not None}, nbands={self.nbands}, activation={self.activation}")
+
+
+def convert_linears(module, nbands=5, fuse_gelu=False):
+    """Swap every torch.nn.Linear inside `module` (recursively, in place) for a
+    Linear holding the same weights: the fixed-weight use in which the pages
+    replace a model's FP32 layers by an emulated-GEMM layer with its trained
+    weights and shapes unchanged.  Returns `module`, or its replacement when
+    `module` is itself an nn.Linear.
+
+    fuse_gelu: inside nn.Sequential containers, an nn.Linear directly followed
+    by nn.GELU (the exact erf form) becomes one Linear with the GELU applied in
+    the GEMM's epilogue, and the GELU module an nn.Identity.  The fused
+    activation is forward-only (no input gradient), so leave it off where
+    gradients with respect to the inputs are needed (forces)."""
+    if isinstance(module, torch.nn.Linear):
+        return Linear.from_linear(module, nbands)
+    children = list(module.named_children())
+    for i, (name, child) in enumerate(children):
+        new = convert_linears(child, nbands, fuse_gelu)
+        if new is not child:
+            setattr(module, name, new)
+        if (fuse_gelu and isinstance(module, torch.nn.Sequential) and isinstance(child, torch.nn.Linear)
+                and i + 1 < len(children) and isinstance(children[i + 1][1], torch.nn.GELU)
+                and children[i + 1][1].approximate == "none"):
+            new.activation = "gelu"
+            setattr(module, children[i + 1][0], torch.nn.Identity())
+    return module

@@ -238,3 +238,33 @@ def test_module_matches_nn_linear_and_refuses_parameter_grads(fe):
         m.weight.mul_(2.0)
     y2 = m(x.detach())
     assert torch.allclose(y2, 2.0 * (y.detach() - m.bias) + m.bias, rtol=1e-5, atol=1e-5)
+
+
+def test_converted_model_forward_and_input_gradient(fe):
+    """A small MLP converted by convert_linears: the same outputs and input
+    gradients as the FP32 torch model (to FP32 accuracy), with and without the
+    fused GELU."""
+    from fp32_emulated_gemm_amd.linear import Linear, convert_linears
+    torch.manual_seed(11)
+
+    def mlp():
+        torch.manual_seed(11)
+        return torch.nn.Sequential(torch.nn.Linear(64, 256), torch.nn.GELU(), torch.nn.Linear(256, 64)).cuda()
+
+    ref = mlp()
+    x = torch.randn(1200, 64, device="cuda")
+    xr = x.clone().requires_grad_(True)
+    y_ref = ref(xr)
+    y_ref.sum().backward()
+    m = convert_linears(mlp())
+    assert isinstance(m[0], Linear) and isinstance(m[2], Linear)
+    xe = x.clone().requires_grad_(True)
+    y = m(xe)
+    y.sum().backward()
+    assert torch.allclose(y.detach(), y_ref.detach(), rtol=1e-5, atol=1e-5)
+    assert torch.allclose(xe.grad, xr.grad, rtol=1e-4, atol=1e-5)
+    f = convert_linears(mlp(), fuse_gelu=True)
+    assert f[0].activation == "gelu" and isinstance(f[1], torch.nn.Identity)
+    with torch.no_grad():
+        yf = f(x)
+    assert torch.allclose(yf, y_ref.detach(), rtol=1e-5, atol=1e-5)
