@@ -545,12 +545,15 @@ def test_rne_split_identity_exact_and_smaller_ablation_error(fe, orc):
 
 # ---------------------------------------------------------------- IEEE fix-up of non-finite inputs
 
+@pytest.mark.parametrize("extra", [0, 8], ids=["default", "presplit"])
 @pytest.mark.parametrize("shape", [(48, 40, 70), (1030, 300, 128), (200, 140, 1024)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_ieee_specials_fixup(fe, orc, shape):
+def test_ieee_specials_fixup(fe, orc, shape, extra):
     """SGEMM_EMU_IEEE_SPECIALS: outputs whose row of A or column of B holds an Inf
     or NaN equal the oracle's plain FP32 dot product bit for bit (+-Inf where the
-    emulation gives NaN); all other outputs equal the emulation's."""
+    emulation gives NaN); all other outputs equal the emulation's.  `extra` = 8
+    (SGEMM_EMU_PRESPLIT_B) runs both through the workspace planes where M allows."""
+    assert extra in (0, fe.SGEMM_EMU_PRESPLIT_B)
     M, N, K = shape
     g = _rng(M + N + K + 5)
     A = g.standard_normal((M, K)).astype(np.float32)
@@ -562,8 +565,8 @@ def test_ieee_specials_fixup(fe, orc, shape):
     B[10, N - 1] = np.inf                  # last column flagged
     B[11, N // 2] = -np.inf
     A[M - 1, 0] = np.nan                   # last row flagged
-    C_emu = _run_ex(fe, A, B, 5, 0)
-    C = _run_ex(fe, A, B, 5, fe.SGEMM_EMU_IEEE_SPECIALS)
+    C_emu = _run_ex(fe, A, B, 5, extra)
+    C = _run_ex(fe, A, B, 5, fe.SGEMM_EMU_IEEE_SPECIALS | extra)
     rows = np.unique([2, 5, 7, M - 1])
     cols = np.unique([N - 1, N // 2])
     flagged = np.zeros((M, N), bool)
