@@ -47,6 +47,7 @@ SGEMM_EMU_SPLIT_RNE = 1        # flag: round-to-nearest-even split (rounding abl
 SGEMM_EMU_SPLIT_TRANSPOSE = 2  # flag (split_f32_bf16x3_ex): planes of X^T
 SGEMM_EMU_IEEE_SPECIALS = 4    # flag (sgemm_emu_ex): IEEE FP32 results where inputs hold Inf/NaN
 SGEMM_EMU_PRESPLIT_B = 8       # flag (sgemm_emu_ex): split FP32 B once into workspace planes whenever allowed
+SGEMM_EMU_PRESPLIT_A = 16      # flag (sgemm_emu_ex): split FP32 A (and B) once into workspace planes whenever allowed
 
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_linear",
            "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",

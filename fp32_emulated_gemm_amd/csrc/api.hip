@@ -35,6 +35,12 @@ constexpr uint64_t kPresplitMaxElems = (uint64_t)1 << 28;
 // in-kernel split wins at 6144x1024x256 (85 vs 74 TFLOP/s) and
 // 16384x256x1024 (125 vs 116), loses at 2048^3 (114 vs 123) and above.
 constexpr double kPresplitMinFlops = 1.2e10;
+// With B pre-split, FP32 A is split once into workspace planes too where N has
+// this many columns: the kernel that splits A itself repeats that for each of
+// the N / 128 tile columns, the plane kernel copies both operands by DMA.
+// Measured on MI355X (A split included): 4096^3 +6-10 %, 8192^3 +2.5 %; at
+// N = 1024 the separate split of A costs more than the kernel gains.
+constexpr int64_t kPresplitAMinCols = 4096;
 // Largest leading dimension (elements) whose 128-row tile span fits 32-bit byte offsets.
 constexpr int64_t kMaxTileLd = ((int64_t)1 << 32) / (128 * 4) - 64;
 
@@ -255,7 +261,8 @@ void *acquire_workspace(int dev, hipStream_t stream, size_t bytes, WsLease &L)
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
                 int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
-                int act = SGEMM_EMU_ACT_NONE, bool rne = false, bool force_presplit = false)
+                int act = SGEMM_EMU_ACT_NONE, bool rne = false, bool force_presplit = false,
+                bool force_presplit_a = false)
 {
     int rc;
     if ((rc = check_dims(M, N, K)) != SGEMM_EMU_OK) return rc;
@@ -308,6 +315,11 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
                            2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
     const size_t plane = presplit ? (size_t)N * (size_t)kpad * sizeof(uint16_t) : 0;
     const size_t plane_pad = (plane + 255) & ~(size_t)255;
+    // A as well (K needs no padding; A's planes are M x K, k contiguous).
+    const bool presplit_a = presplit && kpad == K && (uint64_t)M * (uint64_t)K <= kPresplitMaxElems &&
+                            (force_presplit_a || N >= kPresplitAMinCols);
+    const size_t aplane = presplit_a ? (size_t)M * (size_t)K * sizeof(uint16_t) : 0;
+    const size_t aplane_pad = (aplane + 255) & ~(size_t)255;
 
     // Grids that would leave CUs idle on the N x K DMA kernel are split along
     // K: each (tile, K slice) recombines its own bands and writes the result to
@@ -320,7 +332,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // one the GEMM splits B itself and runs one unit per tile.
     WsLease lease;
     void *ws = nullptr;
-    if (plane_pad + part_bytes > 0) ws = acquire_workspace(dev, stream, 3 * plane_pad + part_bytes, lease);
+    if (plane_pad + part_bytes > 0)
+        ws = acquire_workspace(dev, stream, 3 * plane_pad + part_bytes + 3 * aplane_pad, lease);
     if (ws != nullptr && presplit) {
         uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
                  *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
@@ -334,6 +347,17 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
         g.splits = sl;
         g.partials = (float *)((char *)ws + 3 * plane_pad);
         g.ldp = N;
+    }
+    if (ws != nullptr && presplit_a) {
+        char *const a_ws = (char *)ws + 3 * plane_pad + part_bytes;
+        uint16_t *Q0 = (uint16_t *)a_ws, *Q1 = (uint16_t *)(a_ws + aplane_pad), *Q2 = (uint16_t *)(a_ws + 2 * aplane_pad);
+        hipError_t e = launch_split(M, K, A, lda, Q0, Q1, Q2, K, num_cus, stream, rne);
+        if (e == hipSuccess) {
+            g.A0 = Q0; g.A1 = Q1; g.A2 = Q2; g.lda = K;
+            e = launch_gemm_planes(g, nbands, stream);
+        }
+        lease.release();
+        return launched(e);
     }
 
     const hipError_t e = launch_gemm(g, nbands, bsrc, stream, rne);
@@ -362,12 +386,13 @@ int sgemm_emu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
 int sgemm_emu_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
                  float *C, int64_t ldc, int nbands, int flags, sgemm_emu_stream_t stream)
 {
-    if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_IEEE_SPECIALS | SGEMM_EMU_PRESPLIT_B)) != 0)
+    if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_IEEE_SPECIALS | SGEMM_EMU_PRESPLIT_B | SGEMM_EMU_PRESPLIT_A)) != 0)
         return SGEMM_EMU_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     int rc = gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32, s, nullptr,
                          SGEMM_EMU_ACT_NONE, (flags & SGEMM_EMU_SPLIT_RNE) != 0,
-                         (flags & SGEMM_EMU_PRESPLIT_B) != 0);
+                         (flags & (SGEMM_EMU_PRESPLIT_B | SGEMM_EMU_PRESPLIT_A)) != 0,
+                         (flags & SGEMM_EMU_PRESPLIT_A) != 0);
     if (rc != SGEMM_EMU_OK || !(flags & SGEMM_EMU_IEEE_SPECIALS) || M == 0 || N == 0 || K == 0) return rc;
     // IEEE fix-up of the outputs touched by non-finite inputs (flags and a
     // column list in a pooled stream-ordered buffer)

@@ -727,34 +727,47 @@ __device__ __forceinline__ void lds_barrier()
 
 __device__ __forceinline__ int bslot(int row, int kg) { return kg ^ ((row >> 2) & 3); }
 
+// Copy one K step (BK columns) of a 128-row tile of three BF16 planes with k
+// contiguous (N x K planes of B, or M x K planes of A), rows r0.. of
+// `nrows`, global -> LDS: wave w copies tile rows RPW w .. RPW w + RPW - 1,
+// 16 rows per copy, lane -> (row, 16-byte slot); rows past the operand
+// re-read its last row (never used).  `buf` receives the three plane tiles,
+// unpadded 64-byte rows with swizzled slots (bslot).
 template <class C>
-__device__ __forceinline__ void dma_b_stage(const GemmArgs &g, int64_t n0, int64_t k0, uint16_t *bbuf, int wave,
-                                            int lane)
+__device__ __forceinline__ void dma_plane_stage(const uint16_t *P0, const uint16_t *P1, const uint16_t *P2,
+                                                int64_t ld, int64_t nrows, int64_t r0, int64_t k0, int64_t K,
+                                                uint16_t *buf, int wave, int lane)
 {
     typedef __attribute__((address_space(3))) void lds_void_t;
     constexpr int RPW = DmaLayout<C>::B_ROWS_PER_WAVE;
-    // wave w copies rows RPW w .. RPW w + RPW - 1 of each plane tile, 16 rows
-    // per copy; lane -> (row, slot)
-    const int64_t cols = lmin((int64_t)C::BN, g.N - n0);
-    const int64_t bytes = ((cols - 1) * g.ldb + (g.K - k0)) * 2;
-    const int64_t base = n0 * g.ldb + k0;
+    const int64_t rows = lmin((int64_t)128, nrows - r0);
+    const int64_t bytes = ((rows - 1) * ld + (K - k0)) * 2;
+    const int64_t base = r0 * ld + k0;
     uint32_t off[DmaLayout<C>::B_COPIES];
 #pragma unroll
     for (int d = 0; d < DmaLayout<C>::B_COPIES; ++d) {
         const int row = wave * RPW + d * 16 + (lane >> 2), kg = bslot(row, lane & 3);
-        const int64_t n = lmin((int64_t)row, cols - 1);
-        off[d] = (uint32_t)((n * g.ldb + kg * 8) * 2);
+        const int64_t n = lmin((int64_t)row, rows - 1);
+        off[d] = (uint32_t)((n * ld + kg * 8) * 2);
     }
-    const uint16_t *planes[3] = {g.B0, g.B1, g.B2};
+    const uint16_t *planes[3] = {P0, P1, P2};
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
         const rsrc_t r = make_rsrc(planes[p] + base, bytes);
 #pragma unroll
         for (int d = 0; d < DmaLayout<C>::B_COPIES; ++d) {
-            uint16_t *dst = bbuf + p * B_DMA_TILE + (wave * RPW + d * 16) * BK;   // wave-uniform 1 KB block
+            uint16_t *dst = buf + p * B_DMA_TILE + (wave * RPW + d * 16) * BK;   // wave-uniform 1 KB block
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)off[d], 0, 0, 0);
         }
     }
+}
+
+template <class C>
+__device__ __forceinline__ void dma_b_stage(const GemmArgs &g, int64_t n0, int64_t k0, uint16_t *bbuf, int wave,
+                                            int lane)
+{
+    static_assert(C::BN == 128, "128-row plane tiles");
+    dma_plane_stage<C>(g.B0, g.B1, g.B2, g.ldb, g.N, n0, k0, g.K, bbuf, wave, lane);
 }
 
 template <class C>
@@ -1084,6 +1097,109 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     wait_vmem_at_most<0>();      // drain the copies issued past the end of K
 }
 
+// ---------------------------------------------------------------- both operands as planes
+//
+// A given as three BF16 planes M x K (lda) like B's N x K planes (ldb), K a
+// multiple of 2 BK, 16-byte aligned planes.  Nothing is split in the kernel:
+// both operands' tiles are copied global -> LDS by buffer loads with LDS
+// destination, two steps ahead, into two rings of three buffers (144 KB), in
+// the swizzled layout of dma_plane_stage.  One K step: copy the step two
+// ahead, read the second slice's fragments, run the first slice, most of the
+// second, wait for the next step's copies, pass the barrier, read the next
+// step's first fragments and finish the second slice.  Same tiles, persistent
+// order, MFMA order and epilogue as gemm_bf16x9_dma_kernel, so the result is
+// bitwise that of the kernels that split A themselves.
+template <class C>
+__device__ __forceinline__ void read_frags_planes(Frags<C> &f, const uint16_t *abuf, const uint16_t *bbuf, int kk,
+                                                  int wm, int wn, int lane)
+{
+    const int frag_row = lane & 31, kg = (kk >> 3) + (lane >> 5);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) {
+            const int row = wm * C::WTM + i * 32 + frag_row;
+            f.a[i][c] = ld_frag(abuf + c * B_DMA_TILE + row * BK + bslot(row, kg) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) {
+            const int row = wn * C::WTN + j * 32 + frag_row;
+            f.b[j][c] = ld_frag(bbuf + c * B_DMA_TILE + row * BK + bslot(row, kg) * 8);
+        }
+    }
+}
+
+template <class C, int NB>
+__global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_planes_kernel(GemmArgs g)
+{
+    static_assert(C::BM == 128 && C::BN == 128, "128-row plane tiles");
+    constexpr int BUF = 3 * B_DMA_TILE;                      // one ring buffer: three plane tiles
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * BUF];
+    uint16_t *const a_base = lds;
+    uint16_t *const b_base = lds + 3 * BUF;
+    constexpr int NV = 2 * 3 * DmaLayout<C>::B_COPIES;       // copies one thread issues per K step
+    constexpr int NM = products(NB) * C::MI * C::NI;          // MFMAs per k slice
+    constexpr int TAIL = C::DMA_TAIL < NM ? C::DMA_TAIL : NM;
+
+    const int T = g.tiles_m * g.tiles_n, G = (int)gridDim.x;
+    const int units = T * g.splits;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int64_t nk = g.K / BK / g.splits;
+
+    int v = (int)blockIdx.x;
+    StepSrc<C> cur;                              // the work unit being computed
+    unit_src<C>(cur, v, T, nk, g);
+    auto copy = [&](const StepSrc<C> &u, int64_t k0, int slot) {
+        dma_plane_stage<C>(g.A0, g.A1, g.A2, g.lda, g.M, u.m0, k0, g.K, a_base + slot * BUF, wave, lane);
+        dma_plane_stage<C>(g.B0, g.B1, g.B2, g.ldb, g.N, u.n0, k0, g.K, b_base + slot * BUF, wave, lane);
+    };
+
+    Acc<C, NB> acc;
+    clear_acc<C, NB>(acc);
+    Frags<C> f0, f1;
+
+    // Prologue: steps 0 and 1 in flight, step 0 landed, its first fragments read.
+    copy(cur, cur.kb, 0);
+    copy(cur, cur.kb + BK, 1);
+    wait_vmem_at_most<NV>();
+    lds_barrier();
+    read_frags_planes<C>(f0, a_base, b_base, 0, wm, wn, lane);
+
+    int bs = 0;                                  // ring slot of the current step
+    for (;;) {
+        float bias[C::NI];                       // issued now, needed by the unit's epilogue
+        load_bias<C>(bias, g, cur.n0, wn, lane);
+        // The next unit, or (none left) the current one again, whose steps
+        // past its K slice then serve as harmless dummy copies.
+        const int64_t vn = (int64_t)v + G;
+        const bool has_next = vn < units;
+        StepSrc<C> nxt = cur;
+        if (has_next) unit_src<C>(nxt, (int)vn, T, nk, g);
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int b1 = bs == 2 ? 0 : bs + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+            if (kt + 2 < nk || !has_next) copy(cur, cur.kb + (kt + 2) * BK, b2);
+            else copy(nxt, nxt.kb + (kt + 2 - nk) * BK, b2);
+            read_frags_planes<C>(f1, a_base + bs * BUF, b_base + bs * BUF, 16, wm, wn, lane);
+            mfma_slice<C, NB>(acc, f0);
+            mfma_slice_part<C, NB, 0, NM - TAIL>(acc, f1);
+            // the next step's tiles must have landed; only this step's copies may be in flight
+            wait_vmem_at_most<NV>();
+            lds_barrier();
+            read_frags_planes<C>(f0, a_base + b1 * BUF, b_base + b1 * BUF, 0, wm, wn, lane);
+            mfma_slice_part<C, NB, NM - TAIL, NM>(acc, f1);
+            bs = b1;
+        }
+        if (g.splits > 1) store_c_act<C, NB, -1>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane, cur.slice);
+        else store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
+        if (!has_next) break;
+        clear_acc<C, NB>(acc);
+        v = (int)vn;
+        cur = nxt;
+    }
+    wait_vmem_at_most<0>();      // drain the copies issued past the end of K
+}
+
 // ---------------------------------------------------------------- split-K reduction
 
 // C = act(sum over K slices of the slices' recombined results + bias), per
@@ -1216,6 +1332,41 @@ static hipError_t launch_dma(const GemmArgs &args, int nbands, hipStream_t strea
     case 3: launch_dma_nb<C, 3, RNE, KTAIL>(g, avec, stream); break;
     case 4: launch_dma_nb<C, 4, RNE, KTAIL>(g, avec, stream); break;
     default: launch_dma_nb<C, 5, RNE, KTAIL>(g, avec, stream); break;
+    }
+    return hipGetLastError();
+}
+
+template <class C, int NB>
+static void launch_planes_nb(const GemmArgs &g, hipStream_t stream)
+{
+    const int64_t units = (int64_t)g.tiles_m * g.tiles_n * g.splits;
+    int64_t slots = (int64_t)(g.num_cus > 8 ? g.num_cus & ~7 : 8);
+    const dim3 grid((unsigned)(units < slots ? units : slots)), block(C::NT);
+    hipLaunchKernelGGL((gemm_bf16x9_planes_kernel<C, NB>), grid, block, 0, stream, g);
+    if (g.splits > 1) {
+        int64_t blocks = (g.M * g.N + 255) / 256;
+        if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g);
+    }
+}
+
+hipError_t launch_gemm_planes(const GemmArgs &args, int nbands, hipStream_t stream)
+{
+    using C = Cfg8S;
+    if (args.K % (2 * BK) != 0 || args.lda % 8 != 0 || args.ldb % 8 != 0 || !aligned(args.A0, 16) ||
+        !aligned(args.A1, 16) || !aligned(args.A2, 16) || !aligned(args.B0, 16) || !aligned(args.B1, 16) ||
+        !aligned(args.B2, 16))
+        return hipErrorInvalidValue;
+    GemmArgs g = args;
+    g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
+    g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
+    g.group_m = group_rows(g.tiles_n, g.num_cus);
+    switch (nbands) {
+    case 1: launch_planes_nb<C, 1>(g, stream); break;
+    case 2: launch_planes_nb<C, 2>(g, stream); break;
+    case 3: launch_planes_nb<C, 3>(g, stream); break;
+    case 4: launch_planes_nb<C, 4>(g, stream); break;
+    default: launch_planes_nb<C, 5>(g, stream); break;
     }
     return hipGetLastError();
 }

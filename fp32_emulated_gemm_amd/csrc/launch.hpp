@@ -21,6 +21,9 @@ struct GemmArgs {
     const float *A;
     int64_t lda;
     const float *B;          // B_FP32
+    const uint16_t *A0;      // A as three BF16 planes M x K (lda), launch_gemm_planes only
+    const uint16_t *A1;
+    const uint16_t *A2;
     const uint16_t *B0;      // B_PLANES
     const uint16_t *B1;
     const uint16_t *B2;
@@ -51,6 +54,11 @@ hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, in
 // rne: the in-kernel split of A (and of FP32 B) rounds to nearest even; only
 // B_FP32 and B_PLANES_NK (DMA kernel) support it.
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne = false);
+
+// Both operands as BF16 planes with k contiguous: A0..A2 M x K (lda), B0..B2
+// N x K (ldb); K a multiple of 64, leading dimensions multiples of 8,
+// 16-byte aligned planes (else hipErrorInvalidValue, nothing launched).
+hipError_t launch_gemm_planes(const GemmArgs &args, int nbands, hipStream_t stream);
 
 // K slices the N x K DMA kernel should use for this shape (1 = no split-K):
 // grids that leave a quarter of the CUs idle get split along K.

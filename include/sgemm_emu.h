@@ -43,9 +43,14 @@
  *   of BF16 planes, zero past K (6 K' N bytes), where that is faster than
  *   splitting B inside the GEMM kernel: when the tile grid is small enough
  *   for split-K, or when 2 M N K >= 1.2e10 (sgemm_emu_ex's
- *   SGEMM_EMU_PRESPLIT_B asks for it whenever M and K' N allow).  Both ways
- *   give bitwise the same result.  GEMMs on small tile grids also need a
- *   split-K buffer (see sgemm_emu_split_k).  Both live in one grow-only
+ *   SGEMM_EMU_PRESPLIT_B asks for it whenever M and K' N allow).  Where B is
+ *   split so and N >= 4096 (each A element would be split again in each of
+ *   the N / 128 tile columns), with K % 64 == 0 and M K <= 2^28, A is split
+ *   into workspace planes too (6 M K more bytes) and a kernel that copies
+ *   both operands' planes runs (SGEMM_EMU_PRESPLIT_A asks for it whenever
+ *   those allow).  All ways give bitwise the same result.  GEMMs on small
+ *   tile grids also need a split-K buffer (see sgemm_emu_split_k).  All of
+ *   it lives in one grow-only
  *   workspace block per stream, which the stream's later calls reuse (stream
  *   order keeps them apart; an event recorded after each use orders the next
  *   user of the block, and calls from several host threads on one stream
@@ -131,14 +136,17 @@ enum sgemm_emu_flags {
                                        IEEE-754 FP32 (+-Inf where the emulation's Inf x 0 component
                                        gives NaN); other outputs are unchanged.  Costs one more read
                                        of A and B and a pooled (2 (M + N) + 1)-int buffer. */
-    SGEMM_EMU_PRESPLIT_B = 8        /* sgemm_emu_ex only: split FP32 B once into workspace planes
+    SGEMM_EMU_PRESPLIT_B = 8,       /* sgemm_emu_ex only: split FP32 B once into workspace planes
                                        whenever M >= 1024 and K' N <= 2^28, not only where the default
                                        expects it to be faster (same result, bitwise) */
+    SGEMM_EMU_PRESPLIT_A = 16       /* sgemm_emu_ex only: as SGEMM_EMU_PRESPLIT_B, and split FP32 A
+                                       into workspace planes too whenever K % 64 == 0 and M K <= 2^28,
+                                       not only for N >= 4096 (same result, bitwise) */
 };
 
 /*
  * sgemm_emu_ex -- sgemm_emu with flags (SGEMM_EMU_SPLIT_RNE,
- * SGEMM_EMU_IEEE_SPECIALS, SGEMM_EMU_PRESPLIT_B; other bits give
+ * SGEMM_EMU_IEEE_SPECIALS, SGEMM_EMU_PRESPLIT_B, SGEMM_EMU_PRESPLIT_A; other bits give
  * SGEMM_EMU_EINVAL).  With SGEMM_EMU_SPLIT_RNE both A and B are split
  * with the round-to-nearest rule: with all nine products the result is the
  * same emulated product up to FP32 rounding (both splits are exact); with

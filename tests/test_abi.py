@@ -108,8 +108,9 @@ def test_split_validation(L):
 
 def test_ex_entry_flags(L):
     assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 2, None) == -1     # transpose is a split flag
-    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 16, None) == -1    # unknown flag
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 32, None) == -1    # unknown flag
     assert L.sgemm_emu_ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 5, 8 | 1, None) == 0  # pre-split B flag: empty
+    assert L.sgemm_emu_ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 5, 16 | 1, None) == 0  # pre-split A flag: empty
     assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 0, 1, None) == -1     # nbands
     assert L.sgemm_emu_ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 5, 1, None) == 0      # empty
     assert L.split_f32_bf16x3_ex(4, 4, P, 4, P, P, P, 4, 4, None) == -1    # unknown flag

@@ -52,6 +52,8 @@ def run(fe, A, B, nbands=5, entry="fused", ldc_pad=0, a_offset=0):
         fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, max(K, 1), fe.SGEMM_EMU_B_NK, Cd, max(ldc, 1), nbands)
     elif entry == "fused_ws":
         fe.sgemm_emu_ex(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1), nbands, fe.SGEMM_EMU_PRESPLIT_B)
+    elif entry == "fused_ws_a":
+        fe.sgemm_emu_ex(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1), nbands, fe.SGEMM_EMU_PRESPLIT_A)
     elif nbands == 5 and entry == "fused":
         fe.sgemm_bf16x9(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1))
     else:
@@ -153,6 +155,81 @@ def test_fp32_b_workspace_path(fe, shape):
         assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
     if fe.sgemm_emu_split_k(M, N, kpad) == 1:
         assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, 5).view(np.uint32))
+
+
+AB_SHAPES = [(1024, 130, 64), (1100, 257, 128), (1500, 1000, 512), (2048, 64, 192), (1030, 300, 1024)]
+
+
+@pytest.mark.parametrize("shape", AB_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp32_a_and_b_workspace_path(fe, shape):
+    """SGEMM_EMU_PRESPLIT_A: A is split once into M x K planes beside B's N x K
+    planes and the plane kernel copies both (no split in the kernel).  Within
+    the FP64 bound, and bit for bit the B-only workspace path (the same split,
+    tiles, MFMA order and, on small grids, the same K slices) and the
+    in-kernel split of A."""
+    M, N, K = shape
+    g = _rng(M + 5 * N + 13 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="fused_ws_a")
+    check_against_fp64(C, A, B, label=f"A and B workspace {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_ws").view(np.uint32))
+    if fe.sgemm_emu_split_k(M, N, K) == 1:
+        assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
+
+
+@pytest.mark.parametrize("nbands", [1, 2, 3, 4])
+def test_fp32_a_and_b_workspace_path_bands(fe, nbands):
+    M, N, K = 1030, 200, 128
+    g = _rng(910 + nbands)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, nbands, "fused_ws_a")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, nbands, "fused_ws").view(np.uint32))
+
+
+def test_fp32_a_and_b_workspace_path_rne(fe):
+    M, N, K = 1100, 260, 256
+    g = _rng(920)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    for nbands in (5, 2):
+        C = _run_ex(fe, A, B, nbands, fe.SGEMM_EMU_SPLIT_RNE | fe.SGEMM_EMU_PRESPLIT_A)
+        W = _run_ex(fe, A, B, nbands, fe.SGEMM_EMU_SPLIT_RNE | fe.SGEMM_EMU_PRESPLIT_B)
+        assert np.array_equal(C.view(np.uint32), W.view(np.uint32)), f"nbands={nbands}"
+
+
+@pytest.mark.parametrize("nbands", [5, 3, 1])
+def test_fp32_a_and_b_workspace_exact_class_vs_oracle(fe, orc, nbands):
+    """Through the plane kernel, elements whose band sums are exact in any order
+    equal the oracle emulation bit for bit."""
+    g = _rng(930)
+    M, N, K = 1024, 36, 64
+
+    def draw(shape):
+        m = g.integers(1 << 15, 1 << 16, size=shape).astype(np.float64)
+        return (m * np.where(g.integers(0, 2, size=shape) == 1, -1.0, 1.0)).astype(np.float32)
+
+    A, B = draw((M, K)), draw((K, N))
+    mask = exact_class_mask(A, B)
+    assert mask.mean() > 0.3
+    C = run(fe, A, B, nbands, "fused_ws_a")
+    E = orc.gemm_emu(A, B, nbands)
+    assert np.array_equal(C.view(np.uint32)[mask], E.view(np.uint32)[mask])
+
+
+def test_presplit_a_rule_at_4096_columns(fe):
+    """sgemm_bf16x9 with N >= 4096 (and the B workspace rule met) splits A into
+    planes as well by default: within the bound on sampled rows, and bit for bit
+    the caller-split N x K planes whose kernel splits A itself."""
+    M, N, K = 1024, 4096, 192
+    g = _rng(940)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="fused")
+    rows = np.sort(g.choice(M, size=32, replace=False))
+    check_against_fp64(C[rows], A, B, rows=rows, label="A pre-split rule")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
 
 
 @pytest.mark.parametrize("nbands", [1, 2, 3, 4])
@@ -545,15 +622,16 @@ def test_rne_split_identity_exact_and_smaller_ablation_error(fe, orc):
 
 # ---------------------------------------------------------------- IEEE fix-up of non-finite inputs
 
-@pytest.mark.parametrize("extra", [0, 8], ids=["default", "presplit"])
+@pytest.mark.parametrize("extra", [0, 8, 16], ids=["default", "presplit", "presplit_a"])
 @pytest.mark.parametrize("shape", [(48, 40, 70), (1030, 300, 128), (200, 140, 1024)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_ieee_specials_fixup(fe, orc, shape, extra):
     """SGEMM_EMU_IEEE_SPECIALS: outputs whose row of A or column of B holds an Inf
     or NaN equal the oracle's plain FP32 dot product bit for bit (+-Inf where the
     emulation gives NaN); all other outputs equal the emulation's.  `extra` = 8
-    (SGEMM_EMU_PRESPLIT_B) runs both through the workspace planes where M allows."""
-    assert extra in (0, fe.SGEMM_EMU_PRESPLIT_B)
+    (SGEMM_EMU_PRESPLIT_B) runs both through the workspace planes where M allows,
+    16 (SGEMM_EMU_PRESPLIT_A) also A's planes where K allows."""
+    assert extra in (0, fe.SGEMM_EMU_PRESPLIT_B, fe.SGEMM_EMU_PRESPLIT_A)
     M, N, K = shape
     g = _rng(M + N + K + 5)
     A = g.standard_normal((M, K)).astype(np.float32)
