@@ -40,8 +40,8 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "4660bddbf60e1203ce6da771e0f385694664370e3ce89bcef7af4e3b49cea320",
-                "bytes_per_launch": [2843993344, 3264154752]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "edd8fa5e77203c0d71e15af9a0e785b440c843e9609a3bb17906497175ed70e2",
+                "bytes_per_launch": [2843967260, 3264076805]}
 
 # MFMA activity of the same launches, from one rocprofv3 --pmc run of the same
 # probe (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE).
@@ -51,8 +51,8 @@ GEMM_TRAFFIC = {"gemm_hip_sha256": "4660bddbf60e1203ce6da771e0f385694664370e3ce8
 # divided by the kernel's own time in this run gives the shader clock the chip
 # held under the load; roofline.frac = busy x clock / 2.4 GHz.
 GEMM_MFMA_PMC = {"gemm_hip_sha256": GEMM_TRAFFIC["gemm_hip_sha256"],
-                 "mfma_busy": [0.6396, 0.7160],
-                 "active_cycles_per_xcd": [3903776, 3478247]}
+                 "mfma_busy": [0.6444, 0.7166],
+                 "active_cycles_per_xcd": [3874693, 3475354]}
 
 
 def log(msg):
