@@ -313,10 +313,19 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
                           (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !(rne && kpad != K) &&
                           (force_presplit || gemm_split_count(M, N, kpad, nbands, num_cus) > 1 ||
                            2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
-    const size_t plane = presplit ? (size_t)N * (size_t)kpad * sizeof(uint16_t) : 0;
+    // K x N planes, by the same rule: transposed once into N x K' planes in the
+    // workspace, so the LDS-DMA kernel runs instead of the kernel that stages
+    // K x N planes through registers (same planes and products, same order:
+    // bitwise the same result).
+    const bool transpose_kn = bsrc == B_PLANES_KN && M >= kPresplitMinRows &&
+                              (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !rne &&
+                              (gemm_split_count(M, N, kpad, nbands, num_cus) > 1 ||
+                               2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
+    const size_t plane = (presplit || transpose_kn) ? (size_t)N * (size_t)kpad * sizeof(uint16_t) : 0;
     const size_t plane_pad = (plane + 255) & ~(size_t)255;
     // A as well (K needs no padding; A's planes are M x K, k contiguous).
-    const bool presplit_a = presplit && kpad == K && (uint64_t)M * (uint64_t)K <= kPresplitMaxElems &&
+    const bool presplit_a = (presplit || transpose_kn) && kpad == K &&
+                            (uint64_t)M * (uint64_t)K <= kPresplitMaxElems &&
                             (force_presplit_a || N >= kPresplitAMinCols);
     const size_t aplane = presplit_a ? (size_t)M * (size_t)K * sizeof(uint16_t) : 0;
     const size_t aplane_pad = (aplane + 255) & ~(size_t)255;
@@ -324,8 +333,8 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // Grids that would leave CUs idle on the N x K DMA kernel are split along
     // K: each (tile, K slice) recombines its own bands and writes the result to
     // a partial buffer; a reduction kernel adds the slices in order.
-    const bool dma = presplit || (bsrc == B_PLANES_NK && gemm_uses_dma(K, ldb, B0, B1, B2));
-    const int sl = dma ? gemm_split_count(M, N, presplit ? kpad : K, nbands, num_cus) : 1;
+    const bool dma = presplit || transpose_kn || (bsrc == B_PLANES_NK && gemm_uses_dma(K, ldb, B0, B1, B2));
+    const int sl = dma ? gemm_split_count(M, N, (presplit || transpose_kn) ? kpad : K, nbands, num_cus) : 1;
     const size_t part_bytes = sl > 1 ? (size_t)sl * (size_t)M * (size_t)N * sizeof(float) : 0;
 
     // The stream's workspace block holds the planes and the partials; without
@@ -338,6 +347,15 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
         uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
                  *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
         const hipError_t e = launch_split_transpose(K, N, B, ldb, P0, P1, P2, kpad, num_cus, stream, rne, kpad);
+        if (e != hipSuccess) return launched(e);
+        g.B0 = P0; g.B1 = P1; g.B2 = P2; g.ldb = kpad;
+        g.K = kpad;
+        bsrc = B_PLANES_NK;
+    }
+    if (ws != nullptr && transpose_kn) {
+        uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
+                 *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
+        const hipError_t e = launch_transpose_planes(K, N, B0, B1, B2, ldb, P0, P1, P2, kpad, kpad, stream);
         if (e != hipSuccess) return launched(e);
         g.B0 = P0; g.B1 = P1; g.B2 = P2; g.ldb = kpad;
         g.K = kpad;

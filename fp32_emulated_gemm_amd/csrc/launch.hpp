@@ -51,6 +51,12 @@ hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, in
                                   uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream,
                                   bool rne = false, int64_t rows_out = 0);
 
+// Three BF16 planes rows x cols (ldp) -> cols x rows_out (ldq), zero past
+// rows; rows_out and ldq multiples of 8, 16-byte aligned outputs.
+hipError_t launch_transpose_planes(int64_t rows, int64_t cols, const uint16_t *P0, const uint16_t *P1,
+                                   const uint16_t *P2, int64_t ldp, uint16_t *Q0, uint16_t *Q1, uint16_t *Q2,
+                                   int64_t ldq, int64_t rows_out, hipStream_t stream);
+
 // rne: the in-kernel split of A (and of FP32 B) rounds to nearest even; only
 // B_FP32 and B_PLANES_NK (DMA kernel) support it.
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne = false);

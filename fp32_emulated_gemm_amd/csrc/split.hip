@@ -131,6 +131,69 @@ static hipError_t split_transpose_with(int64_t rows, int64_t cols, const float *
     return hipGetLastError();
 }
 
+// Transpose three BF16 planes: P (rows x cols, leading dimension ldp) -> Q
+// (cols x rows_out, leading dimension ldq), Q[c][r] = P[r][c] for r < rows and
+// zero for rows <= r < rows_out (K x N planes of B into the N x K' layout of
+// the DMA kernel).  One workgroup per 64 x 64 tile of Q's index space: each
+// wave reads 128-byte runs of P's rows, the tile goes through LDS, and four
+// neighbouring lanes write one 128-byte run of a row of Q.
+constexpr int kPT = 64;
+
+__global__ __launch_bounds__(256) void transpose_planes_kernel(
+    const uint16_t *__restrict__ P0, const uint16_t *__restrict__ P1, const uint16_t *__restrict__ P2, int64_t ldp,
+    uint16_t *__restrict__ Q0, uint16_t *__restrict__ Q1, uint16_t *__restrict__ Q2, int64_t ldq, int64_t rows,
+    int64_t rows_out, int64_t cols, int64_t tiles_c)
+{
+    __shared__ uint16_t tile[3][kPT][kPT + 2];
+    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kPT;
+    const int64_t c0 = (int64_t)(blockIdx.x % tiles_c) * kPT;
+    const int tid = threadIdx.x;
+    const uint16_t *P[3] = {P0, P1, P2};
+    {
+        const int c = tid & (kPT - 1);
+        const bool col_in = c0 + c < cols;
+#pragma unroll
+        for (int i = 0; i < kPT / 4; ++i) {
+            const int r = (tid >> 6) + 4 * i;
+            const bool in = col_in && r0 + r < rows;
+#pragma unroll
+            for (int p = 0; p < 3; ++p) tile[p][r][c] = in ? P[p][(r0 + r) * ldp + c0 + c] : (uint16_t)0;
+        }
+    }
+    __syncthreads();
+    uint16_t *Q[3] = {Q0, Q1, Q2};
+    const int n = tid >> 2, q = tid & 3;         // row of Q in the tile, quarter of its 64 elements
+    if (c0 + n >= cols) return;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int rb = 16 * q + 8 * h;       // first of 8 consecutive elements of Q's row
+            if (r0 + rb >= rows_out) continue;   // rows_out % 8 == 0: groups are whole
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = (uint32_t)tile[p][rb + 2 * e][n] | ((uint32_t)tile[p][rb + 2 * e + 1][n] << 16);
+            *reinterpret_cast<uint4 *>(Q[p] + (c0 + n) * ldq + r0 + rb) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+hipError_t launch_transpose_planes(int64_t rows, int64_t cols, const uint16_t *P0, const uint16_t *P1,
+                                   const uint16_t *P2, int64_t ldp, uint16_t *Q0, uint16_t *Q1, uint16_t *Q2,
+                                   int64_t ldq, int64_t rows_out, hipStream_t stream)
+{
+    if (rows_out < rows || rows_out % 8 != 0 || ldq % 8 != 0 || ldq < rows_out || !aligned(Q0, 16) ||
+        !aligned(Q1, 16) || !aligned(Q2, 16))
+        return hipErrorInvalidValue;
+    if (rows_out == 0 || cols == 0) return hipSuccess;
+    const int64_t tiles_c = (cols + kPT - 1) / kPT, tiles_r = (rows_out + kPT - 1) / kPT;
+    if (tiles_r > (int64_t)0x7FFFFFFF / tiles_c) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(transpose_planes_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, stream, P0, P1,
+                       P2, ldp, Q0, Q1, Q2, ldq, rows, rows_out, cols, tiles_c);
+    return hipGetLastError();
+}
+
 hipError_t launch_split_transpose(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0,
                                   uint16_t *X1, uint16_t *X2, int64_t ldo, int num_cus, hipStream_t stream, bool rne,
                                   int64_t rows_out)

@@ -173,8 +173,13 @@ enum sgemm_emu_b_layout {
  * as the linear layers of an interatomic potential do).  B0, B1, B2 are uint16
  * BF16 bit patterns in the layout given by b_layout, with leading dimension
  * ldb >= max(1, N) for SGEMM_EMU_B_KN and ldb >= max(1, K) for SGEMM_EMU_B_NK.
- * A is split inside the kernel.  The result equals sgemm_emu on the FP32 B
- * bit for bit.  An unknown b_layout gives SGEMM_EMU_EINVAL.
+ * A is split inside the kernel (and, for N >= 4096, into workspace planes as
+ * for sgemm_bf16x9).  SGEMM_EMU_B_KN planes are copied once, transposed, into
+ * N x K' workspace planes (6 K' N bytes; zero past K) where sgemm_bf16x9
+ * would pre-split an FP32 B of this shape, since the kernel for N x K planes
+ * copies them into LDS without passing through registers.  The result equals
+ * sgemm_emu on the FP32 B bit for bit either way.  An unknown b_layout gives
+ * SGEMM_EMU_EINVAL.
  */
 int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
                          const float *A, int64_t lda,

@@ -232,6 +232,36 @@ def test_presplit_a_rule_at_4096_columns(fe):
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
 
 
+KN_SHAPES = [(2048, 2048, 2048), (1024, 300, 1024), (1030, 300, 1000), (1100, 4096, 128)]
+
+
+@pytest.mark.parametrize("shape", KN_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_kn_planes_transposed_into_workspace(fe, shape):
+    """K x N planes where the workspace rule holds (2 M N K >= 1.2e10, or a grid
+    small enough for split-K): copied, transposed, into N x K' workspace planes
+    (zero past K) for the LDS-DMA kernel.  Within the bound on sampled rows and
+    bit for bit the FP32 B workspace path, which runs the same kernel, K slices
+    and (for N >= 4096) the same A planes."""
+    M, N, K = shape
+    g = _rng(M + 7 * N + 3 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="presplit")
+    rows = np.sort(g.choice(M, size=48, replace=False))
+    check_against_fp64(C[rows], A, B, rows=rows, label=f"K x N planes {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_ws").view(np.uint32))
+
+
+@pytest.mark.parametrize("nbands", [1, 3])
+def test_kn_planes_transposed_bands(fe, nbands):
+    M, N, K = 1024, 300, 1024
+    g = _rng(950 + nbands)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    assert np.array_equal(run(fe, A, B, nbands, "presplit").view(np.uint32),
+                          run(fe, A, B, nbands, "fused_ws").view(np.uint32))
+
+
 @pytest.mark.parametrize("nbands", [1, 2, 3, 4])
 def test_fp32_b_workspace_path_bands(fe, nbands):
     M, N, K = 1030, 200, 128
