@@ -199,6 +199,26 @@ def test_fp32_a_and_b_workspace_path_rne(fe):
         assert np.array_equal(C.view(np.uint32), W.view(np.uint32)), f"nbands={nbands}"
 
 
+@pytest.mark.parametrize("pad", [4, 5])
+def test_fp32_a_and_b_workspace_padded_lda(fe, pad):
+    """A with lda = K + pad and NaN in every gap between rows, through the A
+    split into workspace planes: the gaps never reach the planes, so the result
+    equals the compact layout's bit for bit (pad = 5 also leaves A's rows
+    without 16-byte alignment, which the split's scalar path takes)."""
+    M, N, K = 1100, 300, 128
+    g = _rng(960 + pad)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    lda = K + pad
+    Apad = np.full((M, lda), np.nan, np.float32)
+    Apad[:, :K] = A
+    Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    print(f"gemm ex padded lda={lda} M={M} N={N} K={K}", flush=True, file=sys.stderr)
+    fe.sgemm_emu_ex(M, N, K, dev(Apad), lda, dev(B), N, Cd, N, 5, fe.SGEMM_EMU_PRESPLIT_A)
+    C = host(Cd)
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_ws_a").view(np.uint32))
+
+
 @pytest.mark.parametrize("nbands", [5, 3, 1])
 def test_fp32_a_and_b_workspace_exact_class_vs_oracle(fe, orc, nbands):
     """Through the plane kernel, elements whose band sums are exact in any order
