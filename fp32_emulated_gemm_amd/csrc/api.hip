@@ -323,8 +323,10 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
                                2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
     const size_t plane = (presplit || transpose_kn) ? (size_t)N * (size_t)kpad * sizeof(uint16_t) : 0;
     const size_t plane_pad = (plane + 255) & ~(size_t)255;
-    // A as well (K needs no padding; A's planes are M x K, k contiguous).
-    const bool presplit_a = (presplit || transpose_kn) && kpad == K &&
+    // A as well (K needs no padding; A's planes are M x K, k contiguous), also
+    // beside a caller's N x K planes that the DMA kernel reads as they are.
+    const bool nk_dma = bsrc == B_PLANES_NK && gemm_uses_dma(K, ldb, B0, B1, B2);
+    const bool presplit_a = (presplit || transpose_kn || (nk_dma && M >= kPresplitMinRows)) && kpad == K &&
                             (uint64_t)M * (uint64_t)K <= kPresplitMaxElems &&
                             (force_presplit_a || N >= kPresplitAMinCols);
     const size_t aplane = presplit_a ? (size_t)M * (size_t)K * sizeof(uint16_t) : 0;
@@ -333,7 +335,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // Grids that would leave CUs idle on the N x K DMA kernel are split along
     // K: each (tile, K slice) recombines its own bands and writes the result to
     // a partial buffer; a reduction kernel adds the slices in order.
-    const bool dma = presplit || transpose_kn || (bsrc == B_PLANES_NK && gemm_uses_dma(K, ldb, B0, B1, B2));
+    const bool dma = presplit || transpose_kn || nk_dma;
     const int sl = dma ? gemm_split_count(M, N, (presplit || transpose_kn) ? kpad : K, nbands, num_cus) : 1;
     const size_t part_bytes = sl > 1 ? (size_t)sl * (size_t)M * (size_t)N * sizeof(float) : 0;
 
@@ -341,7 +343,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // one the GEMM splits B itself and runs one unit per tile.
     WsLease lease;
     void *ws = nullptr;
-    if (plane_pad + part_bytes > 0)
+    if (plane_pad + part_bytes + aplane_pad > 0)
         ws = acquire_workspace(dev, stream, 3 * plane_pad + part_bytes + 3 * aplane_pad, lease);
     if (ws != nullptr && presplit) {
         uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),

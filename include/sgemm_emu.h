@@ -173,8 +173,10 @@ enum sgemm_emu_b_layout {
  * as the linear layers of an interatomic potential do).  B0, B1, B2 are uint16
  * BF16 bit patterns in the layout given by b_layout, with leading dimension
  * ldb >= max(1, N) for SGEMM_EMU_B_KN and ldb >= max(1, K) for SGEMM_EMU_B_NK.
- * A is split inside the kernel (and, for N >= 4096, into workspace planes as
- * for sgemm_bf16x9).  SGEMM_EMU_B_KN planes are copied once, transposed, into
+ * A is split inside the kernel, or, with M >= 1024, N >= 4096, K % 64 == 0
+ * and M K <= 2^28 (and planes the LDS-DMA kernel takes: N x K, or K x N
+ * copied as below), once into M x K workspace planes as for sgemm_bf16x9
+ * (6 M K bytes).  SGEMM_EMU_B_KN planes are copied once, transposed, into
  * N x K' workspace planes (6 K' N bytes; zero past K) where sgemm_bf16x9
  * would pre-split an FP32 B of this shape, since the kernel for N x K planes
  * copies them into LDS without passing through registers.  The result equals

@@ -239,17 +239,21 @@ def test_fp32_a_and_b_workspace_exact_class_vs_oracle(fe, orc, nbands):
 
 
 def test_presplit_a_rule_at_4096_columns(fe):
-    """sgemm_bf16x9 with N >= 4096 (and the B workspace rule met) splits A into
-    planes as well by default: within the bound on sampled rows, and bit for bit
-    the caller-split N x K planes whose kernel splits A itself."""
-    M, N, K = 1024, 4096, 192
+    """With N >= 4096 (M >= 1024, K % 64 == 0) A is split into workspace planes
+    by default, for FP32 B (sgemm_bf16x9) and beside a caller's N x K planes
+    alike: within the bound on sampled rows, and bit for bit the N x K planes
+    run in row blocks below 1024 rows, where the kernel splits A itself."""
+    M, N, K = 1100, 4096, 192
     g = _rng(940)
     A = g.standard_normal((M, K)).astype(np.float32)
     B = g.standard_normal((K, N)).astype(np.float32)
     C = run(fe, A, B, entry="fused")
     rows = np.sort(g.choice(M, size=32, replace=False))
     check_against_fp64(C[rows], A, B, rows=rows, label="A pre-split rule")
-    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
+    Cnk = run(fe, A, B, entry="presplit_t")
+    blocks = np.concatenate([run(fe, A[i:i + 550], B, entry="presplit_t") for i in range(0, M, 550)])
+    assert np.array_equal(C.view(np.uint32), Cnk.view(np.uint32))
+    assert np.array_equal(C.view(np.uint32), blocks.view(np.uint32))
 
 
 KN_SHAPES = [(2048, 2048, 2048), (1024, 300, 1024), (1030, 300, 1000), (1100, 4096, 128)]
