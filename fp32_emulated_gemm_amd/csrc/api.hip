@@ -338,13 +338,14 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     const bool dma = presplit || transpose_kn || nk_dma;
     const int sl = dma ? gemm_split_count(M, N, (presplit || transpose_kn) ? kpad : K, nbands, num_cus) : 1;
     const size_t part_bytes = sl > 1 ? (size_t)sl * (size_t)M * (size_t)N * sizeof(float) : 0;
+    const size_t part_pad = (part_bytes + 255) & ~(size_t)255;   // keeps A's planes 256-byte aligned
 
     // The stream's workspace block holds the planes and the partials; without
     // one the GEMM splits B itself and runs one unit per tile.
     WsLease lease;
     void *ws = nullptr;
-    if (plane_pad + part_bytes + aplane_pad > 0)
-        ws = acquire_workspace(dev, stream, 3 * plane_pad + part_bytes + 3 * aplane_pad, lease);
+    if (plane_pad + part_pad + aplane_pad > 0)
+        ws = acquire_workspace(dev, stream, 3 * plane_pad + part_pad + 3 * aplane_pad, lease);
     if (ws != nullptr && presplit) {
         uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
                  *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
@@ -369,8 +370,9 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
         g.ldp = N;
     }
     if (ws != nullptr && presplit_a) {
-        char *const a_ws = (char *)ws + 3 * plane_pad + part_bytes;
-        uint16_t *Q0 = (uint16_t *)a_ws, *Q1 = (uint16_t *)(a_ws + aplane_pad), *Q2 = (uint16_t *)(a_ws + 2 * aplane_pad);
+        char *const a_ws = (char *)ws + 3 * plane_pad + part_pad;
+        uint16_t *Q0 = (uint16_t *)a_ws, *Q1 = (uint16_t *)(a_ws + aplane_pad),
+                 *Q2 = (uint16_t *)(a_ws + 2 * aplane_pad);
         hipError_t e = launch_split(M, K, A, lda, Q0, Q1, Q2, K, num_cus, stream, rne);
         if (e == hipSuccess) {
             g.A0 = Q0; g.A1 = Q1; g.A2 = Q2; g.lda = K;

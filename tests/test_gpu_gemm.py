@@ -157,7 +157,8 @@ def test_fp32_b_workspace_path(fe, shape):
         assert np.array_equal(C.view(np.uint32), _fused_in_row_blocks(fe, A, B, 5).view(np.uint32))
 
 
-AB_SHAPES = [(1024, 130, 64), (1100, 257, 128), (1500, 1000, 512), (2048, 64, 192), (1030, 300, 1024)]
+AB_SHAPES = [(1024, 130, 64), (1100, 257, 128), (1500, 1000, 512), (2048, 64, 192), (1030, 300, 1024),
+             (1025, 301, 768)]    # 3 K slices of an odd M N: partials end off a 16-byte boundary
 
 
 @pytest.mark.parametrize("shape", AB_SHAPES, ids=lambda s: "x".join(map(str, s)))
