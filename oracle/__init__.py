@@ -31,7 +31,6 @@ from . import build as _build
 
 _LIB = None
 
-ORC_FLUSH_PRODUCT_SUBNORMALS = 1
 ORC_SPLIT_RNE = 2            # gemm_emu / gemm_trunc_f64 flag: round-to-nearest split
 SPLIT_RZ, SPLIT_RNE = 0, 1   # split modes
 

@@ -198,8 +198,7 @@ int orc_sgemm_naive_f32(int64_t nrows, const int64_t *rows, int64_t N, int64_t K
     return ORC_OK;
 }
 
-/* Flags of the scalar emulation and the truncated-band value. */
-#define ORC_FLUSH_PRODUCT_SUBNORMALS 1  /* product below 2^-126 becomes +-0 (hardware model) */
+/* Flag of the scalar emulation and the truncated-band value (bit 0 is unused). */
 #define ORC_SPLIT_RNE 2                 /* split A and B with ORC_SPLIT_RNE_MODE */
 
 /*
@@ -225,7 +224,7 @@ int orc_gemm_emu(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
                  float *bands_out /* optional: 5 x nrows x N band sums */)
 {
     if (nrows < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return ORC_EINVAL;
-    if (nbands < 1 || nbands > 5) return ORC_EINVAL;
+    if (nbands < 1 || nbands > 5 || (flags & ~ORC_SPLIT_RNE) != 0) return ORC_EINVAL;
     const int smode = (flags & ORC_SPLIT_RNE) ? ORC_SPLIT_RNE_MODE : ORC_SPLIT_RZ_MODE;
 
     /* Step 1 for B: three component planes, each K x N, as FP32 values. */
@@ -259,8 +258,6 @@ int orc_gemm_emu(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
                     float *Ss = S + (size_t)s * N;
                     for (int64_t j = 0; j < N; ++j) {
                         float prod = ap * bq[j];                              /* step 2 */
-                        if ((flags & ORC_FLUSH_PRODUCT_SUBNORMALS) && fabsf(prod) < 0x1p-126f)
-                            prod = copysignf(0.0f, prod);
                         Ss[j] = Ss[j] + prod;                                 /* step 3 */
                     }
                 }
@@ -295,7 +292,7 @@ int orc_gemm_trunc_f64(int64_t nrows, const int64_t *rows, int64_t N, int64_t K,
                        double *T, int64_t ldt, int nbands, int flags)
 {
     if (nrows < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldt < N) return ORC_EINVAL;
-    if (nbands < 1 || nbands > 5) return ORC_EINVAL;
+    if (nbands < 1 || nbands > 5 || (flags & ~ORC_SPLIT_RNE) != 0) return ORC_EINVAL;
     const int smode = (flags & ORC_SPLIT_RNE) ? ORC_SPLIT_RNE_MODE : ORC_SPLIT_RZ_MODE;
     static const double weight[5] = {1.0, 0x1p-8, 0x1p-16, 0x1p-24, 0x1p-32};
     int rc = ORC_OK;

@@ -381,3 +381,39 @@ def test_rne_split_halves_the_dropped_mass(orc):
     e_rz = orc.gemm_trunc_f64(A, B, 2) - ref
     e_rne = orc.gemm_trunc_f64(A, B, 2, flags=orc.ORC_SPLIT_RNE) - ref
     assert np.sqrt(np.mean(e_rne ** 2)) < 0.5 * np.sqrt(np.mean(e_rz ** 2))
+
+
+def test_unknown_emulation_flag_rejected(orc):
+    """The emulation has one mode flag (the round-to-nearest split); any other bit
+    is an error rather than a silently different emulation."""
+    A = np.ones((2, 2), np.float32)
+    for bad in (1, 4, 1 << 30):
+        with pytest.raises(RuntimeError):
+            orc.gemm_emu(A, A, 5, flags=bad)
+        with pytest.raises(RuntimeError):
+            orc.gemm_trunc_f64(A, A, 5, flags=bad)
+
+
+def test_chunked_full_check_catches_one_bad_element(orc):
+    """The whole-output parity helper of the GPU tests, run on the oracle's own
+    emulation (passes) and on a copy with one element pushed just past the
+    elementwise bound in a late row chunk (fails)."""
+    import gpu_util
+    g = np.random.Generator(np.random.Philox(key=77))
+    A = g.standard_normal((300, 100)).astype(np.float32)
+    B = g.standard_normal((100, 50)).astype(np.float32)
+    C = orc.gemm_emu(A, B)
+    abl = {nb: orc.gemm_emu(A, B, nb) for nb in (4, 3, 2)}
+    seen = []
+    gpu_util.check_full("emu", A, B, C, ablations=abl, chunk_elems=50 * 64,
+                        keep_ref=lambda r0, r1, ref: seen.append((r0, r1)))
+    assert seen[0] == (0, 64) and seen[-1] == (256, 300)
+    ref, G = orc.gemm_f64(A, B)
+    bad = C.copy()
+    bad[290, 7] = np.float32(ref[290, 7] + 1.5 * gpu_util.elementwise_bound(100, G[290, 7]))
+    with pytest.raises(AssertionError, match="rows 256..299"):
+        gpu_util.check_full("emu", A, B, bad, chunk_elems=50 * 64)
+    bad = {**abl, 2: abl[2].copy()}
+    bad[2][5, 5] += np.float32(0.5)
+    with pytest.raises(AssertionError, match="nbands=2"):
+        gpu_util.check_full("emu", A, B, C, ablations=bad, chunk_elems=50 * 64)
