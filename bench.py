@@ -5,7 +5,7 @@ One step is one pass of the whole path over the large PET-like workload
 (17,280 atoms x 32 neighbour tokens = 552,960 rows, d = 256, FFN = 1024):
     split W1 [256 x 1024] and W2 [1024 x 256] into BF16 planes   (standalone split)
     C1 = X [552960 x 256]  . W1     (A split inside the GEMM, nine products)
-    C2 = H [552960 x 1024] . W2
+    C2 = H [552960 x 1024] . W2     (H = GELU(X W1), computed once before timing)
 Inputs are seeded synthetic data already resident in HBM when timing starts.
 Reported value: effective FP32 TFLOP/s = (2 M N1 K1 + 2 M N2 K2) / t_step.
 
@@ -67,6 +67,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip torch.matmul / fused-B context timings")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--calibrate", action="store_true",
+                   help="only time the platform's BF16 and FP32 GEMMs (torch.matmul) on the square and "
+                        "PET shapes and print them as one JSON line")
+    p.add_argument("--calibrate-reps", type=int, default=10)
     p.add_argument("--traffic-probe", action="store_true",
                    help="for HBM counter runs: two steps, one split of X, then one plain 2 GiB device copy "
                         "whose FETCH/WRITE counts calibrate the counters; prints no JSON line")
@@ -79,6 +83,9 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate:
+        calibrate(args.calibrate_reps)
+        return
 
     import numpy as np
     import torch
@@ -93,11 +100,10 @@ def main():
     t0 = time.perf_counter()
     w = workloads.pet_large()
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
-    X, W1, W2, H = w["X"], w["W1"], w["W2"], w["H"]
+    X, W1, W2 = w["X"], w["W1"], w["W2"]
     M, D = X.shape
     F = W1.shape[1]
     Xd = torch.from_numpy(X).to(dev)
-    Hd = torch.from_numpy(H).to(dev)
     W1d = torch.from_numpy(W1).to(dev)
     W2d = torch.from_numpy(W2).to(dev)
     # The weights as a linear layer stores them, [out_features][in_features].
@@ -109,6 +115,13 @@ def main():
     P2 = [torch.empty((D, F), dtype=torch.int16, device=dev) for _ in range(3)]
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
+    # The hidden layer H = GELU(X W1), chained as in the network: computed once,
+    # before timing, by the library's linear layer with its fused GELU epilogue
+    # (within a few ulp of fp32(GELU) of the exact product).
+    Hd = torch.empty((M, F), dtype=torch.float32, device=dev)
+    fe.split_f32_bf16x3(F, D, W1t, D, *P1, D, sp)
+    fe.sgemm_emu_linear(M, F, D, Xd, D, *P1, D, None, fe.SGEMM_EMU_ACT_GELU, Hd, F, 5, sp)
+    torch.cuda.synchronize()
 
     ev = []
 
@@ -191,15 +204,13 @@ def main():
     if not rel < 1e-5:
         raise SystemExit(f"bench: output check failed (relative error {rel:.3g})")
 
-    probe = mfma_probe(torch, stream)
-
     context = None
     if not args.no_context:
         context = context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp)
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(X, W1, H, W2, args.cpu_seconds)
+        cpu = cpu_baseline(X, W1, Hd.cpu().numpy(), W2, args.cpu_seconds)
 
     out = {
         "metric": METRIC,
@@ -216,8 +227,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "pet_large: X[552960x256] @ W1[256x1024] and H[552960x1024] @ W2[1024x256] "
-                        "(17280 atoms x 32 tokens), weights held [out][in] and split once per step, "
-                        "all nine products",
+                        "(17280 atoms x 32 tokens), H = GELU(X W1) chained once before timing, "
+                        "weights held [out][in] and split once per step, all nine products",
             "M": M, "d": D, "ffn": F, "nbands": 5,
             "entry": "split_f32_bf16x3 + sgemm_emu_presplit_b(SGEMM_EMU_B_NK)",
         },
@@ -240,8 +251,6 @@ def main():
             "flops_per_launch": bf16_flops_per_launch,
             "mfma_busy_per_launch_pmc": mfma_busy,
             "sclk_ghz_under_load": sclk,
-            "probe_mfma_only_tflops": probe,
-            "frac_of_probe_random_operands": round(achieved / probe["random_operands"], 4),
         },
         "cpu_baseline": cpu,
         "context": context,
@@ -270,38 +279,58 @@ def timed(fn, stream, reps):
     return a.elapsed_time(b) / reps
 
 
-def mfma_probe(torch, stream):
-    """The practical ceiling of the GEMM's instruction: BF16 TFLOP/s of a kernel
-    that only issues v_mfma_f32_32x32x16_bf16 (one workgroup of 8 waves per CU,
-    four independent accumulators), on random and on constant operand bits."""
-    import ctypes
-    L = ctypes.CDLL(os.path.join(HERE, "fp32_emulated_gemm_amd", "libsgemm_probe.so"))
-    L.sgemm_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    L.sgemm_probe_mfma.restype = ctypes.c_int
-    L.sgemm_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
-    L.sgemm_probe_mfma_flops.restype = ctypes.c_double
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    iters = 4000                                  # ~2-3 ms per launch
-    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
-    flops = L.sgemm_probe_mfma_flops(cus, iters)
+def vendor_bf16(torch, stream, shapes, reps=10):
+    """Context for the ceiling: the platform's own BF16 GEMM (torch.matmul on BF16
+    operands, i.e. hipBLASLt; run, never inspected) on the given M x N x K shapes,
+    random operands, HIP events on the same stream.  One BF16 product per FP32
+    multiply-add pair, so its rate compares with the roofline's achieved rate."""
     res = {}
-    for name, rnd in (("random_operands", 1), ("constant_operands", 0)):
-        def call():
-            rc = L.sgemm_probe_mfma(cus, iters, rnd, out.data_ptr(), stream.cuda_stream)
-            if rc != 0:
-                raise SystemExit(f"bench: MFMA probe failed with status {rc}")
-        t = timed(call, stream, 5)
-        res[name] = round(flops / t / 1e9, 1)
-    if not bool(torch.isfinite(out).all()):
-        raise SystemExit("bench: MFMA probe produced non-finite sums")
-    log(f"MFMA-only probe: {res} TFLOP/s BF16 (nominal {MI355X_BF16_DENSE_TFLOPS})")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for name, (m, n, k) in shapes.items():
+        A = (torch.rand((m, k), device="cuda", generator=g) * 2 - 1).to(torch.bfloat16)
+        B = (torch.rand((k, n), device="cuda", generator=g) * 2 - 1).to(torch.bfloat16)
+        C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        t = timed(lambda: torch.matmul(A, B, out=C), stream, reps)
+        tf = 2.0 * m * n * k / t / 1e9
+        res[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / MI355X_BF16_DENSE_TFLOPS, 4)}
+        del A, B, C
+    log(f"vendor BF16 GEMM (torch.matmul, hipBLASLt): {res}")
     return res
+
+
+CALIBRATION_SHAPES = {"4096^3": (4096, 4096, 4096), "8192^3": (8192, 8192, 8192),
+                      "X@W1 552960x1024x256": (552960, 1024, 256), "H@W2 552960x256x1024": (552960, 256, 1024)}
+
+
+def calibrate(reps):
+    """--calibrate: the platform's BF16 and FP32 GEMMs on the square and PET shapes,
+    one JSON line (the ceiling the chip reaches with a vendor BF16 kernel on random
+    data; for rocprofv3 counter runs beside the emulated GEMM's)."""
+    import torch
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    bf16 = vendor_bf16(torch, stream, CALIBRATION_SHAPES, reps)
+    fp32 = {}
+    g = torch.Generator(device="cuda").manual_seed(8)
+    for name, (m, n, k) in CALIBRATION_SHAPES.items():
+        A = torch.rand((m, k), device="cuda", generator=g) * 2 - 1
+        B = torch.rand((k, n), device="cuda", generator=g) * 2 - 1
+        C = torch.empty((m, n), device="cuda")
+        t = timed(lambda: torch.matmul(A, B, out=C), stream, reps)
+        fp32[name] = round(2.0 * m * n * k / t / 1e9, 1)
+        del A, B, C
+    print(json.dumps({"calibration": "torch.matmul BF16 / FP32 (hipBLASLt), random operands",
+                      "reps": reps, "bf16": bf16, "fp32_tflops": fp32,
+                      "bf16_dense_peak_tflops": MI355X_BF16_DENSE_TFLOPS}), flush=True)
 
 
 def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     """torch.matmul FP32 and the fused-B entry point on the same GEMMs (context only)."""
     res = {}
     fl = 2.0 * M * F * D
+    # the platform's BF16 GEMM on the same shapes: one product per multiply-add
+    # (memory-bound here), against the emulation's nine on the same bytes
+    res["torch_bf16_same_shapes"] = vendor_bf16(torch, stream, {"X@W1": (M, F, D), "H@W2": (M, D, F)}, 5)
     t = timed(lambda: torch.matmul(Xd, W1d, out=C1), stream, 5)
     res["torch_fp32_X@W1_tflops"] = round(fl / t / 1e9, 2)
     t = timed(lambda: torch.matmul(Hd, W2d, out=C2), stream, 5)

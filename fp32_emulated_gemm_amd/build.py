@@ -20,9 +20,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsgemm_emu.so")
 SOURCES = ["api.hip", "gemm.hip", "split.hip", "ieee.hip"]
-# The benchmark's matrix-pipe probe: its own library, not part of the GEMM ABI.
-PROBE_LIB = os.path.join(HERE, "libsgemm_probe.so")
-PROBE_SOURCE = "probe.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-mcode-object-version=5",
@@ -42,19 +39,17 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Always recompiles (each source in parallel, then one link per library);
-    returns the path of the GEMM library.  The probe library is built beside it."""
+    """Always recompiles (each source in parallel, then one link); returns the
+    path of the library."""
     with tempfile.TemporaryDirectory(prefix="sgemm_emu_build_") as tmpdir:
-        srcs = SOURCES + [PROBE_SOURCE]
-        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in srcs]
-        cmds = [[HIPCC, *FLAGS, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(srcs, objs)]
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[HIPCC, *FLAGS, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
         with ThreadPoolExecutor(max_workers=len(cmds)) as pool:
             for f in [pool.submit(_run, c, verbose) for c in cmds]:
                 f.result()
-        for lib, lib_objs in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
-            tmp = lib + ".tmp"
-            _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs], verbose)
-            os.replace(tmp, lib)
+        tmp = LIB + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+        os.replace(tmp, LIB)
     return LIB
 
 

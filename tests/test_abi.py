@@ -40,7 +40,7 @@ def test_single_hip_runtime_loaded(L):
 def test_products_and_strings(L):
     import fp32_emulated_gemm_amd as fe
     assert [fe.sgemm_emu_products(b) for b in range(0, 7)] == [-1, 1, 3, 6, 8, 9, -1]
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert fe.sgemm_emu_strerror(s) != "unknown status"
     assert fe.sgemm_emu_strerror(7) == "unknown status"
     assert "gfx950" in fe.sgemm_emu_version()
@@ -134,23 +134,7 @@ def test_valid_call_without_gpu_reports_arch(L):
         pytest.skip("a GPU is present")
     assert L.sgemm_bf16x9(4, 4, 4, P, 4, P, 4, P, 4, None) == -3
     assert L.split_f32_bf16x3(4, 4, P, 4, P, P, P, 4, None) == -3
-
-
-def test_probe_library_loads_and_validates():
-    """The benchmark's MFMA probe library (not part of the GEMM ABI): it loads,
-    exports its two functions, counts flops as documented, and rejects bad
-    arguments before any HIP call."""
-    import fp32_emulated_gemm_amd  # noqa: F401  (binds the HIP runtime torch loaded)
-    P = ctypes.CDLL(os.path.join(ROOT, "fp32_emulated_gemm_amd", "libsgemm_probe.so"))
-    P.sgemm_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    P.sgemm_probe_mfma.restype = ctypes.c_int
-    P.sgemm_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
-    P.sgemm_probe_mfma_flops.restype = ctypes.c_double
-    # 8 waves x 16 MFMAs x 32768 flops per iteration and workgroup
-    assert P.sgemm_probe_mfma_flops(3, 5) == 3 * 8 * 5 * 16 * 32768
-    assert P.sgemm_probe_mfma(0, 5, 1, None, None) == -1
-    assert P.sgemm_probe_mfma(1, 0, 1, None, None) == -1
-    assert P.sgemm_probe_mfma(1, 5, 1, None, None) == -1
+    assert L.sgemm_emu_release_workspace() == -3
 
 
 def test_leading_dimension_limit(L):
@@ -160,3 +144,37 @@ def test_leading_dimension_limit(L):
     assert L.sgemm_bf16x9(4, 4, 4, P, top + 1, P, 4, P, 4, None) == -1
     assert L.sgemm_bf16x9(4, 4, 4, P, 4, P, top + 1, P, 4, None) == -1
     assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, P, P, top + 1, 1, P, 4, 5, None) == -1
+    # the C stores of a 128-row tile use 32-bit offsets too: ldc and the linear
+    # layer's ldy have the same limit
+    assert L.sgemm_bf16x9(4, 4, 4, P, 4, P, 4, P, top + 1, None) == -1
+    assert L.sgemm_emu(4, 4, 4, P, 4, P, 4, P, top + 1, 5, None) == -1
+    assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, P, P, 4, 1, P, top + 1, 5, None) == -1
+    assert L.sgemm_emu_linear(4, 4, 4, P, 4, P, P, P, 4, None, 0, P, top + 1, 5, None) == -1
+
+
+def test_tensor_wrappers_reject_bad_tensors():
+    """The tensor conveniences check dtype, layout and device before the
+    library sees a pointer (a wrong tensor would otherwise be read out of
+    bounds on the GPU)."""
+    import torch
+    import fp32_emulated_gemm_amd as fe
+    a = torch.zeros((8, 8), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        fe.matmul(a.half(), a)                                  # float16 would be read at twice its size
+    with pytest.raises(TypeError):
+        fe.split(a.double())
+    with pytest.raises(ValueError):
+        fe.matmul(torch.zeros(8, dtype=torch.float32).expand(8, 8), a)   # broadcast rows overlap
+    with pytest.raises(ValueError):
+        fe.matmul(a.t(), a)                                     # column stride != 1
+    with pytest.raises(ValueError):
+        fe.split_t(torch.zeros((2, 4, 4)))                      # not 2-D
+    with pytest.raises(ValueError):
+        fe.matmul(a, a)                                         # host memory
+    planes = [torch.zeros((8, 8), dtype=torch.int16) for _ in range(3)]
+    with pytest.raises(TypeError):
+        fe.matmul_presplit(a, [planes[0], planes[1], planes[2].float()])
+    with pytest.raises(ValueError):
+        fe.matmul_presplit(a, [planes[0], planes[1], torch.zeros((8, 9), dtype=torch.int16)[:, :8]])
+    with pytest.raises(ValueError):
+        fe.matmul_presplit(a, planes[:2])
