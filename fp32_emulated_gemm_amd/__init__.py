@@ -13,13 +13,17 @@ memory and streams only.  The functions keep the C names and argument order:
     split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     split_f32_bf16x3_ex(rows, cols, X, ldx, X0, X1, X2, ldo, flags, stream=None)
     sgemm_emu_split_k(M, N, K, nbands)
+    sgemm_emu_release_workspace()
     sgemm_emu_products(nbands), sgemm_emu_strerror(status), sgemm_emu_version()
 
 Matrix arguments may be torch tensors (their data pointer is passed; they must
 live on the current HIP device) or raw integer device addresses.  `stream`
 defaults to torch's current stream.  A nonzero status raises SgemmEmuError.
 
-Convenience wrappers that allocate outputs: ``matmul``, ``split``.
+Convenience wrappers that allocate outputs: ``matmul``, ``matmul_presplit``,
+``split``, ``split_t``.  They check their tensors first (dtype, the current HIP
+device, 2-D row-major with non-overlapping rows, matching planes) and raise
+TypeError / ValueError before the library sees a pointer.
 
 The library links the same HIP runtime soname as PyTorch, so torch is imported
 first: the library then binds to the runtime torch already loaded and both see
@@ -39,6 +43,7 @@ SGEMM_EMU_EINVAL = -1
 SGEMM_EMU_ENULL = -2
 SGEMM_EMU_EARCH = -3
 SGEMM_EMU_ELAUNCH = -4
+SGEMM_EMU_ENOMEM = -5
 SGEMM_EMU_B_KN = 0   # pre-split planes K x N (split of B)
 SGEMM_EMU_B_NK = 1   # pre-split planes N x K (split of B^T, e.g. a weight stored [out][in])
 SGEMM_EMU_ACT_NONE = 0
@@ -51,7 +56,7 @@ SGEMM_EMU_PRESPLIT_A = 16      # flag (sgemm_emu_ex): split FP32 A (and B) once 
 
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_linear",
            "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
-           "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
+           "sgemm_emu_release_workspace", "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
 
 
 class SgemmEmuError(RuntimeError):
@@ -80,6 +85,7 @@ def lib():
         L.split_f32_bf16x3_transposed.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.split_f32_bf16x3_ex.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, ci, vp]
         L.sgemm_emu_split_k.argtypes = [i64, i64, i64, ci]
+        L.sgemm_emu_release_workspace.argtypes = []
         L.sgemm_emu_products.argtypes = [ci]
         L.sgemm_emu_strerror.argtypes = [ci]
         L.sgemm_emu_strerror.restype = ctypes.c_char_p
@@ -87,7 +93,7 @@ def lib():
         L.sgemm_emu_version.restype = ctypes.c_char_p
         for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_linear",
                   "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
-                  "sgemm_emu_products"):
+                  "sgemm_emu_release_workspace", "sgemm_emu_products"):
             getattr(L, n).restype = ci
         _LIB = L
     return _LIB
@@ -172,6 +178,10 @@ def sgemm_emu_split_k(M, N, K, nbands=5):
     return _ok(status, "sgemm_emu_split_k") if status < 0 else status
 
 
+def sgemm_emu_release_workspace():
+    return _ok(lib().sgemm_emu_release_workspace(), "sgemm_emu_release_workspace")
+
+
 def sgemm_emu_products(nbands):
     return lib().sgemm_emu_products(nbands)
 
@@ -186,55 +196,120 @@ def sgemm_emu_version():
 
 # ---------------------------------------------------------------- tensor conveniences
 
+_PLANE_DTYPES = (torch.int16, torch.bfloat16)
+_F32 = (torch.float32,)
+
+
+def _layout(t, name, dtypes):
+    """Leading dimension of t after checking that it is a 2-D row-major tensor of
+    one of `dtypes` whose rows do not overlap.  The library reads and writes
+    through raw pointers: a tensor that failed these checks would make it touch
+    memory the tensor does not own."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: expected dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D tensor, got {t.dim()} dimensions")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: expected unit stride along columns, got {t.stride(1)}")
+    if rows > 1 and t.stride(0) < max(cols, 1):
+        raise ValueError(f"{name}: rows overlap (row stride {t.stride(0)} < {cols} columns)")
+    return max(t.stride(0), cols, 1)
+
+
+def _on_device(*named):
+    """Every (name, tensor) must live on the current HIP device."""
+    for name, t in named:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: expected a tensor on the current HIP device, got {t.device}")
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{name}: expected a tensor on the current HIP device "
+                             f"(cuda:{torch.cuda.current_device()}), got {t.device}")
+
+
 def _ld(t):
-    """Leading dimension of a row-major 2-D tensor (unit stride along columns)."""
-    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
-        raise ValueError("expected a 2-D tensor with unit column stride")
-    return max(t.stride(0), t.size(1), 1)
+    """Leading dimension of a row-major 2-D FP32 tensor on the current device."""
+    ld = _layout(t, "tensor", _F32)
+    _on_device(("tensor", t))
+    return ld
+
+
+def _planes(parts, name):
+    """Layout of three BF16 component planes of one shape and leading dimension."""
+    if len(parts) != 3:
+        raise ValueError(f"{name}: expected three planes, got {len(parts)}")
+    lds = [_layout(p, f"{name}[{i}]", _PLANE_DTYPES) for i, p in enumerate(parts)]
+    if any(p.shape != parts[0].shape for p in parts) or len(set(lds)) != 1:
+        raise ValueError(f"{name}: the three planes differ in shape or leading dimension")
+    return lds[0]
+
+
+def _out(out, M, N, like):
+    """The output tensor (allocated on `like`'s device if None) and its leading dimension."""
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=like.device)
+    ld = _layout(out, "out", _F32)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out: expected shape {(M, N)}, got {tuple(out.shape)}")
+    return out, ld
 
 
 def matmul(A, B, nbands=5, out=None, stream=None):
     """C = A @ B for float32 CUDA tensors, through sgemm_emu (nbands=5: sgemm_bf16x9)."""
+    lda, ldb = _layout(A, "A", _F32), _layout(B, "B", _F32)
     M, K = A.shape
     K2, N = B.shape
     if K2 != K:
         raise ValueError("inner dimensions differ")
-    C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _on_device(("A", A), ("B", B))
+    C, ldc = _out(out, M, N, A)
+    _on_device(("out", C))
     if nbands == 5:
-        sgemm_bf16x9(M, N, K, A, _ld(A), B, _ld(B), C, _ld(C), stream)
+        sgemm_bf16x9(M, N, K, A, lda, B, ldb, C, ldc, stream)
     else:
-        sgemm_emu(M, N, K, A, _ld(A), B, _ld(B), C, _ld(C), nbands, stream)
+        sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream)
     return C
 
 
 def split(X, stream=None):
     """Three uint16 tensors (BF16 bit patterns, stored as int16) holding X's components."""
+    ldx = _layout(X, "X", _F32)
+    _on_device(("X", X))
     rows, cols = X.shape
     outs = [torch.empty((rows, cols), dtype=torch.int16, device=X.device) for _ in range(3)]
-    split_f32_bf16x3(rows, cols, X, _ld(X), outs[0], outs[1], outs[2], max(cols, 1), stream)
+    split_f32_bf16x3(rows, cols, X, ldx, outs[0], outs[1], outs[2], max(cols, 1), stream)
     return tuple(outs)
 
 
 def split_t(X, stream=None):
     """The components of X^T (cols x rows) as three int16 tensors, from X directly."""
+    ldx = _layout(X, "X", _F32)
+    _on_device(("X", X))
     rows, cols = X.shape
     outs = [torch.empty((cols, rows), dtype=torch.int16, device=X.device) for _ in range(3)]
-    split_f32_bf16x3_transposed(rows, cols, X, _ld(X), outs[0], outs[1], outs[2], max(rows, 1), stream)
+    split_f32_bf16x3_transposed(rows, cols, X, ldx, outs[0], outs[1], outs[2], max(rows, 1), stream)
     return tuple(outs)
 
 
 def matmul_presplit(A, Bparts, nbands=5, out=None, stream=None, b_layout=SGEMM_EMU_B_KN):
     """C = A @ B with B given as its three component planes (from `split`):
     planes of B (K x N) for SGEMM_EMU_B_KN, planes of B^T (N x K) for SGEMM_EMU_B_NK."""
+    lda = _layout(A, "A", _F32)
+    ldb = _planes(Bparts, "Bparts")
     M, K = A.shape
     if b_layout == SGEMM_EMU_B_KN:
         K2, N = Bparts[0].shape
-    else:
+    elif b_layout == SGEMM_EMU_B_NK:
         N, K2 = Bparts[0].shape
+    else:
+        raise ValueError(f"unknown b_layout {b_layout}")
     if K2 != K:
         raise ValueError("inner dimensions differ")
-    C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=A.device)
-    ldb = _ld(Bparts[0])
-    sgemm_emu_presplit_b(M, N, K, A, _ld(A), Bparts[0], Bparts[1], Bparts[2], ldb, b_layout, C, _ld(C),
+    _on_device(("A", A), *((f"Bparts[{i}]", p) for i, p in enumerate(Bparts)))
+    C, ldc = _out(out, M, N, A)
+    _on_device(("out", C))
+    sgemm_emu_presplit_b(M, N, K, A, lda, Bparts[0], Bparts[1], Bparts[2], ldb, b_layout, C, ldc,
                          nbands, stream)
     return C

@@ -283,8 +283,9 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     if ((rc = check_matrix(M, N, C, ldc, 4)) != SGEMM_EMU_OK) return rc;
     if (((uintptr_t)bias % 4) != 0) return SGEMM_EMU_EINVAL;
     if (act != SGEMM_EMU_ACT_NONE && act != SGEMM_EMU_ACT_GELU) return SGEMM_EMU_EINVAL;
-    // The kernels address one K step of a 128 x 128 tile with 32-bit byte offsets.
-    if (lda > kMaxTileLd || ldb > kMaxTileLd) return SGEMM_EMU_EINVAL;
+    // The kernels address one K step of a 128 x 128 tile, and the C stores of a
+    // 128-row tile, with 32-bit byte offsets.
+    if (lda > kMaxTileLd || ldb > kMaxTileLd || ldc > kMaxTileLd) return SGEMM_EMU_EINVAL;
     if (M == 0 || N == 0) return SGEMM_EMU_OK;
 
     int num_cus = 0, dev = 0;
@@ -340,12 +341,15 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     const size_t part_bytes = sl > 1 ? (size_t)sl * (size_t)M * (size_t)N * sizeof(float) : 0;
     const size_t part_pad = (part_bytes + 255) & ~(size_t)255;   // keeps A's planes 256-byte aligned
 
-    // The stream's workspace block holds the planes and the partials; without
-    // one the GEMM splits B itself and runs one unit per tile.
+    // The stream's workspace block holds the planes and the partials.  Without
+    // one the GEMM splits B itself (bitwise the same result); a K-split shape
+    // cannot run without its partial buffer (one pass per tile would round
+    // differently), so it reports SGEMM_EMU_ENOMEM with nothing enqueued.
     WsLease lease;
     void *ws = nullptr;
     if (plane_pad + part_pad + aplane_pad > 0)
         ws = acquire_workspace(dev, stream, 3 * plane_pad + part_pad + 3 * aplane_pad, lease);
+    if (ws == nullptr && sl > 1) return SGEMM_EMU_ENOMEM;
     if (ws != nullptr && presplit) {
         uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
                  *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
@@ -517,10 +521,51 @@ const char *sgemm_emu_strerror(int status)
     case SGEMM_EMU_ENULL: return "null pointer for a nonempty operand";
     case SGEMM_EMU_EARCH: return "no HIP device, or the current device is not gfx950";
     case SGEMM_EMU_ELAUNCH: return "kernel launch failed";
+    case SGEMM_EMU_ENOMEM: return "no device memory for the K-split partial sums";
     default: return "unknown status";
     }
 }
 
-const char *sgemm_emu_version(void) { return "libsgemm_emu 0.1.0 (gfx950, BF16x9)"; }
+int sgemm_emu_release_workspace(void)
+{
+    int num_cus = 0, dev = 0;
+    int rc;
+    if ((rc = current_device(&num_cus, &dev)) != SGEMM_EMU_OK) return rc;
+    hipError_t err = hipSuccess;
+    {
+        DeviceWs &D = g_ws[dev];
+        std::lock_guard<std::mutex> lock(D.mutex);
+        for (StreamWs &x : D.slot) {
+            if (!x.used) continue;
+            // the block's last user has finished with it before it is freed
+            if (x.recorded) {
+                const hipError_t e = hipEventSynchronize(x.done);
+                if (e != hipSuccess && err == hipSuccess) err = e;
+            }
+            if (x.ptr != nullptr) {
+                const hipError_t e = hipFreeAsync(x.ptr, nullptr);
+                if (e != hipSuccess && err == hipSuccess) err = e;
+            }
+            if (x.done != nullptr) (void)hipEventDestroy(x.done);
+            x = StreamWs{};
+        }
+        D.clock = 0;
+    }
+    const hipError_t e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    hipMemPool_t pool = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        if (g_devices[dev].pool_state == 1) pool = g_devices[dev].pool;
+    }
+    if (pool != nullptr) {
+        const hipError_t t = hipMemPoolTrimTo(pool, 0);
+        if (t != hipSuccess && err == hipSuccess) err = t;
+    }
+    (void)hipGetLastError();
+    return err == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_ELAUNCH;
+}
+
+const char *sgemm_emu_version(void) { return "libsgemm_emu 0.2.0 (gfx950, BF16x9)"; }
 
 }  // extern "C"

@@ -22,8 +22,12 @@
  *     acc = 2^-32 S4, acc = fma(S3, 2^-24, acc), acc = fma(S2, 2^-16, acc),
  *     acc = fma(S1, 2^-8, acc), C = acc + S0;
  *   - the order of additions inside a band is the matrix unit's; results are
- *     deterministic (no atomics, no split-K) but not bitwise equal to a
- *     sequential sum.
+ *     deterministic for a given shape, entry point and device (no atomics) but
+ *     not bitwise equal to a sequential sum.  Small tile grids split K into
+ *     slices (sgemm_emu_split_k): each slice runs the method on its K range and
+ *     the slices' FP32 results are added in slice order; if the device memory
+ *     for those partial sums cannot be had, the call returns SGEMM_EMU_ENOMEM
+ *     rather than round another way.
  *   - non-finite inputs follow IEEE rules on the components (Inf times a zero
  *     component is NaN), so results are not IEEE-754 SGEMM results for them.
  *
@@ -58,12 +62,14 @@
  *   streams; a ninth stream takes over the least recently used block.  The
  *   blocks come from a memory pool the library creates per device
  *   (hipMallocFromPoolAsync on the calling stream) and stay allocated until
- *   the process ends.  A stream being captured into a graph gets a block of
- *   its own per call instead (freed with hipFreeAsync in the graph).  If no
- *   workspace can be had the GEMM splits B inside its kernel (bitwise the
- *   same result) and runs one pass over K per tile (the one-pass rounding
- *   order of sgemm_emu_split_k's S = 1).  No other device memory is
- *   allocated (sgemm_emu_ex's IEEE fix-up aside, documented there).  The
+ *   sgemm_emu_release_workspace gives them back (or the process ends).  A
+ *   stream being captured into a graph gets a block of its own per call
+ *   instead (freed with hipFreeAsync in the graph).  If no workspace can be
+ *   had the GEMM splits B inside its kernel (bitwise the same result); a
+ *   small-grid shape whose K-split partial buffer cannot be had returns
+ *   SGEMM_EMU_ENOMEM with nothing enqueued, so the bits of a shape never
+ *   depend on the memory available.  No other device memory is allocated
+ *   (sgemm_emu_ex's IEEE fix-up aside, documented there).  The
  *   pool, the blocks and their events belong to the device's primary
  *   context: after hipDeviceReset the library must not be called again in
  *   that process.
@@ -94,7 +100,10 @@ enum sgemm_emu_status {
                                misaligned pointer, or a size whose byte offsets overflow */
     SGEMM_EMU_ENULL = -2,   /* null pointer for an operand with a nonzero extent */
     SGEMM_EMU_EARCH = -3,   /* no HIP device, or the current device is not gfx950 */
-    SGEMM_EMU_ELAUNCH = -4  /* the kernel launch itself failed (hipGetLastError) */
+    SGEMM_EMU_ELAUNCH = -4, /* the kernel launch itself failed (hipGetLastError), or a HIP call of
+                               sgemm_emu_release_workspace failed */
+    SGEMM_EMU_ENOMEM = -5   /* a GEMM on a small tile grid could not get device memory for its
+                               K-split partial sums (see sgemm_emu_split_k); nothing was enqueued */
 };
 
 /*
@@ -274,11 +283,27 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
  * device-memory conventions above); a reduction kernel adds the
  * S results in slice order, then the bias and activation.  Results differ in
  * rounding from the one-pass order (still within the same error bound) and
- * are deterministic for a given shape and device.  If no workspace can be
- * had the GEMM runs one pass per tile.  Returns S >= 1, or a negative
+ * are deterministic for a given shape and device.  If that workspace cannot
+ * be had the GEMM returns SGEMM_EMU_ENOMEM.  Returns S >= 1, or a negative
  * status (invalid sizes or nbands, no gfx950 device).
  */
 int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands);
+
+/*
+ * sgemm_emu_release_workspace -- gives back the workspace the library keeps on
+ * the current device (the per-stream blocks described at the top of this file)
+ * and trims the library's memory pool to zero, so the memory returns to the
+ * device.  The pages keep the caller in charge of memory ("inputs and outputs
+ * remain FP32", only the multiplication changes: NVIDIA blog, section "How
+ * Tensor Core FP32 closes the hardware gap"); this call hands the library's
+ * retained share back.  Waits on the host until the last call that used each
+ * block has finished with it, then frees the blocks; GEMM calls from other
+ * host threads wait for it (the table lock) and allocate afresh afterwards.
+ * Blocks owned by graphs being captured or replayed are not affected.
+ * Returns SGEMM_EMU_OK, SGEMM_EMU_EARCH (no gfx950 device current) or
+ * SGEMM_EMU_ELAUNCH (a HIP call failed; the table is cleared regardless).
+ */
+int sgemm_emu_release_workspace(void);
 
 /* Number of BF16 products evaluated for nbands (1, 3, 6, 8, 9), or -1 if invalid. */
 int sgemm_emu_products(int nbands);
