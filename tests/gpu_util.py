@@ -55,6 +55,55 @@ def check_against_fp64(C, A, B, rows=None, label="", normwise=True):
     return ratio, e_emu, e_naive
 
 
+def check_full(label, A, B, C, ablations=None, chunk_elems=1 << 25, keep_ref=None):
+    """check_against_fp64 on every element of C = A B, computed in row chunks so the
+    FP64 reference, G and the naive FP32 comparator never need to be held whole.
+
+    Asserts the elementwise bound on every finite reference element of every chunk
+    and the normwise gate over the whole matrix.  `ablations` maps nbands -> a
+    band-drop result of the same product, each held to |C_b - C_ref| <=
+    (dropped-mass bound_b + 2 K 2^-24) G + 9 K 2^-149.  `keep_ref(r0, r1, ref)`,
+    if given, receives each chunk's FP64 reference (rows r0..r1-1).
+    Returns (max ratio to the bound, normwise error, naive normwise error)."""
+    M, K = A.shape
+    N = B.shape[1]
+    rows_per = max(1, min(M, chunk_elems // max(N, 1)))
+    drop = {4: 2.0 ** -30, 3: 2.0 ** -21 + 2.0 ** -30, 2: 2.0 ** -13 + 2.0 ** -21 + 2.0 ** -30}
+    sq_emu = sq_naive = sq_ref = 0.0
+    worst = 0.0
+    for r0 in range(0, M, rows_per):
+        r1 = min(M, r0 + rows_per)
+        rows = np.arange(r0, r1, dtype=np.int64)
+        ref, G = oracle.gemm_f64(A, B, rows=rows)
+        if keep_ref is not None:
+            keep_ref(r0, r1, ref)
+        Cd = C[r0:r1].astype(np.float64)
+        err = np.abs(Cd - ref)
+        bound = elementwise_bound(K, G)
+        finite = np.isfinite(ref)
+        bad = finite & ~(err <= bound)
+        assert not bad.any(), (f"{label}: {int(bad.sum())} elements of rows {r0}..{r1 - 1} exceed the bound; "
+                               f"first at {np.argwhere(bad)[0] + [r0, 0]}")
+        worst = max(worst, float(np.max(np.where(finite, err / np.maximum(bound, 1e-300), 0.0))))
+        for nb, Cb in (ablations or {}).items():
+            eb = np.abs(Cb[r0:r1].astype(np.float64) - ref)
+            bb = (drop[nb] + 2.0 * K * U) * G + 9.0 * K * FLOOR
+            badb = finite & ~(eb <= bb)
+            assert not badb.any(), f"{label} nbands={nb}: {int(badb.sum())} elements of rows {r0}..{r1 - 1} exceed"
+        naive = oracle.sgemm_naive_f32(A, B, rows=rows).astype(np.float64)
+        fin = np.where(finite, 1.0, 0.0)
+        sq_emu += float(np.sum(np.where(finite, (Cd - ref) ** 2, 0.0)))
+        sq_naive += float(np.sum(np.where(finite, (naive - ref) ** 2, 0.0)))
+        sq_ref += float(np.sum(np.where(finite, ref, 0.0) ** 2))
+        del ref, G, Cd, err, bound, naive, fin
+    if sq_ref == 0.0:
+        assert np.all(C == 0), f"{label}: reference is zero but C is not"
+        return worst, 0.0, 0.0
+    e_emu, e_naive = (sq_emu / sq_ref) ** 0.5, (sq_naive / sq_ref) ** 0.5
+    assert e_emu <= 2.0 * e_naive, f"{label}: normwise {e_emu:.3g} > 2 x naive {e_naive:.3g}"
+    return worst, e_emu, e_naive
+
+
 def _lsb_exponents(v):
     """Exponent of the lowest set bit of each nonzero double (0 -> huge)."""
     m, e = np.frexp(v)

@@ -424,6 +424,33 @@ def test_split_k_special_values_class(fe, orc):
     assert np.array_equal(cls(C), cls(E))
 
 
+@pytest.mark.parametrize("entry", ["fused", "presplit_t"])
+def test_split_k_exact_integers_bitwise_vs_oracle(fe, orc, entry):
+    """Split-K on a shape where every partial result is exact: 1024 x 512 x 2048
+    runs as 8 K slices of 256.  A holds 48 nonzero integers per row (|a| < 2^9, so
+    the split puts them into bands 0-2), B nonzero integers of the same size.
+    Each band sum, each slice's recombination and the sum of the slices are then
+    integers below 2^24, exact in any order, so the GPU result must equal the
+    exact dot product and the oracle's one-pass emulation (slices recombined
+    separately and added give the same bits as one recombination over all K)."""
+    M, N, K = 1024, 512, 2048
+    assert fe.sgemm_emu_split_k(M, N, K) == 8
+    g = _rng(2048)
+    A = np.zeros((M, K), np.float32)
+    for i in range(M):
+        cols = g.choice(K, size=48, replace=False)
+        A[i, cols] = g.integers(1, 512, size=48) * np.where(g.integers(0, 2, size=48) == 1, -1, 1)
+    B = (g.integers(1, 512, size=(K, N)) * np.where(g.integers(0, 2, size=(K, N)) == 1, -1, 1)).astype(np.float32)
+    exact = (A.astype(np.int64) @ B.astype(np.int64))
+    assert np.abs(exact).max() < 1 << 24
+    C = run(fe, A, B, entry=entry)
+    E = orc.gemm_emu(A, B)
+    assert np.array_equal(E.astype(np.int64), exact)
+    assert np.array_equal(C.astype(np.int64), exact)
+    nz = exact != 0
+    assert np.array_equal(C.view(np.uint32)[nz], E.view(np.uint32)[nz])
+
+
 def test_presplit_equals_fused_bitwise(fe):
     g = _rng(5)
     A = g.standard_normal((200, 150)).astype(np.float32)

@@ -162,3 +162,71 @@ def test_two_host_threads_on_one_stream(fe, problems):
     for t in plan:
         for n, (i, C) in enumerate(zip(plan[t], outs[t])):
             _same(refs[i], probs[i].result(C), f"thread {t} call {n}: case {probs[i].case}")
+
+
+def test_release_workspace_gives_memory_back(fe, problems):
+    """sgemm_emu_release_workspace frees every retained block of the device and
+    trims the library's pool: the driver's free memory rises by at least the
+    planes of a 4096^3 call (A and B split into workspace planes, 2 x 96 MiB),
+    and later calls allocate afresh and give the same bits."""
+    n = 4096
+    g = torch.Generator(device="cuda").manual_seed(11)
+    A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+    B = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+    C = torch.empty((n, n), device="cuda")
+    print("workspace: 4096^3 then release", flush=True, file=sys.stderr)
+    fe.sgemm_bf16x9(n, n, n, A, n, B, n, C, n)
+    torch.cuda.synchronize()
+    first = C.clone()
+    free_before = torch.cuda.mem_get_info()[0]
+    fe.sgemm_emu_release_workspace()
+    free_after = torch.cuda.mem_get_info()[0]
+    assert free_after - free_before >= 150 << 20, (free_before, free_after)
+    fe.sgemm_emu_release_workspace()          # nothing left: still fine
+    fe.sgemm_bf16x9(n, n, n, A, n, B, n, C, n)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int32), C.view(torch.int32))
+    del A, B, C, first
+    print("workspace: the small cases after a release", flush=True, file=sys.stderr)
+    s = torch.cuda.Stream()
+    _run_schedule(fe, problems, [(i, s) for i in range(len(problems[0]))])
+
+
+def test_graph_capture_of_workspace_paths(fe, problems):
+    """Calls that take workspace (FP32 B split into planes, split-K partials,
+    A and B planes) captured into a graph get a block of their own per call
+    from the library's pool inside the graph.  Three replays, with eager calls
+    and synchronisation between them, each equal the eager result bit for bit."""
+    probs, refs = problems
+    picks = [1, 2, 3]                                  # planes + partials, planes, partials only
+    outs = [probs[i].out() for i in picks]
+    n = 2048
+    g = torch.Generator(device="cuda").manual_seed(12)
+    A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+    B = torch.rand((n, 4096), device="cuda", generator=g) * 2 - 1
+    ref_a = torch.empty((n, 4096), device="cuda")
+    fe.sgemm_bf16x9(n, 4096, n, A, n, B, 4096, ref_a, 4096)   # N >= 4096: A and B planes
+    torch.cuda.synchronize()
+    out_a = torch.full_like(ref_a, float("nan"))
+    print("workspace: capture into a graph", flush=True, file=sys.stderr)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=s):
+        for i, C in zip(picks, outs):
+            probs[i].launch(fe, C, s)
+        fe.sgemm_bf16x9(n, 4096, n, A, n, B, 4096, out_a, 4096, s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print(f"workspace: graph replay {rep}", flush=True, file=sys.stderr)
+        for C in outs:
+            C.fill_(float("nan"))
+        out_a.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, C in zip(picks, outs):
+            _same(refs[i], probs[i].result(C), f"replay {rep}: case {probs[i].case}")
+        assert torch.equal(ref_a.view(torch.int32), out_a.view(torch.int32)), f"replay {rep}: A and B planes"
+        # eager calls between replays use the streams' own blocks
+        _run_schedule(fe, problems, [(picks[rep], None)])
+    del graph

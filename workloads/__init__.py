@@ -18,9 +18,8 @@ Interatomic Potentials", section "Benchmarking on PET"):
   pet_small   X 6144x256 N(0,1); W1 256x1024 N(0,1/256); W2 1024x256 N(0,1/1024)
               (hidden layer H = GELU(X W1) is built by the caller)
   square4096  A, B 4096x4096 i.i.d. U(-1,1)
-  pet_large   X 552960x256 N(0,1); W1, W2 as pet_small; H 552960x1024 drawn
-              i.i.d. as fp32(GELU(z)), z ~ N(0,1) (the law of an entry of X W1
-              is N(0,1) because K = 256 and Var(W1) = 1/256)
+  pet_large   X 552960x256 N(0,1); W1, W2 as pet_small (hidden layer
+              H = GELU(X W1) is built by the caller, as for pet_small)
   stress8192  A, B 8192x8192, entries z 2^u (z ~ N(0,1), u uniform integer in
               [-20, 20]); 1% of A's rows rebuilt as near-cancelling partners of
               other rows, row_j = fp32(-row_i + 2^-20 n); 0.1% of the entries of A
@@ -36,7 +35,7 @@ SEED_BASE = 0x5EED0000
 BLOCK_ROWS = 4096
 
 # matrix ids inside a workload (seed = SEED_BASE + 16 * workload_index + matrix_id)
-MID_A, MID_B, MID_W2, MID_NOISE, MID_MASK, MID_H = 0, 1, 2, 3, 4, 5
+MID_A, MID_B, MID_W2, MID_NOISE, MID_MASK = 0, 1, 2, 3, 4
 
 WORKLOADS = {
     # name: (index, description)
@@ -92,19 +91,6 @@ def normal(shape, sigma: float, seed: int) -> np.ndarray:
 def uniform(shape, seed: int) -> np.ndarray:
     """fp32_RNE(2u - 1), u ~ U[0,1) with 53 random bits."""
     return _fill(shape, seed, lambda g, r, c: (2.0 * g.random((r, c)) - 1.0).astype(np.float32))
-
-
-def _erf(x):
-    from scipy.special import erf  # library routine
-    return erf(x)
-
-
-def gelu_of_normal(shape, seed: int) -> np.ndarray:
-    """fp32_RNE(GELU(z)) with GELU(z) = z (1 + erf(z / sqrt 2)) / 2, z ~ N(0,1) i.i.d."""
-    def draw(g, r, c):
-        z = g.standard_normal((r, c))
-        return (0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))).astype(np.float32)
-    return _fill(shape, seed, draw)
 
 
 def scaled_normal(shape, seed: int, umin: int = -20, umax: int = 20) -> np.ndarray:
@@ -172,13 +158,11 @@ def pet_small(atoms: int = PET_SMALL_ATOMS):
     return out
 
 
-def pet_large(atoms: int = PET_LARGE_ATOMS, with_h: bool = True):
+def pet_large(atoms: int = PET_LARGE_ATOMS):
     w = "pet_large"
     rows = atoms * PET_TOKENS
     out = {"X": normal((rows, PET_D), 1.0, seed_of(w, MID_A))}
     out.update(pet_weights(w))
-    if with_h:
-        out["H"] = gelu_of_normal((rows, PET_FFN), seed_of(w, MID_H))
     return out
 
 
