@@ -36,7 +36,9 @@ import os
 import torch  # noqa: F401  (must be loaded before the library, see above)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsgemm_emu.so")
+# SGEMM_EMU_LIB_OVERRIDE: load another build of the library (the test suite's
+# host-only sanitizer build); unset, the in-tree build.
+LIB_PATH = os.environ.get("SGEMM_EMU_LIB_OVERRIDE") or os.path.join(HERE, "libsgemm_emu.so")
 
 SGEMM_EMU_OK = 0
 SGEMM_EMU_EINVAL = -1
@@ -44,6 +46,7 @@ SGEMM_EMU_ENULL = -2
 SGEMM_EMU_EARCH = -3
 SGEMM_EMU_ELAUNCH = -4
 SGEMM_EMU_ENOMEM = -5
+SGEMM_EMU_ECAPTURE = -6
 SGEMM_EMU_B_KN = 0   # pre-split planes K x N (split of B)
 SGEMM_EMU_B_NK = 1   # pre-split planes N x K (split of B^T, e.g. a weight stored [out][in])
 SGEMM_EMU_ACT_NONE = 0
@@ -53,6 +56,8 @@ SGEMM_EMU_SPLIT_TRANSPOSE = 2  # flag (split_f32_bf16x3_ex): planes of X^T
 SGEMM_EMU_IEEE_SPECIALS = 4    # flag (sgemm_emu_ex): IEEE FP32 results where inputs hold Inf/NaN
 SGEMM_EMU_PRESPLIT_B = 8       # flag (sgemm_emu_ex): split FP32 B once into workspace planes whenever allowed
 SGEMM_EMU_PRESPLIT_A = 16      # flag (sgemm_emu_ex): split FP32 A (and B) once into workspace planes whenever allowed
+SGEMM_EMU_PERFORMANT = 32      # flag (sgemm_emu_ex): emulate only where faster than the native FP32 kernel
+SGEMM_EMU_NATIVE_FP32 = 64     # flag (sgemm_emu_ex): the library's native FP32 kernel
 
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_linear",
            "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
@@ -214,7 +219,7 @@ def _layout(t, name, dtypes):
     rows, cols = t.shape
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name}: expected unit stride along columns, got {t.stride(1)}")
-    if rows > 1 and t.stride(0) < max(cols, 1):
+    if rows > 1 and cols > 0 and t.stride(0) < cols:
         raise ValueError(f"{name}: rows overlap (row stride {t.stride(0)} < {cols} columns)")
     return max(t.stride(0), cols, 1)
 

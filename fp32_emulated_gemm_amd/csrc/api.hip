@@ -151,8 +151,9 @@ int launched(hipError_t e) { return e == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_E
 // block in stream order).
 // The device's table lock is held from the lookup until the call's last
 // launch, so calls from several host threads on one stream cannot interleave
-// their kernels.  A stream being captured into a graph takes a per-call block
-// from the pool instead, so the graph owns its memory.
+// their kernels.  Nothing is allocated on a stream being captured into a
+// graph (stream_capturing): the callers fall back to paths without workspace
+// or report SGEMM_EMU_ECAPTURE.
 struct StreamWs {
     bool used = false;
     uintptr_t key = 0;           // the stream handle
@@ -177,38 +178,37 @@ DeviceWs g_ws[kMaxDevices];
 struct WsLease {
     std::unique_lock<std::mutex> lock;
     StreamWs *entry = nullptr;
-    void *pooled = nullptr;      // per-call block (graph capture), freed at release
     hipStream_t stream = nullptr;
 
     void release()
     {
         if (entry != nullptr) entry->recorded = hipEventRecord(entry->done, stream) == hipSuccess;
-        if (pooled != nullptr) (void)hipFreeAsync(pooled, stream);
         entry = nullptr;
-        pooled = nullptr;
         if (lock.owns_lock()) lock.unlock();
     }
     ~WsLease() { release(); }
 };
 
+// True if `stream` is being captured into a graph (or its state cannot be
+// read, which is treated the same way).
+bool stream_capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
 // A workspace of at least `bytes` for `stream`, or nullptr if none can be had
-// (the caller then runs without one).
+// (the caller then runs without one).  Never allocates on a capturing stream.
 void *acquire_workspace(int dev, hipStream_t stream, size_t bytes, WsLease &L)
 {
     L.stream = stream;
+    if (stream_capturing(stream)) return nullptr;
     hipMemPool_t pool = workspace_pool(dev);
     if (pool == nullptr) return nullptr;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-        (void)hipGetLastError();
-        void *p = nullptr;
-        if (hipMallocFromPoolAsync(&p, bytes, pool, stream) != hipSuccess || p == nullptr) {
-            (void)hipGetLastError();
-            return nullptr;
-        }
-        L.pooled = p;
-        return p;
-    }
     DeviceWs &D = g_ws[dev];
     L.lock = std::unique_lock<std::mutex>(D.mutex);
     StreamWs *e = nullptr;
@@ -258,11 +258,10 @@ void *acquire_workspace(int dev, hipStream_t stream, size_t bytes, WsLease &L)
 }
 
 
-int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
-                const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
-                int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
-                int act = SGEMM_EMU_ACT_NONE, bool rne = false, bool force_presplit = false,
-                bool force_presplit_a = false)
+// Every check of a GEMM call's arguments, before any HIP call.
+int validate_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                  const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
+                  int64_t ldc, int nbands, BSource bsrc, const float *bias, int act)
 {
     int rc;
     if ((rc = check_dims(M, N, K)) != SGEMM_EMU_OK) return rc;
@@ -286,6 +285,18 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // The kernels address one K step of a 128 x 128 tile, and the C stores of a
     // 128-row tile, with 32-bit byte offsets.
     if (lda > kMaxTileLd || ldb > kMaxTileLd || ldc > kMaxTileLd) return SGEMM_EMU_EINVAL;
+    return SGEMM_EMU_OK;
+}
+
+int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
+                int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
+                int act = SGEMM_EMU_ACT_NONE, bool rne = false, bool force_presplit = false,
+                bool force_presplit_a = false)
+{
+    int rc;
+    if ((rc = validate_gemm(M, N, K, A, lda, B, B0, B1, B2, ldb, C, ldc, nbands, bsrc, bias, act)) != SGEMM_EMU_OK)
+        return rc;
     if (M == 0 || N == 0) return SGEMM_EMU_OK;
 
     int num_cus = 0, dev = 0;
@@ -349,7 +360,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     void *ws = nullptr;
     if (plane_pad + part_pad + aplane_pad > 0)
         ws = acquire_workspace(dev, stream, 3 * plane_pad + part_pad + 3 * aplane_pad, lease);
-    if (ws == nullptr && sl > 1) return SGEMM_EMU_ENOMEM;
+    if (ws == nullptr && sl > 1) return stream_capturing(stream) ? SGEMM_EMU_ECAPTURE : SGEMM_EMU_ENOMEM;
     if (ws != nullptr && presplit) {
         uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
                  *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
@@ -391,6 +402,51 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     return launched(e);
 }
 
+// ---------------------------------------------------------------- native FP32
+// C = A B with FP32 products and FP32 accumulation on the FP32 matrix
+// instruction (the library's native path; sgemm_emu_ex's strategy flags).
+int gemm_native(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+                float *C, int64_t ldc, hipStream_t stream)
+{
+    int rc;
+    if ((rc = validate_gemm(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, 5, B_FP32, nullptr,
+                            SGEMM_EMU_ACT_NONE)) != SGEMM_EMU_OK)
+        return rc;
+    if (M == 0 || N == 0) return SGEMM_EMU_OK;
+    int num_cus = 0, dev = 0;
+    if ((rc = current_device(&num_cus, &dev)) != SGEMM_EMU_OK) return rc;
+    if (K == 0) return launched(launch_zero(M, N, C, ldc, nullptr, SGEMM_EMU_ACT_NONE, num_cus, stream));
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K; g.ka = K;
+    g.A = A; g.lda = lda;
+    g.B = B; g.ldb = ldb;
+    g.C = C; g.ldc = ldc;
+    g.act = SGEMM_EMU_ACT_NONE;
+    g.num_cus = num_cus;
+    g.splits = 1;
+    const NativePlan plan = native_plan(M, N, K, num_cus);
+    WsLease lease;
+    if (plan.splits > 1) {
+        void *ws = acquire_workspace(dev, stream, (size_t)plan.splits * (size_t)M * (size_t)N * sizeof(float), lease);
+        if (ws == nullptr) return stream_capturing(stream) ? SGEMM_EMU_ECAPTURE : SGEMM_EMU_ENOMEM;
+        g.partials = (float *)ws;
+        g.ldp = N;
+    }
+    const hipError_t e = launch_native(g, plan, stream);
+    lease.release();
+    return launched(e);
+}
+
+// The performant strategy's choice (sgemm_emu_ex with SGEMM_EMU_PERFORMANT):
+// true where the native FP32 kernel is expected to be faster than all nine
+// BF16 products on this device.
+bool performant_prefers_native(int64_t M, int64_t N, int64_t K, int num_cus)
+{
+    (void)K;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    return tiles < 2 * (int64_t)num_cus;
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,10 +468,37 @@ int sgemm_emu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
 int sgemm_emu_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
                  float *C, int64_t ldc, int nbands, int flags, sgemm_emu_stream_t stream)
 {
-    if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_IEEE_SPECIALS | SGEMM_EMU_PRESPLIT_B | SGEMM_EMU_PRESPLIT_A)) != 0)
+    if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_IEEE_SPECIALS | SGEMM_EMU_PRESPLIT_B | SGEMM_EMU_PRESPLIT_A |
+                   SGEMM_EMU_PERFORMANT | SGEMM_EMU_NATIVE_FP32)) != 0)
         return SGEMM_EMU_EINVAL;
     hipStream_t s = (hipStream_t)stream;
-    int rc = gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32, s, nullptr,
+    int rc;
+    // The strategy flags choose between all nine products and native FP32, so
+    // they take nbands = 5 and the default (truncating) split only.
+    const bool strategy = (flags & (SGEMM_EMU_PERFORMANT | SGEMM_EMU_NATIVE_FP32)) != 0;
+    if (strategy && (nbands != 5 || (flags & SGEMM_EMU_SPLIT_RNE))) return SGEMM_EMU_EINVAL;
+    if ((flags & SGEMM_EMU_IEEE_SPECIALS) && M > 0 && N > 0 && K > 0) {
+        // the fix-up needs a flag buffer: refuse before anything is enqueued
+        if ((rc = validate_gemm(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32, nullptr,
+                                SGEMM_EMU_ACT_NONE)) != SGEMM_EMU_OK)
+            return rc;
+        int num_cus = 0;
+        if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
+        if (stream_capturing(s)) return SGEMM_EMU_ECAPTURE;
+    }
+    bool native = (flags & SGEMM_EMU_NATIVE_FP32) != 0;
+    if ((flags & SGEMM_EMU_PERFORMANT) && !native) {
+        if ((rc = validate_gemm(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, 5, B_FP32, nullptr,
+                                SGEMM_EMU_ACT_NONE)) != SGEMM_EMU_OK)
+            return rc;
+        int num_cus = 0;
+        if (M > 0 && N > 0 && (rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
+        native = M > 0 && N > 0 && performant_prefers_native(M, N, K, num_cus);
+    }
+    if (native)
+        rc = gemm_native(M, N, K, A, lda, B, ldb, C, ldc, s);
+    else
+        rc = gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32, s, nullptr,
                          SGEMM_EMU_ACT_NONE, (flags & SGEMM_EMU_SPLIT_RNE) != 0,
                          (flags & (SGEMM_EMU_PRESPLIT_B | SGEMM_EMU_PRESPLIT_A)) != 0,
                          (flags & SGEMM_EMU_PRESPLIT_A) != 0);
@@ -522,6 +605,7 @@ const char *sgemm_emu_strerror(int status)
     case SGEMM_EMU_EARCH: return "no HIP device, or the current device is not gfx950";
     case SGEMM_EMU_ELAUNCH: return "kernel launch failed";
     case SGEMM_EMU_ENOMEM: return "no device memory for the K-split partial sums";
+    case SGEMM_EMU_ECAPTURE: return "the call needs workspace and the stream is being captured into a graph";
     default: return "unknown status";
     }
 }

@@ -1234,6 +1234,249 @@ int gemm_split_count(int64_t M, int64_t N, int64_t K, int nbands, int num_cus)
     return best;
 }
 
+static int group_rows(int tiles_n, int num_cus);
+
+// ---------------------------------------------------------------- native FP32 (performant strategy)
+//
+// The pages' "performant" strategy uses the emulation only where it expects
+// a speed-up over the platform's native FP32 GEMM (NVIDIA blog, section
+// "BF16x9 on NVIDIA Blackwell GPUs", Fig. 4; discuss.pytorch.kr summary,
+// "PyTorch에서 직접 써 보려면").  This is the library's own native path: the
+// FP32 matrix instruction v_mfma_f32_32x32x2_f32, one FP32 accumulator per
+// output, no split.
+//
+// One workgroup per (tile, K slice); waves as in Cfg, each (MI x 32) x (NI x 32)
+// of accumulators.  K advances in steps of NBK = 16, double-buffered in LDS:
+//   * A rows hold 16 k values plus 4 of padding (80 bytes): 16 consecutive
+//     rows read with 128-bit loads touch 64 distinct banks;
+//   * B rows (one k each) hold the tile's BN columns plus 4 of padding, so
+//     the two half-waves reading k and k + 8 land on disjoint banks.
+// Within a step, half-wave h (lanes 32h..32h+31) feeds k = 8h + kk to the
+// kk-th MFMA: the instruction's two k rows come from k and k + 8, so each
+// lane reads its eight A values of a step with two 128-bit loads.  Every
+// k < K is multiplied in exactly once, in an order the bound allows.
+
+constexpr int NBK = 16;                 // k per step
+constexpr int NAP = NBK + 4;            // A row pitch in LDS (floats)
+
+template <class C>
+struct NativeLayout {
+    static constexpr int BNP = C::BN + 4;                 // B row pitch in LDS (floats)
+    static constexpr int A_FLOATS = C::BM * NAP;
+    static constexpr int B_FLOATS = NBK * BNP;
+    static constexpr int STAGE = A_FLOATS + B_FLOATS;
+    static constexpr int A_VECS = C::BM * (NBK / 4) / C::NT;   // 16-byte A chunks per thread and step
+    static constexpr int B_VECS = NBK * (C::BN / 4) / C::NT;   // 16-byte B chunks per thread and step
+    static_assert(C::BM * (NBK / 4) % C::NT == 0 && NBK * (C::BN / 4) % C::NT == 0, "loader mapping");
+};
+
+template <class C>
+struct NativeStage {
+    float a[NativeLayout<C>::A_VECS][4];
+    float b[NativeLayout<C>::B_VECS][4];
+};
+
+// Thread -> A chunk (row, 4-wide k group): 16 consecutive lanes take 16 rows of
+// one k group (conflict-free 128-bit LDS writes at the 80-byte pitch).
+__device__ __forceinline__ void native_a_chunk(int q, int &row, int &kg)
+{
+    const int lane = q & 63, blk = q >> 6;
+    row = blk * 16 + (lane & 15);
+    kg = lane >> 4;
+}
+
+// Load one step (k0 .. k0 + 15) of A and B into registers.  VEC: 128-bit
+// loads (16-byte aligned operands, leading dimensions and K / N multiples of
+// 4), else one dword at a time.  A past K reads the next row's values and is
+// masked by the caller; B rows past K and A, B beyond the operands read zero
+// or values whose outputs are never stored.
+template <class C, bool VEC>
+__device__ __forceinline__ void native_load(NativeStage<C> &st, const GemmArgs &g, int64_t m0, int64_t n0, int64_t k0)
+{
+    using L = NativeLayout<C>;
+    const int tid = threadIdx.x;
+    {
+        const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
+        const rsrc_t ra = make_rsrc(g.A + m0 * g.lda + k0, ((rows - 1) * g.lda + (g.K - k0)) * 4);
+#pragma unroll
+        for (int c = 0; c < L::A_VECS; ++c) {
+            int row, kg;
+            native_a_chunk(c * C::NT + tid, row, kg);
+            const int64_t r = lmin((int64_t)row, rows - 1);
+            const uint32_t off = (uint32_t)((r * g.lda + kg * 4) * 4);
+            if (VEC) {
+                const u32x4_t v = bload_u32x4(ra, off, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.a[c][e] = __uint_as_float(v[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.a[c][e] = bload_f32(ra, off + 4 * e, 0);
+            }
+        }
+    }
+    {
+        // base at row k0; the descriptor ends at element (K-1, N-1)
+        const rsrc_t rb = make_rsrc(g.B + k0 * g.ldb, ((g.K - 1 - k0) * g.ldb + g.N) * 4);
+#pragma unroll
+        for (int c = 0; c < L::B_VECS; ++c) {
+            const int q = c * C::NT + tid, col = (q % (C::BN / 4)) * 4, k = q / (C::BN / 4);
+            const int64_t n = lmin(n0 + col, (g.N - 1) & ~(int64_t)3);
+            const uint32_t off = (uint32_t)(((int64_t)k * g.ldb + (VEC ? n : n0 + col)) * 4);
+            if (VEC) {
+                const u32x4_t v = bload_u32x4(rb, off, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.b[c][e] = __uint_as_float(v[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.b[c][e] = bload_f32(rb, off + 4 * e, 0);
+            }
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void native_store(const NativeStage<C> &st, float *buf, int64_t kvalid)
+{
+    using L = NativeLayout<C>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < L::A_VECS; ++c) {
+        int row, kg;
+        native_a_chunk(c * C::NT + tid, row, kg);
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (kg * 4 + e < kvalid) ? st.a[c][e] : 0.0f;
+        *reinterpret_cast<u32x4_t *>(buf + row * NAP + kg * 4) =
+            u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    }
+#pragma unroll
+    for (int c = 0; c < L::B_VECS; ++c) {
+        const int q = c * C::NT + tid, col = (q % (C::BN / 4)) * 4, k = q / (C::BN / 4);
+        *reinterpret_cast<u32x4_t *>(buf + L::A_FLOATS + k * L::BNP + col) =
+            u32x4_t{__float_as_uint(st.b[c][0]), __float_as_uint(st.b[c][1]), __float_as_uint(st.b[c][2]),
+                    __float_as_uint(st.b[c][3])};
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void native_step(Acc<C, 1> &acc, const float *buf, int wm, int wn, int lane)
+{
+    using L = NativeLayout<C>;
+    const int h = lane >> 5, r = lane & 31;
+    float a[C::MI][8];
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
+        const float *p = buf + (wm * C::WTM + i * 32 + r) * NAP + 8 * h;
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t *>(p);
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t *>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a[i][e] = __uint_as_float(v0[e]); a[i][4 + e] = __uint_as_float(v1[e]); }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        float b[C::NI];
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) b[j] = buf[L::A_FLOATS + (8 * h + kk) * L::BNP + wn * C::WTN + j * 32 + r];
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j)
+                acc.v[i][j][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][kk], b[j], acc.v[i][j][0], 0, 0, 0);
+    }
+}
+
+template <class C, bool VEC>
+__global__ __launch_bounds__(C::NT, 2) void gemm_f32_native_kernel(GemmArgs g)
+{
+    using L = NativeLayout<C>;
+    __shared__ __attribute__((aligned(16))) float lds[2 * L::STAGE];
+    int tm, tn;
+    tile_of_index((int)blockIdx.x, (int)gridDim.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    // K slice of this workgroup (split-K): steps [s0, s1)
+    const int64_t nsteps = (g.K + NBK - 1) / NBK;
+    const int64_t per = (nsteps + g.splits - 1) / g.splits;
+    const int64_t s0 = (int64_t)blockIdx.y * per, s1 = lmin(nsteps, s0 + per);
+
+    Acc<C, 1> acc;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) acc.v[i][j][0] = f32x16_t{};
+
+    if (s0 < s1) {
+        NativeStage<C> st;
+        native_load<C, VEC>(st, g, m0, n0, s0 * NBK);
+        native_store<C>(st, lds, g.K - s0 * NBK);
+        __syncthreads();
+        for (int64_t s = s0; s < s1; ++s) {
+            const float *cur = lds + ((s - s0) & 1) * L::STAGE;
+            float *nxt = lds + ((s - s0 + 1) & 1) * L::STAGE;
+            const bool more = s + 1 < s1;
+            if (more) native_load<C, VEC>(st, g, m0, n0, (s + 1) * NBK);
+            native_step<C>(acc, cur, wm, wn, lane);
+            if (more) native_store<C>(st, nxt, g.K - (s + 1) * NBK);
+            __syncthreads();
+        }
+    }
+    float bias[C::NI];
+    load_bias<C>(bias, g, n0, wn, lane);
+    if (g.splits > 1) store_c_act<C, 1, -1>(acc, bias, g, m0, n0, wm, wn, lane, (int)blockIdx.y);
+    else store_c<C, 1>(acc, bias, g, m0, n0, wm, wn, lane);
+}
+
+using CfgN128 = Cfg<2, 2, 64, 64>;    // 4 waves, 128 x 128 tile
+using CfgN64 = Cfg<2, 2, 32, 32>;     // 4 waves, 64 x 64 tile
+
+template <class C>
+static hipError_t launch_native_cfg(const GemmArgs &args, int splits, hipStream_t stream)
+{
+    GemmArgs g = args;
+    g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
+    g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
+    g.group_m = group_rows(g.tiles_n, g.num_cus);
+    g.splits = splits;
+    const bool vec = aligned(g.A, 16) && aligned(g.B, 16) && g.lda % 4 == 0 && g.ldb % 4 == 0 && g.K % 4 == 0 &&
+                     g.N % 4 == 0;
+    const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n), (unsigned)splits), block(C::NT);
+    if (vec) hipLaunchKernelGGL((gemm_f32_native_kernel<C, true>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((gemm_f32_native_kernel<C, false>), grid, block, 0, stream, g);
+    if (splits > 1) {
+        int64_t blocks = (g.M * g.N + 255) / 256;
+        if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g);
+    }
+    return hipGetLastError();
+}
+
+NativePlan native_plan(int64_t M, int64_t N, int64_t K, int num_cus)
+{
+    NativePlan p{};
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    if (t128 >= num_cus) {
+        p.tile = 128;
+        p.splits = 1;
+        return p;
+    }
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    p.tile = 64;
+    p.splits = 1;
+    // small grids: slices of at least 8 steps until about two workgroups per CU
+    const int64_t nsteps = (K + NBK - 1) / NBK;
+    while (p.splits < 16 && t64 * (p.splits + 1) <= 2 * (int64_t)num_cus && nsteps / (p.splits + 1) >= 8)
+        ++p.splits;
+    return p;
+}
+
+hipError_t launch_native(const GemmArgs &args, const NativePlan &plan, hipStream_t stream)
+{
+    if (plan.splits > 1 && args.partials == nullptr) return hipErrorInvalidValue;
+    if (plan.tile == 128) return launch_native_cfg<CfgN128>(args, plan.splits, stream);
+    return launch_native_cfg<CfgN64>(args, plan.splits, stream);
+}
+
 // ---------------------------------------------------------------- K == 0
 
 __global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ C, int64_t ldc, int64_t M, int64_t N,

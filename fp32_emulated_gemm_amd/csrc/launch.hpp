@@ -73,6 +73,16 @@ int gemm_split_count(int64_t M, int64_t N, int64_t K, int nbands, int num_cus);
 // True when launch_gemm takes the LDS-DMA kernel for N x K planes of this shape.
 bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const void *B2);
 
+// The library's native FP32 GEMM (v_mfma_f32_32x32x2_f32, no split): output
+// tile 128 or 64, and the K slices it uses (> 1 needs args.partials with
+// splits x M x N floats, ldp = N; the slices are added in order).
+struct NativePlan {
+    int tile;
+    int splits;
+};
+NativePlan native_plan(int64_t M, int64_t N, int64_t K, int num_cus);
+hipError_t launch_native(const GemmArgs &args, const NativePlan &plan, hipStream_t stream);
+
 // C := act(0 + bias[j]) (K == 0); without bias and activation C := 0.
 // Recompute, as plain FP32 dot products, every output of C = A B whose row of
 // A or column of B holds an Inf or NaN.  work: 2 (M + N) + 1 ints.

@@ -62,13 +62,15 @@
  *   streams; a ninth stream takes over the least recently used block.  The
  *   blocks come from a memory pool the library creates per device
  *   (hipMallocFromPoolAsync on the calling stream) and stay allocated until
- *   sgemm_emu_release_workspace gives them back (or the process ends).  A
- *   stream being captured into a graph gets a block of its own per call
- *   instead (freed with hipFreeAsync in the graph).  If no workspace can be
- *   had the GEMM splits B inside its kernel (bitwise the same result); a
- *   small-grid shape whose K-split partial buffer cannot be had returns
- *   SGEMM_EMU_ENOMEM with nothing enqueued, so the bits of a shape never
- *   depend on the memory available.  No other device memory is allocated
+ *   sgemm_emu_release_workspace gives them back (or the process ends).  On a
+ *   stream being captured into a graph the library allocates nothing.  If
+ *   no workspace can be had (or the stream is capturing) the GEMM splits B
+ *   inside its kernel (bitwise the same result); a small-grid shape whose
+ *   K-split partial buffer cannot be had returns SGEMM_EMU_ENOMEM (while
+ *   capturing: SGEMM_EMU_ECAPTURE) with nothing enqueued, so the bits of a
+ *   shape never depend on the memory available.  Callers that must capture
+ *   such shapes, or cannot let the library allocate, use
+ *   sgemm_emu_presplit_b_noalloc.  No other device memory is allocated
  *   (sgemm_emu_ex's IEEE fix-up aside, documented there).  The
  *   pool, the blocks and their events belong to the device's primary
  *   context: after hipDeviceReset the library must not be called again in
@@ -102,8 +104,11 @@ enum sgemm_emu_status {
     SGEMM_EMU_EARCH = -3,   /* no HIP device, or the current device is not gfx950 */
     SGEMM_EMU_ELAUNCH = -4, /* the kernel launch itself failed (hipGetLastError), or a HIP call of
                                sgemm_emu_release_workspace failed */
-    SGEMM_EMU_ENOMEM = -5   /* a GEMM on a small tile grid could not get device memory for its
+    SGEMM_EMU_ENOMEM = -5,  /* a GEMM on a small tile grid could not get device memory for its
                                K-split partial sums (see sgemm_emu_split_k); nothing was enqueued */
+    SGEMM_EMU_ECAPTURE = -6 /* the call needs workspace (K-split partial sums, the IEEE fix-up's
+                               flags) and its stream is being captured into a graph, where the
+                               library allocates nothing; nothing was enqueued */
 };
 
 /*
@@ -148,15 +153,36 @@ enum sgemm_emu_flags {
     SGEMM_EMU_PRESPLIT_B = 8,       /* sgemm_emu_ex only: split FP32 B once into workspace planes
                                        whenever M >= 1024 and K' N <= 2^28, not only where the default
                                        expects it to be faster (same result, bitwise) */
-    SGEMM_EMU_PRESPLIT_A = 16       /* sgemm_emu_ex only: as SGEMM_EMU_PRESPLIT_B, and split FP32 A
+    SGEMM_EMU_PRESPLIT_A = 16,      /* sgemm_emu_ex only: as SGEMM_EMU_PRESPLIT_B, and split FP32 A
                                        into workspace planes too whenever K % 64 == 0 and M K <= 2^28,
                                        not only for N >= 4096 (same result, bitwise) */
+    SGEMM_EMU_PERFORMANT = 32,      /* sgemm_emu_ex only, nbands 5, truncating split: the "performant"
+                                       strategy -- all nine BF16 products only where the library expects
+                                       them to be faster than its native FP32 kernel on this shape, the
+                                       native FP32 kernel elsewhere (see sgemm_emu_ex) */
+    SGEMM_EMU_NATIVE_FP32 = 64      /* sgemm_emu_ex only, nbands 5, truncating split: always the native
+                                       FP32 kernel (the strategy's other branch, on its own) */
 };
 
 /*
  * sgemm_emu_ex -- sgemm_emu with flags (SGEMM_EMU_SPLIT_RNE,
- * SGEMM_EMU_IEEE_SPECIALS, SGEMM_EMU_PRESPLIT_B, SGEMM_EMU_PRESPLIT_A; other bits give
- * SGEMM_EMU_EINVAL).  With SGEMM_EMU_SPLIT_RNE both A and B are split
+ * SGEMM_EMU_IEEE_SPECIALS, SGEMM_EMU_PRESPLIT_B, SGEMM_EMU_PRESPLIT_A,
+ * SGEMM_EMU_PERFORMANT, SGEMM_EMU_NATIVE_FP32; other bits give
+ * SGEMM_EMU_EINVAL).
+ * Strategy flags: the pages' cuBLAS integration offers an "eager" strategy
+ * (emulate whenever the operation allows) and a "performant" one (emulate only
+ * where a speed-up over native FP32 is expected) (NVIDIA blog, section "BF16x9
+ * on NVIDIA Blackwell GPUs", Fig. 4; discuss.pytorch.kr summary, section
+ * "PyTorch에서 직접 써 보려면").  Without a strategy flag every entry point is
+ * eager.  With SGEMM_EMU_PERFORMANT the library runs its native FP32 kernel
+ * (v_mfma_f32_32x32x2_f32: FP32 products, FP32 accumulation, one pass over K
+ * per output, or K slices added in order on small tile grids) for shapes whose
+ * 128 x 128 tile grid holds fewer than two tiles per compute unit, and the
+ * nine-product emulation otherwise; SGEMM_EMU_NATIVE_FP32 always runs the
+ * native kernel.  The native kernel's results are IEEE FP32 dot products in
+ * the matrix unit's order of additions (within the same elementwise bound as
+ * the emulation); they differ in rounding from the emulation's.  Both flags
+ * need nbands = 5 and no SGEMM_EMU_SPLIT_RNE (else SGEMM_EMU_EINVAL).  With SGEMM_EMU_SPLIT_RNE both A and B are split
  * with the round-to-nearest rule: with all nine products the result is the
  * same emulated product up to FP32 rounding (both splits are exact); with
  * fewer bands the dropped terms are about half as large and unsigned-biased

@@ -40,7 +40,7 @@ def test_single_hip_runtime_loaded(L):
 def test_products_and_strings(L):
     import fp32_emulated_gemm_amd as fe
     assert [fe.sgemm_emu_products(b) for b in range(0, 7)] == [-1, 1, 3, 6, 8, 9, -1]
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert fe.sgemm_emu_strerror(s) != "unknown status"
     assert fe.sgemm_emu_strerror(7) == "unknown status"
     assert "gfx950" in fe.sgemm_emu_version()
@@ -108,7 +108,11 @@ def test_split_validation(L):
 
 def test_ex_entry_flags(L):
     assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 2, None) == -1     # transpose is a split flag
-    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 32, None) == -1    # unknown flag
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 128, None) == -1   # unknown flag
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 4, 32, None) == -1    # performant needs nbands 5
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 64 | 1, None) == -1  # native: no RNE split
+    assert L.sgemm_emu_ex(4, 4, 4, P, 3, P, 4, P, 4, 5, 64, None) == -1    # native: lda < K
+    assert L.sgemm_emu_ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 5, 32, None) == 0     # performant: empty
     assert L.sgemm_emu_ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 5, 8 | 1, None) == 0  # pre-split B flag: empty
     assert L.sgemm_emu_ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 5, 16 | 1, None) == 0  # pre-split A flag: empty
     assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 0, 1, None) == -1     # nbands
