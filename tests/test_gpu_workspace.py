@@ -192,41 +192,62 @@ def test_release_workspace_gives_memory_back(fe, problems):
     _run_schedule(fe, problems, [(i, s) for i in range(len(problems[0]))])
 
 
-def test_graph_capture_of_workspace_paths(fe, problems):
-    """Calls that take workspace (FP32 B split into planes, split-K partials,
-    A and B planes) captured into a graph get a block of their own per call
-    from the library's pool inside the graph.  Three replays, with eager calls
-    and synchronisation between them, each equal the eager result bit for bit."""
-    probs, refs = problems
-    picks = [1, 2, 3]                                  # planes + partials, planes, partials only
-    outs = [probs[i].out() for i in picks]
-    n = 2048
-    g = torch.Generator(device="cuda").manual_seed(12)
-    A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
-    B = torch.rand((n, 4096), device="cuda", generator=g) * 2 - 1
-    ref_a = torch.empty((n, 4096), device="cuda")
-    fe.sgemm_bf16x9(n, 4096, n, A, n, B, 4096, ref_a, 4096)   # N >= 4096: A and B planes
+def test_graph_capture_allocates_nothing(fe):
+    """On a stream being captured into a graph the library allocates nothing.
+    Calls that need no workspace capture as usual (a forced pre-split of B falls
+    back to the kernel that splits B itself: the same bits as the eager call,
+    which used workspace planes); a K-split shape reports SGEMM_EMU_ECAPTURE
+    with nothing enqueued.  Three replays, with eager calls and
+    synchronisation between them, each equal the eager results bit for bit."""
+    g = np.random.Generator(np.random.Philox(key=4242))
+
+    def mat(r, c):
+        return dev(g.standard_normal((r, c)).astype(np.float32))
+
+    # (a) N x K planes, a grid with no K split and N < 4096 (no A planes)
+    M1, N1, K1 = 1024, 512, 256
+    A1, Bt1 = mat(M1, K1), mat(N1, K1)
+    P1 = [torch.empty((N1, K1), dtype=torch.int16, device="cuda") for _ in range(3)]
+    fe.split_f32_bf16x3(N1, K1, Bt1, K1, *P1, K1)
+    # (b) FP32 B with the pre-split forced (workspace planes when eager)
+    M2, N2, K2 = 2048, 1024, 256
+    A2, B2 = mat(M2, K2), mat(K2, N2)
+    assert fe.sgemm_emu_split_k(M1, N1, K1) == 1 and fe.sgemm_emu_split_k(M2, N2, K2) == 1
+    ref1 = torch.empty((M1, N1), device="cuda")
+    ref2 = torch.empty((M2, N2), device="cuda")
+    fe.sgemm_emu_presplit_b(M1, N1, K1, A1, K1, *P1, K1, fe.SGEMM_EMU_B_NK, ref1, N1, 5)
+    fe.sgemm_emu_ex(M2, N2, K2, A2, K2, B2, N2, ref2, N2, 5, fe.SGEMM_EMU_PRESPLIT_B)
+    # (c) a K-split shape
+    M3, N3, K3 = 129, 130, 1024
+    A3, B3 = mat(M3, K3), mat(K3, N3)
+    assert fe.sgemm_emu_split_k(M3, N3, K3) > 1
+    out1 = torch.empty_like(ref1)
+    out2 = torch.empty_like(ref2)
+    out3 = torch.zeros((M3, N3), device="cuda")
     torch.cuda.synchronize()
-    out_a = torch.full_like(ref_a, float("nan"))
-    print("workspace: capture into a graph", flush=True, file=sys.stderr)
+    print("graph capture: two calls without workspace, one K-split call", flush=True, file=sys.stderr)
     graph = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(graph, stream=s):
-        for i, C in zip(picks, outs):
-            probs[i].launch(fe, C, s)
-        fe.sgemm_bf16x9(n, 4096, n, A, n, B, 4096, out_a, 4096, s)
+        fe.sgemm_emu_presplit_b(M1, N1, K1, A1, K1, *P1, K1, fe.SGEMM_EMU_B_NK, out1, N1, 5, s)
+        fe.sgemm_emu_ex(M2, N2, K2, A2, K2, B2, N2, out2, N2, 5, fe.SGEMM_EMU_PRESPLIT_B, s)
+        with pytest.raises(fe.SgemmEmuError) as err:
+            fe.sgemm_bf16x9(M3, N3, K3, A3, K3, B3, N3, out3, N3, s)
+        assert err.value.status == fe.SGEMM_EMU_ECAPTURE
     torch.cuda.synchronize()
     for rep in range(3):
-        print(f"workspace: graph replay {rep}", flush=True, file=sys.stderr)
-        for C in outs:
-            C.fill_(float("nan"))
-        out_a.fill_(float("nan"))
+        print(f"graph capture: replay {rep}", flush=True, file=sys.stderr)
+        out1.fill_(float("nan"))
+        out2.fill_(float("nan"))
+        torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for i, C in zip(picks, outs):
-            _same(refs[i], probs[i].result(C), f"replay {rep}: case {probs[i].case}")
-        assert torch.equal(ref_a.view(torch.int32), out_a.view(torch.int32)), f"replay {rep}: A and B planes"
-        # eager calls between replays use the streams' own blocks
-        _run_schedule(fe, problems, [(picks[rep], None)])
+        assert torch.equal(ref1.view(torch.int32), out1.view(torch.int32)), f"replay {rep}: N x K planes"
+        assert torch.equal(ref2.view(torch.int32), out2.view(torch.int32)), f"replay {rep}: forced pre-split"
+        assert bool((out3 == 0).all()), "the refused call enqueued work"
+        # eager work between replays, on the default stream, with its workspace
+        fe.sgemm_emu_ex(M2, N2, K2, A2, K2, B2, N2, out2, N2, 5, fe.SGEMM_EMU_PRESPLIT_B)
+        torch.cuda.synchronize()
+        assert torch.equal(ref2.view(torch.int32), out2.view(torch.int32)), f"eager after replay {rep}"
     del graph
