@@ -24,8 +24,10 @@ def pins_lib():
     global _PINS
     if _PINS is None:
         src = os.path.join(ROOT, "tests", "native", "pins.c")
-        out = os.path.join(ROOT, "tests", "native", "libpins.so")
-        if not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        out = os.environ.get("PINS_LIB_OVERRIDE") or os.path.join(ROOT, "tests", "native", "libpins.so")
+        if "PINS_LIB_OVERRIDE" in os.environ:
+            pass              # a prebuilt copy (the sanitizer run builds its own)
+        elif not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
             subprocess.run(["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off",
                             "-fopenmp", "-fPIC", "-shared", "-o", out + ".tmp", src, "-lm"],
                            check=True)

@@ -55,6 +55,22 @@ def test_split_rne_exhaustive_all_encodings(orc, pins):
         assert bad == 0, f"{bad} encodings fail from {start:#x}; first {first.value:#010x}"
 
 
+@pytest.mark.parametrize("rne", [False, True])
+def test_split_sampled_encodings(orc, pins, rne):
+    """The checks of the exhaustive tests on 256 runs of 2^14 consecutive
+    encodings spread over the whole space (every exponent, both signs, the
+    special classes): a fast version, also run under the sanitizers."""
+    first = ctypes.c_uint64()
+    run = 1 << 14
+    for i in range(256):
+        start = (i << 24) + (i * 40503 % (1 << 24 - 14)) * run
+        x = np.arange(start, start + run, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        c0, c1, c2 = orc.split(x, orc.SPLIT_RNE if rne else orc.SPLIT_RZ)
+        check = pins.pin_split_rne_range if rne else pins.pin_split_range
+        bad = check(start, run, c0.ctypes.data, c1.ctypes.data, c2.ctypes.data, ctypes.byref(first))
+        assert bad == 0, f"{bad} encodings fail from {start:#x}; first {first.value:#010x}"
+
+
 def test_split_shapes_and_strides(orc):
     X = np.arange(12, dtype=np.float32).reshape(3, 4) * np.float32(1.0009765625)
     c = orc.split(X)
