@@ -8,6 +8,7 @@ memory and streams only.  The functions keep the C names and argument order:
     sgemm_emu(M, N, K, A, lda, B, ldb, C, ldc, nbands, stream=None)
     sgemm_emu_ex(M, N, K, A, lda, B, ldb, C, ldc, nbands, flags, stream=None)
     sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nbands, stream=None)
+    sgemm_emu_presplit_b_noalloc(M, N, K, A, lda, B0, B1, B2, ldb, C, ldc, nbands, stream=None)
     sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, activation, Y, ldy, nbands, stream=None)
     split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
@@ -59,7 +60,8 @@ SGEMM_EMU_PRESPLIT_A = 16      # flag (sgemm_emu_ex): split FP32 A (and B) once 
 SGEMM_EMU_PERFORMANT = 32      # flag (sgemm_emu_ex): emulate only where faster than the native FP32 kernel
 SGEMM_EMU_NATIVE_FP32 = 64     # flag (sgemm_emu_ex): the library's native FP32 kernel
 
-EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_linear",
+EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_presplit_b_noalloc",
+           "sgemm_emu_linear",
            "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
            "sgemm_emu_release_workspace", "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
 
@@ -85,6 +87,7 @@ def lib():
         L.sgemm_emu.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp]
         L.sgemm_emu_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, vp]
         L.sgemm_emu_presplit_b.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, ci, vp, i64, ci, vp]
+        L.sgemm_emu_presplit_b_noalloc.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, i64, ci, vp]
         L.sgemm_emu_linear.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, ci, vp, i64, ci, vp]
         L.split_f32_bf16x3.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.split_f32_bf16x3_transposed.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
@@ -96,7 +99,8 @@ def lib():
         L.sgemm_emu_strerror.restype = ctypes.c_char_p
         L.sgemm_emu_version.argtypes = []
         L.sgemm_emu_version.restype = ctypes.c_char_p
-        for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_linear",
+        for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_presplit_b_noalloc",
+                  "sgemm_emu_linear",
                   "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
                   "sgemm_emu_release_workspace", "sgemm_emu_products"):
             getattr(L, n).restype = ci
@@ -156,6 +160,12 @@ def sgemm_emu_presplit_b(M, N, K, A, lda, B0, B1, B2, ldb, b_layout, C, ldc, nba
     return _ok(lib().sgemm_emu_presplit_b(M, N, K, _addr(A), lda, _addr(B0), _addr(B1), _addr(B2), ldb,
                                           b_layout, _addr(C), ldc, nbands, _stream(stream)),
                "sgemm_emu_presplit_b")
+
+
+def sgemm_emu_presplit_b_noalloc(M, N, K, A, lda, B0, B1, B2, ldb, C, ldc, nbands, stream=None):
+    return _ok(lib().sgemm_emu_presplit_b_noalloc(M, N, K, _addr(A), lda, _addr(B0), _addr(B1), _addr(B2), ldb,
+                                                  _addr(C), ldc, nbands, _stream(stream)),
+               "sgemm_emu_presplit_b_noalloc")
 
 
 def sgemm_emu_linear(M, N, K, X, ldx, W0, W1, W2, ldw, bias, activation, Y, ldy, nbands, stream=None):

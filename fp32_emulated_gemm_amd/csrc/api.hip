@@ -447,6 +447,77 @@ bool performant_prefers_native(int64_t M, int64_t N, int64_t K, int num_cus)
     return tiles < 2 * (int64_t)num_cus;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+// sgemm_emu_presplit_b_noalloc keeps the K-split partial sums of small tile
+// grids in this array instead of allocated workspace.  A K-split GEMM uses
+// S slices with S x (its 128 x 128 tiles) <= the device's CU count, so its
+// partials take at most CUs x 128 x 128 floats: 16 MiB on a 256-CU MI355X.
+// Each device holds its own copy for the life of the process.  In host code
+// the array's name is only a stand-in for it; the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchFloats = (size_t)256 * 128 * 128;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+struct ScratchAddr {
+    int state = 0;        // 0 not looked up, 1 known, -1 lookup failed
+    float *ptr = nullptr;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// Device address of `scratch` on device `dev` (the current device), or nullptr.
+float *scratch_address(int dev)
+{
+    std::lock_guard<std::mutex> lock(g_mutex);
+    ScratchAddr &a = g_scratch[dev];
+    if (a.state == 0) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr) {
+            a.ptr = (float *)p;
+            a.state = 1;
+        } else {
+            (void)hipGetLastError();
+            a.state = -1;
+        }
+    }
+    return a.ptr;
+}
+
+// sgemm_emu_presplit_b with N x K planes, no device memory allocated: the
+// same kernels and K split as that entry point (its separate split of A into
+// planes is skipped; the kernel that splits A itself gives the same bits),
+// with the split-K partials in `scratch`.
+int gemm_noalloc(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const uint16_t *B0,
+                 const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C, int64_t ldc, int nbands,
+                 hipStream_t stream)
+{
+    int rc;
+    if ((rc = validate_gemm(M, N, K, A, lda, nullptr, B0, B1, B2, ldb, C, ldc, nbands, B_PLANES_NK, nullptr,
+                            SGEMM_EMU_ACT_NONE)) != SGEMM_EMU_OK)
+        return rc;
+    if (M == 0 || N == 0) return SGEMM_EMU_OK;
+    int num_cus = 0, dev = 0;
+    if ((rc = current_device(&num_cus, &dev)) != SGEMM_EMU_OK) return rc;
+    if (K == 0) return launched(launch_zero(M, N, C, ldc, nullptr, SGEMM_EMU_ACT_NONE, num_cus, stream));
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K; g.ka = K;
+    g.A = A; g.lda = lda;
+    g.B0 = B0; g.B1 = B1; g.B2 = B2; g.ldb = ldb;
+    g.C = C; g.ldc = ldc;
+    g.act = SGEMM_EMU_ACT_NONE;
+    g.num_cus = num_cus;
+    g.splits = 1;
+    const int sl = gemm_uses_dma(K, ldb, B0, B1, B2) ? gemm_split_count(M, N, K, nbands, num_cus) : 1;
+    if (sl > 1) {
+        if ((uint64_t)sl * (uint64_t)M * (uint64_t)N > kScratchFloats) return SGEMM_EMU_ENOMEM;
+        float *p = scratch_address(dev);
+        if (p == nullptr) return SGEMM_EMU_ELAUNCH;
+        g.splits = sl;
+        g.partials = p;
+        g.ldp = N;
+    }
+    return launched(launch_gemm(g, nbands, B_PLANES_NK, stream, false));
+}
+
 }  // namespace
 
 extern "C" {
@@ -535,6 +606,13 @@ int sgemm_emu_linear(int64_t M, int64_t N, int64_t K, const float *X, int64_t ld
 {
     return gemm_common(M, N, K, X, ldx, nullptr, W0, W1, W2, ldw, Y, ldy, nbands, B_PLANES_NK,
                        (hipStream_t)stream, bias, activation);
+}
+
+int sgemm_emu_presplit_b_noalloc(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const uint16_t *B0,
+                                 const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C, int64_t ldc,
+                                 int nbands, sgemm_emu_stream_t stream)
+{
+    return gemm_noalloc(M, N, K, A, lda, B0, B1, B2, ldb, C, ldc, nbands, (hipStream_t)stream);
 }
 
 int split_f32_bf16x3(int64_t rows, int64_t cols, const float *X, int64_t ldx, uint16_t *X0, uint16_t *X1,

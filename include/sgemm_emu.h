@@ -225,6 +225,30 @@ int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
                          float *C, int64_t ldc,
                          int nbands, sgemm_emu_stream_t stream);
 
+/*
+ * sgemm_emu_presplit_b_noalloc -- sgemm_emu_presplit_b with N x K planes
+ * (SGEMM_EMU_B_NK layout, ldb >= max(1, K)) that allocates no device memory,
+ * for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same kernels and K split as
+ * sgemm_emu_presplit_b, so the same bits (the separate split of A into
+ * workspace planes that sgemm_emu_presplit_b makes for N >= 4096 is skipped;
+ * the kernel that splits A itself gives the same result).  The K-split partial
+ * sums of small tile grids go to a fixed array in device memory, 16 MiB per
+ * device (256 x 128 x 128 floats), held from the library's first such call on
+ * the device until the process ends; a shape that would need more (S x M x N
+ * floats, see sgemm_emu_split_k; never on a 256-CU MI355X) returns
+ * SGEMM_EMU_ENOMEM.  All calls on one device share that array: calls that
+ * overlap in time on one device (two streams, or two host threads) race on
+ * it and must be ordered by the caller.  Every element a call reads from the
+ * array it has written first, so nothing needs clearing.  Other arguments and
+ * errors as sgemm_emu_presplit_b.
+ */
+int sgemm_emu_presplit_b_noalloc(int64_t M, int64_t N, int64_t K,
+                                 const float *A, int64_t lda,
+                                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb,
+                                 float *C, int64_t ldc,
+                                 int nbands, sgemm_emu_stream_t stream);
+
 /* Activation applied by sgemm_emu_linear after the bias. */
 enum sgemm_emu_activation {
     SGEMM_EMU_ACT_NONE = 0,
