@@ -217,9 +217,11 @@ def test_graph_capture_allocates_nothing(fe):
     ref2 = torch.empty((M2, N2), device="cuda")
     fe.sgemm_emu_presplit_b(M1, N1, K1, A1, K1, *P1, K1, fe.SGEMM_EMU_B_NK, ref1, N1, 5)
     fe.sgemm_emu_ex(M2, N2, K2, A2, K2, B2, N2, ref2, N2, 5, fe.SGEMM_EMU_PRESPLIT_B)
-    # (c) a K-split shape
+    # (c) a K-split shape (N x K planes: the kernel that splits K)
     M3, N3, K3 = 129, 130, 1024
-    A3, B3 = mat(M3, K3), mat(K3, N3)
+    A3, Bt3 = mat(M3, K3), mat(N3, K3)
+    P3 = [torch.empty((N3, K3), dtype=torch.int16, device="cuda") for _ in range(3)]
+    fe.split_f32_bf16x3(N3, K3, Bt3, K3, *P3, K3)
     assert fe.sgemm_emu_split_k(M3, N3, K3) > 1
     out1 = torch.empty_like(ref1)
     out2 = torch.empty_like(ref2)
@@ -233,7 +235,7 @@ def test_graph_capture_allocates_nothing(fe):
         fe.sgemm_emu_presplit_b(M1, N1, K1, A1, K1, *P1, K1, fe.SGEMM_EMU_B_NK, out1, N1, 5, s)
         fe.sgemm_emu_ex(M2, N2, K2, A2, K2, B2, N2, out2, N2, 5, fe.SGEMM_EMU_PRESPLIT_B, s)
         with pytest.raises(fe.SgemmEmuError) as err:
-            fe.sgemm_bf16x9(M3, N3, K3, A3, K3, B3, N3, out3, N3, s)
+            fe.sgemm_emu_presplit_b(M3, N3, K3, A3, K3, *P3, K3, fe.SGEMM_EMU_B_NK, out3, N3, 5, s)
         assert err.value.status == fe.SGEMM_EMU_ECAPTURE
     torch.cuda.synchronize()
     for rep in range(3):
