@@ -71,6 +71,10 @@ def parse():
                    help="only time the platform's BF16 and FP32 GEMMs (torch.matmul) on the square and "
                         "PET shapes and print them as one JSON line")
     p.add_argument("--calibrate-reps", type=int, default=10)
+    p.add_argument("--shape", type=str, default=None,
+                   help="M,N,K: only time the library's entry points (and torch.matmul FP32) on this one "
+                        "shape, random N(0,1) operands, and print them as one JSON line (for kernel traces)")
+    p.add_argument("--shape-reps", type=int, default=20)
     p.add_argument("--traffic-probe", action="store_true",
                    help="for HBM counter runs: two steps, one split of X, then one plain 2 GiB device copy "
                         "whose FETCH/WRITE counts calibrate the counters; prints no JSON line")
@@ -85,6 +89,9 @@ def main():
         sys.exit(2)
     if args.calibrate:
         calibrate(args.calibrate_reps)
+        return
+    if args.shape:
+        one_shape(tuple(int(x) for x in args.shape.split(",")), args.shape_reps)
         return
 
     import numpy as np
@@ -296,6 +303,32 @@ def vendor_bf16(torch, stream, shapes, reps=10):
         del A, B, C
     log(f"vendor BF16 GEMM (torch.matmul, hipBLASLt): {res}")
     return res
+
+
+def one_shape(shape, reps):
+    """--shape: every entry point on one M x N x K shape, effective TFLOP/s."""
+    import torch
+    import fp32_emulated_gemm_amd as fe
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    m, n, k = shape
+    g = torch.Generator(device="cuda").manual_seed(5)
+    A = torch.randn((m, k), device="cuda", generator=g)
+    B = torch.randn((k, n), device="cuda", generator=g) / max(k, 1) ** 0.5
+    C = torch.empty((m, n), device="cuda")
+    Bt_planes = fe.split(B.t().contiguous())
+    fl = 2.0 * m * n * k
+    entries = {
+        "sgemm_bf16x9": lambda: fe.sgemm_bf16x9(m, n, k, A, k, B, n, C, n, sp),
+        "presplit_nk": lambda: fe.sgemm_emu_presplit_b(m, n, k, A, k, *Bt_planes, k, fe.SGEMM_EMU_B_NK, C, n, 5, sp),
+        "native_fp32": lambda: fe.sgemm_emu_ex(m, n, k, A, k, B, n, C, n, 5, fe.SGEMM_EMU_NATIVE_FP32, sp),
+        "performant": lambda: fe.sgemm_emu_ex(m, n, k, A, k, B, n, C, n, 5, fe.SGEMM_EMU_PERFORMANT, sp),
+        "torch_fp32": lambda: torch.matmul(A, B, out=C),
+    }
+    res = {name: round(fl / timed(fn, stream, reps) / 1e9, 2) for name, fn in entries.items()}
+    print(json.dumps({"shape": [m, n, k], "reps": reps, "tflops": res,
+                      "split_k": fe.sgemm_emu_split_k(m, n, k, 5)}), flush=True)
 
 
 CALIBRATION_SHAPES = {"4096^3": (4096, 4096, 4096), "8192^3": (8192, 8192, 8192),

@@ -6,7 +6,8 @@
 // without one).  The library keeps no state besides a per-device cache of
 // "is this a gfx950", its CU count, a memory pool and a per-stream workspace
 // table.  The only device memory it allocates is stream-ordered workspace: the
-// planes of a pre-split FP32 B and the partial sums of a K-split GEMM (one
+// planes of a pre-split FP32 B and the stream-K partial results of small tile
+// grids (one
 // grow-only block per stream, kept for the stream's later calls), and the
 // flags of the IEEE fix-up (hipMallocFromPoolAsync / hipFreeAsync on the
 // caller's stream, from the library's own pool).
@@ -31,7 +32,7 @@ constexpr int64_t kPresplitMinRows = 1024;
 constexpr uint64_t kPresplitMaxElems = (uint64_t)1 << 28;
 // ... and by default only where it pays: a separate split launch and the
 // workspace cost a few microseconds, the in-kernel split of B a few percent of
-// the GEMM; the in-kernel path also has no split-K.  Measured on MI355X: the
+// the GEMM; the in-kernel path also has no stream-K.  Measured on MI355X: the
 // in-kernel split wins at 6144x1024x256 (85 vs 74 TFLOP/s) and
 // 16384x256x1024 (125 vs 116), loses at 2048^3 (114 vs 123) and above.
 constexpr double kPresplitMinFlops = 1.2e10;
@@ -41,6 +42,10 @@ constexpr double kPresplitMinFlops = 1.2e10;
 // Measured on MI355X (A split included): 4096^3 +6-10 %, 8192^3 +2.5 %; at
 // N = 1024 the separate split of A costs more than the kernel gains.
 constexpr int64_t kPresplitAMinCols = 4096;
+// Stream-K: one 128 x 128 FP32 partial slot per workgroup, and a flag word per
+// workgroup at the head of every workspace block (at most 1024 workgroups).
+constexpr size_t kSkSlotBytes = (size_t)128 * 128 * sizeof(float);
+constexpr size_t kFlagBytes = 4096;
 // Largest leading dimension (elements) whose 128-row tile span fits 32-bit byte offsets.
 constexpr int64_t kMaxTileLd = ((int64_t)1 << 32) / (128 * 4) - 64;
 
@@ -162,6 +167,7 @@ struct StreamWs {
     hipEvent_t done = nullptr;   // recorded on the stream after the last call that used ptr
     bool recorded = false;
     uint64_t tick = 0;           // last use, for eviction
+    uint32_t epoch = 0;          // stream-K flag value of the block's last call (flags start at 0)
 };
 
 constexpr int kStreamSlots = 8;
@@ -179,10 +185,17 @@ struct WsLease {
     std::unique_lock<std::mutex> lock;
     StreamWs *entry = nullptr;
     hipStream_t stream = nullptr;
+    uint32_t *flags = nullptr;   // the block's stream-K flags (its first kFlagBytes)
+    uint32_t epoch = 0;          // this call's flag value
 
-    void release()
+    // The event of the held block, for the launch helpers to tie to the call's
+    // last kernel (a separate event record costs the stream a few microseconds).
+    void *event() const { return entry != nullptr ? (void *)entry->done : nullptr; }
+
+    // attached: the call's last kernel already carries the event.
+    void release(bool attached = false)
     {
-        if (entry != nullptr) entry->recorded = hipEventRecord(entry->done, stream) == hipSuccess;
+        if (entry != nullptr) entry->recorded = attached || hipEventRecord(entry->done, stream) == hipSuccess;
         entry = nullptr;
         if (lock.owns_lock()) lock.unlock();
     }
@@ -203,8 +216,11 @@ bool stream_capturing(hipStream_t stream)
 
 // A workspace of at least `bytes` for `stream`, or nullptr if none can be had
 // (the caller then runs without one).  Never allocates on a capturing stream.
+// Every block starts with kFlagBytes of stream-K flags (zeroed when the block
+// is allocated; each call gets the next epoch), then the caller's bytes.
 void *acquire_workspace(int dev, hipStream_t stream, size_t bytes, WsLease &L)
 {
+    bytes += kFlagBytes;
     L.stream = stream;
     if (stream_capturing(stream)) return nullptr;
     hipMemPool_t pool = workspace_pool(dev);
@@ -249,12 +265,22 @@ void *acquire_workspace(int dev, hipStream_t stream, size_t bytes, WsLease &L)
             L.lock.unlock();
             return nullptr;
         }
+        if (hipMemsetAsync(p, 0, kFlagBytes, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFreeAsync(p, stream);
+            L.lock.unlock();
+            return nullptr;
+        }
         e->ptr = p;
         e->bytes = want;
+        e->epoch = 0;
     }
     e->tick = ++D.clock;
+    e->epoch = e->epoch == UINT32_MAX ? 1 : e->epoch + 1;
     L.entry = e;
-    return e->ptr;
+    L.flags = (uint32_t *)e->ptr;
+    L.epoch = e->epoch;
+    return (char *)e->ptr + kFlagBytes;
 }
 
 
@@ -323,7 +349,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     const int64_t kpad = (K + 63) / 64 * 64;
     const bool presplit = bsrc == B_FP32 && M >= kPresplitMinRows &&
                           (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !(rne && kpad != K) &&
-                          (force_presplit || gemm_split_count(M, N, kpad, nbands, num_cus) > 1 ||
+                          (force_presplit || gemm_streamk_grid(M, N, kpad, num_cus) > 0 ||
                            2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
     // K x N planes, by the same rule: transposed once into N x K' planes in the
     // workspace, so the LDS-DMA kernel runs instead of the kernel that stages
@@ -331,36 +357,36 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // bitwise the same result).
     const bool transpose_kn = bsrc == B_PLANES_KN && M >= kPresplitMinRows &&
                               (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !rne &&
-                              (gemm_split_count(M, N, kpad, nbands, num_cus) > 1 ||
+                              (gemm_streamk_grid(M, N, kpad, num_cus) > 0 ||
                                2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
     const size_t plane = (presplit || transpose_kn) ? (size_t)N * (size_t)kpad * sizeof(uint16_t) : 0;
     const size_t plane_pad = (plane + 255) & ~(size_t)255;
     // A as well (K needs no padding; A's planes are M x K, k contiguous), also
     // beside a caller's N x K planes that the DMA kernel reads as they are.
     const bool nk_dma = bsrc == B_PLANES_NK && gemm_uses_dma(K, ldb, B0, B1, B2);
+    // Grids that would leave CUs idle on the N x K DMA kernel share the (tile,
+    // K pair) units among all CUs (stream-K): partial slots and flags in the
+    // workspace.  Stream-K splits A inside the kernel.
+    const bool dma = presplit || transpose_kn || nk_dma;
+    const int skg = dma ? gemm_streamk_grid(M, N, (presplit || transpose_kn) ? kpad : K, num_cus) : 0;
     const bool presplit_a = (presplit || transpose_kn || (nk_dma && M >= kPresplitMinRows)) && kpad == K &&
-                            (uint64_t)M * (uint64_t)K <= kPresplitMaxElems &&
+                            (uint64_t)M * (uint64_t)K <= kPresplitMaxElems && skg == 0 &&
                             (force_presplit_a || N >= kPresplitAMinCols);
     const size_t aplane = presplit_a ? (size_t)M * (size_t)K * sizeof(uint16_t) : 0;
     const size_t aplane_pad = (aplane + 255) & ~(size_t)255;
 
-    // Grids that would leave CUs idle on the N x K DMA kernel are split along
-    // K: each (tile, K slice) recombines its own bands and writes the result to
-    // a partial buffer; a reduction kernel adds the slices in order.
-    const bool dma = presplit || transpose_kn || nk_dma;
-    const int sl = dma ? gemm_split_count(M, N, (presplit || transpose_kn) ? kpad : K, nbands, num_cus) : 1;
-    const size_t part_bytes = sl > 1 ? (size_t)sl * (size_t)M * (size_t)N * sizeof(float) : 0;
+    const size_t part_bytes = skg > 0 ? (size_t)skg * kSkSlotBytes : 0;
     const size_t part_pad = (part_bytes + 255) & ~(size_t)255;   // keeps A's planes 256-byte aligned
 
     // The stream's workspace block holds the planes and the partials.  Without
-    // one the GEMM splits B itself (bitwise the same result); a K-split shape
-    // cannot run without its partial buffer (one pass per tile would round
+    // one the GEMM splits B itself (bitwise the same result); a stream-K shape
+    // cannot run without its partial slots (one pass per tile would round
     // differently), so it reports SGEMM_EMU_ENOMEM with nothing enqueued.
     WsLease lease;
     void *ws = nullptr;
     if (plane_pad + part_pad + aplane_pad > 0)
         ws = acquire_workspace(dev, stream, 3 * plane_pad + part_pad + 3 * aplane_pad, lease);
-    if (ws == nullptr && sl > 1) return stream_capturing(stream) ? SGEMM_EMU_ECAPTURE : SGEMM_EMU_ENOMEM;
+    if (ws == nullptr && skg > 0) return stream_capturing(stream) ? SGEMM_EMU_ECAPTURE : SGEMM_EMU_ENOMEM;
     if (ws != nullptr && presplit) {
         uint16_t *P0 = (uint16_t *)ws, *P1 = (uint16_t *)((char *)ws + plane_pad),
                  *P2 = (uint16_t *)((char *)ws + 2 * plane_pad);
@@ -379,10 +405,11 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
         g.K = kpad;
         bsrc = B_PLANES_NK;
     }
-    if (ws != nullptr && sl > 1) {
-        g.splits = sl;
+    if (ws != nullptr && skg > 0) {
+        g.sk_grid = skg;
+        g.sk_flags = lease.flags;
+        g.sk_epoch = lease.epoch;
         g.partials = (float *)((char *)ws + 3 * plane_pad);
-        g.ldp = N;
     }
     if (ws != nullptr && presplit_a) {
         char *const a_ws = (char *)ws + 3 * plane_pad + part_pad;
@@ -391,14 +418,16 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
         hipError_t e = launch_split(M, K, A, lda, Q0, Q1, Q2, K, num_cus, stream, rne);
         if (e == hipSuccess) {
             g.A0 = Q0; g.A1 = Q1; g.A2 = Q2; g.lda = K;
+            g.done = lease.event();
             e = launch_gemm_planes(g, nbands, stream);
         }
-        lease.release();
+        lease.release(e == hipSuccess && g.done != nullptr);
         return launched(e);
     }
 
+    g.done = lease.event();
     const hipError_t e = launch_gemm(g, nbands, bsrc, stream, rne);
-    lease.release();
+    lease.release(e == hipSuccess && g.done != nullptr && launch_done_attached(g, bsrc));
     return launched(e);
 }
 
@@ -432,8 +461,9 @@ int gemm_native(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
         g.partials = (float *)ws;
         g.ldp = N;
     }
+    g.done = lease.event();
     const hipError_t e = launch_native(g, plan, stream);
-    lease.release();
+    lease.release(e == hipSuccess && g.done != nullptr);
     return launched(e);
 }
 
@@ -448,24 +478,27 @@ bool performant_prefers_native(int64_t M, int64_t N, int64_t K, int num_cus)
 }
 
 // ---------------------------------------------------------------- fixed scratch
-// sgemm_emu_presplit_b_noalloc keeps the K-split partial sums of small tile
-// grids in this array instead of allocated workspace.  A K-split GEMM uses
-// S slices with S x (its 128 x 128 tiles) <= the device's CU count, so its
-// partials take at most CUs x 128 x 128 floats: 16 MiB on a 256-CU MI355X.
-// Each device holds its own copy for the life of the process.  In host code
+// sgemm_emu_presplit_b_noalloc keeps the stream-K partial slots and flags of
+// small tile grids in this array instead of allocated workspace: one 128 x 128
+// slot per workgroup (at most one workgroup per CU, 256 on MI355X), then one
+// flag word per workgroup: 16 MiB + 1 KiB.  Each device holds its own copy for
+// the life of the process (zero-initialised, as the flags need).  In host code
 // the array's name is only a stand-in for it; the device address comes from
 // hipGetSymbolAddress, once per device, with that device current.
-constexpr size_t kScratchFloats = (size_t)256 * 128 * 128;
+constexpr size_t kScratchSlots = 256;
+constexpr size_t kScratchFloats = kScratchSlots * 128 * 128 + kScratchSlots;
 static __device__ __align__(256) float scratch[kScratchFloats];
 
 struct ScratchAddr {
     int state = 0;        // 0 not looked up, 1 known, -1 lookup failed
     float *ptr = nullptr;
+    uint32_t epoch = 0;   // stream-K flag value of the last call on this device
 };
 ScratchAddr g_scratch[kMaxDevices];
 
-// Device address of `scratch` on device `dev` (the current device), or nullptr.
-float *scratch_address(int dev)
+// Device address of `scratch` on device `dev` (the current device), or nullptr;
+// *epoch receives the next flag value for a call.
+float *scratch_address(int dev, uint32_t *epoch)
 {
     std::lock_guard<std::mutex> lock(g_mutex);
     ScratchAddr &a = g_scratch[dev];
@@ -479,13 +512,15 @@ float *scratch_address(int dev)
             a.state = -1;
         }
     }
+    a.epoch = a.epoch == UINT32_MAX ? 1 : a.epoch + 1;
+    *epoch = a.epoch;
     return a.ptr;
 }
 
 // sgemm_emu_presplit_b with N x K planes, no device memory allocated: the
-// same kernels and K split as that entry point (its separate split of A into
-// planes is skipped; the kernel that splits A itself gives the same bits),
-// with the split-K partials in `scratch`.
+// same kernels and K partition as that entry point (its separate split of A
+// into planes is skipped; the kernel that splits A itself gives the same
+// bits), with the stream-K partial slots and flags in `scratch`.
 int gemm_noalloc(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const uint16_t *B0,
                  const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C, int64_t ldc, int nbands,
                  hipStream_t stream)
@@ -506,14 +541,16 @@ int gemm_noalloc(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, c
     g.act = SGEMM_EMU_ACT_NONE;
     g.num_cus = num_cus;
     g.splits = 1;
-    const int sl = gemm_uses_dma(K, ldb, B0, B1, B2) ? gemm_split_count(M, N, K, nbands, num_cus) : 1;
-    if (sl > 1) {
-        if ((uint64_t)sl * (uint64_t)M * (uint64_t)N > kScratchFloats) return SGEMM_EMU_ENOMEM;
-        float *p = scratch_address(dev);
+    const int skg = gemm_uses_dma(K, ldb, B0, B1, B2) ? gemm_streamk_grid(M, N, K, num_cus) : 0;
+    if (skg > 0) {
+        if ((size_t)skg > kScratchSlots) return SGEMM_EMU_ENOMEM;
+        uint32_t epoch = 0;
+        float *p = scratch_address(dev, &epoch);
         if (p == nullptr) return SGEMM_EMU_ELAUNCH;
-        g.splits = sl;
+        g.sk_grid = skg;
         g.partials = p;
-        g.ldp = N;
+        g.sk_flags = (uint32_t *)(p + kScratchSlots * 128 * 128);
+        g.sk_epoch = epoch;
     }
     return launched(launch_gemm(g, nbands, B_PLANES_NK, stream, false));
 }
@@ -665,7 +702,7 @@ int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands)
     int num_cus = 0;
     if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
     if (M == 0 || N == 0 || K == 0) return 1;
-    return gemm_split_count(M, N, K, nbands, num_cus);
+    return gemm_streamk_pieces(M, N, K, gemm_streamk_grid(M, N, K, num_cus));
 }
 
 int sgemm_emu_products(int nbands)
@@ -682,7 +719,7 @@ const char *sgemm_emu_strerror(int status)
     case SGEMM_EMU_ENULL: return "null pointer for a nonempty operand";
     case SGEMM_EMU_EARCH: return "no HIP device, or the current device is not gfx950";
     case SGEMM_EMU_ELAUNCH: return "kernel launch failed";
-    case SGEMM_EMU_ENOMEM: return "no device memory for the K-split partial sums";
+    case SGEMM_EMU_ENOMEM: return "no device memory for the stream-K partial results";
     case SGEMM_EMU_ECAPTURE: return "the call needs workspace and the stream is being captured into a graph";
     default: return "unknown status";
     }

@@ -14,7 +14,8 @@
 // (a linear layer's [out][in] weight, or FP32 B split once into a workspace)
 // with K a multiple of 2 BK:
 //   * persistent: one workgroup of 8 waves per CU walks 128 x 128 output
-//     tiles (or, for small grids, (tile, K slice) units: split-K);
+//     tiles (small grids: gemm_bf16x9_streamk_kernel, the same pipeline over
+//     equal runs of (tile, K pair) units);
 //   * each wave owns 64 x 32 of the tile: two 32 x 32 MFMA blocks, each with
 //     NB band accumulators of 16 FP32 registers per lane
 //     (v_mfma_f32_32x32x16_bf16);
@@ -44,6 +45,8 @@
 //     (then the bias and the activation of the linear entry point).
 // Edges: rows of A beyond M and columns of B beyond N are clamped to valid
 // memory (their results are never stored); k beyond K is zero-filled.
+#include <hip/hip_ext.h>
+
 #include "split_device.hpp"
 #include "launch.hpp"
 
@@ -52,6 +55,19 @@ namespace sgemm_emu_dev {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Launch the last kernel of a call.  With g.done set (a call that used the
+// stream's workspace block), the event is tied to that kernel's completion, so
+// the next user of the block can wait for it without a separate marker on the
+// stream.
+template <typename K>
+static void launch_last(K kernel, dim3 grid, dim3 block, hipStream_t stream, const GemmArgs &g)
+{
+    if (g.done != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, nullptr, (hipEvent_t)g.done, 0, g);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, g);
+}
 
 constexpr int BK = 32;
 constexpr int KP = BK + 8;          // LDS row pitch in BF16 elements (80 bytes)
@@ -890,8 +906,7 @@ __device__ __forceinline__ void a_offsets(uint32_t (&a_off)[C::A_CHUNKS], const 
 template <class C>
 struct StepSrc {
     int64_t m0, n0, k0;
-    int64_t kb;                  // first k of the work unit (its K slice)
-    int slice;                   // K slice of the work unit (split-K), 0 without split
+    int64_t kb;                  // first k of the work unit (its K range)
     uint32_t a_off[C::A_CHUNKS];
 };
 
@@ -980,19 +995,16 @@ __device__ __forceinline__ void clear_acc(Acc<C, NB> &acc)
                 acc.v[i][j][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16_t{}, 0, 0, 0);
 }
 
-// Work unit v -> its tile, K slice and first k.  Without split-K a unit is a
-// tile; with S slices, unit v covers K slice v / T of tile v % T.
+// Work unit v (a tile) -> its origin; its K range starts at 0.
 template <class C>
-__device__ __forceinline__ void unit_src(StepSrc<C> &u, int v, int T, int64_t steps_per_unit, const GemmArgs &g)
+__device__ __forceinline__ void unit_src(StepSrc<C> &u, int v, int T, const GemmArgs &g)
 {
-    const int t = v % T, sl = v / T;
     int tm, tn;
-    tile_of_index(t, T, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    tile_of_index(v, T, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
     u.m0 = (int64_t)tm * C::BM;
     u.n0 = (int64_t)tn * C::BN;
-    u.slice = sl;
-    u.kb = (int64_t)sl * steps_per_unit * BK;
-    u.k0 = u.kb;
+    u.kb = 0;
+    u.k0 = 0;
     a_offsets<C>(u.a_off, g, u.m0);
 }
 
@@ -1010,11 +1022,11 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     constexpr int A_BUF = 3 * DmaLayout<C>::A_TILE, B_BUF = 3 * B_DMA_TILE;
 
     const int T = g.tiles_m * g.tiles_n, G = (int)gridDim.x;
-    const int units = T * g.splits;
+    const int units = T;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    // K is a multiple of 2 BK on this path and each K slice an even number of steps
-    const int64_t nk = g.K / BK / g.splits;
+    // K is a multiple of 2 BK on this path: an even number of steps per tile
+    const int64_t nk = g.K / BK;
 
     int a_lds[C::A_CHUNKS];
 #pragma unroll
@@ -1026,7 +1038,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
 
     int v = (int)blockIdx.x;
     StepSrc<C> cur;                              // the work unit being computed
-    unit_src<C>(cur, v, T, nk, g);
+    unit_src<C>(cur, v, T, g);
 
     Acc<C, NB> acc;
     clear_acc<C, NB>(acc);
@@ -1055,7 +1067,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
         const int64_t vn = (int64_t)v + G;
         const bool has_next = vn < units;
         StepSrc<C> nxt = cur;
-        if (has_next) unit_src<C>(nxt, (int)vn, T, nk, g);
+        if (has_next) unit_src<C>(nxt, (int)vn, T, g);
 
         // Two steps per trip keep the register sets static: an even step
         // splits a_next (its successor) and loads a_cur (two ahead); an odd
@@ -1085,16 +1097,344 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
             bs = b2;
         }
 
-        // Split-K: the slice's bands are recombined as usual and the result goes
-        // to the partial buffer; splitk_reduce_kernel adds the slices.
-        if (g.splits > 1) store_c_act<C, NB, -1>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane, cur.slice);
-        else store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
+        store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
         if (!has_next) break;
         clear_acc<C, NB>(acc);
         v = (int)vn;
         cur = nxt;
     }
     wait_vmem_at_most<0>();      // drain the copies issued past the end of K
+}
+
+// ---------------------------------------------------------------- stream-K (small tile grids)
+//
+// A grid with fewer 128 x 128 tiles than three quarters of the CUs would leave
+// CUs idle.  There the work is cut along K instead: the T tiles x (K / 64)
+// pairs of K steps form one sequence of P units (tile-major, K ascending
+// inside a tile), and workgroup w of G takes units [w P / G, (w + 1) P / G):
+// every CU gets the same number of MFMAs.  A workgroup's run covers the end of
+// one tile, whole tiles, and the start of another; it walks its run from the
+// end, so the pieces it shares with lower-numbered workgroups come last.
+//   * a tile inside one run is stored as usual;
+//   * a piece that does not hold the tile's last K pair (at most one per
+//     workgroup: the first it computes) recombines its bands, writes the FP32
+//     result to its own partial slot (128 x 128 floats at slot w) and
+//     publishes it by setting flags[w] to this launch's epoch;
+//   * the workgroup holding the tile's last K pair recombines its own piece,
+//     waits for the flags of the lower workgroups that hold the tile's earlier
+//     pieces (already done: they computed those pieces first), adds their
+//     partials in K order and then its own, then the bias and activation, and
+//     stores the tile.
+// Each piece runs the method on its K range (five band sums, recombined
+// smallest first); the pieces' FP32 results are added in K order: a fixed
+// order for a given shape and CU count.  Waits point only at lower-numbered
+// workgroups, which the dispatcher starts first, and every wait is bounded: a
+// piece that never arrives turns its tile into NaN instead of hanging.
+//
+// Where the tiles divide evenly enough, the sequence is cut into 8 domains,
+// one per XCD: the dispatcher deals workgroups to the XCDs in turn, so the
+// workgroups w = d (mod 8) share XCD d's L2, and domain d gives them its own
+// block of tiles (groups of tile-rows, column-major inside a group); the
+// same rules then hold inside each domain.  The partial slots and flags are
+// written and read with system-coherent cache policy, because the L2 caches
+// of the XCDs are not coherent with each other.
+
+constexpr int SK_TILE = 128 * 128;                 // floats of one partial slot
+constexpr int kStreamkGroupRows = 4;               // tile-rows per group of the stream-K order
+constexpr uint32_t SK_SPIN_LIMIT = 1u << 24;       // bounded wait (about a second)
+
+// One piece of a workgroup's run: where its steps load from (StepSrc) and
+// what it is within its tile.
+template <class C>
+struct SkPiece {
+    StepSrc<C> s;
+    int64_t nk;          // K steps of the piece (an even number)
+    uint32_t t;          // tile index inside the domain
+    bool full;           // the whole tile
+    bool last;           // holds the tile's last K pair
+};
+
+// The stream-K index arithmetic is 32-bit: the launcher keeps units x
+// workgroups below 2^32, so every product below fits.
+__device__ __forceinline__ uint32_t sk_owner_of(uint32_t p, uint32_t P, uint32_t G) { return ((p + 1) * G - 1) / P; }
+
+// Tile index v of the stream-K order -> (tile_m, tile_n): groups of group_m
+// tile-rows, column-major inside a group, so a domain's consecutive tiles form
+// a block that shares A and B panels.
+__device__ __forceinline__ void sk_tile(uint32_t v, const GemmArgs &g, uint32_t &tm, uint32_t &tn)
+{
+    const uint32_t group_size = (uint32_t)g.group_m * (uint32_t)g.tiles_n;
+    const uint32_t group = v / group_size, in = v - group * group_size;
+    const uint32_t first_m = group * (uint32_t)g.group_m;
+    const uint32_t gm = (uint32_t)imin(g.tiles_m - (int)first_m, g.group_m);
+    tn = in / gm;
+    tm = first_m + (in - tn * gm);
+}
+
+// Piece i of this workgroup's run, counted from the run's end; t_first is the
+// domain's first tile.
+template <class C>
+__device__ __forceinline__ void sk_piece(SkPiece<C> &q, uint32_t i, uint32_t pb, uint32_t pe, uint32_t ppt,
+                                         uint32_t t_first, const GemmArgs &g)
+{
+    const uint32_t t = (pe - 1) / ppt - i;
+    const uint32_t pa = t * ppt > pb ? t * ppt : pb;
+    const uint32_t pz = (t + 1) * ppt < pe ? (t + 1) * ppt : pe;
+    q.t = t;
+    uint32_t tm, tn;
+    sk_tile(t_first + t, g, tm, tn);
+    q.s.m0 = (int64_t)tm * C::BM;
+    q.s.n0 = (int64_t)tn * C::BN;
+    q.s.kb = (int64_t)(pa - t * ppt) * 2 * BK;
+    q.s.k0 = q.s.kb;
+    q.nk = (int64_t)(pz - pa) * 2;
+    q.full = pa == t * ppt && pz == (t + 1) * ppt;
+    q.last = pz == (t + 1) * ppt;
+    a_offsets<C>(q.s.a_off, g, q.s.m0);
+}
+
+// The five-band recombination of one output (smallest band first).
+template <class C, int NB>
+__device__ __forceinline__ float recombine(const Acc<C, NB> &acc, int i, int j, int r)
+{
+    float v = 0.0f;
+    if constexpr (NB >= 5) v = 0x1p-32f * acc.v[i][j][4][r];
+    if constexpr (NB >= 4) v = __builtin_fmaf(acc.v[i][j][3][r], 0x1p-24f, v);
+    if constexpr (NB >= 3) v = __builtin_fmaf(acc.v[i][j][2][r], 0x1p-16f, v);
+    if constexpr (NB >= 2) v = __builtin_fmaf(acc.v[i][j][1][r], 0x1p-8f, v);
+    return v + acc.v[i][j][0][r];
+}
+
+// Byte offset of this lane's first output inside a 128 x 128 partial slot;
+// output (i, j, r) lies sk_slot_step(i, j, r) bytes further.  The base is made
+// opaque to the optimiser, which would otherwise keep all 32 offsets live
+// through the whole kernel.
+template <class C>
+__device__ __forceinline__ uint32_t sk_slot_base(int wm, int wn, int lane)
+{
+    uint32_t b = (uint32_t)(((wm * C::WTM + 4 * (lane >> 5)) * 128 + wn * C::WTN + (lane & 31)) * 4);
+    asm volatile("" : "+v"(b));
+    return b;
+}
+
+__device__ __forceinline__ constexpr uint32_t sk_slot_step(int i, int j, int r)
+{
+    return (uint32_t)(((i * 32 + 8 * (r >> 2) + (r & 3)) * 128 + j * 32) * 4);
+}
+
+// Cache policy of the partial slots and flags: system-coherent (SC0 | SC1),
+// so the stores write through and the loads bypass the caches of the XCD
+// that issues them (the L2 caches of the eight XCDs are not coherent with
+// each other).  This replaces release/acquire fences at device scope, which
+// would write back or invalidate a whole L2 cache.
+constexpr int kCoherent = 1 | 16;
+
+// A piece without the tile's last pair: write the recombined result to slot w,
+// then publish it: every wave waits until its stores are acknowledged, then
+// thread 0 sets the flag.
+template <class C, int NB>
+__device__ __forceinline__ void sk_publish(const Acc<C, NB> &acc, const GemmArgs &g, int w, int wm, int wn, int lane)
+{
+    const rsrc_t rs = make_rsrc(g.partials + (int64_t)w * SK_TILE, (int64_t)SK_TILE * 4);
+    const uint32_t base = sk_slot_base<C>(wm, wn, lane);
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(recombine<C, NB>(acc, i, j, r)), rs,
+                                                      (int)(base + sk_slot_step(i, j, r)), 0, kCoherent);
+    wait_vmem_at_most<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(g.sk_flags + w, g.sk_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// The piece with the tile's last pair: wait for the workgroups [w0, w) that
+// hold the tile's earlier pieces, add their partials in K order, then this
+// piece's own result, the bias and the activation; store the tile.
+template <class C, int NB, int ACT>
+__device__ __forceinline__ void sk_finish(const Acc<C, NB> &acc, const float (&bv)[C::NI], const GemmArgs &g,
+                                          int64_t m0, int64_t n0, int64_t w0, int w, int D, int wm, int wn, int lane)
+{
+    // This piece's own result first, pinned so that it is not recomputed
+    // later: the band accumulators die here, which leaves the registers for
+    // whole batches of partial loads.
+    float own[C::MI][C::NI][16];
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                own[i][j][r] = recombine<C, NB>(acc, i, j, r);
+                asm volatile("" : "+v"(own[i][j][r]));
+            }
+    __shared__ int sk_ok;
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        for (int64_t u = w0; u < w && ok; u += D) {
+            uint32_t n = 0;
+            while (__hip_atomic_load(g.sk_flags + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != g.sk_epoch) {
+                if (++n == SK_SPIN_LIMIT) { ok = 0; break; }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        sk_ok = ok;
+    }
+    __syncthreads();
+    const bool ok = sk_ok != 0;
+    // The earlier pieces' sum, in K order (this runs at the very end of the
+    // kernel, when no later piece's data is held in registers).
+    float sum[C::MI][C::NI][16];
+    for (int64_t u = w0; u < w; u += D) {
+        const rsrc_t rs = make_rsrc(g.partials + u * SK_TILE, (int64_t)SK_TILE * 4);
+        const uint32_t base = sk_slot_base<C>(wm, wn, lane);
+        float p[C::MI][C::NI][16];
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    p[i][j][r] = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(base + sk_slot_step(i, j, r)), 0, kCoherent));
+        // the whole slot's loads in flight before the first add
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sum[i][j][r] = u == w0 ? p[i][j][r] : sum[i][j][r] + p[i][j][r];
+    }
+    const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
+    const rsrc_t rc = make_rsrc(g.C + m0 * g.ldc, ((rows - 1) * g.ldc + g.N) * 4);
+    const uint32_t ldc4 = (uint32_t)g.ldc * 4u;
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) {
+        const int64_t col = n0 + wn * C::WTN + j * 32 + (lane & 31);
+        if (col < g.N) {
+            uint32_t lane_off = (uint32_t)col * 4u + (uint32_t)(wm * C::WTM + 4 * (lane >> 5)) * ldc4;
+            asm volatile("" : "+v"(lane_off));
+#pragma unroll
+            for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float x = w0 < w ? sum[i][j][r] + own[i][j][r] : own[i][j][r];
+                    x = x + bv[j];
+                    if constexpr (ACT == 1) x = gelu_erf(x);
+                    if (!ok) x = __builtin_nanf("");
+                    const uint32_t row = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rc, (int)(lane_off + row * ldc4), 0,
+                                                          kStreamingStore);
+                }
+        }
+    }
+}
+
+// The DMA kernel's pipeline over a stream-K run: the same steps, B copies,
+// A split, MFMA order and per-piece band recombination.
+template <class C, int NB, bool AVEC, bool RNE, bool KTAIL>
+__global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_streamk_kernel(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[DmaLayout<C>::TOTAL / 2];
+    uint16_t *const a_base = lds;
+    uint16_t *const b_base = lds + DmaLayout<C>::A_BYTES / 2;
+    constexpr int A_BUF = 3 * DmaLayout<C>::A_TILE, B_BUF = 3 * B_DMA_TILE;
+
+    // workgroup w is number j of the Gd workgroups of domain d, which owns
+    // tiles [t_first, t_first + Td) of the stream-K order
+    const uint32_t T = (uint32_t)g.tiles_m * (uint32_t)g.tiles_n, G = gridDim.x, w = blockIdx.x;
+    const bool xcd = g.sk_domains == 8;
+    const uint32_t D = xcd ? 8 : 1, d = xcd ? w & 7 : 0, j = xcd ? w >> 3 : w, Gd = xcd ? G >> 3 : G;
+    const uint32_t t_first = xcd ? d * T >> 3 : 0, Td = xcd ? ((d + 1) * T >> 3) - t_first : T;
+    const uint32_t ppt = (uint32_t)(g.K / (2 * BK));     // K pairs per tile
+    const uint32_t P = Td * ppt;
+    const uint32_t pb = j * P / Gd, pe = (j + 1) * P / Gd;  // this workgroup's units (at least two)
+    const uint32_t npieces = (pe - 1) / ppt - pb / ppt + 1;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+
+    int a_lds[C::A_CHUNKS];
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        int row, kg;
+        chunk_rc(c * C::NT + threadIdx.x, row, kg);
+        a_lds[c] = row * KP + kg * 8;
+    }
+
+    SkPiece<C> cur;
+    sk_piece<C>(cur, 0, pb, pe, ppt, t_first, g);
+
+    Acc<C, NB> acc;
+    clear_acc<C, NB>(acc);
+    float a_next[C::A_CHUNKS][8], a_cur[C::A_CHUNKS][8];
+    Frags<C> f0, f1;
+
+    dma_b_stage<C>(g, cur.s.n0, cur.s.kb, b_base, wave, lane);
+    load_a_stage<C, AVEC>(a_cur, cur.s.a_off, g, cur.s.m0, cur.s.kb);
+    dma_b_stage<C>(g, cur.s.n0, cur.s.kb + BK, b_base + B_BUF, wave, lane);
+    load_a_stage<C, AVEC>(a_next, cur.s.a_off, g, cur.s.m0, cur.s.kb + BK);
+    if (store_a_stage<C, RNE, KTAIL>(a_cur, a_lds, a_base, g.ka - cur.s.kb))
+        restage_a_special<C, AVEC, RNE, KTAIL>(cur.s.a_off, a_lds, g, cur.s.m0, cur.s.kb, a_base);
+    wait_vmem_at_most<dma_vmem_per_step<C, AVEC>()>();
+    lds_barrier();
+    read_frags_dma<C>(f0, a_base, b_base, 0, wm, wn, lane);
+
+    int bs = 0;
+    for (uint32_t i = 0;; ++i) {
+        float bias[C::NI];
+        load_bias<C>(bias, g, cur.s.n0, wn, lane);
+        const bool has_next = i + 1 < npieces;
+        SkPiece<C> nxt = cur;
+        if (has_next) sk_piece<C>(nxt, i + 1, pb, pe, ppt, t_first, g);
+        for (int64_t kt = 0; kt < cur.nk; kt += 2) {
+            const bool last = kt + 2 >= cur.nk;
+            const bool roll = last && has_next;
+            StepSrc<C> ld = roll ? nxt.s : cur.s;
+            ld.k0 = roll ? nxt.s.kb : cur.s.kb + (kt + 2) * BK;
+            StepSrc<C> sp = cur.s;
+            sp.k0 = cur.s.kb + (kt + 1) * BK;
+            const int b1 = bs == 2 ? 0 : bs + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+            dma_step<C, NB, AVEC, RNE, KTAIL>(acc, f0, f1, a_cur, a_next, ld, sp, a_lds, g, a_base, b_base + bs * B_BUF,
+                                              a_base + A_BUF, b_base + b1 * B_BUF, b_base + b2 * B_BUF, wave, wm, wn,
+                                              lane);
+            ld.k0 += BK;
+            if (last) {
+                sp = nxt.s;
+                sp.k0 = has_next ? nxt.s.kb : cur.s.kb + cur.nk * BK;
+            } else {
+                sp.k0 += BK;
+            }
+            dma_step<C, NB, AVEC, RNE, KTAIL>(acc, f0, f1, a_next, a_cur, ld, sp, a_lds, g, a_base + A_BUF,
+                                              b_base + b1 * B_BUF, a_base, b_base + b2 * B_BUF, b_base + bs * B_BUF,
+                                              wave, wm, wn, lane);
+            bs = b2;
+        }
+        if (!has_next) break;
+        // an earlier piece: a whole tile, or the first piece of the run (the
+        // start of a tile whose last pair a higher workgroup holds)
+        if (cur.full) store_c<C, NB>(acc, bias, g, cur.s.m0, cur.s.n0, wm, wn, lane);
+        else sk_publish<C, NB>(acc, g, (int)w, wm, wn, lane);
+        clear_acc<C, NB>(acc);
+        cur = nxt;
+    }
+    // The run's last piece.  Only it can hold the last pair of a tile shared
+    // with lower workgroups (runs are walked from their end), so the wait and
+    // the sum happen here, with no later piece's data left in registers.
+    wait_vmem_at_most<0>();      // drain the copies issued past the end of the run
+    float bias[C::NI];
+    load_bias<C>(bias, g, cur.s.n0, wn, lane);
+    if (cur.full) {
+        store_c<C, NB>(acc, bias, g, cur.s.m0, cur.s.n0, wm, wn, lane);
+    } else if (!cur.last) {
+        sk_publish<C, NB>(acc, g, (int)w, wm, wn, lane);
+    } else {
+        const int64_t w0 = (int64_t)(sk_owner_of(cur.t * ppt, P, Gd) * D + d);
+        if (g.act == 1) sk_finish<C, NB, 1>(acc, bias, g, cur.s.m0, cur.s.n0, w0, (int)w, (int)D, wm, wn, lane);
+        else sk_finish<C, NB, 0>(acc, bias, g, cur.s.m0, cur.s.n0, w0, (int)w, (int)D, wm, wn, lane);
+    }
 }
 
 // ---------------------------------------------------------------- both operands as planes
@@ -1142,14 +1482,14 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_planes_kernel(GemmArgs g
     constexpr int TAIL = C::DMA_TAIL < NM ? C::DMA_TAIL : NM;
 
     const int T = g.tiles_m * g.tiles_n, G = (int)gridDim.x;
-    const int units = T * g.splits;
+    const int units = T;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int64_t nk = g.K / BK / g.splits;
+    const int64_t nk = g.K / BK;
 
     int v = (int)blockIdx.x;
     StepSrc<C> cur;                              // the work unit being computed
-    unit_src<C>(cur, v, T, nk, g);
+    unit_src<C>(cur, v, T, g);
     auto copy = [&](const StepSrc<C> &u, int64_t k0, int slot) {
         dma_plane_stage<C>(g.A0, g.A1, g.A2, g.lda, g.M, u.m0, k0, g.K, a_base + slot * BUF, wave, lane);
         dma_plane_stage<C>(g.B0, g.B1, g.B2, g.ldb, g.N, u.n0, k0, g.K, b_base + slot * BUF, wave, lane);
@@ -1175,7 +1515,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_planes_kernel(GemmArgs g
         const int64_t vn = (int64_t)v + G;
         const bool has_next = vn < units;
         StepSrc<C> nxt = cur;
-        if (has_next) unit_src<C>(nxt, (int)vn, T, nk, g);
+        if (has_next) unit_src<C>(nxt, (int)vn, T, g);
         for (int64_t kt = 0; kt < nk; ++kt) {
             const int b1 = bs == 2 ? 0 : bs + 1, b2 = b1 == 2 ? 0 : b1 + 1;
             if (kt + 2 < nk || !has_next) copy(cur, cur.kb + (kt + 2) * BK, b2);
@@ -1190,8 +1530,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_planes_kernel(GemmArgs g
             mfma_slice_part<C, NB, NM - TAIL, NM>(acc, f1);
             bs = b1;
         }
-        if (g.splits > 1) store_c_act<C, NB, -1>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane, cur.slice);
-        else store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
+        store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
         if (!has_next) break;
         clear_acc<C, NB>(acc);
         v = (int)vn;
@@ -1220,18 +1559,45 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g)
     }
 }
 
-int gemm_split_count(int64_t M, int64_t N, int64_t K, int nbands, int num_cus)
+// Domains of a stream-K grid of G workgroups over T tiles of ppt K pairs.
+// Workgroup w runs on XCD w % 8 (the dispatcher deals workgroups to the XCDs
+// in turn), so 8 domains, domain d holding workgroups w = d (mod 8) and tile
+// block d of the stream-K order, keep each block's A and B panels in one L2.
+// Taken when every workgroup still gets two K pairs and the largest block is
+// within 10 % of an even share of the tiles; otherwise one domain.
+static int64_t streamk_domains(int64_t T, int64_t ppt, int64_t G)
 {
-    (void)nbands;
+    if (G % 8 != 0 || T < 8) return 1;
+    if (T / 8 * ppt < 2 * (G / 8)) return 1;
+    if ((T + 7) / 8 * 80 > T * 11) return 1;
+    return 8;
+}
+
+int gemm_streamk_grid(int64_t M, int64_t N, int64_t K, int num_cus)
+{
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t pairs = K / (2 * BK);
-    if (K % (2 * BK) != 0 || tiles * 4 >= (int64_t)num_cus * 3) return 1;   // 3/4 of the CUs busy already
-    int best = 1;
-    for (int sl = 2; sl <= 16; ++sl) {
-        if (tiles * sl > num_cus || pairs / sl < 4) break;     // one round, at least 8 K steps per slice
-        if (pairs % sl == 0) best = sl;
+    if (K % (2 * BK) != 0 || tiles * 4 >= (int64_t)num_cus * 3) return 0;   // 3/4 of the CUs busy already
+    const int64_t units = tiles * (K / (2 * BK));
+    int64_t G = num_cus > 8 ? num_cus & ~7 : 8;
+    if (units < 2 * G) G = units / 2;                  // at least two K pairs per workgroup
+    if (units * G >= ((int64_t)1 << 32)) return 0;     // the kernel's index arithmetic is 32-bit
+    return G > tiles ? (int)G : 0;
+}
+
+int gemm_streamk_pieces(int64_t M, int64_t N, int64_t K, int grid)
+{
+    if (grid <= 0) return 1;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128), ppt = K / (2 * BK);
+    const int64_t D = streamk_domains(tiles, ppt, grid), G = grid / D;
+    int64_t most = 1;
+    for (int64_t d = 0; d < D; ++d) {
+        const int64_t Td = (d + 1) * tiles / D - d * tiles / D, P = Td * ppt;
+        for (int64_t t = 0; t < Td; ++t) {
+            const int64_t first = ((t * ppt + 1) * G - 1) / P, last = (((t + 1) * ppt) * G - 1) / P;
+            if (last - first + 1 > most) most = last - first + 1;
+        }
     }
-    return best;
+    return (int)most;
 }
 
 static int group_rows(int tiles_n, int num_cus);
@@ -1441,12 +1807,14 @@ static hipError_t launch_native_cfg(const GemmArgs &args, int splits, hipStream_
     const bool vec = aligned(g.A, 16) && aligned(g.B, 16) && g.lda % 4 == 0 && g.ldb % 4 == 0 && g.K % 4 == 0 &&
                      g.N % 4 == 0;
     const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n), (unsigned)splits), block(C::NT);
-    if (vec) hipLaunchKernelGGL((gemm_f32_native_kernel<C, true>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((gemm_f32_native_kernel<C, false>), grid, block, 0, stream, g);
+    GemmArgs gk = g;
+    if (splits > 1) gk.done = nullptr;          // the reduction is the last kernel
+    if (vec) launch_last(gemm_f32_native_kernel<C, true>, grid, block, stream, gk);
+    else launch_last(gemm_f32_native_kernel<C, false>, grid, block, stream, gk);
     if (splits > 1) {
         int64_t blocks = (g.M * g.N + 255) / 256;
         if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g);
+        launch_last(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), stream, g);
     }
     return hipGetLastError();
 }
@@ -1548,16 +1916,22 @@ static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
 {
     // One resident workgroup per CU (LDS-limited); a multiple of 8 keeps each
     // workgroup on one XCD for all of its tiles.
-    const int64_t units = (int64_t)g.tiles_m * g.tiles_n * g.splits;
-    int64_t slots = (int64_t)(g.num_cus > 8 ? g.num_cus & ~7 : 8);
-    const dim3 grid((unsigned)(units < slots ? units : slots)), block(C::NT);
-    if (avec) hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, true, RNE, KTAIL>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((gemm_bf16x9_dma_kernel<C, NB, false, RNE, KTAIL>), grid, block, 0, stream, g);
-    if (g.splits > 1) {
-        int64_t blocks = (g.M * g.N + 255) / 256;
-        if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g);
+    const dim3 block(C::NT);
+    if (g.sk_grid > 0) {
+        // small tile grid: stream-K over sk_grid workgroups
+        GemmArgs s = g;
+        s.sk_domains = streamk_domains((int64_t)g.tiles_m * g.tiles_n, g.K / (2 * BK), g.sk_grid);
+        s.group_m = kStreamkGroupRows;
+        const dim3 grid((unsigned)g.sk_grid);
+        if (avec) launch_last(gemm_bf16x9_streamk_kernel<C, NB, true, RNE, KTAIL>, grid, block, stream, s);
+        else launch_last(gemm_bf16x9_streamk_kernel<C, NB, false, RNE, KTAIL>, grid, block, stream, s);
+        return;
     }
+    const int64_t units = (int64_t)g.tiles_m * g.tiles_n;
+    int64_t slots = (int64_t)(g.num_cus > 8 ? g.num_cus & ~7 : 8);
+    const dim3 grid((unsigned)(units < slots ? units : slots));
+    if (avec) launch_last(gemm_bf16x9_dma_kernel<C, NB, true, RNE, KTAIL>, grid, block, stream, g);
+    else launch_last(gemm_bf16x9_dma_kernel<C, NB, false, RNE, KTAIL>, grid, block, stream, g);
 }
 
 template <class C, bool RNE, bool KTAIL>
@@ -1582,15 +1956,10 @@ static hipError_t launch_dma(const GemmArgs &args, int nbands, hipStream_t strea
 template <class C, int NB>
 static void launch_planes_nb(const GemmArgs &g, hipStream_t stream)
 {
-    const int64_t units = (int64_t)g.tiles_m * g.tiles_n * g.splits;
+    const int64_t units = (int64_t)g.tiles_m * g.tiles_n;
     int64_t slots = (int64_t)(g.num_cus > 8 ? g.num_cus & ~7 : 8);
     const dim3 grid((unsigned)(units < slots ? units : slots)), block(C::NT);
-    hipLaunchKernelGGL((gemm_bf16x9_planes_kernel<C, NB>), grid, block, 0, stream, g);
-    if (g.splits > 1) {
-        int64_t blocks = (g.M * g.N + 255) / 256;
-        if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g);
-    }
+    launch_last(gemm_bf16x9_planes_kernel<C, NB>, grid, block, stream, g);
 }
 
 hipError_t launch_gemm_planes(const GemmArgs &args, int nbands, hipStream_t stream)
@@ -1651,6 +2020,11 @@ bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const
 // Configuration per B source, chosen by measurement on MI355X: the explicit
 // MFMA / split interleaving pays off where the kernel splits FP32 B or copies
 // N x K planes; with K x N planes the compiler's own schedule is faster.
+bool launch_done_attached(const GemmArgs &args, BSource bsrc)
+{
+    return bsrc == B_PLANES_NK && gemm_uses_dma(args.K, args.ldb, args.B0, args.B1, args.B2);
+}
+
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
 {
     if (bsrc == B_PLANES_KN) return launch_with<Cfg8>(args, nbands, bsrc, stream, rne);

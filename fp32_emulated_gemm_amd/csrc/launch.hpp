@@ -35,9 +35,15 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int group_m;             // tile-rows per group of the tile order
     int num_cus;             // compute units of the device (persistent grids)
-    int splits;              // K slices (split-K, N x K DMA kernel only); 1 = none
-    float *partials;         // splits planes of M x ldp floats, one recombined result per K slice
+    int splits;              // K slices of the native kernel (1 = none)
+    float *partials;         // native: splits planes of M x ldp floats, one per K slice;
+                             // stream-K: one 128 x 128 slot per workgroup
     int64_t ldp;
+    void *done;              // host only: hipEvent_t to tie to the call's last kernel (or null)
+    uint32_t *sk_flags;      // stream-K: one flag per workgroup (G words), zero or older epochs on entry
+    uint32_t sk_epoch;       // stream-K: this launch's flag value (never 0)
+    int sk_grid;             // stream-K: workgroups G (0: no stream-K)
+    int sk_domains;          // stream-K: 1, or 8 (one block of tiles per XCD); set by the launcher
 };
 
 // rne: round each split stage to nearest even instead of truncating (ablation).
@@ -58,7 +64,10 @@ hipError_t launch_transpose_planes(int64_t rows, int64_t cols, const uint16_t *P
                                    int64_t ldq, int64_t rows_out, hipStream_t stream);
 
 // rne: the in-kernel split of A (and of FP32 B) rounds to nearest even; only
-// B_FP32 and B_PLANES_NK (DMA kernel) support it.
+// B_FP32 and B_PLANES_NK (DMA kernel) support it.  launch_gemm,
+// launch_gemm_planes and launch_native tie args.done (if set) to the last
+// kernel they launch on the N x K DMA, plane and native paths; the caller
+// checks launch_done_attached() for the others.
 hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne = false);
 
 // Both operands as BF16 planes with k contiguous: A0..A2 M x K (lda), B0..B2
@@ -66,9 +75,19 @@ hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream
 // 16-byte aligned planes (else hipErrorInvalidValue, nothing launched).
 hipError_t launch_gemm_planes(const GemmArgs &args, int nbands, hipStream_t stream);
 
-// K slices the N x K DMA kernel should use for this shape (1 = no split-K):
-// grids that leave a quarter of the CUs idle get split along K.
-int gemm_split_count(int64_t M, int64_t N, int64_t K, int nbands, int num_cus);
+// Stream-K for the N x K DMA kernel: the number of workgroups G sharing the
+// shape's (tile, K pair) units, or 0 for one workgroup per tile (grids that
+// fill three quarters of the CUs, K not a multiple of 64, too few units).
+// A stream-K launch needs args.sk_flags (G words), args.partials (G x 128 x 128
+// floats) and a nonzero args.sk_epoch that differs from the flags' values.
+int gemm_streamk_grid(int64_t M, int64_t N, int64_t K, int num_cus);
+
+// Most K pieces any tile is cut into by a stream-K grid of `grid` workgroups.
+int gemm_streamk_pieces(int64_t M, int64_t N, int64_t K, int grid);
+
+// True when launch_gemm ties args.done to its last kernel for this call (the
+// N x K DMA path).
+bool launch_done_attached(const GemmArgs &args, BSource bsrc);
 
 // True when launch_gemm takes the LDS-DMA kernel for N x K planes of this shape.
 bool gemm_uses_dma(int64_t K, int64_t ldb, const void *B0, const void *B1, const void *B2);

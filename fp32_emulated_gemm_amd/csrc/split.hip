@@ -60,41 +60,41 @@ __global__ __launch_bounds__(256) void split_scalar_kernel(
 
 // Split with transposition: X is rows x cols (ldx), the planes are cols x rows
 // (leading dimension ldo); turns an FP32 K x N operand into N x K planes.
-// One workgroup per 64 x 64 tile of X.  The tile goes through LDS: read along
-// X's rows (each wave reads 256 contiguous bytes per row), then each thread
-// takes 8 consecutive rows of one column, splits them, and writes one 16-byte
-// run of each plane row; eight neighbouring lanes cover 128 contiguous bytes.
-// The LDS row pitch of 65 floats makes both the row-wise writes and the
+// One workgroup per TT x TT tile of X (TT = 64, or 32 for matrices too small
+// to give every CU a 64 x 64 tile).  The tile goes through LDS: read along X's
+// rows (each wave reads TT contiguous floats per row), then each thread takes
+// 8 consecutive rows of one column, splits them, and writes one 16-byte run of
+// each plane row; eight neighbouring lanes cover 128 contiguous bytes.  The
+// LDS row pitch of TT + 1 floats makes both the row-wise writes and the
 // column-wise reads free of bank conflicts.
 // Requires rows % 8 == 0, ldo % 8 == 0 and 16-byte aligned planes; other
 // layouts take split_scalar_kernel<true>.
-constexpr int kTT = 64;
-
-template <bool RNE>
+template <bool RNE, int TT>
 __global__ __launch_bounds__(256) void split_transpose_kernel(
     const float *__restrict__ X, int64_t ldx, uint16_t *__restrict__ X0, uint16_t *__restrict__ X1,
     uint16_t *__restrict__ X2, int64_t ldo, int64_t rows_in, int64_t rows, int64_t cols, int64_t tiles_c)
 {
     // rows_in <= rows: X rows past rows_in read as zero (a zero-padded K extent)
-    __shared__ float tile[kTT][kTT + 1];
-    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTT;
-    const int64_t c0 = (int64_t)(blockIdx.x % tiles_c) * kTT;
+    __shared__ float tile[TT][TT + 1];
+    constexpr int RPP = 256 / TT;                       // rows read per pass
+    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * TT;
+    const int64_t c0 = (int64_t)(blockIdx.x % tiles_c) * TT;
     const int tid = threadIdx.x;
-    const int c = tid & (kTT - 1);
+    const int c = tid & (TT - 1);
     const bool col_in = c0 + c < cols;
 #pragma unroll
-    for (int i = 0; i < kTT / 4; ++i) {
-        const int r = (tid >> 6) + 4 * i;
+    for (int i = 0; i < TT / RPP; ++i) {
+        const int r = tid / TT + RPP * i;
         float v = 0.0f;
         if (col_in && r0 + r < rows_in) v = X[(r0 + r) * ldx + c0 + c];
         tile[r][c] = v;
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < (TT * TT / 8 + 255) / 256; ++j) {
         const int u = tid + 256 * j;
-        const int kg = u & 7, n = u >> 3;
-        if (c0 + n >= cols || r0 + 8 * kg >= rows) continue;  // rows % 8 == 0: groups are whole
+        const int kg = u % (TT / 8), n = u / (TT / 8);
+        if (n >= TT || c0 + n >= cols || r0 + 8 * kg >= rows) continue;  // rows % 8 == 0: groups are whole
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = tile[8 * kg + e][n];
@@ -124,10 +124,17 @@ static hipError_t split_transpose_with(int64_t rows, int64_t cols, const float *
                            X0, X1, X2, ldo, rows, cols);
         return hipGetLastError();
     }
-    const int64_t tiles_c = (cols + kTT - 1) / kTT, tiles_r = (rows + kTT - 1) / kTT;
-    if (tiles_r > (int64_t)0x7FFFFFFF / tiles_c) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(split_transpose_kernel<RNE>, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, stream, X,
-                       ldx, X0, X1, X2, ldo, rows_in, rows, cols, tiles_c);
+    const int64_t tiles64 = ((cols + 63) / 64) * ((rows + 63) / 64);
+    if (tiles64 >= num_cus) {
+        const int64_t tiles_c = (cols + 63) / 64, tiles_r = (rows + 63) / 64;
+        if (tiles_r > (int64_t)0x7FFFFFFF / tiles_c) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((split_transpose_kernel<RNE, 64>), dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0,
+                           stream, X, ldx, X0, X1, X2, ldo, rows_in, rows, cols, tiles_c);
+    } else {
+        const int64_t tiles_c = (cols + 31) / 32, tiles_r = (rows + 31) / 32;
+        hipLaunchKernelGGL((split_transpose_kernel<RNE, 32>), dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0,
+                           stream, X, ldx, X0, X1, X2, ldo, rows_in, rows, cols, tiles_c);
+    }
     return hipGetLastError();
 }
 

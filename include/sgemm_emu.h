@@ -23,11 +23,12 @@
  *     acc = fma(S1, 2^-8, acc), C = acc + S0;
  *   - the order of additions inside a band is the matrix unit's; results are
  *     deterministic for a given shape, entry point and device (no atomics) but
- *     not bitwise equal to a sequential sum.  Small tile grids split K into
- *     slices (sgemm_emu_split_k): each slice runs the method on its K range and
- *     the slices' FP32 results are added in slice order; if the device memory
- *     for those partial sums cannot be had, the call returns SGEMM_EMU_ENOMEM
- *     rather than round another way.
+ *     not bitwise equal to a sequential sum.  Small tile grids share their
+ *     (tile, K range) work among all CUs (stream-K, see sgemm_emu_split_k):
+ *     each piece of a tile runs the method on its K range and the pieces' FP32
+ *     results are added in K order; if the device memory for those partial
+ *     results cannot be had, the call returns SGEMM_EMU_ENOMEM rather than
+ *     round another way.
  *   - non-finite inputs follow IEEE rules on the components (Inf times a zero
  *     component is NaN), so results are not IEEE-754 SGEMM results for them.
  *
@@ -46,14 +47,14 @@
  *   (K' = K rounded up to a multiple of 64) split B once into an N x K' set
  *   of BF16 planes, zero past K (6 K' N bytes), where that is faster than
  *   splitting B inside the GEMM kernel: when the tile grid is small enough
- *   for split-K, or when 2 M N K >= 1.2e10 (sgemm_emu_ex's
+ *   for stream-K, or when 2 M N K >= 1.2e10 (sgemm_emu_ex's
  *   SGEMM_EMU_PRESPLIT_B asks for it whenever M and K' N allow).  Where B is
  *   split so and N >= 4096 (each A element would be split again in each of
  *   the N / 128 tile columns), with K % 64 == 0 and M K <= 2^28, A is split
  *   into workspace planes too (6 M K more bytes) and a kernel that copies
  *   both operands' planes runs (SGEMM_EMU_PRESPLIT_A asks for it whenever
  *   those allow).  All ways give bitwise the same result.  GEMMs on small
- *   tile grids also need a split-K buffer (see sgemm_emu_split_k).  All of
+ *   tile grids also need stream-K partial slots (see sgemm_emu_split_k).  All of
  *   it lives in one grow-only
  *   workspace block per stream, which the stream's later calls reuse (stream
  *   order keeps them apart; an event recorded after each use orders the next
@@ -66,7 +67,7 @@
  *   stream being captured into a graph the library allocates nothing.  If
  *   no workspace can be had (or the stream is capturing) the GEMM splits B
  *   inside its kernel (bitwise the same result); a small-grid shape whose
- *   K-split partial buffer cannot be had returns SGEMM_EMU_ENOMEM (while
+ *   stream-K partial slots cannot be had returns SGEMM_EMU_ENOMEM (while
  *   capturing: SGEMM_EMU_ECAPTURE) with nothing enqueued, so the bits of a
  *   shape never depend on the memory available.  Callers that must capture
  *   such shapes, or cannot let the library allocate, use
@@ -105,8 +106,8 @@ enum sgemm_emu_status {
     SGEMM_EMU_ELAUNCH = -4, /* the kernel launch itself failed (hipGetLastError), or a HIP call of
                                sgemm_emu_release_workspace failed */
     SGEMM_EMU_ENOMEM = -5,  /* a GEMM on a small tile grid could not get device memory for its
-                               K-split partial sums (see sgemm_emu_split_k); nothing was enqueued */
-    SGEMM_EMU_ECAPTURE = -6 /* the call needs workspace (K-split partial sums, the IEEE fix-up's
+                               stream-K partial results (see sgemm_emu_split_k); nothing was enqueued */
+    SGEMM_EMU_ECAPTURE = -6 /* the call needs workspace (stream-K partial results, the IEEE fix-up's
                                flags) and its stream is being captured into a graph, where the
                                library allocates nothing; nothing was enqueued */
 };
@@ -229,19 +230,20 @@ int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
  * sgemm_emu_presplit_b_noalloc -- sgemm_emu_presplit_b with N x K planes
  * (SGEMM_EMU_B_NK layout, ldb >= max(1, K)) that allocates no device memory,
  * for callers that cannot allocate: code under HIP graph capture, tight
- * serving loops, harnesses that forbid hipMalloc.  Same kernels and K split as
- * sgemm_emu_presplit_b, so the same bits (the separate split of A into
- * workspace planes that sgemm_emu_presplit_b makes for N >= 4096 is skipped;
- * the kernel that splits A itself gives the same result).  The K-split partial
- * sums of small tile grids go to a fixed array in device memory, 16 MiB per
- * device (256 x 128 x 128 floats), held from the library's first such call on
- * the device until the process ends; a shape that would need more (S x M x N
- * floats, see sgemm_emu_split_k; never on a 256-CU MI355X) returns
- * SGEMM_EMU_ENOMEM.  All calls on one device share that array: calls that
- * overlap in time on one device (two streams, or two host threads) race on
- * it and must be ordered by the caller.  Every element a call reads from the
- * array it has written first, so nothing needs clearing.  Other arguments and
- * errors as sgemm_emu_presplit_b.
+ * serving loops, harnesses that forbid hipMalloc.  Same kernels and K
+ * partition as sgemm_emu_presplit_b, so the same bits (the separate split of
+ * A into workspace planes that sgemm_emu_presplit_b makes for N >= 4096 is
+ * skipped; the kernel that splits A itself gives the same result).  The
+ * stream-K partial results and flags of small tile grids go to a fixed array
+ * in device memory, 16 MiB + 1 KiB per device (one 128 x 128 FP32 slot and one
+ * flag word for each of at most 256 workgroups), held from the library's load
+ * on the device until the process ends; a device whose stream-K grid would
+ * have more workgroups (more than 256 CUs) gets SGEMM_EMU_ENOMEM for such
+ * shapes.  All calls on one device share that array: calls that overlap in
+ * time on one device (two streams, or two host threads) race on it and must
+ * be ordered by the caller.  Each call marks its flags with a new value and
+ * reads only slots whose flags carry it, so nothing needs clearing.  Other
+ * arguments and errors as sgemm_emu_presplit_b.
  */
 int sgemm_emu_presplit_b_noalloc(int64_t M, int64_t N, int64_t K,
                                  const float *A, int64_t lda,
@@ -321,21 +323,24 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
                                 sgemm_emu_stream_t stream);
 
 /*
- * sgemm_emu_split_k -- the number of K slices (split-K) the GEMM uses for an
- * M x N x K product on the current device when it runs the N x K plane kernel
- * (sgemm_emu_presplit_b with SGEMM_EMU_B_NK and sgemm_emu_linear, which need
- * K % 64 == 0 and 16-byte aligned planes with ldb % 8 == 0; sgemm_bf16x9 /
- * sgemm_emu when they pre-split B, with K rounded up to a multiple of 64).
- * 1 means one pass over K per output tile.  With S > 1 slices (grids that
- * would leave a quarter of the CUs idle), each (tile, slice) runs the method
- * on its K range (five band sums, recombined smallest band first) and writes
- * its FP32 result to the stream's workspace (S * M * N floats, see the
- * device-memory conventions above); a reduction kernel adds the
- * S results in slice order, then the bias and activation.  Results differ in
- * rounding from the one-pass order (still within the same error bound) and
- * are deterministic for a given shape and device.  If that workspace cannot
- * be had the GEMM returns SGEMM_EMU_ENOMEM.  Returns S >= 1, or a negative
- * status (invalid sizes or nbands, no gfx950 device).
+ * sgemm_emu_split_k -- the largest number of pieces along K that any output
+ * tile of an M x N x K product is cut into on the current device when the
+ * GEMM runs the N x K plane kernel (sgemm_emu_presplit_b with SGEMM_EMU_B_NK
+ * and sgemm_emu_linear, which need K % 64 == 0 and 16-byte aligned planes with
+ * ldb % 8 == 0; sgemm_bf16x9 / sgemm_emu when they pre-split B, with K rounded
+ * up to a multiple of 64).  1 means one pass over K per 128 x 128 output tile.
+ * Grids that would leave a quarter of the CUs idle are shared out stream-K
+ * style: the (tile, 64-wide K range) units, tile by tile, are cut into equal
+ * runs, one per workgroup (at most one per CU, each run at least two units);
+ * each piece of a tile runs the method on its K range (five band sums,
+ * recombined smallest band first); the workgroup holding a tile's last K range
+ * adds the other pieces' FP32 results (from the stream's workspace: a
+ * 128 x 128 slot and a flag word per workgroup) in K order, then its own, then
+ * the bias and activation.  Results differ in rounding from the one-pass order
+ * (still within the same error bound) and are deterministic for a given shape
+ * and device.  If that workspace cannot be had the GEMM returns
+ * SGEMM_EMU_ENOMEM.  Returns the count >= 1, or a negative status (invalid
+ * sizes or nbands, no gfx950 device).
  */
 int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands);
 

@@ -30,7 +30,11 @@ hipError_t launch_gemm(const GemmArgs &, int, BSource, hipStream_t, bool) { retu
 
 hipError_t launch_gemm_planes(const GemmArgs &, int, hipStream_t) { return hipErrorNotSupported; }
 
-int gemm_split_count(int64_t, int64_t, int64_t, int, int) { return 1; }
+int gemm_streamk_grid(int64_t, int64_t, int64_t, int) { return 0; }
+
+int gemm_streamk_pieces(int64_t, int64_t, int64_t, int) { return 1; }
+
+bool launch_done_attached(const GemmArgs &, BSource) { return false; }
 
 bool gemm_uses_dma(int64_t, int64_t, const void *, const void *, const void *) { return false; }
 

@@ -243,8 +243,9 @@ def test_presplit_a_rule_at_4096_columns(fe):
     """With N >= 4096 (M >= 1024, K % 64 == 0) A is split into workspace planes
     by default, for FP32 B (sgemm_bf16x9) and beside a caller's N x K planes
     alike: within the bound on sampled rows, and bit for bit the N x K planes
-    run in row blocks below 1024 rows, where the kernel splits A itself."""
-    M, N, K = 1100, 4096, 192
+    run in row blocks below 1024 rows, where the kernel splits A itself (each
+    block still at least 192 tiles, so no block is cut along K)."""
+    M, N, K = 1600, 4096, 192
     g = _rng(940)
     A = g.standard_normal((M, K)).astype(np.float32)
     B = g.standard_normal((K, N)).astype(np.float32)
@@ -252,7 +253,7 @@ def test_presplit_a_rule_at_4096_columns(fe):
     rows = np.sort(g.choice(M, size=32, replace=False))
     check_against_fp64(C[rows], A, B, rows=rows, label="A pre-split rule")
     Cnk = run(fe, A, B, entry="presplit_t")
-    blocks = np.concatenate([run(fe, A[i:i + 550], B, entry="presplit_t") for i in range(0, M, 550)])
+    blocks = np.concatenate([run(fe, A[i:i + 800], B, entry="presplit_t") for i in range(0, M, 800)])
     assert np.array_equal(C.view(np.uint32), Cnk.view(np.uint32))
     assert np.array_equal(C.view(np.uint32), blocks.view(np.uint32))
 
@@ -372,8 +373,8 @@ SPLITK_SHAPES = [(1024, 1024, 1024), (6144, 256, 1024), (129, 130, 1024), (64, 3
 
 @pytest.mark.parametrize("shape", SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_split_k_within_bound_and_deterministic(fe, shape):
-    """Small tile grids split K: per-slice band sums, added slice by slice, then
-    recombined.  Within the bound, identical on repeat, and sgemm_bf16x9 on FP32 B
+    """Small tile grids share their work stream-K style: each piece of a tile
+    runs the method on its K range, the pieces' results are added in K order.  Within the bound, identical on repeat, and sgemm_bf16x9 on FP32 B
     agrees with the caller-split planes whenever both take the plane kernel."""
     M, N, K = shape
     assert fe.sgemm_emu_split_k(M, N, K) > 1
@@ -426,15 +427,16 @@ def test_split_k_special_values_class(fe, orc):
 
 @pytest.mark.parametrize("entry", ["fused", "presplit_t"])
 def test_split_k_exact_integers_bitwise_vs_oracle(fe, orc, entry):
-    """Split-K on a shape where every partial result is exact: 1024 x 512 x 2048
-    runs as 8 K slices of 256.  A holds 48 nonzero integers per row (|a| < 2^9, so
-    the split puts them into bands 0-2), B nonzero integers of the same size.
-    Each band sum, each slice's recombination and the sum of the slices are then
-    integers below 2^24, exact in any order, so the GPU result must equal the
-    exact dot product and the oracle's one-pass emulation (slices recombined
-    separately and added give the same bits as one recombination over all K)."""
+    """Stream-K on a shape where every partial result is exact: 1024 x 512 x 2048
+    (32 tiles of 32 K pairs shared by all CUs, each tile cut into several
+    pieces).  A holds 48 nonzero integers per row (|a| < 2^9, so the split puts
+    them into bands 0-2), B nonzero integers of the same size.  Each band sum,
+    each piece's recombination and the sum of the pieces are then integers below
+    2^24, exact in any order, so the GPU result must equal the exact dot product
+    and the oracle's one-pass emulation (pieces recombined separately and added
+    give the same bits as one recombination over all K)."""
     M, N, K = 1024, 512, 2048
-    assert fe.sgemm_emu_split_k(M, N, K) == 8
+    assert fe.sgemm_emu_split_k(M, N, K) > 1
     g = _rng(2048)
     A = np.zeros((M, K), np.float32)
     for i in range(M):

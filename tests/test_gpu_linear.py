@@ -161,12 +161,13 @@ def test_input_gradient_transposed_planes_bitwise(fe, shape):
     fe.sgemm_emu_presplit_b(M, K, N, dYd, N, *P, K, fe.SGEMM_EMU_B_KN, a, K, 5)
     fe.sgemm_emu_presplit_b(M, K, N, dYd, N, *T, N, fe.SGEMM_EMU_B_NK, b, K, 5)
     check_against_fp64(host(b), dY, W, label=f"dX planes of W^T {shape}")
-    if fe.sgemm_emu_split_k(M, K, N) == 1:          # else the N x K kernel adds slice by slice
+    if fe.sgemm_emu_split_k(M, K, N) == 1:          # else the N x K kernel adds K pieces
         assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
 
 
 def test_forward_split_k_with_bias_and_gelu(fe, orc):
-    """A small grid (split-K): bias and GELU are applied by the reduction."""
+    """A small grid (stream-K): bias and GELU are applied by the workgroup that
+    adds a tile's K pieces."""
     M, N, K = 200, 140, 1024
     assert fe.sgemm_emu_split_k(M, N, K) > 1
     g = _rng(808)

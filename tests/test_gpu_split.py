@@ -66,9 +66,11 @@ def test_split_empty_is_noop(fe):
 
 
 @pytest.mark.parametrize("rows,cols,ldx,ldo", [
-    (64, 64, 64, 64),           # one LDS tile
-    (256, 1024, 1024, 256),     # a [out][in] weight, tiled kernel
+    (64, 64, 64, 64),           # small: 32 x 32 LDS tiles
+    (256, 1024, 1024, 256),     # a [out][in] weight, 32 x 32 tiles
     (1024, 257, 260, 1032),     # ragged columns, padded leading dimensions
+    (1024, 1024, 1024, 1024),   # 64 x 64 LDS tiles (at least one per CU)
+    (2048, 520, 530, 2056),     # 64 x 64 tiles, ragged, padded
     (130, 70, 70, 130),         # rows not a multiple of 8: scalar kernel
     (24, 5, 7, 40),
 ])
@@ -113,7 +115,8 @@ def test_split_rne_all_encodings_bit_exact(fe, orc):
 @pytest.mark.parametrize("rows,cols,ldx,ldo,flags", [
     (37, 53, 53, 53, 1),        # scalar kernel, RNE
     (64, 256, 256, 256, 1),     # vector kernel, RNE
-    (256, 1024, 1024, 256, 3),  # transposed, tiled, RNE
+    (256, 1024, 1024, 256, 3),  # transposed, 32 x 32 tiles, RNE
+    (1024, 1024, 1024, 1024, 3),  # transposed, 64 x 64 tiles, RNE
     (130, 70, 70, 130, 3),      # transposed, element-wise, RNE
 ])
 def test_split_ex_layouts(fe, orc, rows, cols, ldx, ldo, flags):

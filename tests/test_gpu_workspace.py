@@ -204,13 +204,13 @@ def test_graph_capture_allocates_nothing(fe):
     def mat(r, c):
         return dev(g.standard_normal((r, c)).astype(np.float32))
 
-    # (a) N x K planes, a grid with no K split and N < 4096 (no A planes)
-    M1, N1, K1 = 1024, 512, 256
+    # (a) N x K planes, a grid with no K split (192 tiles) and N < 4096 (no A planes)
+    M1, N1, K1 = 4096, 768, 256
     A1, Bt1 = mat(M1, K1), mat(N1, K1)
     P1 = [torch.empty((N1, K1), dtype=torch.int16, device="cuda") for _ in range(3)]
     fe.split_f32_bf16x3(N1, K1, Bt1, K1, *P1, K1)
     # (b) FP32 B with the pre-split forced (workspace planes when eager)
-    M2, N2, K2 = 2048, 1024, 256
+    M2, N2, K2 = 4096, 1024, 256
     A2, B2 = mat(M2, K2), mat(K2, N2)
     assert fe.sgemm_emu_split_k(M1, N1, K1) == 1 and fe.sgemm_emu_split_k(M2, N2, K2) == 1
     ref1 = torch.empty((M1, N1), device="cuda")

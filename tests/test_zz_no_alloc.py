@@ -1,8 +1,8 @@
 """The entry point that allocates nothing, against the one it mirrors.
 
 sgemm_emu_presplit_b_noalloc runs the kernels of sgemm_emu_presplit_b with
-N x K planes and keeps the K-split partial sums of small tile grids in a fixed
-device array instead of allocated workspace.  Called through the C ABI twice in
+N x K planes and keeps the stream-K partial results and flags of small tile
+grids in a fixed device array instead of allocated workspace.  Called through the C ABI twice in
 a row (the second call smaller, so it reuses the array the first one left
 behind), each result must equal sgemm_emu_presplit_b's bit for bit, and the
 first is also held to the oracle's FP64 bound.
@@ -46,8 +46,8 @@ def _case(fe, M, N, K, seed):
 def test_noalloc_matches_presplit_b_twice(fe):
     f = _noalloc(fe)
     stream = torch.cuda.current_stream().cuda_stream
-    # both shapes split K (8 slices of 1024 x 512, then 4 of 129 x 130), so both
-    # keep partial sums in the fixed array; the second finds the first's there
+    # both shapes cut their tiles along K (stream-K), so both keep partial
+    # results and flags in the fixed array; the second finds the first's there
     for n, (M, N, K, nb) in enumerate([(1024, 512, 2048, 5), (129, 130, 1024, 5), (300, 260, 192, 3)]):
         print(f"noalloc call {n}: {M}x{N}x{K} nbands={nb} split_k={fe.sgemm_emu_split_k(M, N, K, nb)}",
               flush=True, file=sys.stderr)
