@@ -1543,19 +1543,19 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_planes_kernel(GemmArgs g
 
 // C = act(sum over K slices of the slices' recombined results + bias), per
 // element, adding the slices in slice order.
+// Workgroups walk rows, threads walk a row's columns (no per-element division).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g)
 {
-    const int64_t total = g.M * g.N;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t plane = g.M * g.ldp;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-        const int64_t r = e / g.N, c = e - r * g.N;
-        const float *p = g.partials + r * g.ldp + c;
-        float v = p[0];
-        for (int sl = 1; sl < g.splits; ++sl) v += p[(int64_t)sl * plane];
-        v = v + (g.bias ? g.bias[c] : -0.0f);
-        if (g.act == 1) v = gelu_erf(v);
-        g.C[r * g.ldc + c] = v;
+    for (int64_t r = blockIdx.x; r < g.M; r += gridDim.x) {
+        for (int64_t c = threadIdx.x; c < g.N; c += blockDim.x) {
+            const float *p = g.partials + r * g.ldp + c;
+            float v = p[0];
+            for (int sl = 1; sl < g.splits; ++sl) v += p[(int64_t)sl * plane];
+            v = v + (g.bias ? g.bias[c] : -0.0f);
+            if (g.act == 1) v = gelu_erf(v);
+            g.C[r * g.ldc + c] = v;
+        }
     }
 }
 
@@ -1812,8 +1812,7 @@ static hipError_t launch_native_cfg(const GemmArgs &args, int splits, hipStream_
     if (vec) launch_last(gemm_f32_native_kernel<C, true>, grid, block, stream, gk);
     else launch_last(gemm_f32_native_kernel<C, false>, grid, block, stream, gk);
     if (splits > 1) {
-        int64_t blocks = (g.M * g.N + 255) / 256;
-        if (blocks > (int64_t)g.num_cus * 8) blocks = (int64_t)g.num_cus * 8;
+        const int64_t blocks = g.M < (int64_t)g.num_cus * 8 ? g.M : (int64_t)g.num_cus * 8;   // rows
         launch_last(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), stream, g);
     }
     return hipGetLastError();
@@ -1850,21 +1849,19 @@ hipError_t launch_native(const GemmArgs &args, const NativePlan &plan, hipStream
 __global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ C, int64_t ldc, int64_t M, int64_t N,
                                                    const float *__restrict__ bias, int act)
 {
-    const int64_t total = M * N;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-        const int64_t r = e / N, c = e - r * N;
-        float v = bias ? 0.0f + bias[c] : 0.0f;
-        if (act == 1) v = gelu_erf(v);
-        C[r * ldc + c] = v;
+    for (int64_t r = blockIdx.x; r < M; r += gridDim.x) {
+        for (int64_t c = threadIdx.x; c < N; c += blockDim.x) {
+            float v = bias ? 0.0f + bias[c] : 0.0f;
+            if (act == 1) v = gelu_erf(v);
+            C[r * ldc + c] = v;
+        }
     }
 }
 
 hipError_t launch_zero(int64_t M, int64_t N, float *C, int64_t ldc, const float *bias, int act, int num_cus,
                        hipStream_t stream)
 {
-    int64_t blocks = (M * N + 255) / 256;
-    if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
+    const int64_t blocks = M < (int64_t)num_cus * 8 ? M : (int64_t)num_cus * 8;   // rows
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, ldc, M, N, bias, act);
     return hipGetLastError();
 }

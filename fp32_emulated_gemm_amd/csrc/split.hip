@@ -77,8 +77,10 @@ __global__ __launch_bounds__(256) void split_transpose_kernel(
     // rows_in <= rows: X rows past rows_in read as zero (a zero-padded K extent)
     __shared__ float tile[TT][TT + 1];
     constexpr int RPP = 256 / TT;                       // rows read per pass
-    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * TT;
-    const int64_t c0 = (int64_t)(blockIdx.x % tiles_c) * TT;
+    // 32-bit block arithmetic: the launcher keeps the tile count below 2^31
+    const uint32_t tc = (uint32_t)tiles_c, br = blockIdx.x / tc;
+    const int64_t r0 = (int64_t)br * TT;
+    const int64_t c0 = (int64_t)(blockIdx.x - br * tc) * TT;
     const int tid = threadIdx.x;
     const int c = tid & (TT - 1);
     const bool col_in = c0 + c < cols;
@@ -152,8 +154,9 @@ __global__ __launch_bounds__(256) void transpose_planes_kernel(
     int64_t rows_out, int64_t cols, int64_t tiles_c)
 {
     __shared__ uint16_t tile[3][kPT][kPT + 2];
-    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kPT;
-    const int64_t c0 = (int64_t)(blockIdx.x % tiles_c) * kPT;
+    const uint32_t tc = (uint32_t)tiles_c, br = blockIdx.x / tc;   // fewer than 2^31 tiles
+    const int64_t r0 = (int64_t)br * kPT;
+    const int64_t c0 = (int64_t)(blockIdx.x - br * tc) * kPT;
     const int tid = threadIdx.x;
     const uint16_t *P[3] = {P0, P1, P2};
     {
