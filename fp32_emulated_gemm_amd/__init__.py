@@ -59,6 +59,7 @@ SGEMM_EMU_PRESPLIT_B = 8       # flag (sgemm_emu_ex): split FP32 B once into wor
 SGEMM_EMU_PRESPLIT_A = 16      # flag (sgemm_emu_ex): split FP32 A (and B) once into workspace planes whenever allowed
 SGEMM_EMU_PERFORMANT = 32      # flag (sgemm_emu_ex): emulate only where faster than the native FP32 kernel
 SGEMM_EMU_NATIVE_FP32 = 64     # flag (sgemm_emu_ex): the library's native FP32 kernel
+SGEMM_EMU_NO_WORKSPACE = 128   # flag (sgemm_emu_ex): in-kernel split, no stream-K, nothing allocated
 
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_presplit_b_noalloc",
            "sgemm_emu_linear",

@@ -318,7 +318,7 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
                 int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
                 int act = SGEMM_EMU_ACT_NONE, bool rne = false, bool force_presplit = false,
-                bool force_presplit_a = false)
+                bool force_presplit_a = false, bool no_workspace = false)
 {
     int rc;
     if ((rc = validate_gemm(M, N, K, A, lda, B, B0, B1, B2, ldb, C, ldc, nbands, bsrc, bias, act)) != SGEMM_EMU_OK)
@@ -346,19 +346,21 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // MFMA accumulation, so the result is bitwise identical (zero-padded K
     // steps add zero products).  A K that is not a multiple of 64 is padded in
     // the planes (zeros) and the kernel masks A past its K.
+    // Where pays: grids small enough for stream-K (which only the DMA kernel
+    // runs, whatever M), and from M >= 1024 rows large GEMMs.
     const int64_t kpad = (K + 63) / 64 * 64;
-    const bool presplit = bsrc == B_FP32 && M >= kPresplitMinRows &&
-                          (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !(rne && kpad != K) &&
-                          (force_presplit || gemm_streamk_grid(M, N, kpad, num_cus) > 0 ||
-                           2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
+    const bool small_grid = !no_workspace && gemm_streamk_grid(M, N, kpad, num_cus) > 0;
+    const bool large = !no_workspace && M >= kPresplitMinRows &&
+                       2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops;
+    const bool presplit = bsrc == B_FP32 && (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems &&
+                          !(rne && kpad != K) &&
+                          ((force_presplit && M >= kPresplitMinRows) || small_grid || large);
     // K x N planes, by the same rule: transposed once into N x K' planes in the
     // workspace, so the LDS-DMA kernel runs instead of the kernel that stages
     // K x N planes through registers (same planes and products, same order:
     // bitwise the same result).
-    const bool transpose_kn = bsrc == B_PLANES_KN && M >= kPresplitMinRows &&
-                              (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !rne &&
-                              (gemm_streamk_grid(M, N, kpad, num_cus) > 0 ||
-                               2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops);
+    const bool transpose_kn = bsrc == B_PLANES_KN && (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !rne &&
+                              (small_grid || large);
     const size_t plane = (presplit || transpose_kn) ? (size_t)N * (size_t)kpad * sizeof(uint16_t) : 0;
     const size_t plane_pad = (plane + 255) & ~(size_t)255;
     // A as well (K needs no padding; A's planes are M x K, k contiguous), also
@@ -368,8 +370,9 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // K pair) units among all CUs (stream-K): partial slots and flags in the
     // workspace.  Stream-K splits A inside the kernel.
     const bool dma = presplit || transpose_kn || nk_dma;
-    const int skg = dma ? gemm_streamk_grid(M, N, (presplit || transpose_kn) ? kpad : K, num_cus) : 0;
-    const bool presplit_a = (presplit || transpose_kn || (nk_dma && M >= kPresplitMinRows)) && kpad == K &&
+    const int skg = dma && !no_workspace ? gemm_streamk_grid(M, N, (presplit || transpose_kn) ? kpad : K, num_cus) : 0;
+    const bool presplit_a = !no_workspace && (presplit || transpose_kn || (nk_dma && M >= kPresplitMinRows)) &&
+                            kpad == K &&
                             (uint64_t)M * (uint64_t)K <= kPresplitMaxElems && skg == 0 &&
                             (force_presplit_a || N >= kPresplitAMinCols);
     const size_t aplane = presplit_a ? (size_t)M * (size_t)K * sizeof(uint16_t) : 0;
@@ -469,12 +472,18 @@ int gemm_native(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
 
 // The performant strategy's choice (sgemm_emu_ex with SGEMM_EMU_PERFORMANT):
 // true where the native FP32 kernel is expected to be faster than all nine
-// BF16 products on this device.
+// BF16 products.  Measured on MI355X (256 CUs): the native kernel wins on every
+// shape up to 1024^3 (2.1 GFLOP; e.g. 512^3 17.5 against 11.0 TFLOP/s,
+// 1024^3 58.5 against 53.9), where launch latency and the K pieces' partial
+// sums weigh on the nine products; the emulation from 3.2 GFLOP up
+// (6144 x 256 x 1024 77.7 against 63.0, 6144 x 1024 x 256 92.9 against 82.2,
+// 4096^3 150 against 129).
+constexpr double kPerformantMinFlops = 2.5e9;
+
 bool performant_prefers_native(int64_t M, int64_t N, int64_t K, int num_cus)
 {
-    (void)K;
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    return tiles < 2 * (int64_t)num_cus;
+    (void)num_cus;
+    return 2.0 * (double)M * (double)N * (double)K < kPerformantMinFlops;
 }
 
 // ---------------------------------------------------------------- fixed scratch
@@ -577,7 +586,10 @@ int sgemm_emu_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, c
                  float *C, int64_t ldc, int nbands, int flags, sgemm_emu_stream_t stream)
 {
     if ((flags & ~(SGEMM_EMU_SPLIT_RNE | SGEMM_EMU_IEEE_SPECIALS | SGEMM_EMU_PRESPLIT_B | SGEMM_EMU_PRESPLIT_A |
-                   SGEMM_EMU_PERFORMANT | SGEMM_EMU_NATIVE_FP32)) != 0)
+                   SGEMM_EMU_PERFORMANT | SGEMM_EMU_NATIVE_FP32 | SGEMM_EMU_NO_WORKSPACE)) != 0)
+        return SGEMM_EMU_EINVAL;
+    // no workspace: only the split's rounding may be chosen beside it
+    if ((flags & SGEMM_EMU_NO_WORKSPACE) && (flags & ~(SGEMM_EMU_NO_WORKSPACE | SGEMM_EMU_SPLIT_RNE)) != 0)
         return SGEMM_EMU_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     int rc;
@@ -609,7 +621,7 @@ int sgemm_emu_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, c
         rc = gemm_common(M, N, K, A, lda, B, nullptr, nullptr, nullptr, ldb, C, ldc, nbands, B_FP32, s, nullptr,
                          SGEMM_EMU_ACT_NONE, (flags & SGEMM_EMU_SPLIT_RNE) != 0,
                          (flags & (SGEMM_EMU_PRESPLIT_B | SGEMM_EMU_PRESPLIT_A)) != 0,
-                         (flags & SGEMM_EMU_PRESPLIT_A) != 0);
+                         (flags & SGEMM_EMU_PRESPLIT_A) != 0, (flags & SGEMM_EMU_NO_WORKSPACE) != 0);
     if (rc != SGEMM_EMU_OK || !(flags & SGEMM_EMU_IEEE_SPECIALS) || M == 0 || N == 0 || K == 0) return rc;
     // IEEE fix-up of the outputs touched by non-finite inputs (flags and a
     // column list in a pooled stream-ordered buffer)

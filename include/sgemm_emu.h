@@ -43,12 +43,14 @@
  *   synchronisation, as in BLAS libraries.
  *   Arguments are validated before any HIP call; on an error status nothing
  *   has been enqueued.
- *   Device memory: sgemm_bf16x9 and sgemm_emu with M >= 1024 and K' * N <= 2^28
- *   (K' = K rounded up to a multiple of 64) split B once into an N x K' set
- *   of BF16 planes, zero past K (6 K' N bytes), where that is faster than
- *   splitting B inside the GEMM kernel: when the tile grid is small enough
- *   for stream-K, or when 2 M N K >= 1.2e10 (sgemm_emu_ex's
- *   SGEMM_EMU_PRESPLIT_B asks for it whenever M and K' N allow).  Where B is
+ *   Device memory: sgemm_bf16x9 and sgemm_emu with K' * N <= 2^28 (K' = K
+ *   rounded up to a multiple of 64) split B once into an N x K' set of BF16
+ *   planes, zero past K (6 K' N bytes), where that is faster than splitting
+ *   B inside the GEMM kernel: when the tile grid is small enough for
+ *   stream-K (any M), or when M >= 1024 and 2 M N K >= 1.2e10 (sgemm_emu_ex's
+ *   SGEMM_EMU_PRESPLIT_B asks for it whenever M >= 1024 and K' N allow).
+ *   sgemm_emu_presplit_b with K x N planes follows the same rule, with the
+ *   planes transposed into the workspace instead of split.  Where B is
  *   split so and N >= 4096 (each A element would be split again in each of
  *   the N / 128 tile columns), with K % 64 == 0 and M K <= 2^28, A is split
  *   into workspace planes too (6 M K more bytes) and a kernel that copies
@@ -161,15 +163,22 @@ enum sgemm_emu_flags {
                                        strategy -- all nine BF16 products only where the library expects
                                        them to be faster than its native FP32 kernel on this shape, the
                                        native FP32 kernel elsewhere (see sgemm_emu_ex) */
-    SGEMM_EMU_NATIVE_FP32 = 64      /* sgemm_emu_ex only, nbands 5, truncating split: always the native
+    SGEMM_EMU_NATIVE_FP32 = 64,     /* sgemm_emu_ex only, nbands 5, truncating split: always the native
                                        FP32 kernel (the strategy's other branch, on its own) */
+    SGEMM_EMU_NO_WORKSPACE = 128    /* sgemm_emu_ex only, alone or with SGEMM_EMU_SPLIT_RNE: never use
+                                       the stream's workspace -- B (and A) are split inside the GEMM
+                                       kernel and every tile runs its whole K in one workgroup (no
+                                       stream-K), so nothing is allocated, also while the stream is
+                                       being captured; small grids then run slower, and their bits can
+                                       differ from the default's (both within the same bound) */
 };
 
 /*
  * sgemm_emu_ex -- sgemm_emu with flags (SGEMM_EMU_SPLIT_RNE,
  * SGEMM_EMU_IEEE_SPECIALS, SGEMM_EMU_PRESPLIT_B, SGEMM_EMU_PRESPLIT_A,
- * SGEMM_EMU_PERFORMANT, SGEMM_EMU_NATIVE_FP32; other bits give
- * SGEMM_EMU_EINVAL).
+ * SGEMM_EMU_PERFORMANT, SGEMM_EMU_NATIVE_FP32, SGEMM_EMU_NO_WORKSPACE; other
+ * bits give SGEMM_EMU_EINVAL, and so does SGEMM_EMU_NO_WORKSPACE beside any
+ * flag but SGEMM_EMU_SPLIT_RNE).
  * Strategy flags: the pages' cuBLAS integration offers an "eager" strategy
  * (emulate whenever the operation allows) and a "performant" one (emulate only
  * where a speed-up over native FP32 is expected) (NVIDIA blog, section "BF16x9
@@ -177,8 +186,8 @@ enum sgemm_emu_flags {
  * "PyTorch에서 직접 써 보려면").  Without a strategy flag every entry point is
  * eager.  With SGEMM_EMU_PERFORMANT the library runs its native FP32 kernel
  * (v_mfma_f32_32x32x2_f32: FP32 products, FP32 accumulation, one pass over K
- * per output, or K slices added in order on small tile grids) for shapes whose
- * 128 x 128 tile grid holds fewer than two tiles per compute unit, and the
+ * per output, or K slices added in order on small tile grids) for GEMMs of
+ * fewer than 2.5e9 flops (2 M N K), where it measured faster, and the
  * nine-product emulation otherwise; SGEMM_EMU_NATIVE_FP32 always runs the
  * native kernel.  The native kernel's results are IEEE FP32 dot products in
  * the matrix unit's order of additions (within the same elementwise bound as

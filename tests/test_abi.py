@@ -108,7 +108,11 @@ def test_split_validation(L):
 
 def test_ex_entry_flags(L):
     assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 2, None) == -1     # transpose is a split flag
-    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 128, None) == -1   # unknown flag
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 256, None) == -1   # unknown flag
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 128 | 8, None) == -1   # no workspace and pre-split
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 128 | 32, None) == -1  # no workspace and a strategy
+    assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 128 | 4, None) == -1   # no workspace and IEEE fix-up
+    assert L.sgemm_emu_ex(0, 4, 4, 0, 4, 0, 4, 0, 4, 5, 128 | 1, None) == 0    # no workspace, RNE: empty
     assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 4, 32, None) == -1    # performant needs nbands 5
     assert L.sgemm_emu_ex(4, 4, 4, P, 4, P, 4, P, 4, 5, 64 | 1, None) == -1  # native: no RNE split
     assert L.sgemm_emu_ex(4, 4, 4, P, 3, P, 4, P, 4, 5, 64, None) == -1    # native: lda < K

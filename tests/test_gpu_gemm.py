@@ -52,6 +52,8 @@ def run(fe, A, B, nbands=5, entry="fused", ldc_pad=0, a_offset=0):
         fe.sgemm_emu_presplit_b(M, N, K, Ad, lda, *planes, max(K, 1), fe.SGEMM_EMU_B_NK, Cd, max(ldc, 1), nbands)
     elif entry == "fused_ws":
         fe.sgemm_emu_ex(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1), nbands, fe.SGEMM_EMU_PRESPLIT_B)
+    elif entry == "fused_nows":
+        fe.sgemm_emu_ex(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1), nbands, fe.SGEMM_EMU_NO_WORKSPACE)
     elif entry == "fused_ws_a":
         fe.sgemm_emu_ex(M, N, K, Ad, lda, Bd, max(N, 1), Cd, max(ldc, 1), nbands, fe.SGEMM_EMU_PRESPLIT_A)
     elif nbands == 5 and entry == "fused":
@@ -84,9 +86,10 @@ DMA_SHAPES = [(129, 130, 64), (300, 257, 128), (64, 300, 256), (513, 384, 192), 
 
 def same_order_as_fused(fe, M, N, K):
     """True when the N x K plane GEMM adds in the same order as sgemm_bf16x9 on
-    FP32 B: either both take the plane kernel (M >= 1024, B split into a
-    workspace) or the plane kernel runs without split-K."""
-    return M >= 1024 or fe.sgemm_emu_split_k(M, N, K) == 1
+    FP32 B: neither cuts K (stream-K), or both do it alike (K % 64 == 0: the
+    FP32 B is then split into N x K planes in a workspace for the same kernel)."""
+    kpad = (K + 63) // 64 * 64
+    return K % 64 == 0 or fe.sgemm_emu_split_k(M, N, kpad) == 1
 
 
 @pytest.mark.parametrize("shape", DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -125,11 +128,10 @@ def test_nk_planes_dma_path_padded_ldb_and_bands(fe, orc, nbands):
     assert np.array_equal(C.astype(np.float32).view(np.uint32), run(fe, A, B, nbands, "fused").view(np.uint32))
 
 
-def _fused_in_row_blocks(fe, A, B, nbands, rows=1000):
-    """A B from the in-kernel split of FP32 B: row blocks below the size at which
-    sgemm_bf16x9 / sgemm_emu switch to splitting B once into a workspace.  Rows of
-    C do not depend on the other rows, so the blocks stack to the full product."""
-    return np.concatenate([run(fe, A[i:i + rows], B, nbands, "fused") for i in range(0, A.shape[0], rows)])
+def _fused_in_row_blocks(fe, A, B, nbands):
+    """A B from the in-kernel split of FP32 B, one pass over K per tile
+    (SGEMM_EMU_NO_WORKSPACE)."""
+    return run(fe, A, B, nbands, "fused_nows")
 
 
 WS_SHAPES = [(1024, 130, 64), (1100, 257, 128), (1500, 1000, 512), (2048, 64, 192),
@@ -334,6 +336,25 @@ def test_fp32_b_workspace_path_special_values(fe):
     assert np.array_equal(C[fin].view(np.uint32), R[fin].view(np.uint32))
 
 
+@pytest.mark.parametrize("shape", [(129, 130, 1024), (513, 384, 192), (1000, 1030, 1024), (64, 300, 100)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_no_workspace_one_pass(fe, shape):
+    """SGEMM_EMU_NO_WORKSPACE: B split inside the kernel, each tile's whole K in
+    one workgroup, on grids the default path cuts along K (stream-K): within
+    the bound, deterministic, and bit for bit the default where that does not
+    cut K."""
+    M, N, K = shape
+    g = _rng(M + 17 * N + 5 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="fused_nows")
+    check_against_fp64(C, A, B, label=f"no workspace {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_nows").view(np.uint32))
+    kpad = (K + 63) // 64 * 64
+    if fe.sgemm_emu_split_k(M, N, kpad) == 1:
+        assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
+
+
 PERSIST_SHAPES = [(4100, 1100, 128), (8200, 1030, 64), (4096, 2048, 256)]
 
 
@@ -460,6 +481,11 @@ def test_presplit_equals_fused_bitwise(fe):
     for nb in (1, 3, 5):
         ref = run(fe, A, B, nb, "fused").view(np.uint32)
         assert np.array_equal(ref, run(fe, A, B, nb, "presplit").view(np.uint32))
+        if same_order_as_fused(fe, 200, 190, 150):   # else FP32 B and K x N planes take stream-K
+            assert np.array_equal(ref, run(fe, A, B, nb, "presplit_t").view(np.uint32))
+    # the one-pass kernels agree
+    for nb in (1, 5):
+        ref = run(fe, A, B, nb, "fused_nows").view(np.uint32)
         assert np.array_equal(ref, run(fe, A, B, nb, "presplit_t").view(np.uint32))
 
 

@@ -113,19 +113,17 @@ def test_native_k_zero_and_empty(fe):
     assert run(fe, np.zeros((0, 3), np.float32), np.zeros((3, 4), np.float32), fe.SGEMM_EMU_NATIVE_FP32).size == 0
 
 
-@pytest.mark.parametrize("shape", [(129, 130, 1024), (6144, 256, 1024), (8192, 8192, 256)],
+@pytest.mark.parametrize("shape", [(129, 130, 1024), (1024, 1024, 1024), (6144, 256, 1024), (8192, 8192, 256)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_performant_picks_one_path_and_matches_it(fe, shape):
     """The performant result equals, bit for bit, either the native kernel's or
-    the emulation's on the same shape: small grids take the native kernel,
-    grids with at least two 128 x 128 tiles per CU the emulation."""
+    the emulation's on the same shape: GEMMs below 2.5e9 flops take the native
+    kernel, larger ones the emulation."""
     M, N, K = shape
     g = _rng(K + N)
     A = g.standard_normal((M, K)).astype(np.float32)
     B = g.standard_normal((K, N)).astype(np.float32)
     P = run(fe, A, B, fe.SGEMM_EMU_PERFORMANT)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tiles = ((M + 127) // 128) * ((N + 127) // 128)
-    want = run(fe, A, B, fe.SGEMM_EMU_NATIVE_FP32) if tiles < 2 * cus else run(fe, A, B, 0)
+    want = run(fe, A, B, fe.SGEMM_EMU_NATIVE_FP32) if 2 * M * N * K < 2.5e9 else run(fe, A, B, 0)
     assert np.array_equal(P.view(np.uint32), want.view(np.uint32))
     check_against_fp64(P, A, B, label=f"performant {shape}")

@@ -197,8 +197,9 @@ def test_graph_capture_allocates_nothing(fe):
     Calls that need no workspace capture as usual (a forced pre-split of B falls
     back to the kernel that splits B itself: the same bits as the eager call,
     which used workspace planes); a K-split shape reports SGEMM_EMU_ECAPTURE
-    with nothing enqueued.  Three replays, with eager calls and
-    synchronisation between them, each equal the eager results bit for bit."""
+    with nothing enqueued, and runs with SGEMM_EMU_NO_WORKSPACE (one pass per
+    tile).  Three replays, with eager calls and synchronisation between them,
+    each equal the eager results bit for bit."""
     g = np.random.Generator(np.random.Philox(key=4242))
 
     def mat(r, c):
@@ -226,6 +227,11 @@ def test_graph_capture_allocates_nothing(fe):
     out1 = torch.empty_like(ref1)
     out2 = torch.empty_like(ref2)
     out3 = torch.zeros((M3, N3), device="cuda")
+    # (d) the same small grid from FP32 B without workspace
+    B4 = mat(K3, N3)
+    ref4 = torch.empty((M3, N3), device="cuda")
+    fe.sgemm_emu_ex(M3, N3, K3, A3, K3, B4, N3, ref4, N3, 5, fe.SGEMM_EMU_NO_WORKSPACE)
+    out4 = torch.empty_like(ref4)
     torch.cuda.synchronize()
     print("graph capture: two calls without workspace, one K-split call", flush=True, file=sys.stderr)
     graph = torch.cuda.CUDAGraph()
@@ -237,17 +243,20 @@ def test_graph_capture_allocates_nothing(fe):
         with pytest.raises(fe.SgemmEmuError) as err:
             fe.sgemm_emu_presplit_b(M3, N3, K3, A3, K3, *P3, K3, fe.SGEMM_EMU_B_NK, out3, N3, 5, s)
         assert err.value.status == fe.SGEMM_EMU_ECAPTURE
+        fe.sgemm_emu_ex(M3, N3, K3, A3, K3, B4, N3, out4, N3, 5, fe.SGEMM_EMU_NO_WORKSPACE, s)
     torch.cuda.synchronize()
     for rep in range(3):
         print(f"graph capture: replay {rep}", flush=True, file=sys.stderr)
         out1.fill_(float("nan"))
         out2.fill_(float("nan"))
+        out4.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(ref1.view(torch.int32), out1.view(torch.int32)), f"replay {rep}: N x K planes"
         assert torch.equal(ref2.view(torch.int32), out2.view(torch.int32)), f"replay {rep}: forced pre-split"
         assert bool((out3 == 0).all()), "the refused call enqueued work"
+        assert torch.equal(ref4.view(torch.int32), out4.view(torch.int32)), f"replay {rep}: no workspace"
         # eager work between replays, on the default stream, with its workspace
         fe.sgemm_emu_ex(M2, N2, K2, A2, K2, B2, N2, out2, N2, 5, fe.SGEMM_EMU_PRESPLIT_B)
         torch.cuda.synchronize()
