@@ -40,8 +40,8 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "edd8fa5e77203c0d71e15af9a0e785b440c843e9609a3bb17906497175ed70e2",
-                "bytes_per_launch": [2843967260, 3264076805]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "5d7d40f4d4089f92f1705a3bb5a07c9d4657af7b93d7113c516bba7ab9ed35b2",
+                "bytes_per_launch": [2843947827, 3264118067]}
 
 # MFMA activity of the same launches, from one rocprofv3 --pmc run of the same
 # probe (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE).
@@ -51,8 +51,8 @@ GEMM_TRAFFIC = {"gemm_hip_sha256": "edd8fa5e77203c0d71e15af9a0e785b440c843e9609a
 # divided by the kernel's own time in this run gives the shader clock the chip
 # held under the load; roofline.frac = busy x clock / 2.4 GHz.
 GEMM_MFMA_PMC = {"gemm_hip_sha256": GEMM_TRAFFIC["gemm_hip_sha256"],
-                 "mfma_busy": [0.6444, 0.7166],
-                 "active_cycles_per_xcd": [3874693, 3475354]}
+                 "mfma_busy": [0.6619, 0.7295],
+                 "active_cycles_per_xcd": [3772674, 3413814]}
 
 
 def log(msg):
