@@ -1106,10 +1106,11 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     wait_vmem_at_most<0>();      // drain the copies issued past the end of K
 }
 
-// ---------------------------------------------------------------- stream-K (small tile grids)
+// ---------------------------------------------------------------- stream-K (partly filled grids)
 //
-// A grid with fewer 128 x 128 tiles than three quarters of the CUs would leave
-// CUs idle.  There the work is cut along K instead: the T tiles x (K / 64)
+// A grid whose 128 x 128 tiles leave CUs idle (fewer tiles than CUs, or a last
+// wave of tiles that fills only part of the chip) can cut the work along K
+// instead, where a cost model expects that to pay (gemm_streamk_grid): the T tiles x (K / 64)
 // pairs of K steps form one sequence of P units (tile-major, K ascending
 // inside a tile), and workgroup w of G takes units [w P / G, (w + 1) P / G):
 // every CU gets the same number of MFMAs.  A workgroup's run covers the end of
@@ -1573,15 +1574,32 @@ static int64_t streamk_domains(int64_t T, int64_t ppt, int64_t G)
     return 8;
 }
 
+// Stream-K against the persistent kernel, in K-pair times per CU: the
+// persistent kernel needs ceil(T / G) whole tiles of ppt pairs; stream-K needs
+// ceil(T ppt / G) pairs plus the publication, wait and sum of the cut tiles,
+// which measured about kStreamkFixPairs pair times (6144 x 256 x 1024,
+// 3072 x 1536 x 1024, 8192 x 640 x 1024, 6144 x 768 x 512, 2560^2 x 1024 and
+// 4096 x 2048 x 512 on 256 CUs: stream-K 21-24 % faster on grids of 1.1-1.3
+// waves of tiles with K = 1024, even at 1.56 waves, 11 % slower at 2 full
+// waves).  Stream-K is taken where the model expects it 10 % faster.
+constexpr int64_t kStreamkFixPairs = 6;
+constexpr int64_t kStreamkMaxPieces = 8;               // per tile: the last piece adds the others' slots one by one
+
 int gemm_streamk_grid(int64_t M, int64_t N, int64_t K, int num_cus)
 {
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    if (K % (2 * BK) != 0 || tiles * 4 >= (int64_t)num_cus * 3) return 0;   // 3/4 of the CUs busy already
-    const int64_t units = tiles * (K / (2 * BK));
-    int64_t G = num_cus > 8 ? num_cus & ~7 : 8;
+    if (K % (2 * BK) != 0 || tiles == 0) return 0;
+    const int64_t ppt = K / (2 * BK), units = tiles * ppt;
+    const int64_t G0 = num_cus > 8 ? num_cus & ~7 : 8;
+    int64_t G = G0;
     if (units < 2 * G) G = units / 2;                  // at least two K pairs per workgroup
+    if (G > kStreamkMaxPieces * tiles) G = kStreamkMaxPieces * tiles;
+    if (G < 2) return 0;
+    const int64_t t_persistent = (tiles + G0 - 1) / G0 * ppt;
+    const int64_t t_streamk = (units + G - 1) / G + kStreamkFixPairs;
+    if (t_streamk * 10 >= t_persistent * 9) return 0;
     if (units * G >= ((int64_t)1 << 32)) return 0;     // the kernel's index arithmetic is 32-bit
-    return G > tiles ? (int)G : 0;
+    return (int)G;
 }
 
 int gemm_streamk_pieces(int64_t M, int64_t N, int64_t K, int grid)

@@ -76,8 +76,9 @@ hipError_t launch_gemm(const GemmArgs &args, int nbands, BSource bsrc, hipStream
 hipError_t launch_gemm_planes(const GemmArgs &args, int nbands, hipStream_t stream);
 
 // Stream-K for the N x K DMA kernel: the number of workgroups G sharing the
-// shape's (tile, K pair) units, or 0 for one workgroup per tile (grids that
-// fill three quarters of the CUs, K not a multiple of 64, too few units).
+// shape's (tile, K pair) units, or 0 for the persistent kernel (where the
+// persistent schedule's tile waves are not expected to be 10 % slower, K not
+// a multiple of 64, too few units).
 // A stream-K launch needs args.sk_flags (G words), args.partials (G x 128 x 128
 // floats) and a nonzero args.sk_epoch that differs from the flags' values.
 int gemm_streamk_grid(int64_t M, int64_t N, int64_t K, int num_cus);

@@ -23,8 +23,8 @@
  *     acc = fma(S1, 2^-8, acc), C = acc + S0;
  *   - the order of additions inside a band is the matrix unit's; results are
  *     deterministic for a given shape, entry point and device (no atomics) but
- *     not bitwise equal to a sequential sum.  Small tile grids share their
- *     (tile, K range) work among all CUs (stream-K, see sgemm_emu_split_k):
+ *     not bitwise equal to a sequential sum.  Partly filled tile grids share
+ *     their (tile, K range) work among all CUs (stream-K, see sgemm_emu_split_k):
  *     each piece of a tile runs the method on its K range and the pieces' FP32
  *     results are added in K order; if the device memory for those partial
  *     results cannot be had, the call returns SGEMM_EMU_ENOMEM rather than
@@ -46,8 +46,8 @@
  *   Device memory: sgemm_bf16x9 and sgemm_emu with K' * N <= 2^28 (K' = K
  *   rounded up to a multiple of 64) split B once into an N x K' set of BF16
  *   planes, zero past K (6 K' N bytes), where that is faster than splitting
- *   B inside the GEMM kernel: when the tile grid is small enough for
- *   stream-K (any M), or when M >= 1024 and 2 M N K >= 1.2e10 (sgemm_emu_ex's
+ *   B inside the GEMM kernel: when the tile grid takes stream-K (see
+ *   sgemm_emu_split_k; any M), or when M >= 1024 and 2 M N K >= 1.2e10 (sgemm_emu_ex's
  *   SGEMM_EMU_PRESPLIT_B asks for it whenever M >= 1024 and K' N allow).
  *   sgemm_emu_presplit_b with K x N planes follows the same rule, with the
  *   planes transposed into the workspace instead of split.  Where B is
@@ -338,9 +338,12 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
  * and sgemm_emu_linear, which need K % 64 == 0 and 16-byte aligned planes with
  * ldb % 8 == 0; sgemm_bf16x9 / sgemm_emu when they pre-split B, with K rounded
  * up to a multiple of 64).  1 means one pass over K per 128 x 128 output tile.
- * Grids that would leave a quarter of the CUs idle are shared out stream-K
- * style: the (tile, 64-wide K range) units, tile by tile, are cut into equal
- * runs, one per workgroup (at most one per CU, each run at least two units);
+ * Grids whose tiles leave CUs idle (fewer tiles than CUs, or a last wave of
+ * tiles that fills only part of the chip) are shared out stream-K style where
+ * the library's cost model expects it to be at least 10 % faster: the (tile,
+ * 64-wide K range) units, tile by tile, are cut into equal runs, one per
+ * workgroup (at most one per CU, each run at least two units, at most 8
+ * pieces per tile);
  * each piece of a tile runs the method on its K range (five band sums,
  * recombined smallest band first); the workgroup holding a tile's last K range
  * adds the other pieces' FP32 results (from the stream's workspace: a

@@ -388,7 +388,7 @@ def test_dma_path_special_values_in_next_tile_first_step(fe):
     assert np.array_equal(C[fin].view(np.uint32), R[fin].view(np.uint32))
 
 
-SPLITK_SHAPES = [(1024, 1024, 1024), (6144, 256, 1024), (129, 130, 1024), (64, 300, 512), (256, 256, 512),
+SPLITK_SHAPES = [(1024, 1024, 1024), (6144, 256, 1024), (129, 130, 1024), (64, 300, 1024), (256, 256, 1024),
                  (700, 40, 2048)]
 
 
