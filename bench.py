@@ -40,8 +40,8 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "5d7d40f4d4089f92f1705a3bb5a07c9d4657af7b93d7113c516bba7ab9ed35b2",
-                "bytes_per_launch": [2843947827, 3264118067]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "466737b1e8cece5ae563d5c88181c6d9049c7dd402f0883f08e30db41473bb99",
+                "bytes_per_launch": [2843949158, 3264118477]}
 
 # MFMA activity of the same launches, from one rocprofv3 --pmc run of the same
 # probe (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE).
@@ -51,8 +51,8 @@ GEMM_TRAFFIC = {"gemm_hip_sha256": "5d7d40f4d4089f92f1705a3bb5a07c9d4657af7b93d7
 # divided by the kernel's own time in this run gives the shader clock the chip
 # held under the load; roofline.frac = busy x clock / 2.4 GHz.
 GEMM_MFMA_PMC = {"gemm_hip_sha256": GEMM_TRAFFIC["gemm_hip_sha256"],
-                 "mfma_busy": [0.6619, 0.7295],
-                 "active_cycles_per_xcd": [3772674, 3413814]}
+                 "mfma_busy": [0.6502, 0.7134],
+                 "active_cycles_per_xcd": [3840396, 3491172]}
 
 
 def log(msg):
@@ -413,9 +413,10 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
     t = timed(lambda: fe.split_f32_bf16x3(q, q, Q, q, *Qp, q, sp), stream, 20)
     res["split_4096^2_GBps"] = round(10.0 * q * q / t / 1e6, 1)
     del Q, Qp
-    # the small shapes: 256^3 and the PET GEMMs of a 192-atom system (6144 rows)
+    # the small shapes: 256^3, the PET GEMMs of a 192-atom system (6144 rows) and a
+    # grid of 1.1 waves of tiles (stream-K by the cost model)
     for name, (m, nn, k) in (("256^3", (256, 256, 256)), ("6144x1024x256", (6144, 1024, 256)),
-                             ("6144x256x1024", (6144, 256, 1024))):
+                             ("6144x256x1024", (6144, 256, 1024)), ("3072x1536x1024", (3072, 1536, 1024))):
         A = torch.randn((m, k), device="cuda")
         B = torch.randn((k, nn), device="cuda") / k ** 0.5
         C = torch.empty((m, nn), device="cuda")
@@ -426,6 +427,8 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
         t = timed(lambda: fe.sgemm_emu_presplit_b(m, nn, k, A, k, *Bt_planes, k, fe.SGEMM_EMU_B_NK, C, nn, 5, sp),
                   stream, 20)
         res[f"presplit_nk_{name}_tflops"] = round(fs / t / 1e9, 2)
+        t = timed(lambda: fe.sgemm_emu_ex(m, nn, k, A, k, B, nn, C, nn, 5, fe.SGEMM_EMU_PERFORMANT, sp), stream, 20)
+        res[f"performant_{name}_tflops"] = round(fs / t / 1e9, 2)
         t = timed(lambda: torch.matmul(A, B, out=C), stream, 20)
         res[f"torch_fp32_{name}_tflops"] = round(fs / t / 1e9, 2)
         del A, B, C, Bt_planes
@@ -471,6 +474,7 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
         "8192^3": round(res["sgemm_bf16x9_8192^3_tflops"] / res["torch_fp32_8192^3_tflops"], 3),
         "6144x1024x256": round(res["sgemm_bf16x9_6144x1024x256_tflops"] / res["torch_fp32_6144x1024x256_tflops"], 3),
         "6144x256x1024": round(res["sgemm_bf16x9_6144x256x1024_tflops"] / res["torch_fp32_6144x256x1024_tflops"], 3),
+        "3072x1536x1024": round(res["sgemm_bf16x9_3072x1536x1024_tflops"] / res["torch_fp32_3072x1536x1024_tflops"], 3),
     }
     res["pages_quoted_speedups_other_hardware"] = {
         "BF16x9_vs_FP32_B300_large_PET_GEMMs": "2.2-2.5x", "BF16x9_vs_FP32_B300_4096^3": "2.41x",

@@ -395,8 +395,9 @@ SPLITK_SHAPES = [(1024, 1024, 1024), (6144, 256, 1024), (129, 130, 1024), (64, 3
 @pytest.mark.parametrize("shape", SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_split_k_within_bound_and_deterministic(fe, shape):
     """Small tile grids share their work stream-K style: each piece of a tile
-    runs the method on its K range, the pieces' results are added in K order.  Within the bound, identical on repeat, and sgemm_bf16x9 on FP32 B
-    agrees with the caller-split planes whenever both take the plane kernel."""
+    runs the method on its K range, the pieces' results are added in K order.
+    Within the bound, identical on repeat, and sgemm_bf16x9 on FP32 B agrees
+    with the caller-split planes bit for bit (both take the same kernel)."""
     M, N, K = shape
     assert fe.sgemm_emu_split_k(M, N, K) > 1
     g = _rng(M * 3 + N * 5 + K * 7)
@@ -407,8 +408,30 @@ def test_split_k_within_bound_and_deterministic(fe, shape):
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
     F = run(fe, A, B, entry="fused")
     check_against_fp64(F, A, B, label=f"split-k fused {shape}")
-    if M >= 1024:
-        assert np.array_equal(C.view(np.uint32), F.view(np.uint32))
+    # FP32 B on a stream-K grid is split into N x K workspace planes for the same kernel, at any M
+    assert np.array_equal(C.view(np.uint32), F.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(3072, 1536, 1024), (8192, 640, 1024)], ids=lambda s: "x".join(map(str, s)))
+def test_streamk_on_partly_filled_grids(fe, shape):
+    """Grids of 1.1-1.3 waves of tiles with long K take stream-K too: fewer
+    workgroups than tiles, so runs hold whole tiles between a tile's start and
+    another's end.  Within the bound on sampled rows (every tile row), identical
+    on repeat, FP32 B equal to the caller's N x K planes bit for bit, and the
+    one-pass result (SGEMM_EMU_NO_WORKSPACE) within the same bound."""
+    M, N, K = shape
+    assert fe.sgemm_emu_split_k(M, N, K) > 1
+    g = _rng(M + 3 * N + 5 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="presplit_t")
+    rows = np.unique(np.concatenate([np.arange(0, M, 128) + g.integers(0, 128, size=(M + 127) // 128),
+                                     [M - 1]]).clip(0, M - 1))
+    check_against_fp64(C[rows], A, B, rows=rows, label=f"stream-K {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
+    R = run(fe, A, B, entry="fused_nows")
+    check_against_fp64(R[rows], A, B, rows=rows, label=f"one pass {shape}")
 
 
 @pytest.mark.parametrize("nbands", [1, 2, 3, 4, 5])
