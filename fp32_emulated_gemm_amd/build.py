@@ -1,4 +1,9 @@
-"""Compile the HIP sources into libsgemm_emu.so (gfx950 only).
+"""Compile the HIP sources into libsgemm_emu.so (gfx950 only), and the same
+sources with -DSGEMM_EMU_SERIAL_LDS into libsgemm_emu_serial_lds.so: a debug
+build whose N x K plane GEMM runs a kernel with one LDS buffer per operand and a
+barrier on each side of every K step (no stream-K, A split in that kernel); its
+results must equal the library's bit for bit where the library runs the
+pipelined kernel without stream-K (tests/test_gpu_serial_lds.py).
 
     python -m fp32_emulated_gemm_amd.build
 
@@ -19,6 +24,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsgemm_emu.so")
+DEBUG_LIB = os.path.join(HERE, "libsgemm_emu_serial_lds.so")
 SOURCES = ["api.hip", "gemm.hip", "split.hip", "ieee.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -39,17 +45,23 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Always recompiles (each source in parallel, then one link); returns the
-    path of the library."""
+    """Always recompiles both libraries (every source in parallel, then one
+    link each); returns the path of the library."""
     with tempfile.TemporaryDirectory(prefix="sgemm_emu_build_") as tmpdir:
-        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        cmds = [[HIPCC, *FLAGS, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
-        with ThreadPoolExecutor(max_workers=len(cmds)) as pool:
-            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+        jobs = []
+        for lib, extra, tag in ((LIB, [], ""), (DEBUG_LIB, ["-DSGEMM_EMU_SERIAL_LDS"], "_serial")):
+            objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + tag + ".o") for s in SOURCES]
+            cmds = [[HIPCC, *FLAGS, *extra, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+            jobs.append((lib, objs, cmds))
+        with ThreadPoolExecutor(max_workers=8) as pool:
+            for f in [pool.submit(_run, c, verbose) for _, _, cmds in jobs for c in cmds]:
                 f.result()
-        tmp = LIB + ".tmp"
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-        os.replace(tmp, LIB)
+        for lib, objs, _ in jobs:
+            tmp = lib + ".tmp"
+            # -Bsymbolic: each library's internal calls bind to its own definitions,
+            # also when both are loaded into one process
+            _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-Bsymbolic", "-o", tmp, *objs], verbose)
+            os.replace(tmp, lib)
     return LIB
 
 

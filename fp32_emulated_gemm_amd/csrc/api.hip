@@ -371,7 +371,13 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // workspace.  Stream-K splits A inside the kernel.
     const bool dma = presplit || transpose_kn || nk_dma;
     const int skg = dma && !no_workspace ? gemm_streamk_grid(M, N, (presplit || transpose_kn) ? kpad : K, num_cus) : 0;
-    const bool presplit_a = !no_workspace && (presplit || transpose_kn || (nk_dma && M >= kPresplitMinRows)) &&
+#ifdef SGEMM_EMU_SERIAL_LDS
+    const bool serial_debug = true;                    // the debug build splits A in its one kernel
+#else
+    const bool serial_debug = false;
+#endif
+    const bool presplit_a = !no_workspace && !serial_debug &&
+                            (presplit || transpose_kn || (nk_dma && M >= kPresplitMinRows)) &&
                             kpad == K &&
                             (uint64_t)M * (uint64_t)K <= kPresplitMaxElems && skg == 0 &&
                             (force_presplit_a || N >= kPresplitAMinCols);
@@ -777,6 +783,10 @@ int sgemm_emu_release_workspace(void)
     return err == hipSuccess ? SGEMM_EMU_OK : SGEMM_EMU_ELAUNCH;
 }
 
+#ifdef SGEMM_EMU_SERIAL_LDS
+const char *sgemm_emu_version(void) { return "libsgemm_emu 0.2.0 (gfx950, BF16x9, serial-LDS debug build)"; }
+#else
 const char *sgemm_emu_version(void) { return "libsgemm_emu 0.2.0 (gfx950, BF16x9)"; }
+#endif
 
 }  // extern "C"

@@ -1106,6 +1106,54 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_dma_kernel(GemmArgs g)
     wait_vmem_at_most<0>();      // drain the copies issued past the end of K
 }
 
+#ifdef SGEMM_EMU_SERIAL_LDS
+// Debug build only (SGEMM_EMU_SERIAL_LDS): the N x K plane GEMM with one LDS
+// buffer per operand and a barrier on each side of every K step -- no copies in
+// flight across a barrier, no ring, no fragment prefetch.  Same tiles, split,
+// B copies, fragment reads and MFMA order as gemm_bf16x9_dma_kernel (k slice 0
+// then k slice 1 of each step, products in mfma_slice order), so its results
+// must equal the pipelined kernel's bit for bit.  One tile per workgroup.
+template <class C, int NB, bool AVEC, bool RNE, bool KTAIL>
+__global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_serial_kernel(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[3 * DmaLayout<C>::A_TILE + 3 * B_DMA_TILE];
+    uint16_t *const abuf = lds;
+    uint16_t *const bbuf = lds + 3 * DmaLayout<C>::A_TILE;
+    const int T = g.tiles_m * g.tiles_n;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    int a_lds[C::A_CHUNKS];
+#pragma unroll
+    for (int c = 0; c < C::A_CHUNKS; ++c) {
+        int row, kg;
+        chunk_rc(c * C::NT + threadIdx.x, row, kg);
+        a_lds[c] = row * KP + kg * 8;
+    }
+    StepSrc<C> cur;
+    unit_src<C>(cur, (int)blockIdx.x, T, g);
+    Acc<C, NB> acc;
+    clear_acc<C, NB>(acc);
+    Frags<C> f;
+    for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
+        dma_b_stage<C>(g, cur.n0, k0, bbuf, wave, lane);
+        float a[C::A_CHUNKS][8];
+        load_a_stage<C, AVEC>(a, cur.a_off, g, cur.m0, k0);
+        wait_vmem_at_most<0>();
+        if (store_a_stage<C, RNE, KTAIL>(a, a_lds, abuf, g.ka - k0))
+            restage_a_special<C, AVEC, RNE, KTAIL>(cur.a_off, a_lds, g, cur.m0, k0, abuf);
+        __syncthreads();
+        read_frags_dma<C>(f, abuf, bbuf, 0, wm, wn, lane);
+        mfma_slice<C, NB>(acc, f);
+        read_frags_dma<C>(f, abuf, bbuf, 16, wm, wn, lane);
+        mfma_slice<C, NB>(acc, f);
+        __syncthreads();
+    }
+    float bias[C::NI];
+    load_bias<C>(bias, g, cur.n0, wn, lane);
+    store_c<C, NB>(acc, bias, g, cur.m0, cur.n0, wm, wn, lane);
+}
+#endif
+
 // ---------------------------------------------------------------- stream-K (partly filled grids)
 //
 // A grid whose 128 x 128 tiles leave CUs idle (fewer tiles than CUs, or a last
@@ -1587,6 +1635,10 @@ constexpr int64_t kStreamkMaxPieces = 8;               // per tile: the last pie
 
 int gemm_streamk_grid(int64_t M, int64_t N, int64_t K, int num_cus)
 {
+#ifdef SGEMM_EMU_SERIAL_LDS
+    (void)M; (void)N; (void)K; (void)num_cus;
+    return 0;                                          // the debug build has no stream-K
+#endif
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if (K % (2 * BK) != 0 || tiles == 0) return 0;
     const int64_t ppt = K / (2 * BK), units = tiles * ppt;
@@ -1932,6 +1984,14 @@ static void launch_dma_nb(const GemmArgs &g, bool avec, hipStream_t stream)
     // One resident workgroup per CU (LDS-limited); a multiple of 8 keeps each
     // workgroup on one XCD for all of its tiles.
     const dim3 block(C::NT);
+#ifdef SGEMM_EMU_SERIAL_LDS
+    {
+        const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n));
+        if (avec) launch_last(gemm_bf16x9_serial_kernel<C, NB, true, RNE, KTAIL>, grid, block, stream, g);
+        else launch_last(gemm_bf16x9_serial_kernel<C, NB, false, RNE, KTAIL>, grid, block, stream, g);
+        return;
+    }
+#endif
     if (g.sk_grid > 0) {
         // small tile grid: stream-K over sk_grid workgroups
         GemmArgs s = g;

@@ -32,6 +32,20 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_serial_lds_debug_library_exports_the_same_symbols():
+    """The debug build (one LDS buffer, extra barriers) is built beside the
+    library and exports the same C ABI; it reports itself in its version."""
+    if os.environ.get("SGEMM_EMU_LIB_OVERRIDE"):
+        pytest.skip("a substituted library build is under test")
+    import fp32_emulated_gemm_amd as fe
+    path = os.path.join(os.path.dirname(os.path.abspath(fe.__file__)), "libsgemm_emu_serial_lds.so")
+    D = ctypes.CDLL(path)
+    for name in _declared_functions():
+        assert hasattr(D, name), name
+    D.sgemm_emu_version.restype = ctypes.c_char_p
+    assert b"serial-LDS debug build" in D.sgemm_emu_version()
+
+
 def test_single_hip_runtime_loaded(L):
     import fp32_emulated_gemm_amd as fe
     assert len(fe.hip_runtimes_loaded()) == 1, fe.hip_runtimes_loaded()
