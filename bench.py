@@ -71,6 +71,10 @@ def parse():
                    help="only time the platform's BF16 and FP32 GEMMs (torch.matmul) on the square and "
                         "PET shapes and print them as one JSON line")
     p.add_argument("--calibrate-reps", type=int, default=10)
+    p.add_argument("--sustain", type=float, default=None,
+                   help="SECONDS: only run the vendor BF16 GEMM, sgemm_bf16x9 and the vendor FP32 GEMM on "
+                        "4096^3 and 8192^3 for SECONDS each (normal and uniform operands), sampling the "
+                        "engine clock with rocm-smi, and print them as one JSON line")
     p.add_argument("--shape", type=str, default=None,
                    help="M,N,K: only time the library's entry points (and torch.matmul FP32) on this one "
                         "shape, random N(0,1) operands, and print them as one JSON line (for kernel traces)")
@@ -89,6 +93,9 @@ def main():
         sys.exit(2)
     if args.calibrate:
         calibrate(args.calibrate_reps)
+        return
+    if args.sustain:
+        sustained(args.sustain)
         return
     if args.shape:
         one_shape(tuple(int(x) for x in args.shape.split(",")), args.shape_reps)
@@ -355,6 +362,77 @@ def calibrate(reps):
     print(json.dumps({"calibration": "torch.matmul BF16 / FP32 (hipBLASLt), random operands",
                       "reps": reps, "bf16": bf16, "fp32_tflops": fp32,
                       "bf16_dense_peak_tflops": MI355X_BF16_DENSE_TFLOPS}), flush=True)
+
+
+def engine_clock_mhz():
+    """The engine clock rocm-smi reports now (MHz), or None where it cannot be read."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "-g", "--json"], capture_output=True, text=True, timeout=30).stdout
+        level = json.loads(out[out.index("{"):])["card0"]["sclk clock level"]
+        return int(level.split("(")[1].split("M")[0])
+    except Exception:
+        return None
+
+
+def sustained(seconds):
+    """--sustain: each GEMM back to back for `seconds` (the clock settles under a
+    sustained load), the effective rate from HIP events around all the calls, the
+    engine clock sampled twice in the second half.  Square shapes, operands
+    N(0,1) and U(-1,1): the vendor BF16 GEMM (one product, the ceiling a BF16
+    kernel reaches), sgemm_bf16x9 (nine products) and the vendor FP32 GEMM."""
+    import time
+    import torch
+    import fp32_emulated_gemm_amd as fe
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    out = {}
+
+    def run(name, f, flops, products):
+        f()
+        torch.cuda.synchronize()
+        clocks, calls = [], 0
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.time()
+        e0.record(stream)
+        while time.time() - t0 < seconds:
+            for _ in range(5):
+                f()
+            calls += 5
+            if time.time() - t0 > seconds / 2 and len(clocks) < 2:
+                clocks.append(engine_clock_mhz())
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / calls
+        tf = flops / ms / 1e9
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "calls": calls,
+                     "bf16_frac_of_peak": round(tf * products / MI355X_BF16_DENSE_TFLOPS, 4) if products else None,
+                     "sclk_mhz": clocks}
+        print(name, out[name], file=sys.stderr, flush=True)
+
+    g = torch.Generator(device="cuda").manual_seed(11)
+    for n in (8192, 4096):
+        fl = 2.0 * n ** 3
+        for dist in ("normal", "uniform"):
+            if dist == "normal":
+                A = torch.randn((n, n), device="cuda", generator=g)
+                B = torch.randn((n, n), device="cuda", generator=g)
+            else:
+                A = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+                B = torch.rand((n, n), device="cuda", generator=g) * 2 - 1
+            Ab, Bb = A.bfloat16(), B.bfloat16()
+            Cb = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+            C = torch.empty((n, n), device="cuda")
+            run(f"torch_bf16_{n}^3_{dist}", lambda: torch.matmul(Ab, Bb, out=Cb), fl, 1)
+            run(f"sgemm_bf16x9_{n}^3_{dist}", lambda: fe.sgemm_bf16x9(n, n, n, A, n, B, n, C, n, sp), fl, 9)
+            if dist == "normal":
+                run(f"torch_fp32_{n}^3_{dist}", lambda: torch.matmul(A, B, out=C), fl, 0)
+            del A, B, Ab, Bb, Cb, C
+            torch.cuda.empty_cache()
+    print(json.dumps({"sustained_seconds_each": seconds, "bf16_dense_peak_tflops": MI355X_BF16_DENSE_TFLOPS,
+                      "runs": out}), flush=True)
 
 
 def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
