@@ -1682,7 +1682,8 @@ static int group_rows(int tiles_n, int num_cus);
 // output, no split.
 //
 // One workgroup per (tile, K slice); waves as in Cfg, each (MI x 32) x (NI x 32)
-// of accumulators.  K advances in steps of NBK = 16, double-buffered in LDS:
+// of accumulators.  K advances in steps of NBK = 16, double-buffered in LDS and
+// loaded NLA steps ahead into registers:
 //   * A rows hold 16 k values plus 4 of padding (80 bytes): 16 consecutive
 //     rows read with 128-bit loads touch 64 distinct banks;
 //   * B rows (one k each) hold the tile's BN columns plus 4 of padding, so
@@ -1690,9 +1691,11 @@ static int group_rows(int tiles_n, int num_cus);
 // Within a step, half-wave h (lanes 32h..32h+31) feeds k = 8h + kk to the
 // kk-th MFMA: the instruction's two k rows come from k and k + 8, so each
 // lane reads its eight A values of a step with two 128-bit loads.  Every
-// k < K is multiplied in exactly once, in an order the bound allows.
+// k < K is multiplied in exactly once, in an order the bound allows.  (Steps
+// of 32 k measured 2-3 % slower on most shapes.)
 
 constexpr int NBK = 16;                 // k per step
+constexpr int NLA = 4;                  // steps loaded ahead (register stages)
 constexpr int NAP = NBK + 4;            // A row pitch in LDS (floats)
 
 template <class C>
@@ -1713,12 +1716,15 @@ struct NativeStage {
 };
 
 // Thread -> A chunk (row, 4-wide k group): 16 consecutive lanes take 16 rows of
-// one k group (conflict-free 128-bit LDS writes at the 80-byte pitch).
+// one k group (conflict-free 128-bit LDS writes at the 80-byte pitch); a wave
+// covers 16 rows x 4 k groups, the waves run through the tile's row blocks.
+template <class C>
 __device__ __forceinline__ void native_a_chunk(int q, int &row, int &kg)
 {
+    constexpr int ROW_BLOCKS = C::BM / 16;
     const int lane = q & 63, blk = q >> 6;
-    row = blk * 16 + (lane & 15);
-    kg = lane >> 4;
+    row = (blk % ROW_BLOCKS) * 16 + (lane & 15);
+    kg = (lane >> 4) + 4 * (blk / ROW_BLOCKS);
 }
 
 // Load one step (k0 .. k0 + 15) of A and B into registers.  VEC: 128-bit
@@ -1737,7 +1743,7 @@ __device__ __forceinline__ void native_load(NativeStage<C> &st, const GemmArgs &
 #pragma unroll
         for (int c = 0; c < L::A_VECS; ++c) {
             int row, kg;
-            native_a_chunk(c * C::NT + tid, row, kg);
+            native_a_chunk<C>(c * C::NT + tid, row, kg);
             const int64_t r = lmin((int64_t)row, rows - 1);
             const uint32_t off = (uint32_t)((r * g.lda + kg * 4) * 4);
             if (VEC) {
@@ -1778,7 +1784,7 @@ __device__ __forceinline__ void native_store(const NativeStage<C> &st, float *bu
 #pragma unroll
     for (int c = 0; c < L::A_VECS; ++c) {
         int row, kg;
-        native_a_chunk(c * C::NT + tid, row, kg);
+        native_a_chunk<C>(c * C::NT + tid, row, kg);
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (kg * 4 + e < kvalid) ? st.a[c][e] : 0.0f;
@@ -1799,25 +1805,29 @@ __device__ __forceinline__ void native_step(Acc<C, 1> &acc, const float *buf, in
 {
     using L = NativeLayout<C>;
     const int h = lane >> 5, r = lane & 31;
-    float a[C::MI][8];
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-        const float *p = buf + (wm * C::WTM + i * 32 + r) * NAP + 8 * h;
-        const u32x4_t v0 = *reinterpret_cast<const u32x4_t *>(p);
-        const u32x4_t v1 = *reinterpret_cast<const u32x4_t *>(p + 4);
+    for (int kb = 0; kb < NBK; kb += 16) {
+        float a[C::MI][8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { a[i][e] = __uint_as_float(v0[e]); a[i][4 + e] = __uint_as_float(v1[e]); }
-    }
+        for (int i = 0; i < C::MI; ++i) {
+            const float *p = buf + (wm * C::WTM + i * 32 + r) * NAP + kb + 8 * h;
+            const u32x4_t v0 = *reinterpret_cast<const u32x4_t *>(p);
+            const u32x4_t v1 = *reinterpret_cast<const u32x4_t *>(p + 4);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        float b[C::NI];
+            for (int e = 0; e < 4; ++e) { a[i][e] = __uint_as_float(v0[e]); a[i][4 + e] = __uint_as_float(v1[e]); }
+        }
 #pragma unroll
-        for (int j = 0; j < C::NI; ++j) b[j] = buf[L::A_FLOATS + (8 * h + kk) * L::BNP + wn * C::WTN + j * 32 + r];
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
+        for (int kk = 0; kk < 8; ++kk) {
+            float b[C::NI];
 #pragma unroll
             for (int j = 0; j < C::NI; ++j)
-                acc.v[i][j][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][kk], b[j], acc.v[i][j][0], 0, 0, 0);
+                b[j] = buf[L::A_FLOATS + (kb + 8 * h + kk) * L::BNP + wn * C::WTN + j * 32 + r];
+#pragma unroll
+            for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+                for (int j = 0; j < C::NI; ++j)
+                    acc.v[i][j][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][kk], b[j], acc.v[i][j][0], 0, 0, 0);
+        }
     }
 }
 
@@ -1843,18 +1853,32 @@ __global__ __launch_bounds__(C::NT, 2) void gemm_f32_native_kernel(GemmArgs g)
         for (int j = 0; j < C::NI; ++j) acc.v[i][j][0] = f32x16_t{};
 
     if (s0 < s1) {
-        NativeStage<C> st;
-        native_load<C, VEC>(st, g, m0, n0, s0 * NBK);
-        native_store<C>(st, lds, g.K - s0 * NBK);
+        // A ring of NLA register stages: the loads of step t + NLA go out while
+        // step t is computed, so each step's loads have NLA - 1 steps of MFMA
+        // work to arrive before they are written to LDS (one step of lead
+        // leaves these short K steps waiting on memory latency).
+        // The loads and LDS writes are unconditional, so every wait for a
+        // stage counts only the NLA - 1 stages loaded after it: a load past
+        // the slice re-reads its last step and is never stored for use, and
+        // the LDS write after the last step goes to a buffer no step reads.
+        NativeStage<C> st[NLA];
+#pragma unroll
+        for (int r = 0; r < NLA; ++r)
+            native_load<C, VEC>(st[r], g, m0, n0, lmin(s0 + r, s1 - 1) * NBK);
+        native_store<C>(st[0], lds, g.K - s0 * NBK);
         __syncthreads();
-        for (int64_t s = s0; s < s1; ++s) {
-            const float *cur = lds + ((s - s0) & 1) * L::STAGE;
-            float *nxt = lds + ((s - s0 + 1) & 1) * L::STAGE;
-            const bool more = s + 1 < s1;
-            if (more) native_load<C, VEC>(st, g, m0, n0, (s + 1) * NBK);
-            native_step<C>(acc, cur, wm, wn, lane);
-            if (more) native_store<C>(st, nxt, g.K - (s + 1) * NBK);
-            __syncthreads();
+        for (int64_t s = s0; s < s1; s += NLA) {
+#pragma unroll
+            for (int r = 0; r < NLA; ++r) {
+                const int64_t t = s + r;          // the step computed now; its data is in LDS
+                if (t >= s1) break;
+                const float *cur = lds + ((t - s0) & 1) * L::STAGE;
+                float *nxt = lds + ((t - s0 + 1) & 1) * L::STAGE;
+                native_load<C, VEC>(st[r], g, m0, n0, lmin(t + NLA, s1 - 1) * NBK);
+                native_step<C>(acc, cur, wm, wn, lane);
+                native_store<C>(st[(r + 1) % NLA], nxt, g.K - (t + 1) * NBK);
+                __syncthreads();
+            }
         }
     }
     float bias[C::NI];
