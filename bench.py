@@ -40,8 +40,8 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "c174ac6765d22ec8255c590baf671038a87a016854dd11498e3fa03694907995",
-                "bytes_per_launch": [2843915317, 3264015704]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "a219345c429769c28f18548189d2cd1a8c204129ba7abc1389fd565f064b2d3a",
+                "bytes_per_launch": [2843912040, 3264015192]}
 
 # MFMA activity of the same launches, from one rocprofv3 --pmc run of the same
 # probe (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE).
@@ -51,8 +51,8 @@ GEMM_TRAFFIC = {"gemm_hip_sha256": "c174ac6765d22ec8255c590baf671038a87a016854dd
 # divided by the kernel's own time in this run gives the shader clock the chip
 # held under the load; roofline.frac = busy x clock / 2.4 GHz.
 GEMM_MFMA_PMC = {"gemm_hip_sha256": GEMM_TRAFFIC["gemm_hip_sha256"],
-                 "mfma_busy": [0.6593, 0.7241],
-                 "active_cycles_per_xcd": [3787572, 3439367]}
+                 "mfma_busy": [0.6562, 0.7239],
+                 "active_cycles_per_xcd": [3805006, 3440504]}
 
 
 def log(msg):
