@@ -13,7 +13,7 @@ memory and streams only.  The functions keep the C names and argument order:
     split_f32_bf16x3(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     split_f32_bf16x3_transposed(rows, cols, X, ldx, X0, X1, X2, ldo, stream=None)
     split_f32_bf16x3_ex(rows, cols, X, ldx, X0, X1, X2, ldo, flags, stream=None)
-    sgemm_emu_split_k(M, N, K, nbands)
+    sgemm_emu_split_k(M, N, K, nbands), sgemm_emu_split_k_fp32_b(M, N, K, nbands)
     sgemm_emu_release_workspace()
     sgemm_emu_products(nbands), sgemm_emu_strerror(status), sgemm_emu_version()
 
@@ -64,7 +64,8 @@ SGEMM_EMU_NO_WORKSPACE = 128   # flag (sgemm_emu_ex): in-kernel split, no stream
 EXPORTS = ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_presplit_b_noalloc",
            "sgemm_emu_linear",
            "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
-           "sgemm_emu_release_workspace", "sgemm_emu_products", "sgemm_emu_strerror", "sgemm_emu_version")
+           "sgemm_emu_split_k_fp32_b", "sgemm_emu_release_workspace", "sgemm_emu_products", "sgemm_emu_strerror",
+           "sgemm_emu_version")
 
 
 class SgemmEmuError(RuntimeError):
@@ -94,6 +95,7 @@ def lib():
         L.split_f32_bf16x3_transposed.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, vp]
         L.split_f32_bf16x3_ex.argtypes = [i64, i64, vp, i64, vp, vp, vp, i64, ci, vp]
         L.sgemm_emu_split_k.argtypes = [i64, i64, i64, ci]
+        L.sgemm_emu_split_k_fp32_b.argtypes = [i64, i64, i64, ci]
         L.sgemm_emu_release_workspace.argtypes = []
         L.sgemm_emu_products.argtypes = [ci]
         L.sgemm_emu_strerror.argtypes = [ci]
@@ -103,7 +105,7 @@ def lib():
         for n in ("sgemm_bf16x9", "sgemm_emu", "sgemm_emu_ex", "sgemm_emu_presplit_b", "sgemm_emu_presplit_b_noalloc",
                   "sgemm_emu_linear",
                   "split_f32_bf16x3", "split_f32_bf16x3_transposed", "split_f32_bf16x3_ex", "sgemm_emu_split_k",
-                  "sgemm_emu_release_workspace", "sgemm_emu_products"):
+                  "sgemm_emu_split_k_fp32_b", "sgemm_emu_release_workspace", "sgemm_emu_products"):
             getattr(L, n).restype = ci
         _LIB = L
     return _LIB
@@ -192,6 +194,11 @@ def split_f32_bf16x3_ex(rows, cols, X, ldx, X0, X1, X2, ldo, flags, stream=None)
 def sgemm_emu_split_k(M, N, K, nbands=5):
     status = lib().sgemm_emu_split_k(M, N, K, nbands)
     return _ok(status, "sgemm_emu_split_k") if status < 0 else status
+
+
+def sgemm_emu_split_k_fp32_b(M, N, K, nbands=5):
+    status = lib().sgemm_emu_split_k_fp32_b(M, N, K, nbands)
+    return _ok(status, "sgemm_emu_split_k_fp32_b") if status < 0 else status
 
 
 def sgemm_emu_release_workspace():

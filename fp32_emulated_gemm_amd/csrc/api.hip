@@ -314,6 +314,15 @@ int validate_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, 
     return SGEMM_EMU_OK;
 }
 
+// True where FP32 B may be split into N x K' planes for stream-K (K' = K
+// rounded up to a multiple of 64): a workspace may be used, the planes are
+// within the size limit, and the RNE split needs no K padding.
+static bool fp32_b_streamk_allowed(int64_t N, int64_t K, bool rne, bool no_workspace)
+{
+    const int64_t kpad = (K + 63) / 64 * 64;
+    return !no_workspace && (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !(rne && kpad != K);
+}
+
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
                 int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
@@ -340,6 +349,17 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
 
     g.splits = 1;
 
+    // FP32 B on a partly filled grid where the cost model expects the
+    // one-pass kernel on 64 x 64 tiles (B split inside each tile, four times
+    // the workgroups, no workspace) to beat 128 x 128 tiles, with or without
+    // a split of B and stream-K: the same split, products and MFMA order as
+    // the one-pass kernel on 128 x 128 tiles, so bitwise the result of
+    // SGEMM_EMU_NO_WORKSPACE, and nothing allocated.
+    const int64_t kpad = (K + 63) / 64 * 64;
+    if (bsrc == B_FP32 && !(force_presplit && M >= kPresplitMinRows) &&
+        gemm_tile64_pays(M, N, K, num_cus, fp32_b_streamk_allowed(N, K, rne, no_workspace)))
+        return launched(launch_gemm_tile64(g, nbands, stream, rne));
+
     // FP32 B with many tile rows: split B once into N x K planes in a
     // stream-ordered workspace and run the LDS-DMA kernel, instead of splitting
     // B again in every tile row.  Same split, same products, same order of
@@ -348,7 +368,6 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // the planes (zeros) and the kernel masks A past its K.
     // Where pays: grids small enough for stream-K (which only the DMA kernel
     // runs, whatever M), and from M >= 1024 rows large GEMMs.
-    const int64_t kpad = (K + 63) / 64 * 64;
     const bool small_grid = !no_workspace && gemm_streamk_grid(M, N, kpad, num_cus) > 0;
     const bool large = !no_workspace && M >= kPresplitMinRows &&
                        2.0 * (double)M * (double)N * (double)K >= kPresplitMinFlops;
@@ -721,6 +740,19 @@ int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands)
     if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
     if (M == 0 || N == 0 || K == 0) return 1;
     return gemm_streamk_pieces(M, N, K, gemm_streamk_grid(M, N, K, num_cus));
+}
+
+int sgemm_emu_split_k_fp32_b(int64_t M, int64_t N, int64_t K, int nbands)
+{
+    int rc;
+    if ((rc = check_dims(M, N, K)) != SGEMM_EMU_OK) return rc;
+    if (nbands < 1 || nbands > 5) return SGEMM_EMU_EINVAL;
+    int num_cus = 0;
+    if ((rc = current_device(&num_cus)) != SGEMM_EMU_OK) return rc;
+    if (M == 0 || N == 0 || K == 0) return 1;
+    const int64_t kpad = (K + 63) / 64 * 64;
+    if (!fp32_b_streamk_allowed(N, K, false, false) || gemm_tile64_pays(M, N, K, num_cus, true)) return 1;
+    return gemm_streamk_pieces(M, N, kpad, gemm_streamk_grid(M, N, kpad, num_cus));
 }
 
 int sgemm_emu_products(int nbands)

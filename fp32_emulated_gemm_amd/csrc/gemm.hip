@@ -98,6 +98,7 @@ struct Cfg {
 
 using Cfg8 = Cfg<2, 4, 64, 32>;              // 8 waves, 2 per SIMD, 128 x 128 tile
 using Cfg8S = Cfg<2, 4, 64, 32, true, 4, 4>; // same, staging interleaved with the MFMAs
+using Cfg64S = Cfg<2, 2, 32, 32, true, 4, 4>; // 4 waves, 64 x 64 tile, two workgroups per CU (FP32 B, small grids)
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -1670,6 +1671,34 @@ int gemm_streamk_pieces(int64_t M, int64_t N, int64_t K, int grid)
     return (int)most;
 }
 
+// FP32 B on a partly filled grid: the one-pass kernel on 64 x 64 tiles (B
+// split inside each tile, nothing in a workspace, LDS for two workgroups per
+// CU) against what 128 x 128 tiles would run -- one pass per tile (the kernel
+// that splits B itself, or the N x K plane kernel after a split of B), or,
+// where `streamk` allows it, stream-K on split planes.  Costs in K-pair times
+// of a 128 x 128 tile on one CU, in twentieths: a 64 x 64 tile's K pair
+// measured half of that on a CU of its own and 0.65 beside a second one
+// (512^3, 768^3, 1024^3, 1024 x 1024 x 512, 2048 x 512 x 512,
+// 1280 / 1536 / 2048 x 1024 x 1024, 4096 x 512 x 1024, 6144 x 256 x 1024 and
+// 512 x 512 x 4096 on 256 CUs); stream-K as in gemm_streamk_grid.  Taken where
+// the model expects the 64 x 64 tiles 10 % faster: measured 7-90 % faster
+// there, and where it declines (256^2 x 1024, 512^2 x 2048 and x 4096,
+// 1024^2 x 2048, 2560 x 1024 x 512, 3072 x 1024 x 1024, 3072 x 1536 x 1024)
+// the other path was 3-150 % faster.  Four 64 x 64 tiles cost 1.3 times one
+// 128 x 128 tile once the grid fills the CUs, so full grids never take them.
+bool gemm_tile64_pays(int64_t M, int64_t N, int64_t K, int num_cus, bool streamk)
+{
+    const int64_t kpad = (K + 2 * BK - 1) / (2 * BK) * (2 * BK), ppt = kpad / (2 * BK);
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t G0 = num_cus > 8 ? num_cus & ~7 : 8;
+    int64_t t_other = (tiles + G0 - 1) / G0 * ppt;
+    const int G = streamk ? gemm_streamk_grid(M, N, kpad, num_cus) : 0;
+    if (G > 0) t_other = (tiles * ppt + G - 1) / G + kStreamkFixPairs;
+    const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t t_tile64 = ppt * (tiles64 <= G0 ? 10 : 13 * ((tiles64 + 2 * G0 - 1) / (2 * G0)));
+    return t_tile64 * 10 <= 20 * t_other * 9;
+}
+
 static int group_rows(int tiles_n, int num_cus);
 
 // ---------------------------------------------------------------- native FP32 (performant strategy)
@@ -2092,16 +2121,28 @@ hipError_t launch_gemm_planes(const GemmArgs &args, int nbands, hipStream_t stre
 }
 
 template <class C>
-static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
+static GemmArgs tiled(const GemmArgs &args)
 {
     GemmArgs g = args;
     g.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
     g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
     g.group_m = group_rows(g.tiles_n, g.num_cus);
-    // 128-bit loads along k need every 4 (A) or 8 (N x K planes) elements to
-    // lie entirely below or entirely above K, so that no vector load straddles
-    // the end of its descriptor's range.
-    const bool avec = aligned(g.A, 16) && (g.lda % 4 == 0) && (g.K % 4 == 0);
+    return g;
+}
+
+// 128-bit loads along k need every 4 (A) or 8 (N x K planes) elements to lie
+// entirely below or entirely above K, so that no vector load straddles the
+// end of its descriptor's range.
+static bool a_vec(const GemmArgs &g)
+{
+    return aligned(g.A, 16) && (g.lda % 4 == 0) && (g.K % 4 == 0);
+}
+
+template <class C>
+static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
+{
+    const GemmArgs g = tiled<C>(args);
+    const bool avec = a_vec(g);
     bool bvec = false;
     if (bsrc == B_PLANES_NK)
         bvec = aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && (g.ldb % 8 == 0) && (g.K % 8 == 0);
@@ -2117,6 +2158,14 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
     case B_PLANES_NK: launch_nb<C, B_PLANES_NK>(g, nbands, avec, bvec, stream); break;
     default: launch_nb<C, B_PLANES_KN>(g, nbands, avec, bvec, stream); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_tile64(const GemmArgs &args, int nbands, hipStream_t stream, bool rne)
+{
+    const GemmArgs g = tiled<Cfg64S>(args);
+    if (rne) launch_nb<Cfg64S, B_FP32, true>(g, nbands, a_vec(g), false, stream);
+    else launch_nb<Cfg64S, B_FP32>(g, nbands, a_vec(g), false, stream);
     return hipGetLastError();
 }
 

@@ -86,6 +86,17 @@ int gemm_streamk_grid(int64_t M, int64_t N, int64_t K, int num_cus);
 // Most K pieces any tile is cut into by a stream-K grid of `grid` workgroups.
 int gemm_streamk_pieces(int64_t M, int64_t N, int64_t K, int grid);
 
+// True where the cost model expects the one-pass kernel on 64 x 64 tiles to
+// be faster on FP32 B of this shape than 128 x 128 tiles: one pass per tile,
+// or, if `streamk`, stream-K on planes split with K rounded up to a multiple
+// of 64 where gemm_streamk_grid takes it.
+bool gemm_tile64_pays(int64_t M, int64_t N, int64_t K, int num_cus, bool streamk);
+
+// FP32 B (args.B, ldb) on 64 x 64 tiles, one pass over K per tile: the same
+// split, products and MFMA order as launch_gemm's one-pass kernel on FP32 B,
+// so bitwise the same result.  Needs no workspace; leaves args.done unused.
+hipError_t launch_gemm_tile64(const GemmArgs &args, int nbands, hipStream_t stream, bool rne = false);
+
 // True when launch_gemm ties args.done to its last kernel for this call (the
 // N x K DMA path).
 bool launch_done_attached(const GemmArgs &args, BSource bsrc);

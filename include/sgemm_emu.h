@@ -28,7 +28,8 @@
  *     each piece of a tile runs the method on its K range and the pieces' FP32
  *     results are added in K order; if the device memory for those partial
  *     results cannot be had, the call returns SGEMM_EMU_ENOMEM rather than
- *     round another way.
+ *     round another way.  With FP32 B, some of those grids run one pass over K
+ *     per 64 x 64 tile instead (see sgemm_emu_split_k_fp32_b).
  *   - non-finite inputs follow IEEE rules on the components (Inf times a zero
  *     component is NaN), so results are not IEEE-754 SGEMM results for them.
  *
@@ -47,7 +48,7 @@
  *   rounded up to a multiple of 64) split B once into an N x K' set of BF16
  *   planes, zero past K (6 K' N bytes), where that is faster than splitting
  *   B inside the GEMM kernel: when the tile grid takes stream-K (see
- *   sgemm_emu_split_k; any M), or when M >= 1024 and 2 M N K >= 1.2e10 (sgemm_emu_ex's
+ *   sgemm_emu_split_k_fp32_b; any M), or when M >= 1024 and 2 M N K >= 1.2e10 (sgemm_emu_ex's
  *   SGEMM_EMU_PRESPLIT_B asks for it whenever M >= 1024 and K' N allow).
  *   sgemm_emu_presplit_b with K x N planes follows the same rule, with the
  *   planes transposed into the workspace instead of split.  Where B is
@@ -355,6 +356,27 @@ int split_f32_bf16x3_transposed(int64_t rows, int64_t cols,
  * sizes or nbands, no gfx950 device).
  */
 int sgemm_emu_split_k(int64_t M, int64_t N, int64_t K, int nbands);
+
+/*
+ * sgemm_emu_split_k_fp32_b -- the same count for sgemm_bf16x9 and sgemm_emu
+ * (no flags) on FP32 B on the current device.  Where a tile grid leaves CUs
+ * idle, the library weighs, with a cost model measured on MI355X, a kernel on
+ * 64 x 64 tiles (four times the workgroups of 128 x 128 tiles; B split inside
+ * each tile, one pass over K, no workspace) against 128 x 128 tiles: one pass
+ * per tile, or, where sgemm_emu_split_k(M, N, K', nbands) > 1 (K' = K rounded
+ * up to a multiple of 64), B split into N x K' workspace planes and stream-K.
+ * Returns 1 where the GEMM runs one pass over K per tile (on either tile
+ * size): its result is then bitwise that of SGEMM_EMU_NO_WORKSPACE (the same
+ * split, products and MFMA order for each output).  Otherwise returns
+ * sgemm_emu_split_k(M, N, K', nbands): the result is bitwise that of
+ * sgemm_emu_presplit_b on those planes.  Returns a negative status as
+ * sgemm_emu_split_k does.  Flags of sgemm_emu_ex can change the path:
+ * SGEMM_EMU_PRESPLIT_B / _A with M >= 1024 keep the planes (and their
+ * stream-K), SGEMM_EMU_NO_WORKSPACE never cuts K, SGEMM_EMU_SPLIT_RNE cuts K
+ * only where K % 64 == 0.  The choice depends on the shape and the device's
+ * CU count, never on the values.
+ */
+int sgemm_emu_split_k_fp32_b(int64_t M, int64_t N, int64_t K, int nbands);
 
 /*
  * sgemm_emu_release_workspace -- gives back the workspace the library keeps on

@@ -34,6 +34,10 @@ int gemm_streamk_grid(int64_t, int64_t, int64_t, int) { return 0; }
 
 int gemm_streamk_pieces(int64_t, int64_t, int64_t, int) { return 1; }
 
+bool gemm_tile64_pays(int64_t, int64_t, int64_t, int, bool) { return false; }
+
+hipError_t launch_gemm_tile64(const GemmArgs &, int, hipStream_t, bool) { return hipErrorNotSupported; }
+
 bool launch_done_attached(const GemmArgs &, BSource) { return false; }
 
 bool gemm_uses_dma(int64_t, int64_t, const void *, const void *, const void *) { return false; }

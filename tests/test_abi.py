@@ -87,6 +87,8 @@ def test_sgemm_validation_before_any_hip_call(L, args, status):
 def test_bad_nbands(L, nbands):
     assert L.sgemm_emu(4, 4, 4, P, 4, P, 4, P, 4, nbands, None) == -1
     assert L.sgemm_emu_presplit_b(4, 4, 4, P, 4, P, P, P, 4, 0, P, 4, nbands, None) == -1
+    assert L.sgemm_emu_split_k(4, 4, 4, nbands) == -1
+    assert L.sgemm_emu_split_k_fp32_b(4, 4, 4, nbands) == -1
 
 
 def test_presplit_validation(L):
@@ -157,6 +159,8 @@ def test_valid_call_without_gpu_reports_arch(L):
     assert L.sgemm_bf16x9(4, 4, 4, P, 4, P, 4, P, 4, None) == -3
     assert L.split_f32_bf16x3(4, 4, P, 4, P, P, P, 4, None) == -3
     assert L.sgemm_emu_release_workspace() == -3
+    assert L.sgemm_emu_split_k_fp32_b(1024, 1024, 1024, 5) == -3
+    assert L.sgemm_emu_split_k_fp32_b(-1, 4, 4, 5) == -1
 
 
 def test_leading_dimension_limit(L):

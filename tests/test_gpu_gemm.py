@@ -86,10 +86,11 @@ DMA_SHAPES = [(129, 130, 64), (300, 257, 128), (64, 300, 256), (513, 384, 192), 
 
 def same_order_as_fused(fe, M, N, K):
     """True when the N x K plane GEMM adds in the same order as sgemm_bf16x9 on
-    FP32 B: neither cuts K (stream-K), or both do it alike (K % 64 == 0: the
-    FP32 B is then split into N x K planes in a workspace for the same kernel)."""
-    kpad = (K + 63) // 64 * 64
-    return K % 64 == 0 or fe.sgemm_emu_split_k(M, N, kpad) == 1
+    FP32 B: neither cuts K (stream-K), or both do it alike (K % 64 == 0 and
+    the FP32 B split into N x K planes in a workspace for the same kernel)."""
+    fused = fe.sgemm_emu_split_k_fp32_b(M, N, K)
+    planes = fe.sgemm_emu_split_k(M, N, K) if K % 64 == 0 else 1
+    return (fused == 1 and planes == 1) or (fused > 1 and K % 64 == 0)
 
 
 @pytest.mark.parametrize("shape", DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -151,8 +152,9 @@ def test_fp32_b_workspace_path(fe, shape):
     B = g.standard_normal((K, N)).astype(np.float32)
     C = run(fe, A, B, entry="fused_ws")
     check_against_fp64(C, A, B, label=f"workspace {shape}")
-    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
     kpad = (K + 63) // 64 * 64
+    if fe.sgemm_emu_split_k_fp32_b(M, N, K) == fe.sgemm_emu_split_k(M, N, kpad):
+        assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
     if K == kpad or fe.sgemm_emu_split_k(M, N, kpad) == 1:
         assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
     if fe.sgemm_emu_split_k(M, N, kpad) == 1:
@@ -350,8 +352,7 @@ def test_no_workspace_one_pass(fe, shape):
     C = run(fe, A, B, entry="fused_nows")
     check_against_fp64(C, A, B, label=f"no workspace {shape}")
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_nows").view(np.uint32))
-    kpad = (K + 63) // 64 * 64
-    if fe.sgemm_emu_split_k(M, N, kpad) == 1:
+    if fe.sgemm_emu_split_k_fp32_b(M, N, K) == 1:
         assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
 
 
@@ -397,7 +398,8 @@ def test_split_k_within_bound_and_deterministic(fe, shape):
     """Small tile grids share their work stream-K style: each piece of a tile
     runs the method on its K range, the pieces' results are added in K order.
     Within the bound, identical on repeat, and sgemm_bf16x9 on FP32 B agrees
-    with the caller-split planes bit for bit (both take the same kernel)."""
+    with the caller-split planes bit for bit where it takes the same kernel,
+    else (one pass per 64 x 64 tile) with the one-pass result."""
     M, N, K = shape
     assert fe.sgemm_emu_split_k(M, N, K) > 1
     g = _rng(M * 3 + N * 5 + K * 7)
@@ -408,8 +410,11 @@ def test_split_k_within_bound_and_deterministic(fe, shape):
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
     F = run(fe, A, B, entry="fused")
     check_against_fp64(F, A, B, label=f"split-k fused {shape}")
-    # FP32 B on a stream-K grid is split into N x K workspace planes for the same kernel, at any M
-    assert np.array_equal(C.view(np.uint32), F.view(np.uint32))
+    if fe.sgemm_emu_split_k_fp32_b(M, N, K) > 1:
+        # FP32 B split into N x K workspace planes for the same stream-K kernel, at any M
+        assert np.array_equal(C.view(np.uint32), F.view(np.uint32))
+    else:
+        assert np.array_equal(F.view(np.uint32), run(fe, A, B, entry="fused_nows").view(np.uint32))
 
 
 @pytest.mark.parametrize("shape", [(3072, 1536, 1024), (8192, 640, 1024)], ids=lambda s: "x".join(map(str, s)))
@@ -429,6 +434,7 @@ def test_streamk_on_partly_filled_grids(fe, shape):
                                      [M - 1]]).clip(0, M - 1))
     check_against_fp64(C[rows], A, B, rows=rows, label=f"stream-K {shape}")
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
+    assert fe.sgemm_emu_split_k_fp32_b(M, N, K) == fe.sgemm_emu_split_k(M, N, K)
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
     R = run(fe, A, B, entry="fused_nows")
     check_against_fp64(R[rows], A, B, rows=rows, label=f"one pass {shape}")
@@ -495,6 +501,103 @@ def test_split_k_exact_integers_bitwise_vs_oracle(fe, orc, entry):
     assert np.array_equal(C.astype(np.int64), exact)
     nz = exact != 0
     assert np.array_equal(C.view(np.uint32)[nz], E.view(np.uint32)[nz])
+
+
+TILE64_SHAPES = [(1024, 1024, 1000), (6144, 256, 1000), (1025, 301, 768), (777, 555, 333), (513, 384, 192),
+                 (17, 33, 5)]
+
+
+@pytest.mark.parametrize("shape", TILE64_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp32_b_on_64_tiles(fe, shape):
+    """Partly filled grids of FP32 B that the cost model gives to the one-pass
+    kernel on 64 x 64 tiles (B split inside each tile, nothing allocated):
+    within the FP64 bound, identical on repeat, and bit for bit the caller's
+    N x K planes where those run one pass over K on 128 x 128 tiles (same
+    split, products and MFMA order per output).  Ragged M, N and K."""
+    M, N, K = shape
+    kpad = (K + 63) // 64 * 64
+    assert fe.sgemm_emu_split_k_fp32_b(M, N, K) == 1
+    g = _rng(M + 7 * N + 3 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="fused")
+    check_against_fp64(C, A, B, label=f"64 x 64 tiles {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_nows").view(np.uint32))
+    if K % 64 != 0 or fe.sgemm_emu_split_k(M, N, K) == 1:
+        assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
+    if fe.sgemm_emu_split_k(M, N, kpad) > 1:
+        # the cost model preferred these tiles to stream-K: the caller's planes still take it
+        check_against_fp64(run(fe, A, B, entry="presplit_t"), A, B, label=f"stream-K beside {shape}")
+
+
+@pytest.mark.parametrize("nbands", [1, 2, 3, 4])
+def test_fp32_b_on_64_tiles_bands_offsets_and_ldc(fe, orc, nbands):
+    """The 64 x 64 kernel for every band count, with A off its 16-byte
+    alignment (element loads) and C rows padded: the oracle's truncated-band
+    value within its bound, and the caller's planes on 128 x 128 tiles bit for
+    bit."""
+    M, N, K = 777, 555, 333
+    assert fe.sgemm_emu_split_k_fp32_b(M, N, K) == 1
+    g = _rng(4000 + nbands)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, nbands, "fused", ldc_pad=3, a_offset=1).astype(np.float64)
+    T = orc.gemm_trunc_f64(A, B, nbands)
+    _, G = orc.gemm_f64(A, B)
+    assert np.all(np.abs(C - T) <= 2 * K * 2.0 ** -24 * G)
+    R = run(fe, A, B, nbands, "presplit_t")
+    assert np.array_equal(C.astype(np.float32).view(np.uint32), R.view(np.uint32))
+
+
+def test_fp32_b_on_64_tiles_exact_integers_and_specials(fe, orc):
+    """1024^3 on 64 x 64 tiles (where 128 x 128 tiles would take stream-K):
+    integer operands whose every partial sum is exact give the exact product,
+    as the oracle's emulation does; Inf and NaN in A and B give the oracle
+    emulation's class for every output."""
+    M = N = K = 1024
+    assert fe.sgemm_emu_split_k_fp32_b(M, N, K) == 1 and fe.sgemm_emu_split_k(M, N, K) > 1
+    g = _rng(6464)
+    A = np.zeros((M, K), np.float32)
+    for i in range(M):
+        cols = g.choice(K, size=48, replace=False)
+        A[i, cols] = g.integers(1, 512, size=48) * np.where(g.integers(0, 2, size=48) == 1, -1, 1)
+    B = (g.integers(1, 512, size=(K, N)) * np.where(g.integers(0, 2, size=(K, N)) == 1, -1, 1)).astype(np.float32)
+    exact = A.astype(np.int64) @ B.astype(np.int64)
+    assert np.abs(exact).max() < 1 << 24
+    C = run(fe, A, B, entry="fused")
+    assert np.array_equal(C.astype(np.int64), exact)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    A[3, 700], A[900, 5], A[1023, 1023] = np.inf, -np.inf, np.nan
+    B[700, 64], B[12, 1000] = np.inf, np.nan
+    B[:, 513] = 0.0
+    C = run(fe, A, B, entry="fused")
+    E = orc.gemm_emu(A, B)
+
+    def cls(X):
+        return np.where(np.isnan(X), 0, np.where(X == np.inf, 1, np.where(X == -np.inf, 2, 3)))
+    assert np.array_equal(cls(C), cls(E))
+
+
+def test_fp32_b_on_64_tiles_rne(fe, orc):
+    """SGEMM_EMU_SPLIT_RNE on 64 x 64 tiles: within the bound against the
+    oracle's RNE truncated-band value, and bit for bit the one pass on
+    128 x 128 tiles that SGEMM_EMU_PRESPLIT_B leaves to rows >= 1024 when K
+    is not a multiple of 64 (the RNE split is not padded into planes)."""
+    M, N, K = 1025, 301, 700
+    assert fe.sgemm_emu_split_k_fp32_b(M, N, K) == 1
+    g = _rng(6565)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    rows = np.sort(g.choice(M, size=96, replace=False))
+    _, G = orc.gemm_f64(A, B, rows=rows)
+    for nb in (5, 2):
+        C = _run_ex(fe, A, B, nb, fe.SGEMM_EMU_SPLIT_RNE)
+        T = orc.gemm_trunc_f64(A, B, nb, rows=rows, flags=orc.ORC_SPLIT_RNE)
+        assert np.all(np.abs(C[rows].astype(np.float64) - T) <= 2 * K * 2.0 ** -24 * G), f"nbands={nb}"
+        R = _run_ex(fe, A, B, nb, fe.SGEMM_EMU_SPLIT_RNE | fe.SGEMM_EMU_PRESPLIT_B)
+        assert np.array_equal(C.view(np.uint32), R.view(np.uint32)), f"nbands={nb}"
 
 
 def test_presplit_equals_fused_bitwise(fe):
