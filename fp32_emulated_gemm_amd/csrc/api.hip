@@ -314,6 +314,16 @@ int validate_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, 
     return SGEMM_EMU_OK;
 }
 
+// True where the caller's N x K planes of this shape run on 64 x 64 tiles:
+// where the plane kernel would not take stream-K and the cost model expects
+// the 64 x 64 tiles to beat one pass per 128 x 128 tile.
+static bool nk_tile64(int64_t M, int64_t N, int64_t K, const uint16_t *B0, const uint16_t *B1,
+                      const uint16_t *B2, int64_t ldb, int num_cus)
+{
+    if (gemm_uses_dma(K, ldb, B0, B1, B2) && gemm_streamk_grid(M, N, K, num_cus) > 0) return false;
+    return gemm_tile64_pays(M, N, K, num_cus, false);
+}
+
 // True where FP32 B may be split into N x K' planes for stream-K (K' = K
 // rounded up to a multiple of 64): a workspace may be used, the planes are
 // within the size limit, and the RNE split needs no K padding.
@@ -358,7 +368,12 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     const int64_t kpad = (K + 63) / 64 * 64;
     if (bsrc == B_FP32 && !(force_presplit && M >= kPresplitMinRows) &&
         gemm_tile64_pays(M, N, K, num_cus, fp32_b_streamk_allowed(N, K, rne, no_workspace)))
-        return launched(launch_gemm_tile64(g, nbands, stream, rne));
+        return launched(launch_gemm_tile64(g, nbands, B_FP32, stream, rne));
+    // The caller's N x K planes where stream-K would not run (or cannot: K not
+    // a multiple of 64, unaligned planes): 64 x 64 tiles against one pass per
+    // 128 x 128 tile, by the same model (bitwise the same result).
+    if (bsrc == B_PLANES_NK && nk_tile64(M, N, K, B0, B1, B2, ldb, num_cus))
+        return launched(launch_gemm_tile64(g, nbands, B_PLANES_NK, stream));
 
     // FP32 B with many tile rows: split B once into N x K planes in a
     // stream-ordered workspace and run the LDS-DMA kernel, instead of splitting
@@ -575,6 +590,8 @@ int gemm_noalloc(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, c
     g.act = SGEMM_EMU_ACT_NONE;
     g.num_cus = num_cus;
     g.splits = 1;
+    if (nk_tile64(M, N, K, B0, B1, B2, ldb, num_cus))
+        return launched(launch_gemm_tile64(g, nbands, B_PLANES_NK, stream));
     const int skg = gemm_uses_dma(K, ldb, B0, B1, B2) ? gemm_streamk_grid(M, N, K, num_cus) : 0;
     if (skg > 0) {
         if ((size_t)skg > kScratchSlots) return SGEMM_EMU_ENOMEM;

@@ -2161,11 +2161,20 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_tile64(const GemmArgs &args, int nbands, hipStream_t stream, bool rne)
+hipError_t launch_gemm_tile64(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
 {
     const GemmArgs g = tiled<Cfg64S>(args);
-    if (rne) launch_nb<Cfg64S, B_FP32, true>(g, nbands, a_vec(g), false, stream);
-    else launch_nb<Cfg64S, B_FP32>(g, nbands, a_vec(g), false, stream);
+    if (bsrc == B_PLANES_NK) {
+        if (rne) return hipErrorInvalidValue;
+        const bool bvec = aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && (g.ldb % 8 == 0) &&
+                          (g.K % 8 == 0);
+        launch_nb<Cfg64S, B_PLANES_NK>(g, nbands, a_vec(g), bvec, stream);
+    } else if (bsrc == B_FP32) {
+        if (rne) launch_nb<Cfg64S, B_FP32, true>(g, nbands, a_vec(g), false, stream);
+        else launch_nb<Cfg64S, B_FP32>(g, nbands, a_vec(g), false, stream);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -92,10 +92,13 @@ int gemm_streamk_pieces(int64_t M, int64_t N, int64_t K, int grid);
 // of 64 where gemm_streamk_grid takes it.
 bool gemm_tile64_pays(int64_t M, int64_t N, int64_t K, int num_cus, bool streamk);
 
-// FP32 B (args.B, ldb) on 64 x 64 tiles, one pass over K per tile: the same
-// split, products and MFMA order as launch_gemm's one-pass kernel on FP32 B,
-// so bitwise the same result.  Needs no workspace; leaves args.done unused.
-hipError_t launch_gemm_tile64(const GemmArgs &args, int nbands, hipStream_t stream, bool rne = false);
+// FP32 B (args.B, ldb) or N x K planes (args.B0..B2, ldb) on 64 x 64 tiles,
+// one pass over K per tile: the same split, products and MFMA order as
+// launch_gemm's one-pass kernels, so bitwise the same result.  Needs no
+// workspace; leaves args.done unused.  RNE with planes (split already done)
+// or another B source: hipErrorInvalidValue, nothing launched.
+hipError_t launch_gemm_tile64(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream,
+                              bool rne = false);
 
 // True when launch_gemm ties args.done to its last kernel for this call (the
 // N x K DMA path).

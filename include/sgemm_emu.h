@@ -226,8 +226,11 @@ enum sgemm_emu_b_layout {
  * N x K' workspace planes (6 K' N bytes; zero past K) where sgemm_bf16x9
  * would pre-split an FP32 B of this shape, since the kernel for N x K planes
  * copies them into LDS without passing through registers.  The result equals
- * sgemm_emu on the FP32 B bit for bit either way.  An unknown b_layout gives
- * SGEMM_EMU_EINVAL.
+ * sgemm_emu on the FP32 B bit for bit either way.  SGEMM_EMU_B_NK planes on a
+ * partly filled tile grid that does not take stream-K (see sgemm_emu_split_k)
+ * run one pass over K per 64 x 64 tile, through registers, where the cost model
+ * of sgemm_emu_split_k_fp32_b expects that to be faster (the same bits as one
+ * pass per 128 x 128 tile).  An unknown b_layout gives SGEMM_EMU_EINVAL.
  */
 int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
                          const float *A, int64_t lda,

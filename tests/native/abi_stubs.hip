@@ -36,7 +36,7 @@ int gemm_streamk_pieces(int64_t, int64_t, int64_t, int) { return 1; }
 
 bool gemm_tile64_pays(int64_t, int64_t, int64_t, int, bool) { return false; }
 
-hipError_t launch_gemm_tile64(const GemmArgs &, int, hipStream_t, bool) { return hipErrorNotSupported; }
+hipError_t launch_gemm_tile64(const GemmArgs &, int, BSource, hipStream_t, bool) { return hipErrorNotSupported; }
 
 bool launch_done_attached(const GemmArgs &, BSource) { return false; }
 

@@ -81,7 +81,9 @@ def test_random_shapes_within_bound(fe, shape, entry):
     check_against_fp64(C, A, B, label=f"{entry} {shape}")
 
 
-DMA_SHAPES = [(129, 130, 64), (300, 257, 128), (64, 300, 256), (513, 384, 192), (1000, 1030, 1024)]
+# the first four are small enough for 64 x 64 tiles through registers (same bits)
+DMA_SHAPES = [(129, 130, 64), (300, 257, 128), (64, 300, 256), (513, 384, 192), (1000, 1030, 1024),
+              (4100, 1030, 64), (2500, 2100, 192)]
 
 
 def same_order_as_fused(fe, M, N, K):
@@ -598,6 +600,31 @@ def test_fp32_b_on_64_tiles_rne(fe, orc):
         assert np.all(np.abs(C[rows].astype(np.float64) - T) <= 2 * K * 2.0 ** -24 * G), f"nbands={nb}"
         R = _run_ex(fe, A, B, nb, fe.SGEMM_EMU_SPLIT_RNE | fe.SGEMM_EMU_PRESPLIT_B)
         assert np.array_equal(C.view(np.uint32), R.view(np.uint32)), f"nbands={nb}"
+
+
+NK64_SHAPES = [(1024, 1024, 512), (2048, 512, 512), (513, 384, 192), (777, 555, 333)]
+
+
+@pytest.mark.parametrize("shape", NK64_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_nk_planes_on_64_tiles(fe, shape):
+    """The caller's N x K planes on a partly filled grid that stream-K leaves
+    alone (or cannot take: K % 64 != 0) run one pass per 64 x 64 tile: within
+    the bound, bit for bit the K x N planes' one pass on 128 x 128 tiles and
+    FP32 B, and the entry point that allocates nothing gives the same bits."""
+    M, N, K = shape
+    assert fe.sgemm_emu_split_k(M, N, K) == 1 and fe.sgemm_emu_split_k_fp32_b(M, N, K) == 1
+    g = _rng(M + 11 * N + 5 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="presplit_t")
+    check_against_fp64(C, A, B, label=f"N x K planes, 64 x 64 tiles {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit").view(np.uint32))
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
+    P = fe.split(dev(np.ascontiguousarray(B.T)))
+    Cn = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    print(f"noalloc {M}x{N}x{K}", flush=True, file=sys.stderr)
+    fe.sgemm_emu_presplit_b_noalloc(M, N, K, dev(A), K, *P, K, Cn, N, 5)
+    assert np.array_equal(C.view(np.uint32), host(Cn).view(np.uint32))
 
 
 def test_presplit_equals_fused_bitwise(fe):

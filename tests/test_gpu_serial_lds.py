@@ -71,8 +71,9 @@ def _same(x, y):
 
 
 # shapes the library runs on the pipelined kernel without stream-K and without A
-# planes: one and several tiles per workgroup, ragged M and N, the K tail
-NK_SHAPES = [(300, 260, 192), (1100, 300, 128), (4096, 1024, 256), (8200, 1030, 64), (2051, 777, 320)]
+# planes (grids too full for 64 x 64 tiles): one and several tiles per
+# workgroup, ragged M and N, the K tail
+NK_SHAPES = [(3000, 2600, 192), (2200, 1300, 128), (4096, 1024, 256), (8200, 1030, 64), (4100, 1100, 320)]
 
 
 @pytest.mark.parametrize("shape", NK_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -94,7 +95,7 @@ def test_nk_planes_bitwise(fe, dbg, shape):
 
 def test_linear_bias_gelu_bitwise(fe, dbg):
     """The epilogue with bias and GELU on both kernels."""
-    M, N, K = 1100, 300, 128
+    M, N, K = 2200, 1300, 128
     A, B, Ad, P = _nk_case(fe, M, N, K, 77)
     bias = dev(_rng(78).standard_normal(N).astype(np.float32))
     for act in (fe.SGEMM_EMU_ACT_NONE, fe.SGEMM_EMU_ACT_GELU):
