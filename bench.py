@@ -40,8 +40,8 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "a219345c429769c28f18548189d2cd1a8c204129ba7abc1389fd565f064b2d3a",
-                "bytes_per_launch": [2843912040, 3264015192]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "aa099730c6ad89040a8525a424f2a7acee36adedbcacae67fc43e35fe0183def",
+                "bytes_per_launch": [2843920787, 3264021077]}
 
 # MFMA activity of the same launches, from one rocprofv3 --pmc run of the same
 # probe (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE).
@@ -51,8 +51,8 @@ GEMM_TRAFFIC = {"gemm_hip_sha256": "a219345c429769c28f18548189d2cd1a8c204129ba7a
 # divided by the kernel's own time in this run gives the shader clock the chip
 # held under the load; roofline.frac = busy x clock / 2.4 GHz.
 GEMM_MFMA_PMC = {"gemm_hip_sha256": GEMM_TRAFFIC["gemm_hip_sha256"],
-                 "mfma_busy": [0.6562, 0.7239],
-                 "active_cycles_per_xcd": [3805006, 3440504]}
+                 "mfma_busy": [0.6566, 0.7184],
+                 "active_cycles_per_xcd": [3802637, 3466749]}
 
 
 def log(msg):
@@ -298,6 +298,23 @@ def timed(fn, stream, reps):
     return a.elapsed_time(b) / reps
 
 
+def settled_ms(entries, stream, reps, warmup_s=1.0, rounds=2):
+    """Milliseconds per call of each entry point: every entry in turn for
+    warmup_s seconds first, so the clock has settled under load before anything
+    is timed; then `rounds` timed rounds in turn, the fastest of each entry
+    point's kept (the order of the entries then no longer decides which of them
+    meets a ramping clock)."""
+    import time
+    import torch
+    t0 = time.time()
+    while time.time() - t0 < warmup_s:
+        for fn in entries.values():
+            fn()
+        torch.cuda.synchronize()
+    times = [{name: timed(fn, stream, reps) for name, fn in entries.items()} for _ in range(max(rounds, 1))]
+    return {name: min(t[name] for t in times) for name in entries}
+
+
 def vendor_bf16(torch, stream, shapes, reps=10):
     """Context for the ceiling: the platform's own BF16 GEMM (torch.matmul on BF16
     operands, i.e. hipBLASLt; run, never inspected) on the given M x N x K shapes,
@@ -338,18 +355,8 @@ def one_shape(shape, reps, warmup_s=1.0, rounds=2):
         "performant": lambda: fe.sgemm_emu_ex(m, n, k, A, k, B, n, C, n, 5, fe.SGEMM_EMU_PERFORMANT, sp),
         "torch_fp32": lambda: torch.matmul(A, B, out=C),
     }
-    # every entry point in turn for warmup_s seconds first, so the clock has
-    # settled under load before anything is timed; then `rounds` timed rounds in
-    # turn, the fastest of each entry point's kept (the order of the entries
-    # then no longer decides which of them meets a ramping clock)
-    import time
-    t0 = time.time()
-    while time.time() - t0 < warmup_s:
-        for fn in entries.values():
-            fn()
-        torch.cuda.synchronize()
-    times = [{name: timed(fn, stream, reps) for name, fn in entries.items()} for _ in range(max(rounds, 1))]
-    res = {name: round(fl / min(t[name] for t in times) / 1e9, 2) for name in entries}
+    ms = settled_ms(entries, stream, reps, warmup_s, rounds)
+    res = {name: round(fl / ms[name] / 1e9, 2) for name in entries}
     print(json.dumps({"shape": [m, n, k], "reps": reps, "tflops": res,
                       "split_k": fe.sgemm_emu_split_k(m, n, k, 5)}), flush=True)
 
@@ -516,15 +523,14 @@ def context_timings(fe, torch, Xd, Hd, W1d, W2d, C1, C2, M, D, F, stream, sp):
         C = torch.empty((m, nn), device="cuda")
         Bt_planes = fe.split(B.t().contiguous())
         fs = 2.0 * m * nn * k
-        t = timed(lambda: fe.sgemm_bf16x9(m, nn, k, A, k, B, nn, C, nn, sp), stream, 20)
-        res[f"sgemm_bf16x9_{name}_tflops"] = round(fs / t / 1e9, 2)
-        t = timed(lambda: fe.sgemm_emu_presplit_b(m, nn, k, A, k, *Bt_planes, k, fe.SGEMM_EMU_B_NK, C, nn, 5, sp),
-                  stream, 20)
-        res[f"presplit_nk_{name}_tflops"] = round(fs / t / 1e9, 2)
-        t = timed(lambda: fe.sgemm_emu_ex(m, nn, k, A, k, B, nn, C, nn, 5, fe.SGEMM_EMU_PERFORMANT, sp), stream, 20)
-        res[f"performant_{name}_tflops"] = round(fs / t / 1e9, 2)
-        t = timed(lambda: torch.matmul(A, B, out=C), stream, 20)
-        res[f"torch_fp32_{name}_tflops"] = round(fs / t / 1e9, 2)
+        ms = settled_ms({
+            "sgemm_bf16x9": lambda: fe.sgemm_bf16x9(m, nn, k, A, k, B, nn, C, nn, sp),
+            "presplit_nk": lambda: fe.sgemm_emu_presplit_b(m, nn, k, A, k, *Bt_planes, k, fe.SGEMM_EMU_B_NK, C, nn,
+                                                           5, sp),
+            "performant": lambda: fe.sgemm_emu_ex(m, nn, k, A, k, B, nn, C, nn, 5, fe.SGEMM_EMU_PERFORMANT, sp),
+            "torch_fp32": lambda: torch.matmul(A, B, out=C)}, stream, 20, warmup_s=0.3)
+        for entry, t in ms.items():
+            res[f"{entry}_{name}_tflops"] = round(fs / t / 1e9, 2)
         del A, B, C, Bt_planes
     n = 4096
     g = torch.Generator(device="cuda").manual_seed(1)
