@@ -224,7 +224,7 @@ struct Roles {
     bool b_second_ok[C::B_PAIRS];
 };
 
-template <class C, int BSRC, bool BVEC>
+template <class C, int BSRC, int BVEC>
 __device__ __forceinline__ void make_roles(Roles<C, BSRC> &R, const GemmArgs &g, int64_t m0, int64_t n0)
 {
     const int tid = threadIdx.x;
@@ -283,7 +283,7 @@ __device__ __forceinline__ void make_roles(Roles<C, BSRC> &R, const GemmArgs &g,
 //     of the row (or zero past the descriptor's end), so they are masked;
 //   * FP32 B and K x N planes run along k across rows: the row offset is part
 //     of the range-checked vector offset, so rows past K read as zero.
-template <class C, int BSRC, bool AVEC, bool BVEC>
+template <class C, int BSRC, bool AVEC, int BVEC>
 __device__ __forceinline__ void load_stage(Stage<C, BSRC> &st, const Roles<C, BSRC> &R, const GemmArgs &g,
                                            int64_t m0, int64_t n0, int64_t k0)
 {
@@ -324,10 +324,13 @@ __device__ __forceinline__ void load_stage(Stage<C, BSRC> &st, const Roles<C, BS
         for (int c = 0; c < C::B_CHUNKS; ++c)
 #pragma unroll
             for (int p = 0; p < 3; ++p) {
-                if (BVEC) {
+                if constexpr (BVEC == 1) {
                     const u32x4_t v = bload_u32x4(rr[p], R.b_off[c], 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) st.bn[c][p][i] = v[i];
+                } else if constexpr (BVEC == 2) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st.bn[c][p][i] = bload_u32(rr[p], R.b_off[c] + 4 * i, 0);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -432,7 +435,7 @@ __device__ __forceinline__ bool store_stage(const Stage<C, BSRC> &st, const Role
 // Rare path for a lane whose staged values included Inf or NaN: reload the
 // same K step and rewrite its FP32-sourced component tiles with the full
 // special-value split.  Runs before the barrier that publishes the tile.
-template <class C, int BSRC, bool AVEC, bool BVEC, bool RNE>
+template <class C, int BSRC, bool AVEC, int BVEC, bool RNE>
 __device__ __forceinline__ void restage_special(const Roles<C, BSRC> &R, const GemmArgs &g, int64_t m0, int64_t n0,
                                              int64_t k0, uint16_t *buf)
 {
@@ -507,12 +510,12 @@ __device__ __forceinline__ void mfma_slice(Acc<C, NB> &acc, const Frags<C> &f)
 constexpr int products(int nb) { return nb >= 5 ? 9 : nb == 4 ? 8 : nb == 3 ? 6 : nb == 2 ? 3 : 1; }
 
 // Global load instructions one thread issues per K step (see load_stage).
-template <class C, int BSRC, bool AVEC, bool BVEC>
+template <class C, int BSRC, bool AVEC, int BVEC>
 constexpr int global_loads_per_stage()
 {
     const int a = C::A_CHUNKS * (AVEC ? 2 : 8);
     const int b = BSRC == B_FP32 ? C::B_CHUNKS * 8
-                : BSRC == B_PLANES_NK ? C::B_CHUNKS * 3 * (BVEC ? 1 : 8)
+                : BSRC == B_PLANES_NK ? C::B_CHUNKS * 3 * (BVEC == 1 ? 1 : BVEC == 2 ? 4 : 8)
                 : C::B_PAIRS * 3 * 4 * (BVEC ? 1 : 2);
     return a + b;
 }
@@ -523,7 +526,7 @@ constexpr int global_loads_per_stage()
 // the MFMAs of slice 0, and the split arithmetic and LDS writes of the next
 // step under the MFMAs of slice 1, so the matrix cores keep running while the
 // next tile is staged.  The body is a single basic block.
-template <class C, int NB, bool AVEC, int BSRC, bool BVEC, bool RAGGED, bool RNE>
+template <class C, int NB, bool AVEC, int BSRC, int BVEC, bool RAGGED, bool RNE>
 __device__ __forceinline__ void step_staging_next(Acc<C, NB> &acc, Stage<C, BSRC> &st, const Roles<C, BSRC> &R,
                                                   const GemmArgs &g, int64_t m0, int64_t n0, int64_t k_next,
                                                   const uint16_t *cur, uint16_t *nxt, int wm, int wn, int lane)
@@ -635,7 +638,7 @@ __device__ __forceinline__ void store_c(const Acc<C, NB> &acc, const float (&bv)
     else store_c_act<C, NB, 0>(acc, bv, g, m0, n0, wm, wn, lane);
 }
 
-template <class C, int NB, bool AVEC, int BSRC, bool BVEC, bool RNE>
+template <class C, int NB, bool AVEC, int BSRC, int BVEC, bool RNE>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16x9_kernel(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * C::TILE];
@@ -2011,25 +2014,33 @@ static int group_rows(int tiles_n, int num_cus)
     return tiles_n * 4 <= per_xcd ? 1 : 8;
 }
 
-template <class C, int NB, int BSRC, bool RNE>
-static void launch_cfg(const GemmArgs &g, bool avec, bool bvec, hipStream_t stream)
+template <class C, int NB, bool AVEC, int BSRC, bool RNE>
+static void launch_cfg_b(const GemmArgs &g, int bvec, hipStream_t stream)
 {
     const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n)), block(C::NT);
     if constexpr (BSRC == B_FP32) {
         // FP32 B loads element by element; only A has a vector path
-        if (avec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, false, RNE>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, false, RNE>), grid, block, 0, stream, g);
-    } else if (avec) {
-        if (bvec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, true, RNE>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, true, BSRC, false, RNE>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, AVEC, BSRC, 0, RNE>), grid, block, 0, stream, g);
     } else {
-        if (bvec) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, true, RNE>), grid, block, 0, stream, g);
-        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, false, BSRC, false, RNE>), grid, block, 0, stream, g);
+        if (bvec == 1) hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, AVEC, BSRC, 1, RNE>), grid, block, 0, stream, g);
+        else if (BSRC == B_PLANES_NK && bvec == 2)
+            hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, AVEC, BSRC, BSRC == B_PLANES_NK ? 2 : 0, RNE>), grid, block, 0,
+                               stream, g);
+        else hipLaunchKernelGGL((gemm_bf16x9_kernel<C, NB, AVEC, BSRC, 0, RNE>), grid, block, 0, stream, g);
     }
 }
 
+// bvec: B's load width -- 1: 128-bit (N x K planes) or 32-bit (K x N planes);
+// 2: 32-bit for N x K planes; 0: element loads.
+template <class C, int NB, int BSRC, bool RNE>
+static void launch_cfg(const GemmArgs &g, bool avec, int bvec, hipStream_t stream)
+{
+    if (avec) launch_cfg_b<C, NB, true, BSRC, RNE>(g, bvec, stream);
+    else launch_cfg_b<C, NB, false, BSRC, RNE>(g, bvec, stream);
+}
+
 template <class C, int BSRC, bool RNE = false>
-static void launch_nb(const GemmArgs &g, int nbands, bool avec, bool bvec, hipStream_t stream)
+static void launch_nb(const GemmArgs &g, int nbands, bool avec, int bvec, hipStream_t stream)
 {
     switch (nbands) {
     case 1: launch_cfg<C, 1, BSRC, RNE>(g, avec, bvec, stream); break;
@@ -2138,14 +2149,25 @@ static bool a_vec(const GemmArgs &g)
     return aligned(g.A, 16) && (g.lda % 4 == 0) && (g.K % 4 == 0);
 }
 
+// Load width of N x K planes: 128-bit loads need every 8 elements of a row to
+// lie entirely below or above K (16-byte aligned planes, ldb and K multiples of
+// 8); 32-bit loads need pairs (4-byte aligned planes, ldb and K even); else
+// element loads.
+static int nk_bvec(const GemmArgs &g)
+{
+    if (aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && g.ldb % 8 == 0 && g.K % 8 == 0) return 1;
+    if (aligned(g.B0, 4) && aligned(g.B1, 4) && aligned(g.B2, 4) && g.ldb % 2 == 0 && g.K % 2 == 0) return 2;
+    return 0;
+}
+
 template <class C>
 static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
 {
     const GemmArgs g = tiled<C>(args);
     const bool avec = a_vec(g);
-    bool bvec = false;
+    int bvec = 0;
     if (bsrc == B_PLANES_NK)
-        bvec = aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && (g.ldb % 8 == 0) && (g.K % 8 == 0);
+        bvec = nk_bvec(g);
     else if (bsrc == B_PLANES_KN)
         bvec = aligned(g.B0, 4) && aligned(g.B1, 4) && aligned(g.B2, 4) && (g.ldb % 2 == 0) && (g.N % 2 == 0);
     if (rne) {
@@ -2166,9 +2188,7 @@ hipError_t launch_gemm_tile64(const GemmArgs &args, int nbands, BSource bsrc, hi
     const GemmArgs g = tiled<Cfg64S>(args);
     if (bsrc == B_PLANES_NK) {
         if (rne) return hipErrorInvalidValue;
-        const bool bvec = aligned(g.B0, 16) && aligned(g.B1, 16) && aligned(g.B2, 16) && (g.ldb % 8 == 0) &&
-                          (g.K % 8 == 0);
-        launch_nb<Cfg64S, B_PLANES_NK>(g, nbands, a_vec(g), bvec, stream);
+        launch_nb<Cfg64S, B_PLANES_NK>(g, nbands, a_vec(g), nk_bvec(g), stream);
     } else if (bsrc == B_FP32) {
         if (rne) launch_nb<Cfg64S, B_FP32, true>(g, nbands, a_vec(g), false, stream);
         else launch_nb<Cfg64S, B_FP32>(g, nbands, a_vec(g), false, stream);

@@ -627,6 +627,23 @@ def test_nk_planes_on_64_tiles(fe, shape):
     assert np.array_equal(C.view(np.uint32), host(Cn).view(np.uint32))
 
 
+@pytest.mark.parametrize("shape", [(1100, 900, 700), (4100, 1100, 700), (300, 257, 100)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_nk_planes_even_k_word_loads(fe, shape):
+    """N x K planes whose K is even but not a multiple of 8 (ldb = K) load B
+    two elements at a time, on 64 x 64 and on 128 x 128 tiles: within the
+    bound and bit for bit the one pass over FP32 B (SGEMM_EMU_NO_WORKSPACE)."""
+    M, N, K = shape
+    assert K % 2 == 0 and K % 8 != 0
+    g = _rng(M + 3 * N + 7 * K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    C = run(fe, A, B, entry="presplit_t")
+    rows = None if M * N * K < 1e9 else np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    check_against_fp64(C if rows is None else C[rows], A, B, rows=rows, label=f"N x K word loads {shape}")
+    assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_nows").view(np.uint32))
+
+
 def test_presplit_equals_fused_bitwise(fe):
     g = _rng(5)
     A = g.standard_normal((200, 150)).astype(np.float32)
