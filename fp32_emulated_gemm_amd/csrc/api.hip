@@ -333,6 +333,20 @@ static bool fp32_b_streamk_allowed(int64_t N, int64_t K, bool rne, bool no_works
     return !no_workspace && (uint64_t)kpad * (uint64_t)N <= kPresplitMaxElems && !(rne && kpad != K);
 }
 
+// True where the caller's K x N planes of this shape run on 64 x 64 tiles.
+static bool kn_tile64(int64_t M, int64_t N, int64_t K, const uint16_t *B0, const uint16_t *B1,
+                      const uint16_t *B2, int64_t ldb, int num_cus, bool no_workspace)
+{
+    const bool pairs = ((uintptr_t)B0 | (uintptr_t)B1 | (uintptr_t)B2) % 4 == 0 && ldb % 2 == 0 && N % 2 == 0;
+    const bool streamk = fp32_b_streamk_allowed(N, K, false, no_workspace);
+    if (pairs) return gemm_tile64_pays(M, N, K, num_cus, streamk);
+    const int64_t kpad = (K + 63) / 64 * 64;
+    const bool transposed = streamk && (gemm_streamk_grid(M, N, kpad, num_cus) > 0 ||
+                                        (M >= kPresplitMinRows && 2.0 * (double)M * (double)N * (double)K >=
+                                                                      kPresplitMinFlops));
+    return !transposed && gemm_tile64_pays(M, N, K, num_cus, false);
+}
+
 int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int64_t ldb, float *C,
                 int64_t ldc, int nbands, BSource bsrc, hipStream_t stream, const float *bias = nullptr,
@@ -374,6 +388,13 @@ int gemm_common(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     // 128 x 128 tile, by the same model (bitwise the same result).
     if (bsrc == B_PLANES_NK && nk_tile64(M, N, K, B0, B1, B2, ldb, num_cus))
         return launched(launch_gemm_tile64(g, nbands, B_PLANES_NK, stream));
+    // K x N planes read as column pairs follow FP32 B's rule: the alternative
+    // is their transposition into N x K planes plus stream-K, as the split is
+    // for FP32 B.  Element by element (odd N or ldb) the 64 x 64 tiles lose to
+    // the transposition wherever that runs, so only one pass per 128 x 128
+    // tile is weighed against them.
+    if (bsrc == B_PLANES_KN && kn_tile64(M, N, K, B0, B1, B2, ldb, num_cus, no_workspace))
+        return launched(launch_gemm_tile64(g, nbands, B_PLANES_KN, stream));
 
     // FP32 B with many tile rows: split B once into N x K planes in a
     // stream-ordered workspace and run the LDS-DMA kernel, instead of splitting

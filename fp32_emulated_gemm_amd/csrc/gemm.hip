@@ -2160,6 +2160,13 @@ static int nk_bvec(const GemmArgs &g)
     return 0;
 }
 
+// Load width of K x N planes: 32-bit loads (a column pair) need 4-byte
+// aligned planes and ldb, N even; else element loads.
+static int kn_bvec(const GemmArgs &g)
+{
+    return aligned(g.B0, 4) && aligned(g.B1, 4) && aligned(g.B2, 4) && g.ldb % 2 == 0 && g.N % 2 == 0 ? 1 : 0;
+}
+
 template <class C>
 static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hipStream_t stream, bool rne)
 {
@@ -2169,7 +2176,7 @@ static hipError_t launch_with(const GemmArgs &args, int nbands, BSource bsrc, hi
     if (bsrc == B_PLANES_NK)
         bvec = nk_bvec(g);
     else if (bsrc == B_PLANES_KN)
-        bvec = aligned(g.B0, 4) && aligned(g.B1, 4) && aligned(g.B2, 4) && (g.ldb % 2 == 0) && (g.N % 2 == 0);
+        bvec = kn_bvec(g);
     if (rne) {
         if (bsrc != B_FP32) return hipErrorInvalidValue;
         launch_nb<C, B_FP32, true>(g, nbands, avec, false, stream);
@@ -2189,6 +2196,9 @@ hipError_t launch_gemm_tile64(const GemmArgs &args, int nbands, BSource bsrc, hi
     if (bsrc == B_PLANES_NK) {
         if (rne) return hipErrorInvalidValue;
         launch_nb<Cfg64S, B_PLANES_NK>(g, nbands, a_vec(g), nk_bvec(g), stream);
+    } else if (bsrc == B_PLANES_KN) {
+        if (rne) return hipErrorInvalidValue;
+        launch_nb<Cfg64S, B_PLANES_KN>(g, nbands, a_vec(g), kn_bvec(g), stream);
     } else if (bsrc == B_FP32) {
         if (rne) launch_nb<Cfg64S, B_FP32, true>(g, nbands, a_vec(g), false, stream);
         else launch_nb<Cfg64S, B_FP32>(g, nbands, a_vec(g), false, stream);

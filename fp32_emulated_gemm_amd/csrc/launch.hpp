@@ -92,7 +92,7 @@ int gemm_streamk_pieces(int64_t M, int64_t N, int64_t K, int grid);
 // of 64 where gemm_streamk_grid takes it.
 bool gemm_tile64_pays(int64_t M, int64_t N, int64_t K, int num_cus, bool streamk);
 
-// FP32 B (args.B, ldb) or N x K planes (args.B0..B2, ldb) on 64 x 64 tiles,
+// FP32 B (args.B, ldb) or N x K or K x N planes (args.B0..B2, ldb) on 64 x 64 tiles,
 // one pass over K per tile: the same split, products and MFMA order as
 // launch_gemm's one-pass kernels, so bitwise the same result.  Needs no
 // workspace; leaves args.done unused.  RNE with planes (split already done)

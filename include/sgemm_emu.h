@@ -230,7 +230,11 @@ enum sgemm_emu_b_layout {
  * partly filled tile grid that does not take stream-K (see sgemm_emu_split_k)
  * run one pass over K per 64 x 64 tile, through registers, where the cost model
  * of sgemm_emu_split_k_fp32_b expects that to be faster (the same bits as one
- * pass per 128 x 128 tile).  An unknown b_layout gives SGEMM_EMU_EINVAL.
+ * pass per 128 x 128 tile); SGEMM_EMU_B_KN planes with N and ldb even and
+ * 4-byte aligned planes take 64 x 64 tiles wherever sgemm_bf16x9 does for
+ * FP32 B of the shape (sgemm_emu_split_k_fp32_b returns their K pieces too),
+ * other K x N planes only where they would not be copied into the workspace.
+ * An unknown b_layout gives SGEMM_EMU_EINVAL.
  */
 int sgemm_emu_presplit_b(int64_t M, int64_t N, int64_t K,
                          const float *A, int64_t lda,

@@ -513,9 +513,10 @@ TILE64_SHAPES = [(1024, 1024, 1000), (6144, 256, 1000), (1025, 301, 768), (777, 
 def test_fp32_b_on_64_tiles(fe, shape):
     """Partly filled grids of FP32 B that the cost model gives to the one-pass
     kernel on 64 x 64 tiles (B split inside each tile, nothing allocated):
-    within the FP64 bound, identical on repeat, and bit for bit the caller's
-    N x K planes where those run one pass over K on 128 x 128 tiles (same
-    split, products and MFMA order per output).  Ragged M, N and K."""
+    within the FP64 bound, identical on repeat, bit for bit the caller's K x N
+    planes (the same choice, N even) and the caller's N x K planes where those run one
+    pass over K on 128 x 128 tiles (same split, products and MFMA order per
+    output).  Ragged M, N and K."""
     M, N, K = shape
     kpad = (K + 63) // 64 * 64
     assert fe.sgemm_emu_split_k_fp32_b(M, N, K) == 1
@@ -526,6 +527,9 @@ def test_fp32_b_on_64_tiles(fe, shape):
     check_against_fp64(C, A, B, label=f"64 x 64 tiles {shape}")
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_nows").view(np.uint32))
+    # K x N planes read as column pairs (N even) follow FP32 B's choice
+    if N % 2 == 0:
+        assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit").view(np.uint32))
     if K % 64 != 0 or fe.sgemm_emu_split_k(M, N, K) == 1:
         assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="presplit_t").view(np.uint32))
     if fe.sgemm_emu_split_k(M, N, kpad) > 1:
