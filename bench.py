@@ -40,8 +40,8 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "aa099730c6ad89040a8525a424f2a7acee36adedbcacae67fc43e35fe0183def",
-                "bytes_per_launch": [2843920787, 3264021077]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "8532b6d2507672edea0c4508529c180f33f680147b7479b76619472fddc040b4",
+                "bytes_per_launch": [2843938985, 3264038783]}
 
 # MFMA activity of the same launches, from one rocprofv3 --pmc run of the same
 # probe (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE).
@@ -51,8 +51,8 @@ GEMM_TRAFFIC = {"gemm_hip_sha256": "aa099730c6ad89040a8525a424f2a7acee36adedbcac
 # divided by the kernel's own time in this run gives the shader clock the chip
 # held under the load; roofline.frac = busy x clock / 2.4 GHz.
 GEMM_MFMA_PMC = {"gemm_hip_sha256": GEMM_TRAFFIC["gemm_hip_sha256"],
-                 "mfma_busy": [0.6566, 0.7184],
-                 "active_cycles_per_xcd": [3802637, 3466749]}
+                 "mfma_busy": [0.6561, 0.7198],
+                 "active_cycles_per_xcd": [3806509, 3460206]}
 
 
 def log(msg):
