@@ -517,7 +517,7 @@ int gemm_native(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     g.act = SGEMM_EMU_ACT_NONE;
     g.num_cus = num_cus;
     g.splits = 1;
-    const NativePlan plan = native_plan(M, N, K, num_cus);
+    const NativePlan plan = native_plan(M, N, K, num_cus, native_vec(A, lda, B, ldb, K, N));
     WsLease lease;
     if (plan.splits > 1) {
         void *ws = acquire_workspace(dev, stream, (size_t)plan.splits * (size_t)M * (size_t)N * sizeof(float), lease);

@@ -1714,24 +1714,32 @@ static int group_rows(int tiles_n, int num_cus);
 // output, no split.
 //
 // One workgroup per (tile, K slice); waves as in Cfg, each (MI x 32) x (NI x 32)
-// of accumulators.  K advances in steps of NBK = 16, double-buffered in LDS and
-// loaded NLA steps ahead into registers:
-//   * A rows hold 16 k values plus 4 of padding (80 bytes): 16 consecutive
-//     rows read with 128-bit loads touch 64 distinct banks;
+// of accumulators.  K advances in steps of NBK k (32, or 16 with element
+// loads), double-buffered in LDS and loaded NLA steps ahead into registers:
+//   * A rows hold NBK k values plus 4 of padding (144 or 80 bytes): 16
+//     consecutive rows read with 128-bit loads touch 64 distinct banks;
 //   * B rows (one k each) hold the tile's BN columns plus 4 of padding, so
 //     the two half-waves reading k and k + 8 land on disjoint banks.
-// Within a step, half-wave h (lanes 32h..32h+31) feeds k = 8h + kk to the
-// kk-th MFMA: the instruction's two k rows come from k and k + 8, so each
-// lane reads its eight A values of a step with two 128-bit loads.  Every
-// k < K is multiplied in exactly once, in an order the bound allows.  (Steps
-// of 32 k measured 2-3 % slower on most shapes.)
+// Within each 16 k of a step, half-wave h (lanes 32h..32h+31) feeds
+// k = 8h + kk to the kk-th MFMA: the instruction's two k rows come from k and
+// k + 8, so each lane reads its eight A values of the 16 with two 128-bit
+// loads.  Every k < K is multiplied in exactly once, in an order the bound
+// allows.
 
-constexpr int NBK = 16;                 // k per step
-constexpr int NLA = 4;                  // steps loaded ahead (register stages)
-constexpr int NAP = NBK + 4;            // A row pitch in LDS (floats)
+// K per step and register stages: with 128-bit loads 32 k and two stages
+// ahead (against 16 k and four: 768^3 37.4 -> 43.0 TFLOP/s, 1024^3 68.0 ->
+// 77.3, 1024 x 1024 x 512 59.4 -> 66.9, 6144 x 256 x 1024 71.9 -> 76.6, the
+// larger grids unchanged); with element loads 16 k and four stages (32 k
+// measured 10.2 -> 8.0 TFLOP/s on 333 x 444 x 555).
+template <bool VEC>
+struct NativeSteps {
+    static constexpr int NBK = VEC ? 32 : 16;   // k per step
+    static constexpr int NLA = VEC ? 2 : 4;     // steps loaded ahead (register stages)
+};
 
-template <class C>
+template <class C, int NBK>
 struct NativeLayout {
+    static constexpr int NAP = NBK + 4;                   // A row pitch in LDS (floats)
     static constexpr int BNP = C::BN + 4;                 // B row pitch in LDS (floats)
     static constexpr int A_FLOATS = C::BM * NAP;
     static constexpr int B_FLOATS = NBK * BNP;
@@ -1741,10 +1749,10 @@ struct NativeLayout {
     static_assert(C::BM * (NBK / 4) % C::NT == 0 && NBK * (C::BN / 4) % C::NT == 0, "loader mapping");
 };
 
-template <class C>
+template <class C, int NBK>
 struct NativeStage {
-    float a[NativeLayout<C>::A_VECS][4];
-    float b[NativeLayout<C>::B_VECS][4];
+    float a[NativeLayout<C, NBK>::A_VECS][4];
+    float b[NativeLayout<C, NBK>::B_VECS][4];
 };
 
 // Thread -> A chunk (row, 4-wide k group): 16 consecutive lanes take 16 rows of
@@ -1764,10 +1772,11 @@ __device__ __forceinline__ void native_a_chunk(int q, int &row, int &kg)
 // 4), else one dword at a time.  A past K reads the next row's values and is
 // masked by the caller; B rows past K and A, B beyond the operands read zero
 // or values whose outputs are never stored.
-template <class C, bool VEC>
-__device__ __forceinline__ void native_load(NativeStage<C> &st, const GemmArgs &g, int64_t m0, int64_t n0, int64_t k0)
+template <class C, bool VEC, int NBK>
+__device__ __forceinline__ void native_load(NativeStage<C, NBK> &st, const GemmArgs &g, int64_t m0, int64_t n0,
+                                            int64_t k0)
 {
-    using L = NativeLayout<C>;
+    using L = NativeLayout<C, NBK>;
     const int tid = threadIdx.x;
     {
         const int64_t rows = lmin((int64_t)C::BM, g.M - m0);
@@ -1808,10 +1817,10 @@ __device__ __forceinline__ void native_load(NativeStage<C> &st, const GemmArgs &
     }
 }
 
-template <class C>
-__device__ __forceinline__ void native_store(const NativeStage<C> &st, float *buf, int64_t kvalid)
+template <class C, int NBK>
+__device__ __forceinline__ void native_store(const NativeStage<C, NBK> &st, float *buf, int64_t kvalid)
 {
-    using L = NativeLayout<C>;
+    using L = NativeLayout<C, NBK>;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int c = 0; c < L::A_VECS; ++c) {
@@ -1820,7 +1829,7 @@ __device__ __forceinline__ void native_store(const NativeStage<C> &st, float *bu
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (kg * 4 + e < kvalid) ? st.a[c][e] : 0.0f;
-        *reinterpret_cast<u32x4_t *>(buf + row * NAP + kg * 4) =
+        *reinterpret_cast<u32x4_t *>(buf + row * L::NAP + kg * 4) =
             u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
     }
 #pragma unroll
@@ -1832,17 +1841,17 @@ __device__ __forceinline__ void native_store(const NativeStage<C> &st, float *bu
     }
 }
 
-template <class C>
+template <class C, int NBK>
 __device__ __forceinline__ void native_step(Acc<C, 1> &acc, const float *buf, int wm, int wn, int lane)
 {
-    using L = NativeLayout<C>;
+    using L = NativeLayout<C, NBK>;
     const int h = lane >> 5, r = lane & 31;
 #pragma unroll
     for (int kb = 0; kb < NBK; kb += 16) {
         float a[C::MI][8];
 #pragma unroll
         for (int i = 0; i < C::MI; ++i) {
-            const float *p = buf + (wm * C::WTM + i * 32 + r) * NAP + kb + 8 * h;
+            const float *p = buf + (wm * C::WTM + i * 32 + r) * L::NAP + kb + 8 * h;
             const u32x4_t v0 = *reinterpret_cast<const u32x4_t *>(p);
             const u32x4_t v1 = *reinterpret_cast<const u32x4_t *>(p + 4);
 #pragma unroll
@@ -1866,7 +1875,8 @@ __device__ __forceinline__ void native_step(Acc<C, 1> &acc, const float *buf, in
 template <class C, bool VEC>
 __global__ __launch_bounds__(C::NT, 2) void gemm_f32_native_kernel(GemmArgs g)
 {
-    using L = NativeLayout<C>;
+    constexpr int NBK = NativeSteps<VEC>::NBK, NLA = NativeSteps<VEC>::NLA;
+    using L = NativeLayout<C, NBK>;
     __shared__ __attribute__((aligned(16))) float lds[2 * L::STAGE];
     int tm, tn;
     tile_of_index((int)blockIdx.x, (int)gridDim.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
@@ -1893,11 +1903,11 @@ __global__ __launch_bounds__(C::NT, 2) void gemm_f32_native_kernel(GemmArgs g)
         // stage counts only the NLA - 1 stages loaded after it: a load past
         // the slice re-reads its last step and is never stored for use, and
         // the LDS write after the last step goes to a buffer no step reads.
-        NativeStage<C> st[NLA];
+        NativeStage<C, NBK> st[NLA];
 #pragma unroll
         for (int r = 0; r < NLA; ++r)
-            native_load<C, VEC>(st[r], g, m0, n0, lmin(s0 + r, s1 - 1) * NBK);
-        native_store<C>(st[0], lds, g.K - s0 * NBK);
+            native_load<C, VEC, NBK>(st[r], g, m0, n0, lmin(s0 + r, s1 - 1) * NBK);
+        native_store<C, NBK>(st[0], lds, g.K - s0 * NBK);
         __syncthreads();
         for (int64_t s = s0; s < s1; s += NLA) {
 #pragma unroll
@@ -1906,9 +1916,9 @@ __global__ __launch_bounds__(C::NT, 2) void gemm_f32_native_kernel(GemmArgs g)
                 if (t >= s1) break;
                 const float *cur = lds + ((t - s0) & 1) * L::STAGE;
                 float *nxt = lds + ((t - s0 + 1) & 1) * L::STAGE;
-                native_load<C, VEC>(st[r], g, m0, n0, lmin(t + NLA, s1 - 1) * NBK);
-                native_step<C>(acc, cur, wm, wn, lane);
-                native_store<C>(st[(r + 1) % NLA], nxt, g.K - (t + 1) * NBK);
+                native_load<C, VEC, NBK>(st[r], g, m0, n0, lmin(t + NLA, s1 - 1) * NBK);
+                native_step<C, NBK>(acc, cur, wm, wn, lane);
+                native_store<C, NBK>(st[(r + 1) % NLA], nxt, g.K - (t + 1) * NBK);
                 __syncthreads();
             }
         }
@@ -1922,6 +1932,11 @@ __global__ __launch_bounds__(C::NT, 2) void gemm_f32_native_kernel(GemmArgs g)
 using CfgN128 = Cfg<2, 2, 64, 64>;    // 4 waves, 128 x 128 tile
 using CfgN64 = Cfg<2, 2, 32, 32>;     // 4 waves, 64 x 64 tile
 
+bool native_vec(const float *A, int64_t lda, const float *B, int64_t ldb, int64_t K, int64_t N)
+{
+    return aligned(A, 16) && aligned(B, 16) && lda % 4 == 0 && ldb % 4 == 0 && K % 4 == 0 && N % 4 == 0;
+}
+
 template <class C>
 static hipError_t launch_native_cfg(const GemmArgs &args, int splits, hipStream_t stream)
 {
@@ -1930,8 +1945,7 @@ static hipError_t launch_native_cfg(const GemmArgs &args, int splits, hipStream_
     g.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
     g.group_m = group_rows(g.tiles_n, g.num_cus);
     g.splits = splits;
-    const bool vec = aligned(g.A, 16) && aligned(g.B, 16) && g.lda % 4 == 0 && g.ldb % 4 == 0 && g.K % 4 == 0 &&
-                     g.N % 4 == 0;
+    const bool vec = native_vec(g.A, g.lda, g.B, g.ldb, g.K, g.N);
     const dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n), (unsigned)splits), block(C::NT);
     GemmArgs gk = g;
     if (splits > 1) gk.done = nullptr;          // the reduction is the last kernel
@@ -1944,8 +1958,9 @@ static hipError_t launch_native_cfg(const GemmArgs &args, int splits, hipStream_
     return hipGetLastError();
 }
 
-NativePlan native_plan(int64_t M, int64_t N, int64_t K, int num_cus)
+NativePlan native_plan(int64_t M, int64_t N, int64_t K, int num_cus, bool vec)
 {
+    const int NBK = vec ? NativeSteps<true>::NBK : NativeSteps<false>::NBK;
     NativePlan p{};
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (t128 >= num_cus) {
@@ -1961,7 +1976,8 @@ NativePlan native_plan(int64_t M, int64_t N, int64_t K, int num_cus)
     // slice would still be longer than 64 steps.  Measured against two per CU
     // throughout: 1024 x 1024 x 512 45.7 -> 62.2 TFLOP/s, 2048 x 512 x 512
     // 45.2 -> 63.5, 1024^3 65.3 -> 71.0, 1024 x 512 x 4096 unchanged at 82.6
-    // (it keeps four slices).
+    // (it keeps four slices), with 16-k steps; the same counts of the 32-k
+    // steps are what the figures above NativeSteps were measured with.
     const int64_t nsteps = (K + NBK - 1) / NBK;
     auto grow = [&](int64_t per_cu) {
         while (p.splits < 16 && t64 * (p.splits + 1) <= per_cu * (int64_t)num_cus && nsteps / (p.splits + 1) >= 8)

@@ -114,7 +114,10 @@ struct NativePlan {
     int tile;
     int splits;
 };
-NativePlan native_plan(int64_t M, int64_t N, int64_t K, int num_cus);
+// vec: native_vec() of the call's operands (the kernel's K step depends on it).
+NativePlan native_plan(int64_t M, int64_t N, int64_t K, int num_cus, bool vec);
+// True when the native kernel loads A and B 128 bits at a time.
+bool native_vec(const float *A, int64_t lda, const float *B, int64_t ldb, int64_t K, int64_t N);
 hipError_t launch_native(const GemmArgs &args, const NativePlan &plan, hipStream_t stream);
 
 // C := act(0 + bias[j]) (K == 0); without bias and activation C := 0.

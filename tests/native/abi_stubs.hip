@@ -42,7 +42,9 @@ bool launch_done_attached(const GemmArgs &, BSource) { return false; }
 
 bool gemm_uses_dma(int64_t, int64_t, const void *, const void *, const void *) { return false; }
 
-NativePlan native_plan(int64_t, int64_t, int64_t, int) { return NativePlan{128, 1}; }
+NativePlan native_plan(int64_t, int64_t, int64_t, int, bool) { return NativePlan{128, 1}; }
+
+bool native_vec(const float *, int64_t, const float *, int64_t, int64_t, int64_t) { return false; }
 
 hipError_t launch_native(const GemmArgs &, const NativePlan &, hipStream_t) { return hipErrorNotSupported; }
 
