@@ -534,11 +534,12 @@ int gemm_native(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
 // The performant strategy's choice (sgemm_emu_ex with SGEMM_EMU_PERFORMANT):
 // true where the native FP32 kernel is expected to be faster than all nine
 // BF16 products.  Measured on MI355X (256 CUs): the native kernel wins on every
-// shape up to 1024^3 (2.1 GFLOP; e.g. 512^3 18.0 against 9.2 TFLOP/s,
-// 1024^3 73.0 against 62.3), where launch latency and the K pieces' partial
-// sums weigh on the nine products; the emulation from 3.2 GFLOP up
-// (6144 x 256 x 1024 80.5 against 75.0, 6144 x 1024 x 256 97.9 against 86.4,
-// 4096^3 154.4 against 132.8).
+// shape up to 1024^3 (2.1 GFLOP; 512^3 18.3 against 16.4 TFLOP/s, 768^3 46.2
+// against 37.3, 1024^3 85.6 against 70.9), where latency weighs on the nine
+// products; from 3.2 GFLOP up the emulation is level or ahead
+// (1536 x 1024 x 1024 83.4 against 82.6, 6144 x 256 x 1024 89.6 against 82.3,
+// 6144 x 1024 x 256 96.9 against 87.7, 4096^3 154.4 against 132.8), with
+// 2048 x 1024 x 1024 the exception (107.3 against 109.3).
 constexpr double kPerformantMinFlops = 2.5e9;
 
 bool performant_prefers_native(int64_t M, int64_t N, int64_t K, int num_cus)
