@@ -361,7 +361,8 @@ def one_shape(shape, reps, warmup_s=1.0, rounds=2):
     ms = settled_ms(entries, stream, reps, warmup_s, rounds)
     res = {name: round(fl / ms[name] / 1e9, 2) for name in entries}
     print(json.dumps({"shape": [m, n, k], "reps": reps, "tflops": res,
-                      "split_k": fe.sgemm_emu_split_k(m, n, k, 5)}), flush=True)
+                      "split_k": fe.sgemm_emu_split_k(m, n, k, 5),
+                      "split_k_fp32_b": fe.sgemm_emu_split_k_fp32_b(m, n, k, 5)}), flush=True)
 
 
 CALIBRATION_SHAPES = {"4096^3": (4096, 4096, 4096), "8192^3": (8192, 8192, 8192),
