@@ -262,3 +262,57 @@ def test_graph_capture_allocates_nothing(fe):
         torch.cuda.synchronize()
         assert torch.equal(ref2.view(torch.int32), out2.view(torch.int32)), f"eager after replay {rep}"
     del graph
+
+
+def test_graph_capture_of_64_tiles(fe):
+    """Small grids that run on 64 x 64 tiles need no workspace, so the default
+    entry points capture into a graph on them: FP32 B on 1024^3 (where 128 x 128
+    tiles would split B and take stream-K), the caller's N x K and K x N planes
+    on 1024 x 1024 x 512.  Three replays, with eager calls and synchronisation
+    between them, each equal the eager results bit for bit."""
+    g = np.random.Generator(np.random.Philox(key=6464))
+
+    def mat(r, c):
+        return dev(g.standard_normal((r, c)).astype(np.float32))
+
+    M1 = N1 = K1 = 1024
+    assert fe.sgemm_emu_split_k_fp32_b(M1, N1, K1) == 1 and fe.sgemm_emu_split_k(M1, N1, K1) > 1
+    A1, B1 = mat(M1, K1), mat(K1, N1)
+    M2, N2, K2 = 1024, 1024, 512
+    assert fe.sgemm_emu_split_k(M2, N2, K2) == 1 and fe.sgemm_emu_split_k_fp32_b(M2, N2, K2) == 1
+    A2, B2 = mat(M2, K2), mat(K2, N2)
+    Pnk = fe.split(B2.t().contiguous())
+    Pkn = fe.split(B2)
+    refs = [torch.empty((M1, N1), device="cuda"), torch.empty((M2, N2), device="cuda"),
+            torch.empty((M2, N2), device="cuda")]
+    outs = [torch.empty_like(r) for r in refs]
+
+    def calls(o, stream=None):
+        fe.sgemm_bf16x9(M1, N1, K1, A1, K1, B1, N1, o[0], N1, stream)
+        fe.sgemm_emu_presplit_b(M2, N2, K2, A2, K2, *Pnk, K2, fe.SGEMM_EMU_B_NK, o[1], N2, 5, stream)
+        fe.sgemm_emu_presplit_b(M2, N2, K2, A2, K2, *Pkn, N2, fe.SGEMM_EMU_B_KN, o[2], N2, 5, stream)
+
+    calls(refs)
+    torch.cuda.synchronize()
+    assert torch.equal(refs[1].view(torch.int32), refs[2].view(torch.int32))
+    print("graph capture: three calls on 64 x 64 tiles", flush=True, file=sys.stderr)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=s):
+        calls(outs, s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print(f"graph capture of 64 x 64 tiles: replay {rep}", flush=True, file=sys.stderr)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (r, o) in enumerate(zip(refs, outs)):
+            assert torch.equal(r.view(torch.int32), o.view(torch.int32)), f"replay {rep}: call {i}"
+        # eager work between replays, on the default stream
+        fe.sgemm_bf16x9(M1, N1, K1, A1, K1, B1, N1, outs[0], N1)
+        torch.cuda.synchronize()
+        assert torch.equal(refs[0].view(torch.int32), outs[0].view(torch.int32)), f"eager after replay {rep}"
+    del graph
