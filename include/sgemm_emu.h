@@ -72,7 +72,9 @@
  *   inside its kernel (bitwise the same result); a small-grid shape whose
  *   stream-K partial slots cannot be had returns SGEMM_EMU_ENOMEM (while
  *   capturing: SGEMM_EMU_ECAPTURE) with nothing enqueued, so the bits of a
- *   shape never depend on the memory available.  Callers that must capture
+ *   shape never depend on the memory available.  Small grids that run on
+ *   64 x 64 tiles (sgemm_emu_split_k_fp32_b returns 1 for FP32 B) use no
+ *   workspace and capture like any other call.  Callers that must capture
  *   such shapes, or cannot let the library allocate, use
  *   sgemm_emu_presplit_b_noalloc.  No other device memory is allocated
  *   (sgemm_emu_ex's IEEE fix-up aside, documented there).  The
