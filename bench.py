@@ -40,8 +40,8 @@ GEMM_SOURCE = os.path.join(HERE, "fp32_emulated_gemm_amd", "csrc", "gemm.hip")
 # the probe's cold 2 GiB device copy (FETCH_SIZE reads half the copied bytes:
 # x2.0; WRITE_SIZE reads all of them: x1.0).  The figures belong to the kernel
 # source they were taken on; once gemm.hip has changed, roofline.traffic is null.
-GEMM_TRAFFIC = {"gemm_hip_sha256": "089af55dfc23d5ebd9b86010607fee8181b0a9ffbe9191e7371bc23fcf5c46b9",
-                "bytes_per_launch": [2843935835, 3264034644]}
+GEMM_TRAFFIC = {"gemm_hip_sha256": "75195d81894525a370e411dd08d3e74a307f23e645ba9ed56e41630d4769eaeb",
+                "bytes_per_launch": [2843925792, 3264026398]}
 
 # MFMA activity of the same launches, from one rocprofv3 --pmc run of the same
 # probe (SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE).
@@ -51,8 +51,8 @@ GEMM_TRAFFIC = {"gemm_hip_sha256": "089af55dfc23d5ebd9b86010607fee8181b0a9ffbe91
 # divided by the kernel's own time in this run gives the shader clock the chip
 # held under the load; roofline.frac = busy x clock / 2.4 GHz.
 GEMM_MFMA_PMC = {"gemm_hip_sha256": GEMM_TRAFFIC["gemm_hip_sha256"],
-                 "mfma_busy": [0.6568, 0.7254],
-                 "active_cycles_per_xcd": [3801744, 3433328]}
+                 "mfma_busy": [0.6544, 0.7188],
+                 "active_cycles_per_xcd": [3815687, 3465315]}
 
 
 def log(msg):

@@ -534,12 +534,12 @@ int gemm_native(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
 // The performant strategy's choice (sgemm_emu_ex with SGEMM_EMU_PERFORMANT):
 // true where the native FP32 kernel is expected to be faster than all nine
 // BF16 products.  Measured on MI355X (256 CUs): the native kernel wins on every
-// shape up to 1024^3 (2.1 GFLOP; 512^3 18.3 against 16.4 TFLOP/s, 768^3 46.2
-// against 37.3, 1024^3 85.6 against 70.9), where latency weighs on the nine
+// shape up to 1024^3 (2.1 GFLOP; 512^3 18.2 against 17.4 TFLOP/s, 768^3 46.1
+// against 39.7, 1024^3 85.5 against 75.5), where latency weighs on the nine
 // products; from 3.2 GFLOP up the emulation is level or ahead
-// (1536 x 1024 x 1024 83.4 against 82.6, 6144 x 256 x 1024 89.6 against 82.3,
-// 6144 x 1024 x 256 96.9 against 87.7, 4096^3 154.4 against 132.8), with
-// 2048 x 1024 x 1024 the exception (107.3 against 109.3).
+// (1536 x 1024 x 1024 81.3 against 80.9, 6144 x 256 x 1024 86.4 against 80.7,
+// 6144 x 1024 x 256 97.6 against 88.0, 4096^3 154.4 against 132.8), with
+// 2048 x 1024 x 1024 the exception (105.5 against 108.5).
 constexpr double kPerformantMinFlops = 2.5e9;
 
 bool performant_prefers_native(int64_t M, int64_t N, int64_t K, int num_cus)
