@@ -648,6 +648,42 @@ def test_nk_planes_even_k_word_loads(fe, shape):
     assert np.array_equal(C.view(np.uint32), run(fe, A, B, entry="fused_nows").view(np.uint32))
 
 
+def _sweep_shapes(n=20):
+    g = np.random.Generator(np.random.Philox(key=2718))
+    out = []
+    for _ in range(n):
+        M, N = (int(x) for x in g.integers(1, 700, size=2))
+        K = int(g.integers(1, 1500)) if g.integers(0, 2) else int(g.integers(1, 24)) * 64
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("shape", _sweep_shapes(), ids=lambda s: "x".join(map(str, s)))
+def test_dispatch_sweep_bound_and_consistency(fe, shape):
+    """Seeded random shapes across the dispatch rules (one pass on 128 x 128 or
+    64 x 64 tiles, stream-K, pre-split or not): every B source within the FP64
+    bound, and the bit equalities the query calls promise -- FP32 B with one
+    pass equals SGEMM_EMU_NO_WORKSPACE, K x N planes with N even equal FP32 B,
+    N x K planes equal FP32 B where both cut K alike."""
+    M, N, K = shape
+    g = _rng(M * 7919 + N * 31 + K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    F = run(fe, A, B, entry="fused")
+    check_against_fp64(F, A, B, label=f"sweep fused {shape}")
+    KN = run(fe, A, B, entry="presplit")
+    NK = run(fe, A, B, entry="presplit_t")
+    W = run(fe, A, B, entry="fused_nows")
+    for name, X in (("K x N", KN), ("N x K", NK), ("no workspace", W)):
+        check_against_fp64(X, A, B, label=f"sweep {name} {shape}", normwise=False)
+    if fe.sgemm_emu_split_k_fp32_b(M, N, K) == 1:
+        assert np.array_equal(F.view(np.uint32), W.view(np.uint32))
+    if N % 2 == 0:
+        assert np.array_equal(F.view(np.uint32), KN.view(np.uint32))
+    if same_order_as_fused(fe, M, N, K):
+        assert np.array_equal(F.view(np.uint32), NK.view(np.uint32))
+
+
 def test_presplit_equals_fused_bitwise(fe):
     g = _rng(5)
     A = g.standard_normal((200, 150)).astype(np.float32)
