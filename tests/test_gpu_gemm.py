@@ -684,6 +684,32 @@ def test_dispatch_sweep_bound_and_consistency(fe, shape):
         assert np.array_equal(F.view(np.uint32), NK.view(np.uint32))
 
 
+@pytest.mark.parametrize("shape", [(128, 128, 32768), (200, 70, 20000), (64, 1000, 8192)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_long_k_small_grids(fe, shape):
+    """Few tiles and a long K: stream-K cuts each tile into its most pieces
+    (at most 8), with K padded for FP32 B where it is not a multiple of 64.
+    Every B source within the bound and identical on repeat; FP32 B, K x N and
+    N x K planes bit for bit where the query calls say they cut K alike."""
+    M, N, K = shape
+    kpad = (K + 63) // 64 * 64
+    assert fe.sgemm_emu_split_k_fp32_b(M, N, K) == fe.sgemm_emu_split_k(M, N, kpad) > 1
+    g = _rng(M + N + K)
+    A = g.standard_normal((M, K)).astype(np.float32)
+    B = g.standard_normal((K, N)).astype(np.float32)
+    F = run(fe, A, B, entry="fused")
+    check_against_fp64(F, A, B, label=f"long K fused {shape}")
+    assert np.array_equal(F.view(np.uint32), run(fe, A, B, entry="fused").view(np.uint32))
+    KN = run(fe, A, B, entry="presplit")
+    check_against_fp64(KN, A, B, label=f"long K K x N {shape}", normwise=False)
+    if N % 2 == 0:
+        assert np.array_equal(F.view(np.uint32), KN.view(np.uint32))
+    NK = run(fe, A, B, entry="presplit_t")
+    check_against_fp64(NK, A, B, label=f"long K N x K {shape}", normwise=False)
+    if same_order_as_fused(fe, M, N, K):
+        assert np.array_equal(F.view(np.uint32), NK.view(np.uint32))
+
+
 def test_presplit_equals_fused_bitwise(fe):
     g = _rng(5)
     A = g.standard_normal((200, 150)).astype(np.float32)
